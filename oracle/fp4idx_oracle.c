@@ -1,0 +1,380 @@
+/*
+ * fp4idx_oracle.c -- plain, slow CPU reference for the FP4 lightning-indexer scorer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the oracle that the GPU library is checked
+ * against.  Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load it.  It shares no code, header, table or helper with the GPU library under
+ * sparse_attention_fp4_amd/, and it includes nothing from there.
+ *
+ * Every function follows the definition on the pages as directly as possible: decode
+ * each code to its real value, multiply, add, mask, take the max, sort.  There is no
+ * blocking, fusion or reordering.  Sources (cited by page title and section):
+ *
+ *   [SGL]  "[DSv4.1] Speed up the FP4 indexer scorer by decoding keys without exp2"
+ *          (SGLang pull request), sections Modifications and Accuracy Tests.
+ *   [M3]   "M3 FP4 Indexer" README, sections 输入 shape 和类型 (input shapes),
+ *          输出 shape 和类型 (output shapes), FP4 和 scale layout, 数学语义 (math
+ *          semantics) and the causal paragraph that follows it.
+ *   [ISS]  "ISSUE -- Lightning Indexer FP4 dequant decodes E2M1 wrong", sections
+ *          "Why it's wrong" and "Fix (interim, correct FP32 base)".
+ *   [QSA]  vLLM qsa_fp8 API page, _qsa_physical_slots_kernel (invalid pages -> masked).
+ *
+ * Precision: every real value is a double.  A per-head dot product of dequantized FP4
+ * values is a sum of 128 dyadic terms; orc_dot() adds them in double and reports
+ * whether that sum is provably exact (all terms are multiples of 2^L and the sum of
+ * their magnitudes stays below 2^(L+53)).  The exact dot is then rounded once to fp32
+ * (C's double->float conversion rounds to nearest even).  The weighted head sum is
+ * formed in double from the exact dots and rounded once to fp32.
+ *
+ * Parity status of each function is recorded in the comment above it.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_MXFP4 0
+#define ORC_NVFP4 1
+
+/* ---------------------------------------------------------------------------------
+ * Decode of the three code formats.
+ * ------------------------------------------------------------------------------- */
+
+/* E2M1 nibble -> value.  The nibble is an index into the level set
+ * {0, 0.5, 1, 1.5, 2, 3, 4, 6}; bit 3 is the sign ([ISS] "Why it's wrong", "Fix
+ * (interim...)").  Code 8 is negative zero.  Pinned: the level table printed in [ISS],
+ * and the OCP bit-field form (1 exponent-bias, 1 mantissa bit) in the tests. */
+double orc_e2m1(unsigned nibble) {
+    static const double level[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    double mag = level[nibble & 7u];
+    return (nibble & 8u) ? -mag : mag;
+}
+
+/* E8M0 scale code c -> 2^(c-127), written out literally ([SGL] Modifications: the
+ * code is the fp32 exponent field).  Code 255 gives 2^128, which is finite in double
+ * and becomes +inf once a product is rounded to fp32.  Pinned against torch's
+ * float8_e8m0fnu for codes 0..254. */
+double orc_e8m0(unsigned code) {
+    return ldexp(1.0, (int)(code & 0xffu) - 127);
+}
+
+/* E4M3 (fn variant) scale code -> value, bit by bit: sign bit 7, exponent bits 6..3
+ * with bias 7, mantissa bits 2..0; exponent 0 is subnormal (m/8 * 2^-6); 0x7F and 0xFF
+ * are NaN; there is no infinity ([M3] FP4 和 scale layout names float8_e4m3fn as the
+ * NVFP4 block-scale dtype).  Pinned against torch's float8_e4m3fn for all 256 codes. */
+double orc_e4m3(unsigned code) {
+    unsigned s = (code >> 7) & 1u, e = (code >> 3) & 15u, m = code & 7u;
+    double mag;
+    if (e == 15u && m == 7u) return NAN;
+    if (e == 0u) mag = ldexp((double)m / 8.0, -6);
+    else mag = ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+    return s ? -mag : mag;
+}
+
+/* Scale group size S and group count G of a format ([M3] FP4 和 scale layout). */
+static int group_size(int fmt) { return fmt == ORC_MXFP4 ? 32 : 16; }
+int orc_groups(int fmt) { return fmt == ORC_MXFP4 ? 4 : 8; }
+
+/* One packed 128-element vector (64 bytes, element 2j in the low nibble of byte j,
+ * element 2j+1 in the high nibble -- [ISS] "Fix (interim...)", lane 0 = low nibble)
+ * with its G scale codes -> 128 real values:  real[d] = E2M1(d) * scale[floor(d/S)]
+ * ([M3] 数学语义). */
+void orc_dequant_vec(int fmt, const uint8_t* packed, const uint8_t* scales, double* out) {
+    int S = group_size(fmt);
+    for (int d = 0; d < 128; d++) {
+        uint8_t byte = packed[d / 2];
+        unsigned nib = (d % 2 == 0) ? (byte & 15u) : (byte >> 4);
+        double sc = (fmt == ORC_MXFP4) ? orc_e8m0(scales[d / S]) : orc_e4m3(scales[d / S]);
+        out[d] = orc_e2m1(nib) * sc;
+    }
+}
+
+/* Exponent of the lowest set bit of a finite nonzero double. */
+static int lsb_exponent(double x) {
+    int e;
+    double m = frexp(fabs(x), &e);           /* |x| = m * 2^e, m in [0.5, 1) */
+    uint64_t M = (uint64_t)ldexp(m, 53);     /* exact: m has at most 53 bits */
+    return e - 53 + __builtin_ctzll(M);
+}
+
+/* Dot product of two dequantized 128-vectors, summed in double in index order.
+ * Returns 1 when the double sum is provably exact, 0 otherwise (or if a term is not
+ * finite).  *abs_sum receives sum_d |q_d k_d| (used as a tolerance base). */
+int orc_dot(const double* q, const double* k, double* out, double* abs_sum) {
+    double s = 0.0, a = 0.0;
+    int lmin = 100000, finite = 1;
+    for (int d = 0; d < 128; d++) {
+        double t = q[d] * k[d];
+        s += t;
+        a += fabs(t);
+        if (!isfinite(t)) finite = 0;
+        else if (t != 0.0) {
+            int l = lsb_exponent(t);
+            if (l < lmin) lmin = l;
+        }
+    }
+    *out = s;
+    if (abs_sum) *abs_sum = a;
+    if (!finite) return 0;
+    if (a == 0.0) return 1;
+    /* each term is an exact product (8-bit significands at most) and a multiple of
+     * 2^lmin; every partial sum is then a multiple of 2^lmin bounded by a */
+    return a < ldexp(1.0, lmin + 53);
+}
+
+/* ---------------------------------------------------------------------------------
+ * Weighted-ReLU logits over a paged key cache.
+ *
+ *   I[t,s] = sum_h w[t,h] * max(q_{t,h} . k_s, 0)       ([ISS] TL;DR; [SGL])
+ *
+ * Row t belongs to request b when cu_seqlens_q[b] <= t < cu_seqlens_q[b+1].  Key s of
+ * request b is token (s mod page) of physical page block_table[b][s / page].  Key s is
+ * visible for row t iff s < row_lens[t]; every other column of [0, out_cols) is -inf,
+ * whatever the query holds ([SGL] Accuracy Tests: invisible positions stay -inf).  A
+ * visible key whose page id is negative or >= num_pages, or whose logical page is past
+ * the table width, is treated as invisible ([QSA] slot pass).  Query head h reads key
+ * head h / (H / Hkv) ([M3] 数学语义).
+ *
+ * Layouts (element strides in bytes / elements as noted):
+ *   q_fp4   [T][H][64]  bytes, row stride q_rs bytes between rows t (heads contiguous)
+ *   q_scale [T][H][G]   bytes, row stride qs_rs bytes
+ *   w       [T][H]      float, row stride w_rs floats
+ *   k_fp4   [P][Hkv][page][64]  page stride kp_s bytes
+ *   k_scale [P][Hkv][page][G]   page stride ksp_s bytes
+ *   block_table [B][W] int32, row stride bt_rs elements
+ *   logits  [T][out_cols] float, row stride out_rs floats
+ *
+ * rows / n_rows: optional subset of rows to compute (NULL = all T rows).
+ * tolbase (optional, same layout as logits): sum_h |w * max(dot,0)| at each visible
+ * position, 0 elsewhere.
+ * Returns the number of per-head dots whose double sum was not provably exact.
+ * ------------------------------------------------------------------------------- */
+long orc_logits_paged(int fmt,
+                      const uint8_t* q_fp4, int64_t q_rs,
+                      const uint8_t* q_scale, int64_t qs_rs,
+                      const float* w, int64_t w_rs,
+                      const uint8_t* k_fp4, int64_t kp_s,
+                      const uint8_t* k_scale, int64_t ksp_s,
+                      const int32_t* block_table, int64_t bt_rs,
+                      const int32_t* cu_seqlens_q, const int32_t* row_lens,
+                      int T, int B, int H, int Hkv, int page, int num_pages, int W,
+                      int out_cols, float* logits, int64_t out_rs, float* tolbase,
+                      const int32_t* rows, int n_rows, int n_threads) {
+    int G = orc_groups(fmt);
+    int R = H / Hkv;
+    int nr = rows ? n_rows : T;
+    long inexact = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : inexact)
+    for (int ri = 0; ri < nr; ri++) {
+        int t = rows ? rows[ri] : ri;
+        int b = 0;
+        while (b + 1 <= B && cu_seqlens_q[b + 1] <= t) b++;
+        if (b >= B) { /* a row outside every request sees nothing */
+            for (int s = 0; s < out_cols; s++) {
+                logits[(int64_t)t * out_rs + s] = -INFINITY;
+                if (tolbase) tolbase[(int64_t)t * out_rs + s] = 0.0f;
+            }
+            continue;
+        }
+        double* qv = (double*)malloc(sizeof(double) * (size_t)H * 128);
+        double kv[128];
+        for (int h = 0; h < H; h++)
+            orc_dequant_vec(fmt, q_fp4 + (int64_t)t * q_rs + (int64_t)h * 64,
+                            q_scale + (int64_t)t * qs_rs + (int64_t)h * G, qv + (size_t)h * 128);
+        for (int s = 0; s < out_cols; s++) {
+            float* o = logits + (int64_t)t * out_rs + s;
+            if (tolbase) tolbase[(int64_t)t * out_rs + s] = 0.0f;
+            int visible = s < row_lens[t];
+            int lp = s / page, off = s % page;
+            int32_t phys = -1;
+            if (visible && lp < W) phys = block_table[(int64_t)b * bt_rs + lp];
+            if (!visible || phys < 0 || phys >= num_pages) {
+                *o = -INFINITY;
+                continue;
+            }
+            double acc = 0.0, tb = 0.0;
+            for (int h = 0; h < H; h++) {
+                int hk = h / R;
+                const uint8_t* kp = k_fp4 + (int64_t)phys * kp_s + ((int64_t)hk * page + off) * 64;
+                const uint8_t* ks = k_scale + (int64_t)phys * ksp_s + ((int64_t)hk * page + off) * G;
+                orc_dequant_vec(fmt, kp, ks, kv);
+                double dot, asum;
+                if (!orc_dot(qv + (size_t)h * 128, kv, &dot, &asum)) inexact++;
+                /* the exact dot rounded once to fp32 is the per-head logit; the weighted
+                 * sum uses the exact value */
+                double r = dot > 0.0 ? dot : 0.0;
+                if (isnan(dot)) r = dot;
+                double term = (double)w[(int64_t)t * w_rs + h] * r;
+                acc += term;
+                tb += fabs(term);
+            }
+            *o = (float)acc;
+            if (tolbase) tolbase[(int64_t)t * out_rs + s] = (float)tb;
+        }
+        free(qv);
+    }
+    return inexact;
+}
+
+/* ---------------------------------------------------------------------------------
+ * Per-head 128-token block-max scores ([M3] 数学语义 and the causal paragraph).
+ *
+ *   scores[hq][kb][q_global] = max over valid k_local in [128kb, 128kb+128) of
+ *                              sum_d Q_real(q_global,hq,d) * K_real(b,k_local,hk,d)
+ *
+ * q_global = cu_seqlens_q[b] + q_local; k_len[b] = cu_seqlens_k[b+1]-cu_seqlens_k[b];
+ * physical_page = kv_indices[cu_page_offsets[b] + kb]; page_row = k_local - 128 kb.
+ * k_local is valid iff k_local < k_len[b] and, when causal, k_local <= q_local +
+ * offset[b] with offset[b] = qo_offset[b] if given else k_len[b] - q_len[b].  A block
+ * with no valid key, or kb >= ceil(k_len[b]/128), is -inf.  Ktiles =
+ * ceil(max_seqlen_k / 128).  A physical page id outside [0, num_pages) makes its keys
+ * invalid (same reading as for the logits).
+ *
+ * Layouts: q_fp4 [Tq][Hq][64], q_scale [Tq][Hq][G], k_fp4 [P][Hkv][128][64],
+ * k_scale [P][Hkv][128][G], all contiguous; scores [Hq][Ktiles][Tq] float.
+ * errbase (optional, same layout as scores): the largest sum_d |q_d k_d| over the
+ * valid keys of the block (0 for empty blocks).
+ * Returns the number of per-head dots whose double sum was not provably exact.
+ * ------------------------------------------------------------------------------- */
+long orc_block_scores(int fmt,
+                      const uint8_t* q_fp4, const uint8_t* q_scale,
+                      const uint8_t* k_fp4, const uint8_t* k_scale,
+                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                      const int32_t* cu_page_offsets, const int32_t* kv_indices,
+                      const int32_t* qo_offset, int B, int Tq, int Hq, int Hkv, int num_pages,
+                      int max_seqlen_k, int causal, float* scores, float* errbase,
+                      const int32_t* rows, int n_rows, int n_threads) {
+    int G = orc_groups(fmt);
+    int R = Hq / Hkv;
+    int ktiles = (max_seqlen_k + 127) / 128;
+    int nr = rows ? n_rows : Tq;
+    long inexact = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : inexact)
+    for (int ri = 0; ri < nr; ri++) {
+        int qg = rows ? rows[ri] : ri;
+        int b = 0;
+        while (b + 1 <= B && cu_seqlens_q[b + 1] <= qg) b++;
+        if (b >= B) b = B - 1; /* callers guarantee qg < cu_seqlens_q[B] */
+        int q_local = qg - cu_seqlens_q[b];
+        int q_len = cu_seqlens_q[b + 1] - cu_seqlens_q[b];
+        int k_len = cu_seqlens_k[b + 1] - cu_seqlens_k[b];
+        int offset = qo_offset ? qo_offset[b] : k_len - q_len;
+        double qv[128], kv[128];
+        for (int hq = 0; hq < Hq; hq++) {
+            int hk = hq / R;
+            orc_dequant_vec(fmt, q_fp4 + ((int64_t)qg * Hq + hq) * 64,
+                            q_scale + ((int64_t)qg * Hq + hq) * G, qv);
+            for (int kb = 0; kb < ktiles; kb++) {
+                double best = -INFINITY, ebest = 0.0;
+                int any = 0;
+                if (kb < (k_len + 127) / 128) {
+                    int32_t phys = kv_indices[cu_page_offsets[b] + kb];
+                    for (int kl = 128 * kb; kl < 128 * kb + 128; kl++) {
+                        if (kl >= k_len) continue;
+                        if (causal && kl > q_local + offset) continue;
+                        if (phys < 0 || phys >= num_pages) continue;
+                        int row = kl - 128 * kb;
+                        orc_dequant_vec(fmt, k_fp4 + (((int64_t)phys * Hkv + hk) * 128 + row) * 64,
+                                        k_scale + (((int64_t)phys * Hkv + hk) * 128 + row) * G, kv);
+                        double dot, asum;
+                        if (!orc_dot(qv, kv, &dot, &asum)) inexact++;
+                        if (!any || dot > best || isnan(dot)) best = dot;
+                        if (asum > ebest) ebest = asum;
+                        any = 1;
+                    }
+                }
+                int64_t o = ((int64_t)hq * ktiles + kb) * Tq + qg;
+                scores[o] = any ? (float)best : -INFINITY;
+                if (errbase) errbase[o] = (float)ebest;
+            }
+        }
+    }
+    return inexact;
+}
+
+/* ---------------------------------------------------------------------------------
+ * Top-k selection.  For each row, the candidates are the columns s < len (len =
+ * row_lens[t] if given, else cols, clipped to cols) whose score is greater than -inf
+ * (so -inf and NaN are never selected).  They are ordered by score, larger first, ties
+ * broken by the smaller column (the comparisons treat -0 and +0 as equal).  The first min(k, n)
+ * are selected and written in increasing column order, then padded with -1 (index) and
+ * -inf (value).  A full sort of each row is used.
+ * ------------------------------------------------------------------------------- */
+typedef struct { float v; int32_t s; } orc_cand;
+
+static int cand_cmp_desc(const void* a, const void* b) {
+    const orc_cand* x = (const orc_cand*)a;
+    const orc_cand* y = (const orc_cand*)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return (x->s < y->s) ? -1 : (x->s > y->s);
+}
+
+static int int_cmp(const void* a, const void* b) {
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return (x > y) - (x < y);
+}
+
+void orc_topk(const float* scores, int64_t row_stride, int rows, int cols,
+              const int32_t* row_lens, int k, int32_t* out_idx, float* out_vals,
+              int n_threads) {
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int t = 0; t < rows; t++) {
+        int len = row_lens ? row_lens[t] : cols;
+        if (len > cols) len = cols;
+        if (len < 0) len = 0;
+        orc_cand* c = (orc_cand*)malloc(sizeof(orc_cand) * (size_t)(len > 0 ? len : 1));
+        int n = 0;
+        for (int s = 0; s < len; s++) {
+            float v = scores[(int64_t)t * row_stride + s];
+            if (v > -INFINITY) { /* excludes -inf and NaN */
+                c[n].v = v;
+                c[n].s = s;
+                n++;
+            }
+        }
+        qsort(c, (size_t)n, sizeof(orc_cand), cand_cmp_desc);
+        int m = n < k ? n : k;
+        int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)(m > 0 ? m : 1));
+        for (int i = 0; i < m; i++) sel[i] = c[i].s;
+        qsort(sel, (size_t)m, sizeof(int32_t), int_cmp);
+        for (int i = 0; i < k; i++) {
+            out_idx[(int64_t)t * k + i] = i < m ? sel[i] : -1;
+            if (out_vals)
+                out_vals[(int64_t)t * k + i] =
+                    i < m ? scores[(int64_t)t * row_stride + sel[i]] : -INFINITY;
+        }
+        free(sel);
+        free(c);
+    }
+}
+
+/* Threads an OpenMP region would use (for reporting). */
+int orc_max_threads(int n_threads) {
+#ifdef _OPENMP
+    if (n_threads > 0) return n_threads;
+    return omp_get_max_threads();
+#else
+    (void)n_threads;
+    return 1;
+#endif
+}

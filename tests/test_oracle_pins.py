@@ -1,0 +1,393 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test names what it pins and where the fact comes from: a value printed on the
+pages (fixtures under tests/golden/), a library routine (torch's float8 dtypes, numpy's
+float64 matmul and sort), a closed form, or an invariant of the definition.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from sparse_attention_fp4_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    out = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                out.append(line.split())
+    return out
+
+
+# ---------------------------------------------------------------- library / closed-form decoders
+def e2m1_bitfield(n):
+    """OCP E2M1 read as a float format: 1 sign, 2 exponent (bias 1), 1 mantissa bit."""
+    s, e, m = (n >> 3) & 1, (n >> 1) & 3, n & 1
+    mag = m * 0.5 if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 2.0)
+    return -mag if s else mag
+
+
+def torch_e8m0(codes):
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+
+
+def torch_e4m3(codes):
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def lib_dequant(fmt, packed, scales):
+    """Dequantize with library decoders only (torch float8 views + the OCP bit-field
+    E2M1); shares nothing with the oracle's decode."""
+    packed = np.asarray(packed, np.uint8)
+    lo = packed & 15
+    hi = packed >> 4
+    nib = np.stack([lo, hi], axis=-1).reshape(*packed.shape[:-1], 128)
+    lut = np.array([e2m1_bitfield(n) for n in range(16)])
+    vals = lut[nib]
+    S = 32 if fmt == wl.MXFP4 else 16
+    sc = torch_e8m0(scales) if fmt == wl.MXFP4 else torch_e4m3(scales)
+    return vals * np.repeat(sc, S, axis=-1)
+
+
+# ---------------------------------------------------------------- decode pins
+def test_e2m1_matches_issue_level_table_and_not_the_buggy_decode():
+    for idx, val, bug in _rows("e2m1_levels.txt"):
+        i = int(idx)
+        assert orc.e2m1(i) == float(val)
+        assert orc.e2m1(i | 8) == -float(val)
+        if float(val) != float(bug):
+            assert orc.e2m1(i) != float(bug)
+
+
+def test_e2m1_matches_ocp_bitfield_form_for_all_16_codes():
+    for n in range(16):
+        a, b = orc.e2m1(n), e2m1_bitfield(n)
+        assert a == b and math.copysign(1, a) == math.copysign(1, b), n
+
+
+def test_e8m0_matches_torch_for_codes_0_to_254_and_literal_formula_at_255():
+    t = torch_e8m0(np.arange(256))
+    for c in range(255):
+        assert orc.e8m0(c) == t[c], c
+    # torch reads 255 as NaN; the literal 2^(c-127) is 2^128 (finite in double, inf once
+    # rounded to fp32).  The stored codes are 1..254, so parity is required only there.
+    assert math.isnan(t[255])
+    assert orc.e8m0(255) == 2.0 ** 128
+    assert np.float32(orc.e8m0(255)) == np.float32(np.inf)
+
+
+def test_e4m3_matches_torch_for_all_256_codes():
+    t = torch_e4m3(np.arange(256))
+    for c in range(256):
+        a = orc.e4m3(c)
+        if math.isnan(t[c]):
+            assert math.isnan(a), c
+        else:
+            assert a == t[c] and math.copysign(1, a) == math.copysign(1, t[c]), c
+
+
+def test_nibble_order_matches_issue_fixture():
+    for byte, v0, v1 in _rows("nibble_order.txt"):
+        packed = np.zeros(64, np.uint8)
+        packed[5] = int(byte, 16)
+        vals = orc.dequant(wl.MXFP4, packed, np.full(4, 127, np.uint8))
+        assert vals[10] == float(v0) and math.copysign(1, vals[10]) == math.copysign(1, float(v0))
+        assert vals[11] == float(v1) and math.copysign(1, vals[11]) == math.copysign(1, float(v1))
+
+
+@pytest.mark.parametrize("fmt", [wl.MXFP4, wl.NVFP4])
+def test_dequant_matches_library_decoders(fmt):
+    rng = np.random.default_rng(7)
+    G = wl.groups(fmt)
+    packed = rng.integers(0, 256, (50, 64), dtype=np.uint8)
+    if fmt == wl.MXFP4:
+        scales = rng.integers(100, 160, (50, G), dtype=np.uint8)
+    else:
+        scales = rng.integers(0, 256, (50, G), dtype=np.uint8)
+        scales[(scales & 0x7F) == 0x7F] = 0x38
+    np.testing.assert_array_equal(orc.dequant(fmt, packed, scales), lib_dequant(fmt, packed, scales))
+
+
+# ---------------------------------------------------------------- dot pins
+def test_dot_closed_forms():
+    ones = np.full(64, 0x22, np.uint8)  # every element code 2 = 1.0
+    unit = np.full(4, 127, np.uint8)
+    q = orc.dequant(wl.MXFP4, ones, unit)
+    v, exact, a = orc.dot(q, q)
+    assert (v, exact, a) == (128.0, True, 128.0)
+    sixes = np.full(64, 0x77, np.uint8)  # code 7 = 6.0
+    for sa, sb in [(127, 127), (130, 120), (100, 150)]:
+        q = orc.dequant(wl.MXFP4, sixes, np.full(4, sa, np.uint8))
+        k = orc.dequant(wl.MXFP4, sixes, np.full(4, sb, np.uint8))
+        v, exact, _ = orc.dot(q, k)
+        assert exact and v == 4 * 36 * 32 * 2.0 ** (sa - 127 + sb - 127)
+    # one-hot: a single product survives
+    a = np.zeros(64, np.uint8)
+    b = np.zeros(64, np.uint8)
+    a[17] = 0x50  # element 35 = code 5 = 3.0
+    b[17] = 0xF0  # element 35 = code 15 = -6.0
+    b[3] = 0x77   # elements 6,7 -- multiplied by zeros
+    q = orc.dequant(wl.MXFP4, a, np.array([127, 129, 127, 127], np.uint8))
+    k = orc.dequant(wl.MXFP4, b, np.array([127, 126, 127, 127], np.uint8))
+    assert orc.dot(q, k)[0] == 3.0 * 4 * -6.0 * 0.5
+
+
+@pytest.mark.parametrize("fmt,lo,hi", [(wl.MXFP4, 123, 131), (wl.MXFP4, 120, 134), (wl.NVFP4, 0, 0)])
+def test_dot_matches_numpy_float64_matmul_and_is_exact_on_workload_distributions(fmt, lo, hi):
+    rng = np.random.default_rng(11)
+    G = wl.groups(fmt)
+    n = 300
+    pq = rng.integers(0, 256, (n, 64), dtype=np.uint8)
+    pk = rng.integers(0, 256, (n, 64), dtype=np.uint8)
+    if fmt == wl.MXFP4:
+        sq = rng.integers(lo, hi + 1, (n, G), dtype=np.uint8)
+        sk = rng.integers(lo, hi + 1, (n, G), dtype=np.uint8)
+    else:
+        e = rng.integers(-4, 5, (2, n, G))
+        m = rng.integers(0, 8, (2, n, G))
+        c = (((e + 7) << 3) | m).astype(np.uint8)
+        sq, sk = c[0], c[1]
+    Q = lib_dequant(fmt, pq, sq)
+    K = lib_dequant(fmt, pk, sk)
+    ref = np.einsum("nd,nd->n", Q, K)  # float64; exact on these dyadic inputs (< 53 bits)
+    qo = orc.dequant(fmt, pq, sq)
+    ko = orc.dequant(fmt, pk, sk)
+    for i in range(n):
+        v, exact, _ = orc.dot(qo[i], ko[i])
+        assert exact
+        assert v == ref[i]
+
+
+def test_dot_exactness_flag_turns_off_for_extreme_scale_spreads():
+    q = np.zeros(128)
+    k = np.zeros(128)
+    q[0], k[0] = 2.0 ** 60, 1.0
+    q[1], k[1] = 2.0 ** -60, 1.0
+    v, exact, _ = orc.dot(q, k)
+    assert not exact and v == 2.0 ** 60
+
+
+# ---------------------------------------------------------------- logits pins
+def _small_logits(seed=3, H=4, Hkv=1, ctx=(150, 70), q_per_req=(2, 3), fmt=wl.MXFP4, page=64):
+    return wl.make_logits("small", fmt=fmt, q_per_req=list(q_per_req), ctx=list(ctx), H=H,
+                          Hkv=Hkv, page=page, seed=seed)
+
+
+def _run(case, **kw):
+    return orc.logits_paged(case.fmt, case.q_fp4, case.q_scale, case.w, case.k_fp4, case.k_scale,
+                            case.block_table, case.cu_seqlens_q, case.row_lens, case.page_size,
+                            case.out_cols, **kw)
+
+
+def _logical_keys(case, b, n):
+    """Logical keys 0..n-1 of request b, found by scanning every physical page for the
+    block-table entry that names it (no division / modulo arithmetic)."""
+    Hkv, page = case.Hkv, case.page_size
+    kp = np.zeros((n, Hkv, 64), np.uint8)
+    ks = np.zeros((n, Hkv, case.k_scale.shape[-1]), np.uint8)
+    pos = 0
+    for lp in range(case.block_table.shape[1]):
+        phys = case.block_table[b, lp]
+        for off in range(page):
+            if pos >= n:
+                return kp, ks
+            kp[pos] = case.k_fp4[phys, :, off]
+            ks[pos] = case.k_scale[phys, :, off]
+            pos += 1
+    return kp, ks
+
+
+@pytest.mark.parametrize("H,Hkv,fmt", [(4, 1, wl.MXFP4), (6, 2, wl.MXFP4), (4, 2, wl.NVFP4)])
+def test_one_hot_weights_expose_relu_of_each_head_dot(H, Hkv, fmt):
+    case = _small_logits(H=H, Hkv=Hkv, fmt=fmt)
+    R = H // Hkv
+    for h in range(H):
+        case.w[:] = 0
+        case.w[:, h] = 1.0
+        out, _, inexact = _run(case)
+        assert inexact == 0
+        for b in range(case.B):
+            rows = range(case.cu_seqlens_q[b], case.cu_seqlens_q[b + 1])
+            n = int(case.row_lens[list(rows)].max())
+            kp, ks = _logical_keys(case, b, n)
+            K = lib_dequant(fmt, kp[:, h // R], ks[:, h // R])
+            for t in rows:
+                q = lib_dequant(fmt, case.q_fp4[t, h], case.q_scale[t, h])
+                want = np.maximum(K @ q, 0).astype(np.float32)
+                got = out[t, :n]
+                np.testing.assert_array_equal(got, want)
+
+
+def test_head_sum_is_linear_in_weights_within_tolerance():
+    case = _small_logits(H=5, seed=9)
+    out, tb, _ = _run(case, want_tolbase=True)
+    w = case.w.copy()
+    parts = []
+    for h in range(case.H):
+        case.w[:] = 0
+        case.w[:, h] = 1.0
+        parts.append(_run(case)[0].astype(np.float64))
+    vis = np.isfinite(out)
+    comb = sum(w[:, h:h + 1].astype(np.float64) * np.where(vis, parts[h], 0) for h in range(case.H))
+    assert np.all(np.abs(out[vis] - comb[vis]) <= 1e-6 * tb[vis] + 1e-30)
+
+
+def test_visibility_counts_and_boundaries():
+    case = wl.make_logits("bounds", q_per_req=[12], ctx=[200], H=2, seed=4,
+                          row_lens=[0, 1, 63, 64, 65, 127, 128, 129, 191, 192, 199, 200],
+                          out_cols=256)
+    out, _, _ = _run(case)
+    for t in range(case.T):
+        L = case.row_lens[t]
+        assert np.all(np.isfinite(out[t, :L]))
+        assert np.all(out[t, L:] == -np.inf)
+
+
+def test_page_permutation_does_not_change_logits():
+    case = _small_logits(seed=21, ctx=(300, 130))
+    out1, _, _ = _run(case)
+    # move every physical page to a new slot and rewrite the table to match
+    rng = np.random.default_rng(5)
+    P = case.num_pages
+    newpos = rng.permutation(P)
+    k2 = np.empty_like(case.k_fp4)
+    s2 = np.empty_like(case.k_scale)
+    k2[newpos] = case.k_fp4
+    s2[newpos] = case.k_scale
+    bt = case.block_table.copy()
+    bt[bt >= 0] = newpos[bt[bt >= 0]]
+    case.k_fp4, case.k_scale, case.block_table = k2, s2, bt
+    out2, _, _ = _run(case)
+    np.testing.assert_array_equal(out1, out2)
+
+
+def test_invisible_positions_stay_neg_inf_with_nan_queries():
+    case = _small_logits(seed=5, fmt=wl.NVFP4, ctx=(100, 40), q_per_req=(1, 1))
+    case.q_scale[0, 1, 3] = 0x7F  # NaN scale for one head of row 0
+    out, _, _ = _run(case)
+    assert np.all(np.isnan(out[0, :100]))
+    assert np.all(out[0, 100:] == -np.inf)
+    assert np.all(np.isfinite(out[1, :40])) and np.all(out[1, 40:] == -np.inf)
+
+
+def test_invalid_page_ids_are_invisible():
+    case = _small_logits(seed=6, ctx=(200, 70))
+    case.block_table[0, 1] = -1
+    case.block_table[1, 0] = case.num_pages + 3
+    out, _, _ = _run(case)
+    r0 = range(case.cu_seqlens_q[0], case.cu_seqlens_q[1])
+    for t in r0:
+        assert np.all(out[t, 64:128] == -np.inf)
+        assert np.all(np.isfinite(out[t, :64])) and np.all(np.isfinite(out[t, 128:200]))
+    for t in range(case.cu_seqlens_q[1], case.cu_seqlens_q[2]):
+        assert np.all(out[t, :64] == -np.inf)
+
+
+# ---------------------------------------------------------------- block-score pins
+def test_causal_visibility_fixture():
+    for q_len, k_len, qo, ql, vis in _rows("causal_visibility.txt"):
+        q_len, k_len, ql = int(q_len), int(k_len), int(ql)
+        want = [] if vis == "none" else [int(x) for x in vis.split(",")]
+        # a key is seen iff its one-hot score block reports it: give key j a value that
+        # identifies it (dot = j+1 for the single query that is probed)
+        case = wl.make_block("fx", fmt=wl.MXFP4, q_lens=[q_len], k_lens=[k_len], Hq=1, Hkv=1,
+                             seed=1, qo_offset=None if qo == "-" else [int(qo)])
+        case.q_fp4[:] = 0
+        case.q_scale[:] = 127
+        case.q_fp4[:, 0, 0] = 0x02  # q[0] = 1.0, rest 0
+        case.k_fp4[:] = 0
+        case.k_scale[:] = 127
+        seen = []
+        for j in range(k_len):
+            # key j alone carries a positive value; all other keys score 0
+            case.k_fp4[:] = 0
+            phys = case.kv_indices[j // 128]
+            case.k_fp4[phys, 0, j % 128, 0] = 0x02
+            out, _, _ = orc.block_scores(case.fmt, case.q_fp4, case.q_scale, case.k_fp4,
+                                         case.k_scale, case.cu_seqlens_q, case.cu_seqlens_k,
+                                         case.cu_page_offsets, case.kv_indices, case.qo_offset,
+                                         case.max_seqlen_k, True)
+            if out[0, 0, ql] == 1.0:
+                seen.append(j)
+        assert seen == want, (q_len, k_len, qo, ql)
+
+
+@pytest.mark.parametrize("fmt", [wl.MXFP4, wl.NVFP4])
+@pytest.mark.parametrize("causal", [True, False])
+def test_block_scores_brute_force_against_library_dot(fmt, causal):
+    case = wl.make_block("bf", fmt=fmt, q_lens=[5, 3], k_lens=[300, 129], Hq=4, Hkv=2, seed=13,
+                         causal=causal)
+    out, _, inexact = orc.block_scores(case.fmt, case.q_fp4, case.q_scale, case.k_fp4,
+                                       case.k_scale, case.cu_seqlens_q, case.cu_seqlens_k,
+                                       case.cu_page_offsets, case.kv_indices, None,
+                                       case.max_seqlen_k, causal)
+    assert inexact == 0
+    R = case.Hq // case.Hkv
+    for b in range(case.B):
+        ql = case.cu_seqlens_q[b + 1] - case.cu_seqlens_q[b]
+        kl = case.cu_seqlens_k[b + 1] - case.cu_seqlens_k[b]
+        pages = case.kv_indices[case.cu_page_offsets[b]:case.cu_page_offsets[b + 1]]
+        for hq in range(case.Hq):
+            K = np.concatenate([lib_dequant(fmt, case.k_fp4[p, hq // R], case.k_scale[p, hq // R])
+                                for p in pages])[:kl]
+            for qi in range(ql):
+                qg = case.cu_seqlens_q[b] + qi
+                s = K @ lib_dequant(fmt, case.q_fp4[qg, hq], case.q_scale[qg, hq])
+                lim = kl if not causal else min(kl, qi + (kl - ql) + 1)
+                for kb in range(case.ktiles):
+                    seg = s[128 * kb:min(128 * kb + 128, lim)]
+                    want = np.float32(seg.max()) if seg.size else -np.inf
+                    assert out[hq, kb, qg] == want
+
+
+def test_block_max_equals_max_of_one_head_logits():
+    """Cross-API: H=Hkv=1, w=1 logits on 128-token pages equal max(block score, 0)."""
+    bc = wl.make_block("x", fmt=wl.MXFP4, q_lens=[2], k_lens=[300], Hq=1, Hkv=1, seed=17,
+                       causal=False)
+    out_b, _, _ = orc.block_scores(bc.fmt, bc.q_fp4, bc.q_scale, bc.k_fp4, bc.k_scale,
+                                   bc.cu_seqlens_q, bc.cu_seqlens_k, bc.cu_page_offsets,
+                                   bc.kv_indices, None, bc.max_seqlen_k, False)
+    bt = np.full((1, 3), -1, np.int32)
+    bt[0, :3] = bc.kv_indices
+    lg, _, _ = orc.logits_paged(bc.fmt, bc.q_fp4, bc.q_scale, np.ones((2, 1), np.float32),
+                                bc.k_fp4, bc.k_scale, bt, np.array([0, 2], np.int32),
+                                np.array([300, 300], np.int32), 128, 300)
+    for t in range(2):
+        for kb in range(3):
+            assert lg[t, 128 * kb:128 * kb + 128].max() == max(out_b[0, kb, t], 0.0)
+
+
+# ---------------------------------------------------------------- top-k pins
+def test_topk_matches_numpy_stable_sort():
+    rng = np.random.default_rng(2)
+    rows, cols, k = 6, 3000, 100
+    s = rng.integers(-50, 50, (rows, cols)).astype(np.float32) / 4  # many ties
+    s[0, :] = -np.inf
+    s[1, 2000:] = -np.inf
+    s[2, 5] = np.nan
+    s[3, ::7] = -0.0
+    lens = np.array([3000, 3000, 3000, 3000, 50, 0], np.int32)
+    idx, vals = orc.topk(s, k, lens)
+    for t in range(rows):
+        L = min(lens[t], cols)
+        v = s[t, :L].astype(np.float64)
+        v = np.where(v == 0, 0.0, v)
+        cand = np.nonzero(v > -np.inf)[0]
+        order = cand[np.argsort(-v[cand], kind="stable")]
+        want = np.sort(order[:k])
+        m = len(want)
+        np.testing.assert_array_equal(idx[t, :m], want)
+        assert np.all(idx[t, m:] == -1)
+        np.testing.assert_array_equal(vals[t, :m], s[t, want])
+        assert np.all(vals[t, m:] == -np.inf)
+        if m and m < len(cand):
+            unsel = np.setdiff1d(cand, want)
+            assert v[want].min() >= v[unsel].max()
