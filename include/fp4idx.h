@@ -1,0 +1,164 @@
+/*
+ * fp4idx.h -- C ABI of libfp4idx.so, the FP4 lightning-indexer scorer for MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [SGL] "[DSv4.1] Speed up the FP4 indexer scorer by decoding keys without exp2"
+ *         (SGLang pull request): Motivation (the paged scorer and its tile),
+ *         Modifications (E2M1 and E8M0 decode), Accuracy Tests (invisible positions are
+ *         -inf; metadata is read at replay time), and the bench script (4 verify rows,
+ *         shuffled 64-token pages, a request table mapping tokens to pages).
+ *   [M3]  "M3 FP4 Indexer" README: 公共约束 (constraints), 输入 shape 和类型 (input shapes),
+ *         输出 shape 和类型 (output shape), FP4 和 scale layout, 数学语义 (math semantics)
+ *         and the causal paragraph after it.
+ *   [ISS] "ISSUE -- Lightning Indexer FP4 dequant decodes E2M1 wrong": TL;DR (the score
+ *         I[t,s]), "Fix (interim...)" (E2M1 level set, low nibble first), "Fix
+ *         (production target)" (ReLU and head weights in the epilogue, wave-level top-k).
+ *   [QSA] vLLM qsa_fp8 API page, _qsa_physical_slots_kernel: an entry that names no valid
+ *         page is masked; -1 pads a selection.
+ *
+ * Conventions for every entry point
+ *   - Every pointer is device memory owned by the caller, except where a parameter says
+ *     otherwise.  The library allocates nothing, keeps no state between calls and
+ *     never copies device data to the host.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the null
+ *     stream) and the call returns without waiting.  Device metadata (sequence
+ *     lengths, tables) is read by the kernels when they run, so the calls may be
+ *     captured in a hipGraph and replayed with new metadata in the same buffers.
+ *   - Argument errors are detected on the host from the scalar arguments and the
+ *     pointer values only.  On error nothing is enqueued and a nonzero FP4IDX_E* code
+ *     is returned; fp4idx_strerror() names it.
+ *   - Packed FP4: 64 bytes hold 128 E2M1 values; element 2j is the low nibble of byte
+ *     j and element 2j+1 its high nibble; nibble bit 3 is the sign and bits 2..0 index
+ *     the levels {0, 0.5, 1, 1.5, 2, 3, 4, 6} [ISS].
+ *   - Block scales [M3 FP4 和 scale layout]: MXFP4 = one E8M0 code per 32 values (G=4),
+ *     value 2^(code-127); NVFP4 = one E4M3 (fn) code per 16 values (G=8), with no
+ *     tensor-level global scale.  real[d] = E2M1[d] * scale[floor(d / S)].  E8M0 codes
+ *     0 and 255 are outside the stored range 1..254 [SGL Modifications]; what they give
+ *     is not specified.
+ */
+#ifndef FP4IDX_H
+#define FP4IDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* block-scale formats */
+enum { FP4IDX_MXFP4 = 0, FP4IDX_NVFP4 = 1 };
+
+/* status codes */
+enum {
+    FP4IDX_OK = 0,
+    FP4IDX_EINVAL = 1,       /* null required pointer, bad dimension, bad format, ... */
+    FP4IDX_EUNSUPPORTED = 2, /* a valid request this build does not implement */
+    FP4IDX_EALIGN = 3,       /* a pointer or stride that must be 16-byte aligned is not */
+    FP4IDX_EHIP = 4,         /* the HIP runtime reported an error at launch */
+    FP4IDX_EWORKSPACE = 5    /* workspace missing or smaller than required */
+};
+
+/* Weighted-ReLU indexer logits over a paged key cache [ISS TL;DR; SGL]:
+ *
+ *     logits[t][s] = sum_{h<H} w[t][h] * max(q[t][h] . k_b(t)[hk(h)][s], 0)
+ *
+ * for s < row_lens[t], and -inf for every other s in [0, out_cols) whatever the query
+ * holds [SGL Accuracy Tests].  Row t belongs to request b(t), the b with
+ * cu_seqlens_q[b] <= t < cu_seqlens_q[b+1].  Logical key s of request b is token
+ * (s % page_size) of physical page block_table[b * bt_row_stride + s / page_size]; a
+ * visible key whose logical page is >= table_width or whose page id is outside
+ * [0, num_pages) is scored -inf [QSA].  Query head h reads key head hk(h) = h / (H/Hkv)
+ * [M3 数学语义].
+ *
+ * Layouts (strides in bytes for byte arrays, in elements otherwise):
+ *   q_fp4   [T][H][64] uint8     rows t are q_row_stride bytes apart; heads contiguous
+ *   q_scale [T][H][G]  uint8     rows qs_row_stride bytes apart
+ *   w       [T][H]     float     rows w_row_stride floats apart (non-contiguous rows
+ *                                of q/w are allowed [SGL Accuracy Tests])
+ *   k_fp4   [P][Hkv][page_size][64] uint8, pages k_page_stride bytes apart
+ *   k_scale [P][Hkv][page_size][G]  uint8, pages ks_page_stride bytes apart.  A combined
+ *           page (values then scales, [SGL] bench) is k_scale = k_fp4 + Hkv*page_size*64
+ *           with both page strides = Hkv*page_size*(64+G).
+ *   block_table [B][table_width] int32 (rows bt_row_stride apart), -1 = no page
+ *   cu_seqlens_q [B+1] int32, nondecreasing, cu_seqlens_q[0] = 0, cu_seqlens_q[B] = T
+ *   row_lens [T] int32
+ *   logits [T][out_cols] float, rows out_row_stride floats apart
+ * Alignment: q_fp4, k_fp4 and their strides must be multiples of 16 bytes (EALIGN).
+ * Limits: H % Hkv == 0, page_size in {64, 128} (else EUNSUPPORTED), 1 <= H <= 128.
+ * fmt = FP4IDX_MXFP4 or FP4IDX_NVFP4. */
+int fp4idx_logits_paged(int fmt,
+                        const uint8_t* q_fp4, int64_t q_row_stride,
+                        const uint8_t* q_scale, int64_t qs_row_stride,
+                        const float* w, int64_t w_row_stride,
+                        const uint8_t* k_fp4, int64_t k_page_stride,
+                        const uint8_t* k_scale, int64_t ks_page_stride,
+                        const int32_t* block_table, int64_t bt_row_stride,
+                        const int32_t* cu_seqlens_q, const int32_t* row_lens,
+                        int T, int B, int H, int Hkv, int page_size, int num_pages,
+                        int table_width, int out_cols,
+                        float* logits, int64_t out_row_stride,
+                        void* stream);
+
+/* Per-head 128-token block-max scores [M3 数学语义]:
+ *
+ *     scores[hq][kb][q] = max over valid k_local in [128 kb, 128 kb + 128) of
+ *                         q[q][hq] . k[kv_indices[cu_page_offsets[b] + kb]][hq/(Hq/Hkv)][k_local-128kb]
+ *
+ * for query token q = cu_seqlens_q[b] + q_local of batch item b.  k_local is valid iff
+ * k_local < k_len[b] = cu_seqlens_k[b+1] - cu_seqlens_k[b], the page id is in
+ * [0, num_pages), and, when causal, k_local <= q_local + offset[b] with offset[b] =
+ * qo_offset[b] if qo_offset is given, else k_len[b] - q_len[b] (bottom-right).  A
+ * block with no valid key, and every kb >= ceil(k_len[b] / 128), is -inf.  No ReLU and
+ * no weights.
+ *
+ * Layouts (all contiguous): q_fp4 [Tq][Hq][64], q_scale [Tq][Hq][G], k_fp4
+ * [num_pages][Hkv][128][64], k_scale [num_pages][Hkv][128][G]; cu_seqlens_q,
+ * cu_seqlens_k, cu_page_offsets [B+1] int32 (prefix sums from 0; batch b owns logical
+ * pages [cu_page_offsets[b], cu_page_offsets[b+1]) = ceil(k_len[b]/128) of them);
+ * kv_indices [cu_page_offsets[B]] int32; qo_offset [B] int32 or NULL; scores
+ * [Hq][Ktiles][Tq] float with Ktiles = ceil(max_seqlen_k / 128).
+ * Caller guarantees [M3 输入 shape 和类型]: every q_len[b] <= max_seqlen_q and every
+ * k_len[b] <= max_seqlen_k.
+ * Errors: EINVAL for max_seqlen_q <= 0, Hq % Hkv != 0, qo_offset given with causal == 0,
+ * or a bad fmt; EALIGN for q_fp4 / k_fp4 not 16-byte aligned. */
+int fp4idx_block_scores(int fmt,
+                        const uint8_t* q_fp4, const uint8_t* q_scale,
+                        const uint8_t* k_fp4, const uint8_t* k_scale,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        const int32_t* cu_page_offsets, const int32_t* kv_indices,
+                        const int32_t* qo_offset,
+                        int B, int Tq, int Hq, int Hkv, int num_pages,
+                        int max_seqlen_q, int max_seqlen_k, int causal,
+                        float* scores, void* stream);
+
+/* Bytes of device workspace fp4idx_topk needs for these sizes (0 if none). */
+size_t fp4idx_topk_workspace_bytes(int rows, int cols, int k);
+
+/* Top-k selection over score rows [ISS "Fix (production target)"]: for each row t, the
+ * candidates are the columns s < len(t) (len = min(row_lens[t], cols) if row_lens is
+ * given, else cols) whose score is greater than -inf (-inf and NaN are never selected).
+ * The k largest are selected, ties broken toward the smaller column (-0 equals +0).
+ * out_idx[t][0..m) receives the selected columns in increasing order, m = min(k,
+ * #candidates), and out_idx[t][m..k) = -1 [QSA].  out_vals (nullable) receives the
+ * matching scores, -inf in the padding.
+ * scores: [rows][row_stride] float (row_stride >= cols); out_idx, out_vals: [rows][k].
+ * workspace: device memory of at least fp4idx_topk_workspace_bytes(rows, cols, k),
+ * 256-byte aligned, owned by the caller (NULL allowed when that size is 0).
+ * Limits: 1 <= k <= 8192 (else EUNSUPPORTED). */
+int fp4idx_topk(const float* scores, int64_t row_stride, int rows, int cols,
+                const int32_t* row_lens, int k,
+                int32_t* out_idx, float* out_vals,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static string naming a status code. */
+const char* fp4idx_strerror(int code);
+
+/* Library ABI version (major * 100 + minor). */
+int fp4idx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4IDX_H */

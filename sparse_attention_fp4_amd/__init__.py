@@ -1,0 +1,14 @@
+"""sparse_attention_fp4_amd -- FP4 lightning-indexer scorer for MI355X (gfx950).
+
+The compute path lives in libfp4idx.so (HIP kernels + the C ABI of include/fp4idx.h);
+this package is its Python binding:
+
+    logits_paged(...)   weighted-ReLU logits over a paged FP4 key cache
+    block_scores(...)   per-head 128-token block-max scores
+    topk(...)           exact top-k column selection per row
+
+``workloads`` holds seeded synthetic inputs for the benchmark shapes.
+"""
+from .ops import MXFP4, NVFP4, block_scores, logits_paged, topk, topk_workspace_bytes  # noqa: F401
+
+__all__ = ["MXFP4", "NVFP4", "logits_paged", "block_scores", "topk", "topk_workspace_bytes"]

@@ -1,0 +1,229 @@
+// block_scores.hip -- per-head 128-token block-max QK scores over paged FP4 keys, gfx950.
+//
+//   scores[hq][kb][q] = max over valid keys k in [128 kb, 128 kb + 128) of q . k
+//
+// ("M3 FP4 Indexer" README, 数学语义 and the causal paragraph after it: bottom-right
+// causal offset k_len - q_len unless qo_offset is given; keys past k_len never count;
+// an empty block is -inf.)
+//
+// Work split: one wave owns 16 consecutive query tokens (a query tile) and up to NB
+// query heads of one key-head group, walks the key tiles the tile can see in 16-key
+// steps and writes every score block of its (heads, tokens), including the -inf
+// blocks it never reaches.  Query tiles that straddle two batch items are handled one
+// item at a time.
+//
+// MFMA mapping: A = 16 keys x 128, B = 128 x 16 query tokens of one head, so output
+// lane (g, n) holds keys 4g..4g+3 of the tile for token n.  The block max is a running
+// max over tiles in each lane, then two cross-lane steps (over the four lane groups)
+// at each 128-key block boundary; lane group 0 stores 16 consecutive tokens (64 B).
+//
+// MXFP4 uses the scaled FP4 MFMA (one instruction per 16x16 tile covers all 128
+// products).  NVFP4 decodes both operands exactly to fp16 (E2M1 * 2^a * b, b the E4M3
+// significand as an integer) and accumulates four 16x16x32 fp16 MFMAs in fp32.
+#include "device_common.hpp"
+#include "fp4idx_internal.hpp"
+
+namespace fp4idx {
+
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+
+template <int FMT>
+struct QOperand;
+
+template <>
+struct QOperand<0> {
+    v4i v;
+    int s;
+};
+
+template <>
+struct QOperand<1> {
+    v8h v[4];
+};
+
+__device__ __forceinline__ float max4(float a, float b, float c, float d) {
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+template <int FMT, int NB>
+__global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, n = lane & 15;
+    const int n_qtiles = (p.Tq + 15) / 16;
+    const int n_hgrp = (p.R + NB - 1) / NB;
+    // block index -> (kv head, head group, 4 consecutive query tiles)
+    const int qt_blocks = (n_qtiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int bx = blockIdx.x;
+    const int hk = bx / (n_hgrp * qt_blocks);
+    const int rem = bx - hk * n_hgrp * qt_blocks;
+    const int hgrp = rem / qt_blocks;
+    const int qt = (rem - hgrp * qt_blocks) * kWavesPerBlock + (threadIdx.x >> 6);
+    if (hk >= p.Hkv || qt >= n_qtiles) return;  // uniform per wave
+    const int h0 = hk * p.R + hgrp * NB;         // first query head of this wave
+    const int nh = min(NB, p.R - hgrp * NB);
+    const int q_first = qt * 16;
+    const int q_lastp1 = min(q_first + 16, p.Tq);
+
+    int q_seg = q_first;
+    while (q_seg < q_lastp1) {
+        const int b = uniform(find_request(p.cu_q, p.B, q_seg));
+        const int cq0 = p.cu_q[b], cq1 = p.cu_q[b + 1];
+        const bool req_ok = q_seg < cq1;
+        const int seg_end = req_ok ? min(cq1, q_lastp1) : q_lastp1;
+        const int q_len = cq1 - cq0;
+        // keys past the output's Ktiles*128 columns have no block to land in
+        const int k_len = req_ok ? min(p.cu_k[b + 1] - p.cu_k[b], p.ktiles * 128) : 0;
+        const int offset = p.qo_offset ? p.qo_offset[b] : (p.cu_k[b + 1] - p.cu_k[b]) - q_len;
+        const int page0 = p.cu_p[b];
+        // token of this lane's B column and its visible key bound (exclusive)
+        const int qg = q_first + n;
+        const bool col_ok = qg >= q_seg && qg < seg_end;
+        const int q_local = qg - cq0;
+        int kv_lim = k_len;
+        if (p.causal) kv_lim = min(kv_lim, max(q_local + offset + 1, 0));
+        if (!col_ok) kv_lim = 0;
+        // wave-wide bound: largest kv_lim over the columns
+        int kv_max = kv_lim;
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) kv_max = max(kv_max, __shfl_xor(kv_max, d));
+        kv_max = uniform(kv_max);
+        int kv_min = col_ok ? kv_lim : 0x7fffffff;
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) kv_min = min(kv_min, __shfl_xor(kv_min, d));
+        kv_min = uniform(kv_min);
+
+        // query operands (B): token qg, head h0 + hb
+        QOperand<FMT> qop[NB];
+#pragma unroll
+        for (int hb = 0; hb < NB; hb++) {
+            const bool ok = col_ok && hb < nh;
+            const int hq = h0 + hb;
+            const int64_t row = (int64_t)qg * p.Hq + hq;
+            if constexpr (FMT == 0) {
+                if (ok) {
+                    qop[hb].v = load16(p.q + row * 64 + 16 * g);
+                    qop[hb].s = p.qs[row * 4 + g];
+                } else {
+                    qop[hb].v = v4i{0, 0, 0, 0};
+                    qop[hb].s = 127;
+                }
+            } else {
+                v4i raw = v4i{0, 0, 0, 0};
+                uint32_t sc = 0;
+                if (ok) {
+                    raw = load16(p.q + row * 64 + 16 * g);
+                    sc = (uint32_t)p.qs[row * 8 + 2 * g] | ((uint32_t)p.qs[row * 8 + 2 * g + 1] << 8);
+                }
+#pragma unroll
+                for (int c = 0; c < 4; c++) {
+                    float pw, bb;
+                    e4m3_split((sc >> (8 * (c >> 1))) & 0xffu, pw, bb);
+                    qop[hb].v[c] = decode8_f16((uint32_t)raw[c], pw, bb);
+                }
+            }
+        }
+
+        const int n_kt = (kv_max + 15) / 16;      // key tiles with any visible key
+        const int kb_done = (n_kt + 7) / 8;        // blocks this wave computes
+        float run[NB];
+#pragma unroll
+        for (int hb = 0; hb < NB; hb++) run[hb] = -__builtin_inff();
+
+        for (int kt = 0; kt < n_kt; kt++) {
+            const int kb = kt >> 3;
+            const int32_t phys = p.kv_indices ? uniform(p.kv_indices[page0 + kb]) : -1;
+            const bool page_ok = phys >= 0 && phys < p.num_pages;
+            if (page_ok) {
+                const int64_t tok = ((int64_t)phys * p.Hkv + hk) * 128 + (kt & 7) * 16 + n;
+                const v4i kr = load16(p.k + tok * 64 + 16 * g);
+                // keys of this lane's output rows: kt*16 + 4g + i
+                const int kbase = kt * 16 + 4 * g;
+                const bool full = kbase + 3 < kv_min;  // every element of the lane visible
+                if constexpr (FMT == 0) {
+                    const int sk = p.ks[tok * 4 + g];
+#pragma unroll
+                    for (int hb = 0; hb < NB; hb++) {
+                        if (hb >= nh) continue;
+                        v4f d = mfma_fp4_16x16x128(kr, sk, qop[hb].v, qop[hb].s, v4f{0.f, 0.f, 0.f, 0.f});
+                        if (!full) {
+#pragma unroll
+                            for (int i = 0; i < 4; i++)
+                                if (kbase + i >= kv_lim) d[i] = -__builtin_inff();
+                        }
+                        run[hb] = fmaxf(run[hb], max4(d[0], d[1], d[2], d[3]));
+                    }
+                } else {
+                    const uint32_t sc = (uint32_t)p.ks[tok * 8 + 2 * g] | ((uint32_t)p.ks[tok * 8 + 2 * g + 1] << 8);
+                    v8h kd[4];
+#pragma unroll
+                    for (int c = 0; c < 4; c++) {
+                        float pw, bb;
+                        e4m3_split((sc >> (8 * (c >> 1))) & 0xffu, pw, bb);
+                        kd[c] = decode8_f16((uint32_t)kr[c], pw, bb);
+                    }
+#pragma unroll
+                    for (int hb = 0; hb < NB; hb++) {
+                        if (hb >= nh) continue;
+                        v4f d = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int c = 0; c < 4; c++) d = mfma_f16_16x16x32(kd[c], qop[hb].v[c], d);
+                        if (!full) {
+#pragma unroll
+                            for (int i = 0; i < 4; i++)
+                                if (kbase + i >= kv_lim) d[i] = -__builtin_inff();
+                        }
+                        run[hb] = fmaxf(run[hb], max4(d[0], d[1], d[2], d[3]));
+                    }
+                }
+            }
+            // block boundary: reduce over the four lane groups and store
+            if ((kt & 7) == 7 || kt == n_kt - 1) {
+#pragma unroll
+                for (int hb = 0; hb < NB; hb++) {
+                    float v = run[hb];
+                    v = fmaxf(v, __shfl_xor(v, 16));
+                    v = fmaxf(v, __shfl_xor(v, 32));
+                    if (g == 0 && col_ok && hb < nh)
+                        p.scores[((int64_t)(h0 + hb) * p.ktiles + kb) * p.Tq + qg] = v;
+                    run[hb] = -__builtin_inff();
+                }
+            }
+        }
+        // blocks never reached: -inf
+        for (int kb = kb_done; kb < p.ktiles; kb++) {
+            if (g == 0 && col_ok) {
+#pragma unroll
+                for (int hb = 0; hb < NB; hb++)
+                    if (hb < nh) p.scores[((int64_t)(h0 + hb) * p.ktiles + kb) * p.Tq + qg] = -__builtin_inff();
+            }
+        }
+        q_seg = seg_end;
+    }
+}
+
+template <int FMT, int NB>
+hipError_t launch_fmt_nb(const BlockParams& p, hipStream_t stream) {
+    const int n_qtiles = (p.Tq + 15) / 16;
+    const int n_hgrp = (p.R + NB - 1) / NB;
+    const int qt_blocks = (n_qtiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t blocks = (int64_t)p.Hkv * n_hgrp * qt_blocks;
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL((k_block_scores<FMT, NB>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_block_scores(const BlockParams& p, hipStream_t stream) {
+    if (p.fmt == 0) {
+        if (p.R <= 4) return launch_fmt_nb<0, 4>(p, stream);
+        if (p.R <= 8) return launch_fmt_nb<0, 8>(p, stream);
+        return launch_fmt_nb<0, 16>(p, stream);
+    }
+    if (p.R <= 4) return launch_fmt_nb<1, 4>(p, stream);
+    return launch_fmt_nb<1, 8>(p, stream);
+}
+
+}  // namespace fp4idx

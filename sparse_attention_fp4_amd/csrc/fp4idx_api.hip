@@ -1,0 +1,175 @@
+// fp4idx_api.hip -- the extern "C" entry points declared in include/fp4idx.h.
+//
+// Each entry point checks its scalar arguments and pointer values on the host (device
+// metadata is never read here), fills a parameter block and enqueues the kernels on
+// the caller's stream.  Nothing is allocated and no state is kept between calls.
+#include "fp4idx.h"
+#include "fp4idx_internal.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned256(const void* p) { return ((uintptr_t)p & 255u) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FP4IDX_OK : FP4IDX_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fp4idx_version(void) { return 100; }
+
+const char* fp4idx_strerror(int code) {
+    switch (code) {
+        case FP4IDX_OK: return "ok";
+        case FP4IDX_EINVAL: return "invalid argument";
+        case FP4IDX_EUNSUPPORTED: return "unsupported size or layout";
+        case FP4IDX_EALIGN: return "pointer or stride not 16-byte aligned";
+        case FP4IDX_EHIP: return "HIP launch error";
+        case FP4IDX_EWORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+int fp4idx_logits_paged(int fmt,
+                        const uint8_t* q_fp4, int64_t q_row_stride,
+                        const uint8_t* q_scale, int64_t qs_row_stride,
+                        const float* w, int64_t w_row_stride,
+                        const uint8_t* k_fp4, int64_t k_page_stride,
+                        const uint8_t* k_scale, int64_t ks_page_stride,
+                        const int32_t* block_table, int64_t bt_row_stride,
+                        const int32_t* cu_seqlens_q, const int32_t* row_lens,
+                        int T, int B, int H, int Hkv, int page_size, int num_pages,
+                        int table_width, int out_cols,
+                        float* logits, int64_t out_row_stride,
+                        void* stream) {
+    if (fmt != FP4IDX_MXFP4 && fmt != FP4IDX_NVFP4) return FP4IDX_EINVAL;
+    if (T < 0 || B < 1 || H < 1 || Hkv < 1 || num_pages < 0 || table_width < 0 || out_cols < 0)
+        return FP4IDX_EINVAL;
+    if (H % Hkv != 0) return FP4IDX_EINVAL;
+    if (H > 128) return FP4IDX_EUNSUPPORTED;
+    if (page_size != 64 && page_size != 128) return FP4IDX_EUNSUPPORTED;
+    if (T == 0 || out_cols == 0) return FP4IDX_OK;
+    if (!q_fp4 || !q_scale || !w || !cu_seqlens_q || !row_lens || !logits) return FP4IDX_EINVAL;
+    if (num_pages > 0 && table_width > 0 && (!k_fp4 || !k_scale || !block_table))
+        return FP4IDX_EINVAL;
+    const int G = fmt == FP4IDX_MXFP4 ? 4 : 8;
+    if (q_row_stride < (int64_t)H * 64 || qs_row_stride < (int64_t)H * G || w_row_stride < H ||
+        out_row_stride < out_cols || bt_row_stride < table_width)
+        return FP4IDX_EINVAL;
+    if (k_page_stride < (int64_t)Hkv * page_size * 64 || ks_page_stride < (int64_t)Hkv * page_size * G)
+        return FP4IDX_EINVAL;
+    if (!aligned16(q_fp4) || (q_row_stride & 15) || !aligned16(k_fp4) || (k_page_stride & 15))
+        return FP4IDX_EALIGN;
+
+    fp4idx::LogitsParams p{};
+    p.q = q_fp4;
+    p.q_rs = q_row_stride;
+    p.qs = q_scale;
+    p.qs_rs = qs_row_stride;
+    p.w = w;
+    p.w_rs = w_row_stride;
+    p.k = k_fp4;
+    p.kp_s = k_page_stride;
+    p.ks = k_scale;
+    p.ksp_s = ks_page_stride;
+    p.bt = block_table;
+    p.bt_rs = bt_row_stride;
+    p.cu = cu_seqlens_q;
+    p.lens = row_lens;
+    p.out = logits;
+    p.out_rs = out_row_stride;
+    p.T = T;
+    p.B = B;
+    p.H = H;
+    p.Hkv = Hkv;
+    p.page = page_size;
+    p.num_pages = (k_fp4 && block_table) ? num_pages : 0;
+    p.W = table_width;
+    p.out_cols = out_cols;
+    p.fmt = fmt;
+    p.G = G;
+    p.R = H / Hkv;
+    return hip_status(fp4idx::launch_logits(p, (hipStream_t)stream));
+}
+
+int fp4idx_block_scores(int fmt,
+                        const uint8_t* q_fp4, const uint8_t* q_scale,
+                        const uint8_t* k_fp4, const uint8_t* k_scale,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        const int32_t* cu_page_offsets, const int32_t* kv_indices,
+                        const int32_t* qo_offset,
+                        int B, int Tq, int Hq, int Hkv, int num_pages,
+                        int max_seqlen_q, int max_seqlen_k, int causal,
+                        float* scores, void* stream) {
+    if (fmt != FP4IDX_MXFP4 && fmt != FP4IDX_NVFP4) return FP4IDX_EINVAL;
+    if (max_seqlen_q <= 0) return FP4IDX_EINVAL;
+    if (B < 1 || Tq < 0 || Hq < 1 || Hkv < 1 || num_pages < 0 || max_seqlen_k < 0)
+        return FP4IDX_EINVAL;
+    if (Hq % Hkv != 0) return FP4IDX_EINVAL;
+    if (qo_offset && !causal) return FP4IDX_EINVAL;
+    if (Tq == 0 || max_seqlen_k == 0) return FP4IDX_OK;
+    if (!q_fp4 || !q_scale || !cu_seqlens_q || !cu_seqlens_k || !cu_page_offsets || !scores)
+        return FP4IDX_EINVAL;
+    if (num_pages > 0 && (!k_fp4 || !k_scale || !kv_indices)) return FP4IDX_EINVAL;
+    if (!aligned16(q_fp4) || (k_fp4 && !aligned16(k_fp4))) return FP4IDX_EALIGN;
+    fp4idx::BlockParams p{};
+    p.q = q_fp4;
+    p.qs = q_scale;
+    p.k = k_fp4;
+    p.ks = k_scale;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.cu_p = cu_page_offsets;
+    p.kv_indices = kv_indices;
+    p.qo_offset = qo_offset;
+    p.scores = scores;
+    p.B = B;
+    p.Tq = Tq;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.num_pages = (k_fp4 && kv_indices) ? num_pages : 0;
+    p.max_seqlen_q = max_seqlen_q;
+    p.max_seqlen_k = max_seqlen_k;
+    p.causal = causal ? 1 : 0;
+    p.fmt = fmt;
+    p.G = fmt == FP4IDX_MXFP4 ? 4 : 8;
+    p.R = Hq / Hkv;
+    p.ktiles = (max_seqlen_k + 127) / 128;
+    return hip_status(fp4idx::launch_block_scores(p, (hipStream_t)stream));
+}
+
+size_t fp4idx_topk_workspace_bytes(int rows, int cols, int k) {
+    if (rows <= 0 || cols <= 0 || k <= 0) return 0;
+    return fp4idx::topk_workspace_bytes(rows, cols, k);
+}
+
+int fp4idx_topk(const float* scores, int64_t row_stride, int rows, int cols,
+                const int32_t* row_lens, int k,
+                int32_t* out_idx, float* out_vals,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    if (rows < 0 || cols < 0 || k < 1) return FP4IDX_EINVAL;
+    if (k > 8192) return FP4IDX_EUNSUPPORTED;
+    if (rows == 0) return FP4IDX_OK;
+    if (!out_idx) return FP4IDX_EINVAL;
+    if (cols > 0 && (!scores || row_stride < cols)) return FP4IDX_EINVAL;
+    size_t need = fp4idx_topk_workspace_bytes(rows, cols, k);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned256(workspace)))
+        return FP4IDX_EWORKSPACE;
+    fp4idx::TopkParams p{};
+    p.scores = scores;
+    p.row_stride = row_stride;
+    p.rows = rows;
+    p.cols = cols;
+    p.k = k;
+    p.row_lens = row_lens;
+    p.out_idx = out_idx;
+    p.out_vals = out_vals;
+    if (need > 0) {
+        // the workspace layout is decided by the top-k launcher; hand over the base
+        p.cand_vals = (float*)workspace;
+    }
+    return hip_status(fp4idx::launch_topk(p, (hipStream_t)stream));
+}
+
+}  // extern "C"

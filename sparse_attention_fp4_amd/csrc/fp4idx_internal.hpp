@@ -1,0 +1,77 @@
+// fp4idx_internal.hpp -- parameter blocks and launchers shared by the host entry points
+// (fp4idx_api.hip) and the kernel files.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp4idx {
+
+struct LogitsParams {
+    const uint8_t* q;
+    int64_t q_rs;        // bytes between query rows
+    const uint8_t* qs;
+    int64_t qs_rs;       // bytes between query-scale rows
+    const float* w;
+    int64_t w_rs;        // floats between weight rows
+    const uint8_t* k;
+    int64_t kp_s;        // bytes between key pages
+    const uint8_t* ks;
+    int64_t ksp_s;       // bytes between key-scale pages
+    const int32_t* bt;
+    int64_t bt_rs;       // int32 elements between block-table rows
+    const int32_t* cu;   // [B+1]
+    const int32_t* lens; // [T]
+    float* out;
+    int64_t out_rs;      // floats between logits rows
+    int T, B, H, Hkv, page, num_pages, W, out_cols;
+    int fmt;
+    int G;               // scale groups per 128 values (4 or 8)
+    int R;               // H / Hkv
+    int tiles_per_kv;    // A tiles per key head
+    int n_tiles;         // Hkv * tiles_per_kv
+    int ppw;             // pages per wave
+    int n_wchunks;       // column chunks (of ppw pages) per row block
+    int n_rowblocks;
+    int rows_per_block;  // RG: query rows sharing one A tile
+};
+
+struct BlockParams {
+    const uint8_t* q;
+    const uint8_t* qs;
+    const uint8_t* k;
+    const uint8_t* ks;
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    const int32_t* cu_p;
+    const int32_t* kv_indices;
+    const int32_t* qo_offset;  // nullable
+    float* scores;
+    int B, Tq, Hq, Hkv, num_pages, max_seqlen_q, max_seqlen_k, causal;
+    int fmt, G, R;
+    int ktiles;
+    int q_tiles;         // query tiles of 16 tokens in the grid's y dimension
+};
+
+struct TopkParams {
+    const float* scores;
+    int64_t row_stride;
+    int rows, cols, k;
+    const int32_t* row_lens;  // nullable
+    int32_t* out_idx;
+    float* out_vals;          // nullable
+    // chunked mode (rows longer than one chunk): stage-1 candidates in workspace
+    int chunk;                // columns per chunk
+    int n_chunks;             // chunks per row
+    float* cand_vals;         // [rows][n_chunks][k]
+    int32_t* cand_idx;        // [rows][n_chunks][k]
+    int32_t* cand_cnt;        // [rows][n_chunks]
+};
+
+hipError_t launch_logits(const LogitsParams& p, hipStream_t stream);
+hipError_t launch_block_scores(const BlockParams& p, hipStream_t stream);
+hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
+size_t topk_workspace_bytes(int rows, int cols, int k);
+
+}  // namespace fp4idx

@@ -1,0 +1,193 @@
+"""Python binding of the FP4 indexer C ABI (argument marshalling only).
+
+Every function takes torch tensors that already live on the GPU, checks dtypes,
+shapes and devices on the host, and calls the matching ``fp4idx_*`` entry point of
+libfp4idx.so on torch's current HIP stream.  All arithmetic happens in the library's
+HIP kernels; nothing here computes a score.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from ._lib import check, lib
+
+MXFP4 = 0
+NVFP4 = 1
+_FMT = {"mxfp4": MXFP4, "nvfp4": NVFP4, MXFP4: MXFP4, NVFP4: NVFP4}
+
+
+def _fmt(fmt) -> int:
+    try:
+        return _FMT[fmt]
+    except KeyError:
+        raise ValueError(f"unknown FP4 format {fmt!r}") from None
+
+
+def _groups(fmt: int) -> int:
+    return 4 if fmt == MXFP4 else 8
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _u8(t):
+    """Packed codes may arrive as uint8, int8 or a 1-byte float view: read as bytes."""
+    if t.dtype == torch.uint8:
+        return t
+    if t.element_size() == 1:
+        return t.view(torch.uint8)
+    raise ValueError(f"expected a 1-byte dtype, got {t.dtype}")
+
+
+def logits_paged(q_fp4, q_scale, w, k_fp4, k_scale, block_table, cu_seqlens_q, row_lens, *,
+                 fmt="mxfp4", out_cols: int, out: Optional[torch.Tensor] = None,
+                 k_page_stride: Optional[int] = None, ks_page_stride: Optional[int] = None):
+    """Weighted-ReLU logits [T, out_cols] fp32 (-inf where invisible).
+
+    q_fp4 [T,H,64] u8 (row stride may exceed H*64), q_scale [T,H,G] u8, w [T,H] fp32,
+    k_fp4 [P,Hkv,page,64] u8, k_scale [P,Hkv,page,G] u8, block_table [B,W] int32,
+    cu_seqlens_q [B+1] int32, row_lens [T] int32.
+    """
+    f = _fmt(fmt)
+    G = _groups(f)
+    q_fp4, q_scale, k_fp4, k_scale = _u8(q_fp4), _u8(q_scale), _u8(k_fp4), _u8(k_scale)
+    dev = q_fp4.device
+    _need(q_fp4, "q_fp4", torch.uint8, 3, dev)
+    _need(q_scale, "q_scale", torch.uint8, 3, dev)
+    _need(w, "w", torch.float32, 2, dev)
+    _need(k_fp4, "k_fp4", torch.uint8, 4, dev)
+    _need(k_scale, "k_scale", torch.uint8, 4, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, dev)
+    _need(row_lens, "row_lens", torch.int32, 1, dev)
+    T, H, d2 = q_fp4.shape
+    P, Hkv, page, d2k = k_fp4.shape
+    if d2 != 64 or d2k != 64:
+        raise ValueError("q_fp4 / k_fp4 must pack D=128 as 64 bytes")
+    if q_scale.shape != (T, H, G) or w.shape != (T, H):
+        raise ValueError("q_scale must be [T,H,G] and w [T,H]")
+    if k_scale.shape != (P, Hkv, page, G):
+        raise ValueError("k_scale must be [P,Hkv,page,G]")
+    B, W = block_table.shape
+    if cu_seqlens_q.numel() != B + 1 or row_lens.numel() != T:
+        raise ValueError("cu_seqlens_q must have B+1 entries and row_lens T")
+    for name, t in (("q_fp4", q_fp4), ("q_scale", q_scale), ("w", w)):
+        if t.stride(-1) != 1 or (t.dim() == 3 and t.stride(1) != t.shape[2]):
+            raise ValueError(f"{name} must be contiguous within a row")
+    for name, t, width in (("k_fp4", k_fp4, 64), ("k_scale", k_scale, G)):
+        if t.stride(3) != 1 or t.stride(2) != width or t.stride(1) != page * width:
+            raise ValueError(f"{name} must be contiguous inside each page")
+    if block_table.stride(1) != 1 or not cu_seqlens_q.is_contiguous() or not row_lens.is_contiguous():
+        raise ValueError("metadata tensors must be contiguous")
+    if out is None:
+        out = torch.empty((T, out_cols), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", torch.float32, 2, dev)
+        if out.shape != (T, out_cols) or out.stride(1) != 1:
+            raise ValueError("out must be [T, out_cols] with unit column stride")
+    kps = k_page_stride if k_page_stride is not None else (k_fp4.stride(0) if P > 0 else Hkv * page * 64)
+    ksps = ks_page_stride if ks_page_stride is not None else (k_scale.stride(0) if P > 0 else Hkv * page * G)
+    rc = lib().fp4idx_logits_paged(
+        f, _ptr(q_fp4), q_fp4.stride(0), _ptr(q_scale), q_scale.stride(0), _ptr(w), w.stride(0),
+        _ptr(k_fp4), kps, _ptr(k_scale), ksps, _ptr(block_table), block_table.stride(0),
+        _ptr(cu_seqlens_q), _ptr(row_lens), T, B, H, Hkv, page, P, W, out_cols,
+        _ptr(out), out.stride(0), _stream())
+    check("fp4idx_logits_paged", rc)
+    return out
+
+
+def block_scores(q_fp4, k_fp4, q_scale, k_scale, cu_seqlens_q, cu_seqlens_k, cu_page_offsets, *,
+                 max_seqlen_q: int, max_seqlen_k: int, kv_indices, fmt="nvfp4", causal=True,
+                 qo_offset=None, out: Optional[torch.Tensor] = None):
+    """Per-head 128-token block-max scores [Hq, ceil(max_seqlen_k/128), Tq] fp32.
+
+    Argument order follows the M3 README's public API."""
+    f = _fmt(fmt)
+    G = _groups(f)
+    q_fp4, q_scale, k_fp4, k_scale = _u8(q_fp4), _u8(q_scale), _u8(k_fp4), _u8(k_scale)
+    dev = q_fp4.device
+    _need(q_fp4, "q_fp4", torch.uint8, 3, dev)
+    _need(q_scale, "q_scale", torch.uint8, 3, dev)
+    _need(k_fp4, "k_fp4", torch.uint8, 4, dev)
+    _need(k_scale, "k_scale", torch.uint8, 4, dev)
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k),
+                    ("cu_page_offsets", cu_page_offsets), ("kv_indices", kv_indices)):
+        _need(t, name, torch.int32, 1, dev)
+    if qo_offset is not None:
+        _need(qo_offset, "qo_offset", torch.int32, 1, dev)
+        if not causal:
+            raise ValueError("qo_offset is only allowed with causal=True")
+    Tq, Hq, _ = q_fp4.shape
+    P, Hkv, page, _ = k_fp4.shape
+    if page != 128:
+        raise ValueError("block scores need 128-token pages")
+    if q_scale.shape != (Tq, Hq, G) or k_scale.shape != (P, Hkv, 128, G):
+        raise ValueError("scale shapes must be [Tq,Hq,G] and [P,Hkv,128,G]")
+    for name, t in (("q_fp4", q_fp4), ("q_scale", q_scale), ("k_fp4", k_fp4), ("k_scale", k_scale),
+                    ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k),
+                    ("cu_page_offsets", cu_page_offsets), ("kv_indices", kv_indices)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B = cu_seqlens_q.numel() - 1
+    ktiles = (max_seqlen_k + 127) // 128
+    if out is None:
+        out = torch.empty((Hq, ktiles, Tq), dtype=torch.float32, device=dev)
+    elif out.shape != (Hq, ktiles, Tq) or not out.is_contiguous():
+        raise ValueError("out must be contiguous [Hq, Ktiles, Tq]")
+    rc = lib().fp4idx_block_scores(
+        f, _ptr(q_fp4), _ptr(q_scale), _ptr(k_fp4), _ptr(k_scale), _ptr(cu_seqlens_q),
+        _ptr(cu_seqlens_k), _ptr(cu_page_offsets), _ptr(kv_indices), _ptr(qo_offset),
+        B, Tq, Hq, Hkv, P, max_seqlen_q, max_seqlen_k, 1 if causal else 0, _ptr(out), _stream())
+    check("fp4idx_block_scores", rc)
+    return out
+
+
+def topk_workspace_bytes(rows: int, cols: int, k: int) -> int:
+    return int(lib().fp4idx_topk_workspace_bytes(rows, cols, k))
+
+
+def topk(scores, k: int, row_lens=None, *, out_idx=None, out_vals=None, want_vals=True,
+         workspace=None):
+    """Top-k columns per row in increasing column order, -1 padded -> (idx, vals|None)."""
+    _need(scores, "scores", torch.float32, 2)
+    dev = scores.device
+    rows, cols = scores.shape
+    if scores.stride(1) != 1:
+        raise ValueError("scores must have unit column stride")
+    if row_lens is not None:
+        _need(row_lens, "row_lens", torch.int32, 1, dev)
+        if row_lens.numel() != rows or not row_lens.is_contiguous():
+            raise ValueError("row_lens must be a contiguous [rows] tensor")
+    if out_idx is None:
+        out_idx = torch.empty((rows, k), dtype=torch.int32, device=dev)
+    if want_vals and out_vals is None:
+        out_vals = torch.empty((rows, k), dtype=torch.float32, device=dev)
+    need = topk_workspace_bytes(rows, cols, k)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    rc = lib().fp4idx_topk(_ptr(scores), scores.stride(0), rows, cols, _ptr(row_lens), k,
+                           _ptr(out_idx), _ptr(out_vals), _ptr(workspace),
+                           0 if workspace is None else workspace.numel(), _stream())
+    check("fp4idx_topk", rc)
+    return out_idx, out_vals

@@ -1,0 +1,78 @@
+"""GPU parity of fp4idx_block_scores against the CPU oracle.
+
+MXFP4 block maxima are maxima of single scaled-FP4 MFMA results, which add their four
+exact 32-element block sums in fp32: bit-exact unless one of those three additions
+rounds (rare at scale codes 123..131; the exact fraction is reported and must stay
+above 99%).  NVFP4 accumulates four fp16 MFMAs in fp32.  Both are held to
+2^-22 * sum_d |q_d k_d| over the block's keys (errbase).  The -inf pattern must match
+exactly.
+"""
+import numpy as np
+import pytest
+
+from sparse_attention_fp4_amd import workloads as wl
+
+from .gpu_helpers import gpu_block_scores, oracle_block_scores, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(case, rows=None, exact=False):
+    """exact=True: at least 99% of the visible block maxima are bit-exact."""
+    got = gpu_block_scores(case)
+    ref, eb, inexact = oracle_block_scores(case, rows=rows)
+    assert inexact == 0
+    cols = np.arange(case.Tq) if rows is None else np.asarray(rows)
+    g, r, e = got[:, :, cols], ref[:, :, cols], eb[:, :, cols]
+    inv = r == -np.inf
+    assert np.array_equal(g == -np.inf, inv)
+    vis = ~inv
+    diff = np.abs(g[vis].astype(np.float64) - r[vis])
+    n_exact = int((g[vis] == r[vis]).sum())
+    say(f"    bit-exact {n_exact}/{int(vis.sum())}")
+    if exact:
+        assert n_exact >= 0.99 * int(vis.sum())
+    assert np.all(diff <= 2.0 ** -22 * e[vis])
+
+
+CASES = [
+    dict(name="mx_causal", fmt=wl.MXFP4, q_lens=[5, 130, 1], k_lens=[300, 130, 129], Hq=8, Hkv=2,
+         causal=True),
+    dict(name="mx_noncausal", fmt=wl.MXFP4, q_lens=[17, 3], k_lens=[257, 128], Hq=4, Hkv=1,
+         causal=False),
+    dict(name="mx_qo_offset", fmt=wl.MXFP4, q_lens=[20, 33], k_lens=[200, 90], Hq=16, Hkv=1,
+         causal=True, qo_offset=[7, -5]),
+    dict(name="mx_gqa17", fmt=wl.MXFP4, q_lens=[9], k_lens=[257], Hq=17, Hkv=1, causal=True),
+    dict(name="nv_causal", fmt=wl.NVFP4, q_lens=[5, 130, 1], k_lens=[300, 130, 129], Hq=8, Hkv=2,
+         causal=True),
+    dict(name="nv_noncausal", fmt=wl.NVFP4, q_lens=[4, 8], k_lens=[128, 257], Hq=4, Hkv=1,
+         causal=False),
+    dict(name="nv_qo_offset", fmt=wl.NVFP4, q_lens=[20], k_lens=[400], Hq=32, Hkv=4, causal=True,
+         qo_offset=[100]),
+    dict(name="nv_q_longer_than_k", fmt=wl.NVFP4, q_lens=[40], k_lens=[20], Hq=4, Hkv=2,
+         causal=True),
+]
+
+
+@pytest.mark.parametrize("spec", CASES, ids=[c["name"] for c in CASES])
+def test_small_cases(spec):
+    spec = dict(spec)
+    name = spec.pop("name")
+    case = wl.make_block(name, seed=len(name) * 31, **spec)
+    _check(case, exact=spec["fmt"] == wl.MXFP4)
+
+
+def test_ktiles_wider_than_batch_and_bad_pages():
+    case = wl.make_block("wide", fmt=wl.MXFP4, q_lens=[6, 6], k_lens=[140, 600], Hq=4, Hkv=1,
+                         seed=3, causal=False)
+    case.max_seqlen_k = 1000          # more output blocks than any batch item fills
+    case.kv_indices[1] = -1           # batch 0, block 1 has no page
+    _check(case, exact=True)
+
+
+def test_config3_nvfp4_prefill_sampled_queries():
+    case = wl.config3()
+    rng = np.random.default_rng(1030)
+    rows = np.unique(np.concatenate([rng.integers(0, case.Tq, 48), case.cu_seqlens_q[:-1],
+                                     case.cu_seqlens_q[1:] - 1]))
+    _check(case, rows=rows.tolist())

@@ -1,0 +1,184 @@
+"""GPU parity of fp4idx_logits_paged against the CPU oracle.
+
+Bar (per the weighted-head-sum rule): the -inf pattern is identical and every visible
+logit is within 1e-6 * sum_h |w_h ReLU(dot_h)| of the oracle's correctly rounded value.
+Per-head dots, exposed through one-hot weights, are compared bit for bit.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_fp4_amd as fp4
+from oracle import oracle as orc
+from sparse_attention_fp4_amd import workloads as wl
+
+from .gpu_helpers import check_logits, dev, gpu_logits, oracle_logits, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _parity(case, rows=None):
+    got = gpu_logits(case)
+    ref, tb, inexact = oracle_logits(case, rows=rows)
+    assert inexact == 0
+    worst = check_logits(got, ref, tb, rows=rows)
+    say(f"    worst error / tolerance = {worst:.3f}")
+    return got, ref
+
+
+def test_config0_decode_ctx2048():
+    _parity(wl.config0())
+
+
+@pytest.mark.parametrize("ctx", [16384, 100_000])
+def test_config1_decode_contexts(ctx):
+    _parity(wl.config1(ctx))
+
+
+def test_config1_400k_sampled_rows_match():
+    case = wl.config1(400_000)
+    _parity(case, rows=[0, 3])
+
+
+def test_config2_batched_decode_sampled_rows():
+    case = wl.config2()
+    rows = [0, 1, 17, 40, 63]
+    _parity(case, rows=rows)
+
+
+SMALL = [
+    dict(name="ragged_multi_request", q_per_req=[1, 7, 0, 4], ctx=[70, 300, 5, 129], H=32),
+    dict(name="heads_not_multiple_of_16", q_per_req=[3, 2], ctx=[200, 90], H=5),
+    dict(name="gqa_two_key_heads", q_per_req=[4], ctx=[257], H=6, Hkv=2),
+    dict(name="page128", q_per_req=[2, 2], ctx=[300, 129], H=16, page=128),
+    dict(name="wide_scales", q_per_req=[4], ctx=[513], H=32, e8_lo=120, e8_hi=134),
+    dict(name="single_row_requests", q_per_req=[1] * 9, ctx=[64 * i + 3 for i in range(9)], H=64),
+    dict(name="h128", q_per_req=[2], ctx=[100], H=128),
+    dict(name="nvfp4_decode", q_per_req=[4, 1], ctx=[333, 64], H=32, fmt=wl.NVFP4),
+    dict(name="nvfp4_gqa", q_per_req=[2], ctx=[150], H=8, Hkv=4, fmt=wl.NVFP4),
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[s["name"] for s in SMALL])
+def test_small_shapes(spec):
+    spec = dict(spec)
+    name = spec.pop("name")
+    case = wl.make_logits(name, seed=zlib.crc32(name.encode()) % 1000, **spec)
+    # also exercise rows that see less than the whole context and out_cols past it
+    case.row_lens = np.maximum(case.row_lens - np.arange(case.T, dtype=np.int32) % 3, 0)
+    case.out_cols = int(max(spec["ctx"]) + 37)
+    _parity(case)
+
+
+def test_visibility_boundaries():
+    lens = [0, 1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256]
+    case = wl.make_logits("bounds", q_per_req=[len(lens)], ctx=[256], H=32, seed=5,
+                          row_lens=lens, out_cols=300)
+    _parity(case)
+
+
+def test_invalid_pages_and_rows_outside_requests():
+    case = wl.make_logits("invalid", q_per_req=[3, 2], ctx=[300, 200], H=32, seed=8)
+    case.block_table[0, 1] = -1
+    case.block_table[1, 2] = case.num_pages + 5
+    _parity(case)
+
+
+def test_page_permutation_gives_identical_logits():
+    case = wl.make_logits("perm", q_per_req=[4], ctx=[1000], H=32, seed=12)
+    a = gpu_logits(case)
+    rng = np.random.default_rng(3)
+    newpos = rng.permutation(case.num_pages)
+    k2 = np.empty_like(case.k_fp4)
+    s2 = np.empty_like(case.k_scale)
+    k2[newpos] = case.k_fp4
+    s2[newpos] = case.k_scale
+    bt = case.block_table.copy()
+    bt[bt >= 0] = newpos[bt[bt >= 0]]
+    case.k_fp4, case.k_scale, case.block_table = k2, s2, bt
+    b = gpu_logits(case)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_nonfinite_queries_leave_invisible_positions_neg_inf():
+    case = wl.make_logits("nanq", q_per_req=[4], ctx=[500], H=32, seed=9, fmt=wl.NVFP4,
+                          row_lens=[500, 100, 0, 1], out_cols=520)
+    case.q_scale[1, 3, 2] = 0x7F   # NaN scale
+    case.q_scale[2, :, :] = 0xFF   # NaN everywhere in a row that sees nothing
+    got = gpu_logits(case)
+    assert np.all(got[1, 100:] == -np.inf)
+    assert np.all(got[2, :] == -np.inf)
+    assert np.all(got[3, 1:] == -np.inf)
+    assert np.all(np.isfinite(got[0, :500])) and np.all(got[0, 500:] == -np.inf)
+
+
+def test_noncontiguous_query_rows_and_combined_pages():
+    """q/w rows with padding between them; keys in the combined page form (nibbles
+    then scales inside one buffer per page)."""
+    case = wl.make_logits("strided", q_per_req=[4], ctx=[700], H=32, seed=14)
+    ref, tb, _ = oracle_logits(case)
+    T, H = case.T, case.H
+    qbig = np.zeros((T, H + 3, 64), np.uint8)
+    qbig[:, :H] = case.q_fp4
+    sbig = np.zeros((T, H + 1, 4), np.uint8)
+    sbig[:, :H] = case.q_scale
+    wbig = np.zeros((T, H + 7), np.float32)
+    wbig[:, :H] = case.w
+    P, page = case.num_pages, case.page_size
+    comb = np.zeros((P, page * 68), np.uint8)
+    comb[:, :page * 64] = case.k_fp4.reshape(P, page * 64)
+    comb[:, page * 64:] = case.k_scale.reshape(P, page * 4)
+    q_t = dev(qbig)[:, :H]
+    s_t = dev(sbig)[:, :H]
+    w_t = dev(wbig)[:, :H]
+    comb_t = dev(comb)
+    k_view = comb_t[:, :page * 64].view(P, 1, page, 64)
+    ks_view = comb_t[:, page * 64:].view(P, 1, page, 4)
+    say("[gpu] logits strided rows + combined pages")
+    out = fp4.logits_paged(q_t, s_t, w_t, k_view, ks_view, dev(case.block_table),
+                           dev(case.cu_seqlens_q), dev(case.row_lens), fmt=0,
+                           out_cols=case.out_cols)
+    torch.cuda.synchronize()
+    check_logits(out.cpu().numpy(), ref, tb)
+
+
+def _flip_sign(packed):
+    return packed ^ np.uint8(0x88)
+
+
+@pytest.mark.parametrize("e8", [(123, 131), (120, 134)])
+def test_per_head_dots_through_one_hot_weights(e8):
+    """w = e_h gives ReLU(dot_h) with no further rounding; flipping every query sign
+    bit gives ReLU(-dot_h).  The MFMA adds its four exact 32-element block sums in fp32,
+    so a dot differs from the correctly rounded one only when such an addition rounds:
+    at scale codes 123..131 at least 99.9% must be bit-exact; every dot is held to
+    three fp32 roundings, 2^-22 * sum_d |q_d k_d|."""
+    case = wl.make_logits("onehot", q_per_req=[4], ctx=[640], H=32, seed=31, e8_lo=e8[0],
+                          e8_hi=e8[1])
+    K = orc.dequant(0, case.k_fp4[:, 0], case.k_scale[:, 0])      # [P, page, 128] physical
+    Kl = K[case.block_table[0, :10]].reshape(-1, 128)[:640]         # logical order
+    mism = total = 0
+    for h in (0, 5, 17, 31):
+        for sign in (1, -1):
+            c = wl.make_logits("onehot", q_per_req=[4], ctx=[640], H=32, seed=31, e8_lo=e8[0],
+                               e8_hi=e8[1])
+            c.w[:] = 0
+            c.w[:, h] = 1.0
+            if sign < 0:
+                c.q_fp4 = _flip_sign(c.q_fp4)
+            got = gpu_logits(c)
+            ref, _, inexact = oracle_logits(c)
+            assert inexact == 0
+            Q = orc.dequant(0, c.q_fp4[:, h], c.q_scale[:, h])       # [4, 128]
+            absbase = np.abs(Q) @ np.abs(Kl).T                       # [4, 640]
+            vis = ref != -np.inf
+            diff = got[vis] != ref[vis]
+            mism += int(diff.sum())
+            total += int(vis.sum())
+            err = np.abs(got[vis].astype(np.float64) - ref[vis])
+            assert np.all(err <= 2.0 ** -22 * absbase[vis])
+    say(f"    per-head bit-exact: {total - mism}/{total}")
+    if e8 == (123, 131):
+        assert mism <= 1e-3 * total

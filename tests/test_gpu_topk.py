@@ -1,0 +1,63 @@
+"""GPU parity of fp4idx_topk.
+
+On the same scores the selection is integer work and must equal the oracle's exactly
+(columns in increasing order, -1 padding, values copied from the scores).  On logits
+that the GPU and the oracle each computed, the index sets may differ only where the
+oracle's scores tie within the logits tolerance.
+"""
+import numpy as np
+import pytest
+
+from oracle import oracle as orc
+from sparse_attention_fp4_amd import workloads as wl
+
+from .gpu_helpers import gpu_logits, gpu_topk, oracle_logits, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _same(scores, k, row_lens=None):
+    gi, gv = gpu_topk(scores, k, row_lens)
+    oi, ov = orc.topk(scores, k, row_lens)
+    assert np.array_equal(gi, oi)
+    assert np.array_equal(gv.view(np.uint32), ov.view(np.uint32))
+
+
+@pytest.mark.parametrize("rows,cols,k", [(4, 2048, 2048), (4, 5000, 2048), (3, 32768, 2048),
+                                         (2, 32769, 100), (4, 100_000, 2048), (2, 400_000, 2048),
+                                         (64, 131072, 2048), (7, 70_000, 8192), (5, 1000, 1)])
+def test_same_scores_exact(rows, cols, k):
+    rng = np.random.default_rng(rows * 7 + cols)
+    s = rng.standard_normal((rows, cols)).astype(np.float32)
+    s[0, rng.integers(0, cols, 50)] = -np.inf
+    s[-1, rng.integers(0, cols, 50)] = np.nan
+    _same(s, k)
+
+
+def test_ties_zeros_and_lengths():
+    rng = np.random.default_rng(4)
+    rows, cols, k = 6, 40000, 2048
+    s = (rng.integers(-20, 20, (rows, cols)) / 4).astype(np.float32)  # heavy ties
+    s[1, ::3] = -0.0
+    s[2, :] = 1.5                                                     # all equal
+    s[3, :] = -np.inf                                                 # nothing valid
+    s[4, 100:] = -np.inf                                              # fewer than k valid
+    lens = np.array([40000, 39999, 1, 20000, 40000, 0], np.int32)
+    _same(s, k, lens)
+
+
+def test_on_config1_logits_within_tie_tolerance():
+    case = wl.config1(100_000)
+    got = gpu_logits(case)
+    ref, tb, _ = oracle_logits(case)
+    gi, _ = gpu_topk(got, 2048, case.row_lens)
+    oi, _ = orc.topk(ref, 2048, case.row_lens)
+    for t in range(case.T):
+        a, b = set(gi[t][gi[t] >= 0]), set(oi[t][oi[t] >= 0])
+        assert len(a) == len(b) == min(2048, case.row_lens[t])
+        sel = np.array(sorted(b))
+        kcol = sel[np.argmin(ref[t][sel])]        # the oracle's k-th largest
+        for c in a ^ b:
+            gap = abs(float(ref[t, c]) - float(ref[t, kcol]))
+            assert gap <= 1e-6 * (float(tb[t, c]) + float(tb[t, kcol])) + 1e-30, c
+        say(f"    row {t}: symmetric difference {len(a ^ b)}")
