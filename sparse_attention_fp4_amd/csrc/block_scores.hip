@@ -68,9 +68,10 @@ __global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
 
     int q_seg = q_first;
     while (q_seg < q_lastp1) {
-        const int b = uniform(find_request(p.cu_q, p.B, q_seg));
+        const RowRequest rq = find_request(p.cu_q, p.B, q_seg);
+        const int b = rq.b;
         const int cq0 = p.cu_q[b], cq1 = p.cu_q[b + 1];
-        const bool req_ok = q_seg < cq1;
+        const bool req_ok = rq.ok;
         const int seg_end = req_ok ? min(cq1, q_lastp1) : q_lastp1;
         const int q_len = cq1 - cq0;
         // keys past the output's Ktiles*128 columns have no block to land in

@@ -46,15 +46,37 @@ __device__ __forceinline__ v4f mfma_f16_16x16x32(v8h a, v8h b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Largest b in [0, B) with cu[b] <= t (cu[0] == 0).  Wave-uniform when t is.
-__device__ __forceinline__ int find_request(const int32_t* __restrict__ cu, int B, int t) {
-    int lo = 0, hi = B;
-    while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
-        if (cu[mid] <= t) lo = mid;
-        else hi = mid;
+// Request that owns row t of a prefix-sum table cu[0..B] (cu[0] == 0, nondecreasing):
+// the largest b with cu[b] <= t.  The whole wave scans 64 entries per load and counts
+// the prefix with a ballot, so the usual B <= 64 case costs one load.  t must be
+// wave-uniform.  `end` = cu[b+1]; ok = false when t >= cu[B] (no request owns t).
+struct RowRequest {
+    int b;
+    int end;
+    bool ok;
+};
+
+__device__ __forceinline__ RowRequest find_request(const int32_t* __restrict__ cu, int B, int t) {
+    const int lane = threadIdx.x & 63;
+    int m = 0;  // number of entries of cu[0..B] that are <= t (a prefix)
+    int end = 0x7fffffff;
+    for (int base = 0; base <= B; base += 64) {
+        const int idx = base + lane;
+        const int v = idx <= B ? cu[idx] : 0x7fffffff;
+        const unsigned long long le = __ballot(v <= t);
+        const int cnt = __popcll(le);
+        m += cnt;
+        if (cnt < 64) {
+            end = __shfl(v, cnt);  // first entry > t (or past the table)
+            break;
+        }
     }
-    return lo;
+    RowRequest r;
+    r.ok = m >= 1 && m <= B;
+    r.b = r.ok ? m - 1 : (m >= 1 ? min(m - 1, B - 1) : 0);
+    r.end = __builtin_amdgcn_readfirstlane(end);
+    r.b = __builtin_amdgcn_readfirstlane(r.b);
+    return r;
 }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -89,6 +111,57 @@ __device__ __forceinline__ v8h decode8_f16(uint32_t packed, float pow2, float b)
     v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, pow2, 3) * bb;
     v8h r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
     return r;
+}
+
+// Exclusive prefix sum of x over the NT threads of a workgroup (wave scans, then the
+// wave totals through LDS).  wtot: LDS scratch of NT/64 ints.  Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void block_excl_scan(int x, int* wtot, int& excl, int& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int s = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(s, d);
+        if (lane >= d) s += y;
+    }
+    if (lane == 63) wtot[wave] = s;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+    for (int w = 0; w < NT / 64; w++) {
+        const int t = wtot[w];
+        if (w < wave) before += t;
+        total += t;
+    }
+    excl = before + s - x;
+    __syncthreads();
+}
+
+// Thread-parallel bin pick: thread t owns PER bins listed in "before" order (c[b] =
+// count, bin[b] = bin index).  Finds the bin that holds the kk-th element of that
+// order; out[0] = bin, out[1] = elements before it, out[2] = total.  out[0] is left
+// untouched when total < kk.  Ends with a barrier.
+template <int NT, int PER>
+__device__ __forceinline__ void pick_bin(const int (&c)[PER], const int (&bin)[PER], int kk, int* wtot,
+                                         int* out) {
+    int s = 0;
+#pragma unroll
+    for (int b = 0; b < PER; b++) s += c[b];
+    int excl, total;
+    block_excl_scan<NT>(s, wtot, excl, total);
+    if (threadIdx.x == 0) out[2] = total;
+    if (excl < kk && kk <= excl + s) {
+#pragma unroll
+        for (int b = 0; b < PER; b++) {
+            if (excl + c[b] >= kk) {
+                out[0] = bin[b];
+                out[1] = excl;
+                break;
+            }
+            excl += c[b];
+        }
+    }
+    __syncthreads();
 }
 
 }  // namespace fp4idx

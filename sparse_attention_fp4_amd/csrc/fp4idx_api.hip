@@ -149,7 +149,7 @@ int fp4idx_topk(const float* scores, int64_t row_stride, int rows, int cols,
                 int32_t* out_idx, float* out_vals,
                 void* workspace, size_t workspace_bytes, void* stream) {
     if (rows < 0 || cols < 0 || k < 1) return FP4IDX_EINVAL;
-    if (k > 8192) return FP4IDX_EUNSUPPORTED;
+    if (k > 8192 || cols > (1 << 24)) return FP4IDX_EUNSUPPORTED;
     if (rows == 0) return FP4IDX_OK;
     if (!out_idx) return FP4IDX_EINVAL;
     if (cols > 0 && (!scores || row_stride < cols)) return FP4IDX_EINVAL;
@@ -165,10 +165,7 @@ int fp4idx_topk(const float* scores, int64_t row_stride, int rows, int cols,
     p.row_lens = row_lens;
     p.out_idx = out_idx;
     p.out_vals = out_vals;
-    if (need > 0) {
-        // the workspace layout is decided by the top-k launcher; hand over the base
-        p.cand_vals = (float*)workspace;
-    }
+    p.workspace = need > 0 ? workspace : nullptr;
     return hip_status(fp4idx::launch_topk(p, (hipStream_t)stream));
 }
 

@@ -33,6 +33,7 @@ struct LogitsParams {
     int n_tiles;         // Hkv * tiles_per_kv
     int ppw;             // pages per wave
     int n_wchunks;       // column chunks (of ppw pages) per row block
+    int n_wgchunks;      // workgroups per row block (four chunks each)
     int n_rowblocks;
     int rows_per_block;  // RG: query rows sharing one A tile
 };
@@ -61,12 +62,7 @@ struct TopkParams {
     const int32_t* row_lens;  // nullable
     int32_t* out_idx;
     float* out_vals;          // nullable
-    // chunked mode (rows longer than one chunk): stage-1 candidates in workspace
-    int chunk;                // columns per chunk
-    int n_chunks;             // chunks per row
-    float* cand_vals;         // [rows][n_chunks][k]
-    int32_t* cand_idx;        // [rows][n_chunks][k]
-    int32_t* cand_cnt;        // [rows][n_chunks]
+    void* workspace;          // long rows only (see topk_workspace_bytes)
 };
 
 hipError_t launch_logits(const LogitsParams& p, hipStream_t stream);

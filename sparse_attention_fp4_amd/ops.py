@@ -169,7 +169,11 @@ def topk_workspace_bytes(rows: int, cols: int, k: int) -> int:
 
 def topk(scores, k: int, row_lens=None, *, out_idx=None, out_vals=None, want_vals=True,
          workspace=None):
-    """Top-k columns per row in increasing column order, -1 padded -> (idx, vals|None)."""
+    """Top-k columns per row in increasing column order, -1 padded -> (idx, vals|None).
+
+    workspace: optional uint8 tensor of at least topk_workspace_bytes(rows, cols, k)
+    bytes (any contents) to reuse across calls.
+    """
     _need(scores, "scores", torch.float32, 2)
     dev = scores.device
     rows, cols = scores.shape

@@ -1,0 +1,94 @@
+"""Host-side checks of libfp4idx.so (no GPU needed).
+
+The library loads, exports every symbol include/fp4idx.h declares, and rejects bad
+arguments on the host before anything is enqueued (every call here returns before the
+first HIP runtime call).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_fp4_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols():
+    with open(os.path.join(ROOT, "include", "fp4idx.h")) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(fp4idx_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_exactly_the_binding_exports():
+    assert header_symbols() == sorted(_lib.EXPORTS)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in header_symbols():
+        assert hasattr(L, name), name
+    assert L.fp4idx_version() == 100
+    for code in range(6):
+        assert L.fp4idx_strerror(code)
+
+
+def _logits(**kw):
+    L = _lib.lib()
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = ctypes.cast(buf, ctypes.c_void_p).value
+    p16 = (p + 255) & ~255
+    a = dict(fmt=0, q=p16, qrs=32 * 64, qs=p16, qsrs=32 * 4, w=p16, wrs=32, k=p16,
+             kps=64 * 64, ks=p16, ksps=64 * 4, bt=p16, btrs=4, cu=p16, lens=p16, T=4, B=1, H=32,
+             Hkv=1, page=64, P=4, W=4, out_cols=256, out=p16, ors=256, stream=None)
+    a.update(kw)
+    return L.fp4idx_logits_paged(a["fmt"], a["q"], a["qrs"], a["qs"], a["qsrs"], a["w"], a["wrs"],
+                                 a["k"], a["kps"], a["ks"], a["ksps"], a["bt"], a["btrs"], a["cu"],
+                                 a["lens"], a["T"], a["B"], a["H"], a["Hkv"], a["page"], a["P"],
+                                 a["W"], a["out_cols"], a["out"], a["ors"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(fmt=2), 1), (dict(H=6, Hkv=4), 1), (dict(page=32), 2), (dict(H=256, qrs=256 * 64,
+     qsrs=256 * 4, wrs=256), 2), (dict(q=None), 1), (dict(B=0), 1), (dict(qrs=100), 1),
+    (dict(qrs=32 * 64 + 8), 3), (dict(out_cols=300), 1), (dict(kps=100), 1),
+])
+def test_logits_argument_errors(kw, code):
+    assert _logits(**kw) == code
+
+
+def test_logits_empty_work_is_ok_without_launch():
+    assert _logits(T=0) == 0
+    assert _logits(out_cols=0, ors=0) == 0
+
+
+def _blocks(**kw):
+    L = _lib.lib()
+    a = dict(fmt=1, q=256, qs=256, k=256, ks=256, cuq=256, cuk=256, cup=256, kvi=256, qo=None,
+             B=1, Tq=4, Hq=8, Hkv=2, P=4, msq=4, msk=300, causal=1, out=256)
+    a.update(kw)
+    return L.fp4idx_block_scores(a["fmt"], a["q"], a["qs"], a["k"], a["ks"], a["cuq"], a["cuk"],
+                                 a["cup"], a["kvi"], a["qo"], a["B"], a["Tq"], a["Hq"], a["Hkv"],
+                                 a["P"], a["msq"], a["msk"], a["causal"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(msq=0), 1), (dict(Hq=8, Hkv=3), 1), (dict(qo=256, causal=0), 1), (dict(fmt=-1), 1),
+    (dict(q=None), 1), (dict(q=264), 3),
+])
+def test_block_score_argument_errors(kw, code):
+    assert _blocks(**kw) == code
+
+
+def test_topk_argument_errors_and_workspace():
+    L = _lib.lib()
+    assert L.fp4idx_topk(256, 10, 2, 10, None, 0, 256, None, None, 0, None) == 1      # k < 1
+    assert L.fp4idx_topk(256, 10, 2, 10, None, 9000, 256, None, None, 0, None) == 2   # k too big
+    assert L.fp4idx_topk(256, 5, 2, 10, None, 4, 256, None, None, 0, None) == 1       # stride
+    assert L.fp4idx_topk_workspace_bytes(4, 32768, 2048) == 0                        # fits in LDS
+    need = L.fp4idx_topk_workspace_bytes(4, 100_000, 2048)
+    assert need > 0
+    assert L.fp4idx_topk(256, 100_000, 4, 100_000, None, 2048, 256, None, None, 0, None) == 5
+    assert L.fp4idx_topk(256, 100_000, 4, 100_000, None, 2048, 256, None, 512 + 8, need,
+                         None) == 5                                                  # misaligned
