@@ -145,9 +145,11 @@ size_t fp4idx_topk_workspace_bytes(int rows, int cols, int k);
  * scores: [rows][row_stride] float (row_stride >= cols); out_idx, out_vals: [rows][k].
  * workspace: device memory of at least fp4idx_topk_workspace_bytes(rows, cols, k),
  * 256-byte aligned, owned by the caller (NULL allowed when that size is 0; rows of at
- * most 32768 columns need none).  It holds intermediate results of one call; its
- * contents on entry are ignored.  Calls that run concurrently must not share it.
- * Limits: 1 <= k <= 8192 and cols <= 2^24 (else EUNSUPPORTED). */
+ * most 32768 columns need none).  It carries per-row histograms between the kernels
+ * of one call: it must be zero-filled before its first use, and every call that
+ * returns FP4IDX_OK leaves it ready for the next one.  Calls that run concurrently
+ * must not share a workspace.
+ * Limits: 1 <= k <= 8192 and cols <= 524288 (else EUNSUPPORTED). */
 int fp4idx_topk(const float* scores, int64_t row_stride, int rows, int cols,
                 const int32_t* row_lens, int k,
                 int32_t* out_idx, float* out_vals,

@@ -149,7 +149,7 @@ int fp4idx_topk(const float* scores, int64_t row_stride, int rows, int cols,
                 int32_t* out_idx, float* out_vals,
                 void* workspace, size_t workspace_bytes, void* stream) {
     if (rows < 0 || cols < 0 || k < 1) return FP4IDX_EINVAL;
-    if (k > 8192 || cols > (1 << 24)) return FP4IDX_EUNSUPPORTED;
+    if (k > 8192 || cols > (1 << 19)) return FP4IDX_EUNSUPPORTED;
     if (rows == 0) return FP4IDX_OK;
     if (!out_idx) return FP4IDX_EINVAL;
     if (cols > 0 && (!scores || row_stride < cols)) return FP4IDX_EINVAL;

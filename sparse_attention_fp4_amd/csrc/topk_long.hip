@@ -8,19 +8,22 @@
 // and NaN never selected, result in increasing column order, -1 padded).  A row is cut
 // into chunks of 4096 columns.  Workgroups exchange data only across kernel
 // boundaries (a device-wide fence inside a kernel costs microseconds on this
-// multi-die part), through plain stores to their own workspace slots:
+// multi-die part):
 //   1. hist:    each chunk builds the histogram of the top 12 key bits of its elements
-//               in LDS and stores its nonzero bins as (bin, count) pairs.
-//   2. collect: each chunk merges its row's pairs (a few KB) to find the bin d1 that
-//               holds the row's k-th largest key, then stores a bitmap of its columns
-//               above d1 (all selected) and, in column order, the keys and columns in
-//               d1 (the candidates).
+//               in LDS and adds its nonzero bins to the row's histogram (global
+//               atomics that nothing waits for).
+//   2. collect: each chunk reads the row's histogram, finds the bin d1 that holds the
+//               row's k-th largest key, and stores a bitmap of its columns above d1
+//               (all selected) and, in column order, the keys and columns in d1 (the
+//               candidates).
 //   3. finish:  one workgroup per row narrows the candidates to the exact threshold key
-//               T (two more digit passes), finds the column cut among ties at T, sets
-//               the bits of the selected candidates and writes the output by a popcount
-//               scan of the row's bitmap.
-// Every phase issues its global loads together (a round trip costs about a
-// microsecond), and keeps the candidates in registers across its passes.
+//               T (two more digit passes over candidates kept in registers), finds the
+//               column cut among ties at T, ORs the selected candidates into an LDS copy
+//               of the row's bitmap, writes the columns in order from a popcount scan,
+//               gathers their scores, and clears the row's histogram for the next call.
+// Every phase issues its global loads together: a round trip costs about a
+// microsecond here.  The workspace must be zero-filled before its first use; every
+// call leaves the histograms zero-filled again.
 #include "device_common.hpp"
 #include "fp4idx_internal.hpp"
 
@@ -33,7 +36,9 @@ constexpr int kCT = 256;              // threads of a workgroup
 constexpr int kPer = kChunk / kCT;    // elements per thread
 constexpr int kBins = 4096;
 constexpr int kWords = kChunk / 32;   // bitmap words per chunk
-constexpr int kMaxChunks = 4096;
+constexpr int kMaxChunks = 128;    // rows of up to 524288 columns
+constexpr int kMaxWords = kMaxChunks * kWords;
+constexpr int kMaxK = 8192;
 
 struct RowState {
     int d1;         // bin of the k-th largest key, or -1 when every valid key is kept
@@ -42,8 +47,7 @@ struct RowState {
 
 struct LongWs {
     RowState* st;        // [rows]
-    uint32_t* hpair;     // [rows][n_chunks][kBins]  (bin << 16 | count) of nonzero bins
-    int32_t* hnnz;       // [rows][n_chunks]         number of pairs
+    uint32_t* hist;      // [rows][kBins]            zero between calls
     uint32_t* bitmap;    // [rows][n_chunks * kWords] columns above bin d1 (+ selected candidates)
     uint32_t* ckey;      // [rows][n_chunks][kChunk] candidates (bin d1): keys, in column order
     int32_t* ccol;       // [rows][n_chunks][kChunk] candidates: columns
@@ -84,61 +88,26 @@ __device__ __forceinline__ void load_chunk(const TopkParams& p, int row, int chu
     for (int j = 0; j < kPer; j++) key[j] = to_key(v[j]);
 }
 
-// LDS histogram add with the most frequent bins of a wave folded first: lanes that
-// share the first active lane's bin add once (up to four rounds), the rest add alone.
-// Clustered scores put most of a wave in a few bins, where plain atomics would
-// serialize on one LDS address.
-__device__ __forceinline__ void hist_add(uint32_t* h, bool in, uint32_t d) {
-    const int lane = threadIdx.x & 63;
-    unsigned long long act = __ballot(in);
-#pragma unroll
-    for (int it = 0; it < 4; it++) {
-        if (act == 0ull) return;
-        const int first = __ffsll((long long)act) - 1;
-        const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)d, first);
-        const unsigned long long m = act & __ballot(d == d0);
-        if (lane == first) atomicAdd(&h[d0], (uint32_t)__popcll(m));
-        act &= ~m;
-    }
-    if ((act >> lane) & 1ull) atomicAdd(&h[d], 1u);
-}
-
 // ---------------------------------------------------------------- 1. hist
 __global__ __launch_bounds__(kCT) void k_hist(const TopkParams p, LongWs ws) {
     __shared__ uint32_t h[kBins];
-    __shared__ int wtot[kCT / 64];
     const int row = blockIdx.x / ws.n_chunks, chunk = blockIdx.x - row * ws.n_chunks;
     if (row >= p.rows) return;
-    const int nch = ws.n_chunks;
     for (int i = threadIdx.x; i < kBins; i += kCT) h[i] = 0u;
     uint32_t key[kPer];
     load_chunk(p, row, chunk, key);
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kPer; j++) hist_add(h, key[j] != 0u, key[j] >> 20);
+    for (int j = 0; j < kPer; j++)
+        if (key[j]) atomicAdd(&h[key[j] >> 20], 1u);
     __syncthreads();
-    // nonzero bins -> (bin, count) pairs: thread t owns bins [16 t, 16 t + 16)
-    constexpr int per = kBins / kCT;
-    uint32_t v[per];
-    int s = 0;
-#pragma unroll
-    for (int b = 0; b < per; b++) {
-        v[b] = h[threadIdx.x * per + b];
-        s += v[b] != 0u;
-    }
-    int before, total;
-    block_excl_scan<kCT>(s, wtot, before, total);
-    uint32_t* out = ws.hpair + ((int64_t)row * nch + chunk) * kBins;
-#pragma unroll
-    for (int b = 0; b < per; b++)
-        if (v[b]) out[before++] = ((uint32_t)(threadIdx.x * per + b) << 16) | v[b];
-    if (threadIdx.x == 0) ws.hnnz[(int64_t)row * nch + chunk] = total;
+    uint32_t* gh = ws.hist + (int64_t)row * kBins;
+    for (int i = threadIdx.x; i < kBins; i += kCT)
+        if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
 // ---------------------------------------------------------------- 2. collect
 struct CollectShared {
-    uint32_t h[kBins];
-    int poff[kMaxChunks + 1];
     int wtot[kCT / 64];
     int pick[3];
     uint32_t bits[kWords];
@@ -146,61 +115,17 @@ struct CollectShared {
     int off[kPer * (kCT / 64)];
 };
 
-// Merge the row's (bin, count) pairs into sh.h and find the bin of the k-th largest
-// key.  Returns d1 (-1 when every valid key is kept) and kk, the keys wanted in d1.
+// The bin of the row's k-th largest key from the row's histogram.  Returns d1 (-1 when
+// every valid key is kept) and kk, the keys wanted in d1.
 __device__ __forceinline__ void row_threshold_bin(CollectShared& sh, const TopkParams& p, const LongWs& ws,
                                                   int row, int& d1, int& kk) {
-    const int nch = ws.n_chunks;
-    for (int i = threadIdx.x; i < kBins; i += kCT) sh.h[i] = 0u;
-    {
-        constexpr int per = kMaxChunks / kCT;
-        int v[per], s = 0;
-#pragma unroll
-        for (int b = 0; b < per; b++) {
-            const int c = threadIdx.x * per + b;
-            v[b] = c < nch ? ws.hnnz[(int64_t)row * nch + c] : 0;
-            s += v[b];
-        }
-        int before, total;
-        block_excl_scan<kCT>(s, sh.wtot, before, total);
-#pragma unroll
-        for (int b = 0; b < per; b++) {
-            const int c = threadIdx.x * per + b;
-            if (c < nch) sh.poff[c] = before;
-            before += v[b];
-        }
-        if (threadIdx.x == 0) sh.poff[nch] = total;
-    }
-    __syncthreads();
-    const int npairs = sh.poff[nch];
-    constexpr int B = 8;
-    for (int base = 0; base < npairs; base += kCT * B) {
-        uint32_t x[B];
-#pragma unroll
-        for (int j = 0; j < B; j++) {
-            const int i = base + threadIdx.x + kCT * j;
-            x[j] = 0u;
-            if (i < npairs) {
-                int lo = 0, hi = nch;
-                while (hi - lo > 1) {
-                    const int mid = (lo + hi) >> 1;
-                    if (sh.poff[mid] <= i) lo = mid;
-                    else hi = mid;
-                }
-                x[j] = ws.hpair[((int64_t)row * nch + lo) * kBins + (i - sh.poff[lo])];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < B; j++)
-            if (x[j]) atomicAdd(&sh.h[x[j] >> 16], x[j] & 0xffffu);
-    }
-    __syncthreads();
     constexpr int per = kBins / kCT;
     int c[per], bin[per];
+    const uint32_t* gh = ws.hist + (int64_t)row * kBins;
 #pragma unroll
     for (int b = 0; b < per; b++) {  // walked from the top: "before" = larger keys
         bin[b] = kBins - 1 - (threadIdx.x * per + b);
-        c[b] = (int)sh.h[bin[b]];
+        c[b] = (int)gh[bin[b]];
     }
     pick_bin<kCT, per>(c, bin, p.k, sh.wtot, sh.pick);
     if (sh.pick[2] <= p.k) {
@@ -219,7 +144,7 @@ __global__ __launch_bounds__(kCT) void k_collect(const TopkParams p, LongWs ws) 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nch = ws.n_chunks;
     uint32_t key[kPer];
-    load_chunk(p, row, chunk, key);  // in flight while the pairs are merged
+    load_chunk(p, row, chunk, key);  // in flight with the histogram loads
     int d1, kk;
     row_threshold_bin(sh, p, ws, row, d1, kk);
     if (chunk == 0 && threadIdx.x == 0) {
@@ -272,10 +197,14 @@ __global__ __launch_bounds__(kCT) void k_collect(const TopkParams p, LongWs ws) 
 }
 
 // ---------------------------------------------------------------- 3. finish
+constexpr int kFT = 1024;  // threads of the finishing workgroup
+
 struct FinishShared {
     uint32_t h[kBins];
+    uint32_t bits[kMaxWords];  // the row's bitmap
+    int sel[kMaxK];            // selected columns in order
     int coff[kMaxChunks + 1];  // candidate prefix over chunks
-    int wtot[kCT / 64];
+    int wtot[kFT / 64];
     int pick[3];
 };
 
@@ -290,10 +219,10 @@ __device__ __forceinline__ int64_t cand_slot(const FinishShared& sh, int row, in
     return ((int64_t)row * nch + lo) * kChunk + (i - sh.coff[lo]);
 }
 
-// The candidates of the row, kCR per thread per round (candidate i = round * kCT * kCR
-// + threadIdx.x + kCT * j); a row with at most kCT * kCR candidates keeps them in
+// The candidates of the row, kCR per thread per round (candidate i = round * kFT * kCR
+// + threadIdx.x + kFT * j); a row with at most kFT * kCR candidates keeps them in
 // registers for all passes, a larger one reloads them round by round.
-constexpr int kCR = 32;
+constexpr int kCR = 8;
 
 struct CandRegs {
     uint32_t key[kCR];
@@ -304,7 +233,7 @@ __device__ __forceinline__ void load_round(CandRegs& r, const FinishShared& sh, 
                                            int nch, int m, int round) {
 #pragma unroll
     for (int j = 0; j < kCR; j++) {
-        const int i = round * kCT * kCR + threadIdx.x + kCT * j;
+        const int i = round * kFT * kCR + threadIdx.x + kFT * j;
         r.key[j] = 0u;
         r.col[j] = -1;
         if (i < m) {
@@ -320,59 +249,60 @@ __device__ __forceinline__ void load_round(CandRegs& r, const FinishShared& sh, 
 template <typename Keep, typename Digit>
 __device__ __forceinline__ void cand_pass(FinishShared& sh, CandRegs& r, const LongWs& ws, int row, int nch,
                                           int m, int rounds, int kk, bool descending, Keep keep, Digit digit) {
-    for (int i = threadIdx.x; i < kBins; i += kCT) sh.h[i] = 0u;
+    for (int i = threadIdx.x; i < kBins; i += kFT) sh.h[i] = 0u;
     __syncthreads();
     for (int round = 0; round < rounds; round++) {
         if (rounds > 1) load_round(r, sh, ws, row, nch, m, round);
+        const int left = m - round * kFT * kCR;  // candidates of this round
 #pragma unroll
         for (int j = 0; j < kCR; j++) {
-            const bool in = r.col[j] >= 0 && keep(r.key[j], r.col[j]);
-            hist_add(sh.h, in, in ? (uint32_t)digit(r.key[j], r.col[j]) : 0u);
+            // slot j holds candidates only below `left` (a uniform test)
+            if (kFT * j < left && r.col[j] >= 0 && keep(r.key[j], r.col[j]))
+                atomicAdd(&sh.h[digit(r.key[j], r.col[j])], 1u);
         }
     }
     __syncthreads();
-    constexpr int per = kBins / kCT;
+    constexpr int per = kBins / kFT;
     int c[per], bin[per];
 #pragma unroll
     for (int b = 0; b < per; b++) {
         bin[b] = descending ? kBins - 1 - (threadIdx.x * per + b) : threadIdx.x * per + b;
         c[b] = (int)sh.h[bin[b]];
     }
-    pick_bin<kCT, per>(c, bin, kk, sh.wtot, sh.pick);
+    pick_bin<kFT, per>(c, bin, kk, sh.wtot, sh.pick);
 }
 
-__global__ __launch_bounds__(kCT) void k_finish(const TopkParams p, LongWs ws) {
+__global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws) {
     __shared__ FinishShared sh;
     const int row = blockIdx.x;
     if (row >= p.rows) return;
     const int nch = ws.n_chunks;
     const int k = p.k;
+    const int nwords = nch * kWords;
+    const uint32_t* rbits = ws.bitmap + (int64_t)row * nch * kWords;
+    // ---- the row's bitmap into LDS (loads in flight together)
+    for (int w = threadIdx.x; w < nwords; w += kFT * 16) {
+        uint32_t x[16];
+#pragma unroll
+        for (int j = 0; j < 16; j++) x[j] = w + kFT * j < nwords ? rbits[w + kFT * j] : 0u;
+#pragma unroll
+        for (int j = 0; j < 16; j++)
+            if (w + kFT * j < nwords) sh.bits[w + kFT * j] = x[j];
+    }
     const int d1 = ws.st[row].d1;
     int kk = ws.st[row].kk;
     {
-        constexpr int per = kMaxChunks / kCT;
-        int v[per], s = 0;
-#pragma unroll
-        for (int b = 0; b < per; b++) {
-            const int c = threadIdx.x * per + b;
-            v[b] = c < nch ? ws.cnum[(int64_t)row * nch + c] : 0;
-            s += v[b];
-        }
+        const int c = threadIdx.x;  // nch <= kMaxChunks <= kFT
+        const int v = c < nch ? ws.cnum[(int64_t)row * nch + c] : 0;
         int before, total;
-        block_excl_scan<kCT>(s, sh.wtot, before, total);
-#pragma unroll
-        for (int b = 0; b < per; b++) {
-            const int c = threadIdx.x * per + b;
-            if (c < nch) sh.coff[c] = before;
-            before += v[b];
-        }
+        block_excl_scan<kFT>(v, sh.wtot, before, total);
+        if (c < nch) sh.coff[c] = before;
         if (threadIdx.x == 0) sh.coff[nch] = total;
     }
     __syncthreads();
     const int m = sh.coff[nch];
-    uint32_t* rbits = ws.bitmap + (int64_t)row * nch * kWords;
     if (d1 >= 0) {
-        const int rounds = (m + kCT * kCR - 1) / (kCT * kCR);
+        const int rounds = (m + kFT * kCR - 1) / (kFT * kCR);
         CandRegs r;
         load_round(r, sh, ws, row, nch, m, 0);
         cand_pass(sh, r, ws, row, nch, m, rounds, kk, true, [&](uint32_t, int) { return true; },
@@ -402,60 +332,56 @@ __global__ __launch_bounds__(kCT) void k_finish(const TopkParams p, LongWs ws) {
                       [&](uint32_t, int col) { return (int)((uint32_t)col & 0xffu); });
             c_cut = (int)((c2 << 8) | (uint32_t)sh.pick[0]);
         }
-        // selected candidates join the bitmap (device-scope atomics, read back below by
-        // this workgroup only)
+        // selected candidates join the bitmap
         for (int round = 0; round < rounds; round++) {
             if (rounds > 1) load_round(r, sh, ws, row, nch, m, round);
 #pragma unroll
             for (int j = 0; j < kCR; j++) {
                 const uint32_t kx = r.key[j];
                 const int col = r.col[j];
-                if (col >= 0 && (kx > T || (kx == T && col <= c_cut)))
-                    atomicOr(&rbits[col >> 5], 1u << (col & 31));
+                if (col >= 0 && (kx > T || (kx == T && col <= c_cut))) atomicOr(&sh.bits[col >> 5], 1u << (col & 31));
             }
         }
-        __syncthreads();
     }
+    __syncthreads();
 
-    // ---- output: the set bits of the row's bitmap, in column order.  Thread t owns
-    // words [t*wpt, (t+1)*wpt), read kWB at a time with all loads in flight.
-    constexpr int kWB = 16;
-    const int nwords = nch * kWords;
-    const int wpt = (nwords + kCT - 1) / kCT;
+    // ---- columns in order: thread t scans words [t*wpt, (t+1)*wpt) of the LDS bitmap
+    const int wpt = (nwords + kFT - 1) / kFT;
     const int w0 = threadIdx.x * wpt, w1 = min(w0 + wpt, nwords);
     int s = 0;
-    for (int w = w0; w < w1; w += kWB) {
-        uint32_t x[kWB];
-#pragma unroll
-        for (int j = 0; j < kWB; j++)
-            x[j] = w + j < w1 ? __hip_atomic_load(rbits + w + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-#pragma unroll
-        for (int j = 0; j < kWB; j++) s += __popc(x[j]);
-    }
+    for (int w = w0; w < w1; w++) s += __popc(sh.bits[w]);
     int pos, total;
-    block_excl_scan<kCT>(s, sh.wtot, pos, total);
+    block_excl_scan<kFT>(s, sh.wtot, pos, total);
+    for (int w = w0; w < w1 && pos < k; w++) {
+        uint32_t bits = sh.bits[w];
+        while (bits && pos < k) {
+            sh.sel[pos++] = w * 32 + __ffs((int)bits) - 1;
+            bits &= bits - 1u;
+        }
+    }
+    __syncthreads();
+    // ---- output, coalesced; the scores come in with all loads in flight
+    const int n_out = min(total, k);
     const float* srow = p.scores + (int64_t)row * p.row_stride;
-    for (int w = w0; w < w1 && pos < k; w += kWB) {
-        uint32_t x[kWB];
+    for (int base = 0; base < k; base += kFT * 8) {
+        float v[8];
 #pragma unroll
-        for (int j = 0; j < kWB; j++)
-            x[j] = w + j < w1 ? __hip_atomic_load(rbits + w + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+        for (int j = 0; j < 8; j++) {
+            const int i = base + threadIdx.x + kFT * j;
+            v[j] = (p.out_vals && i < n_out) ? srow[sh.sel[i]] : -__builtin_inff();
+        }
 #pragma unroll
-        for (int j = 0; j < kWB; j++) {
-            uint32_t bits = x[j];
-            while (bits && pos < k) {
-                const int col = (w + j) * 32 + __ffs((int)bits) - 1;
-                bits &= bits - 1u;
-                p.out_idx[(int64_t)row * k + pos] = col;
-                if (p.out_vals) p.out_vals[(int64_t)row * k + pos] = srow[col];
-                pos++;
+        for (int j = 0; j < 8; j++) {
+            const int i = base + threadIdx.x + kFT * j;
+            if (i < k) {
+                p.out_idx[(int64_t)row * k + i] = i < n_out ? sh.sel[i] : -1;
+                if (p.out_vals) p.out_vals[(int64_t)row * k + i] = v[j];
             }
         }
     }
-    for (int i = min(total, k) + threadIdx.x; i < k; i += kCT) {
-        p.out_idx[(int64_t)row * k + i] = -1;
-        if (p.out_vals) p.out_vals[(int64_t)row * k + i] = -__builtin_inff();
-    }
+    // ---- leave the row's histogram zero-filled for the next call
+    uint32_t* gh = ws.hist + (int64_t)row * kBins;
+    for (int i = threadIdx.x; i < kBins; i += kFT) gh[i] = 0u;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -468,10 +394,8 @@ LongWs carve(void* base, int rows, int cols, size_t* bytes) {
     size_t o = 0;
     w.st = reinterpret_cast<RowState*>(b + o);
     o = align256(o + (size_t)rows * sizeof(RowState));
-    w.hpair = reinterpret_cast<uint32_t*>(b + o);
-    o = align256(o + rc * kBins * 4);
-    w.hnnz = reinterpret_cast<int32_t*>(b + o);
-    o = align256(o + rc * 4);
+    w.hist = reinterpret_cast<uint32_t*>(b + o);
+    o = align256(o + (size_t)rows * kBins * 4);
     w.bitmap = reinterpret_cast<uint32_t*>(b + o);
     o = align256(o + rc * kWords * 4);
     w.ckey = reinterpret_cast<uint32_t*>(b + o);
@@ -501,7 +425,7 @@ hipError_t launch_topk_long(const TopkParams& p, void* workspace, hipStream_t st
     const unsigned grid = (unsigned)(p.rows * w.n_chunks);
     hipLaunchKernelGGL(k_hist, dim3(grid), dim3(kCT), 0, stream, p, w);
     hipLaunchKernelGGL(k_collect, dim3(grid), dim3(kCT), 0, stream, p, w);
-    hipLaunchKernelGGL(k_finish, dim3(p.rows), dim3(kCT), 0, stream, p, w);
+    hipLaunchKernelGGL(k_finish, dim3(p.rows), dim3(kFT), 0, stream, p, w);
     return hipGetLastError();
 }
 

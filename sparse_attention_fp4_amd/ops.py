@@ -172,7 +172,8 @@ def topk(scores, k: int, row_lens=None, *, out_idx=None, out_vals=None, want_val
     """Top-k columns per row in increasing column order, -1 padded -> (idx, vals|None).
 
     workspace: optional uint8 tensor of at least topk_workspace_bytes(rows, cols, k)
-    bytes (any contents) to reuse across calls.
+    bytes, zero-filled before its first use (torch.zeros); each call leaves it ready for
+    the next, so it can be reused across calls without clearing.
     """
     _need(scores, "scores", torch.float32, 2)
     dev = scores.device
@@ -189,7 +190,7 @@ def topk(scores, k: int, row_lens=None, *, out_idx=None, out_vals=None, want_val
         out_vals = torch.empty((rows, k), dtype=torch.float32, device=dev)
     need = topk_workspace_bytes(rows, cols, k)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)  # zero before first use
     rc = lib().fp4idx_topk(_ptr(scores), scores.stride(0), rows, cols, _ptr(row_lens), k,
                            _ptr(out_idx), _ptr(out_vals), _ptr(workspace),
                            0 if workspace is None else workspace.numel(), _stream())

@@ -85,6 +85,7 @@ def test_topk_argument_errors_and_workspace():
     L = _lib.lib()
     assert L.fp4idx_topk(256, 10, 2, 10, None, 0, 256, None, None, 0, None) == 1      # k < 1
     assert L.fp4idx_topk(256, 10, 2, 10, None, 9000, 256, None, None, 0, None) == 2   # k too big
+    assert L.fp4idx_topk(256, 1 << 20, 1, 1 << 20, None, 8, 256, None, None, 0, None) == 2  # cols
     assert L.fp4idx_topk(256, 5, 2, 10, None, 4, 256, None, None, 0, None) == 1       # stride
     assert L.fp4idx_topk_workspace_bytes(4, 32768, 2048) == 0                        # fits in LDS
     need = L.fp4idx_topk_workspace_bytes(4, 100_000, 2048)

@@ -61,3 +61,23 @@ def test_on_config1_logits_within_tie_tolerance():
             gap = abs(float(ref[t, c]) - float(ref[t, kcol]))
             assert gap <= 1e-6 * (float(tb[t, c]) + float(tb[t, kcol])) + 1e-30, c
         say(f"    row {t}: symmetric difference {len(a ^ b)}")
+
+
+def test_workspace_reused_across_calls_without_clearing():
+    """The long-row path leaves its workspace ready for the next call."""
+    import torch
+
+    import sparse_attention_fp4_amd as fp4
+    from .gpu_helpers import dev
+
+    rng = np.random.default_rng(8)
+    rows, cols, k = 3, 70_000, 2048
+    ws = torch.zeros(fp4.topk_workspace_bytes(rows, cols, k), dtype=torch.uint8, device="cuda")
+    for rep in range(3):
+        s = rng.standard_normal((rows, cols)).astype(np.float32) * (rep + 1)
+        lens = np.array([cols, cols - 5 * rep, 40_000], np.int32)
+        say(f"[gpu] topk workspace reuse {rep}")
+        idx, vals = fp4.topk(dev(s), k, dev(lens), workspace=ws)
+        oi, ov = orc.topk(s, k, lens)
+        assert np.array_equal(idx.cpu().numpy(), oi)
+        assert np.array_equal(vals.cpu().numpy().view(np.uint32), ov.view(np.uint32))
