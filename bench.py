@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=640)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--ctx", type=int, default=100_000)
+    ap.add_argument("--workload", choices=["verify", "batched"], default="verify",
+                    help="verify: 4 rows of one request at --ctx (the headline); batched: 64 "
+                         "requests x 1 row, H=64, contexts 4096..131072")
     ap.add_argument("--topk", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-launches", type=int, default=256,
@@ -82,8 +85,16 @@ def main():
     assert torch.cuda.is_available(), "no GPU visible"
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    case = wl.config1(args.ctx)
-    workload = f"decode_ctx{args.ctx}_h32"
+    if args.workload == "verify":
+        case = wl.config1(args.ctx)
+        workload = f"decode_ctx{args.ctx}_h32"
+        desc = (f"{workload}: 1 request, 4 verify rows seeing ctx-0..3 keys, H=32, D=128, "
+                f"MXFP4, page 64 shuffled, logits + top-{args.topk}")
+    else:
+        case = wl.config2()
+        workload = "batched_decode_b64_h64"
+        desc = (f"{workload}: 64 requests x 1 row, H=64, D=128, contexts U[4096,131072], MXFP4 "
+                f"E8M0 120..134, page 64 shuffled, logits [64,131072] + top-{args.topk}")
     T, H, k = case.T, case.H, args.topk
     out_cols = case.out_cols
 
@@ -95,6 +106,8 @@ def main():
                 lens=up(case.row_lens))
     set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + T * out_cols * 4
     n_sets = int(min(256, max(2, -(-(512 << 20) // set_bytes))))
+    if args.steps % n_sets and args.steps < n_sets:
+        n_sets = max(2, args.steps)
     sets = []
     for i in range(n_sets):
         s = {n: (t if n in ("cu", "lens", "bt") else t.clone()) for n, t in base.items()}
@@ -228,9 +241,9 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp4 (e2m1 x e8m0, fp32 accumulate)",
         "data": "synthetic (seeded codes with the pages' distributions)",
-        "config": {"workload": f"{workload}: 1 request, 4 verify rows seeing ctx-0..3 keys, "
-                               f"H=32, D=128, MXFP4, page 64 shuffled, logits + top-{k}",
-                   "ctx": args.ctx, "rows": T, "heads": H, "topk": k,
+        "config": {"workload": desc,
+                   "ctx": args.ctx if args.workload == "verify" else "4096..131072",
+                   "rows": T, "heads": H, "topk": k,
                    "input_sets_rotated": n_sets, "timing": "hipGraph replay, cache-cold rotation"},
         "us_per_call": {"logits": round(logits_us, 3), "topk": round(topk_us, 3),
                         "step_cold": round(ms_per_step * 1e3, 3),

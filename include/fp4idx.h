@@ -84,7 +84,8 @@ enum {
  *   cu_seqlens_q [B+1] int32, nondecreasing, cu_seqlens_q[0] = 0, cu_seqlens_q[B] = T
  *   row_lens [T] int32
  *   logits [T][out_cols] float, rows out_row_stride floats apart
- * Alignment: q_fp4, k_fp4 and their strides must be multiples of 16 bytes (EALIGN).
+ * Alignment: q_fp4, k_fp4, k_scale and their row/page strides must be multiples of 16
+ * bytes (EALIGN).
  * Limits: H % Hkv == 0, page_size in {64, 128} (else EUNSUPPORTED), 1 <= H <= 128.
  * fmt = FP4IDX_MXFP4 or FP4IDX_NVFP4. */
 int fp4idx_logits_paged(int fmt,

@@ -61,6 +61,8 @@ int fp4idx_logits_paged(int fmt,
         return FP4IDX_EINVAL;
     if (!aligned16(q_fp4) || (q_row_stride & 15) || !aligned16(k_fp4) || (k_page_stride & 15))
         return FP4IDX_EALIGN;
+    if (num_pages > 0 && table_width > 0 && (!aligned16(k_scale) || (ks_page_stride & 15)))
+        return FP4IDX_EALIGN;
 
     fp4idx::LogitsParams p{};
     p.q = q_fp4;
@@ -90,6 +92,7 @@ int fp4idx_logits_paged(int fmt,
     p.fmt = fmt;
     p.G = G;
     p.R = H / Hkv;
+    p.vec_out = aligned16(logits) && (out_row_stride & 3) == 0;
     return hip_status(fp4idx::launch_logits(p, (hipStream_t)stream));
 }
 

@@ -22,19 +22,19 @@
 // epilogue each lane therefore holds partial head sums of one (row, key) pair; with
 // RG < 4 the 4/RG lane groups of a row are added with cross-lane steps.
 //
-// Keys go straight from HBM into the B operand: lane l loads the 16 bytes
-// [16*(l/16), +16) of key l%16 of a 16-key tile (a wave reads 1 KB contiguous per
-// tile, fully coalesced) and the scale byte(s) that cover them.  Each key byte is used
-// by exactly one wave, so keys skip LDS on this path.  A wave walks its pages in
-// 64-key slabs and issues the loads of the next slab before computing the current
-// one; the block-table entries of all its pages come in with a single load.
+// Keys go straight from HBM into the B operand, in 64-token slabs (see the slab
+// section below for which lane reads which bytes); each key byte is used by exactly one
+// wave, so keys skip LDS on this path.  A wave walks its pages slab by slab with the
+// loads of the next two slabs in flight while it computes one; the block-table entries
+// of all its pages come in with a single load.
 //
 // Rounding.  MXFP4: one scaled MFMA per (tile, key head) covers all 128 products.
 // NVFP4: E2M1 x E4M3 is not an MX operand, so both sides are decoded exactly to fp16
 // (value = E2M1 * 2^a * b, at most 6 significant bits) and four fp16 MFMAs accumulate
-// in fp32.  Head sums use eight accumulators per lane (chains of at most H*RG/128
-// fused multiply-adds) and a tree, which bounds the head-sum rounding well inside
-// 1e-6 * sum_h |w_h ReLU(dot_h)|.  ReLU is fmaxf (IEEE maxNum: a NaN dot counts as 0).
+// in fp32.  Head sums use four accumulators per lane (chains of at most 8 fused
+// multiply-adds: one per A tile) and a tree, so each term meets at most 8 + 2 (+ 2
+// cross-lane) roundings, about 7e-7 of sum_h |w_h ReLU(dot_h)| in the worst case,
+// inside the 1e-6 bound.  ReLU is fmaxf (IEEE maxNum: a NaN dot counts as 0).
 #include "device_common.hpp"
 #include "fp4idx_internal.hpp"
 
@@ -43,6 +43,9 @@ namespace fp4idx {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
+#ifndef FP4IDX_LOGITS_WAVES
+#define FP4IDX_LOGITS_WAVES 8192   // target number of waves of one launch
+#endif
 
 // ---------------------------------------------------------------- operand types
 template <int FMT>
@@ -94,7 +97,7 @@ __device__ __forceinline__ v4f tile_dot(const Operand<FMT>& a, const Operand<FMT
     }
 }
 
-// Scale bytes of one 128-value vector that lane group g needs.
+// Scale bytes of one 128-value query vector that lane group g needs.
 template <int FMT>
 __device__ __forceinline__ uint32_t scale_bytes(const uint8_t* s, int g) {
     if constexpr (FMT == 0) return s[g];
@@ -113,8 +116,48 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// ---------------------------------------------------------------- key slabs
+// A slab is 64 consecutive tokens of one key head of one page.  Column n of MFMA tile
+// tt (tt = 0..3) is token 4n + tt of the slab, so lane (g, n) reads bytes [16g, +16)
+// of tokens 4n .. 4n+3 (four loads at 64-byte steps), the scale bytes of those four
+// tokens in one 16-byte (MXFP4) or two (NVFP4) loads, and ends up holding the logits
+// of four adjacent columns, which it writes with one 16-byte store.
+//
+// Loads go through buffer descriptors built per slab in scalar registers (base =
+// the slab's first byte).  A slab that does not exist or whose page is invisible or
+// invalid gets a descriptor of zero bytes: its loads return zeros without touching
+// memory, so every slab issues the same instructions and no branch separates a load
+// from its use.
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 raw-buffer descriptor, word 3
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             (int)kRsrcWord3);
+}
+
+template <int FMT>
+struct Slab {
+    v4i k[4];                    // tile tt: bytes [16g, +16) of token 4n + tt
+    v4i s[FMT == 0 ? 1 : 2];     // the scale bytes of tokens 4n .. 4n+3
+};
+
+// Scale operand of tile tt from the slab's scale bytes.  MXFP4: byte 4tt + g (the
+// E8M0 code of elements [32g, +32) of token 4n + tt).  NVFP4: the E4M3 codes of groups
+// 2g and 2g+1 of that token, bytes 8tt + 2g and 8tt + 2g + 1, as a 16-bit pair.
+template <int FMT>
+__device__ __forceinline__ uint32_t slab_scale(const Slab<FMT>& b, int tt, int g) {
+    if constexpr (FMT == 0) {
+        return ((uint32_t)b.s[0][tt] >> (8 * g)) & 0xffu;
+    } else {
+        const int dw = 2 * tt + (g >> 1);
+        const uint32_t word = (uint32_t)b.s[dw >> 2][dw & 3];
+        return (word >> (16 * (g & 1))) & 0xffffu;
+    }
+}
+
 // ---------------------------------------------------------------- the kernel
-template <int FMT, int RG, int NT>
+// MKV: more than one key head (the tiles of key head hk only meet that head's slabs).
+template <int FMT, int RG, int NT, bool MKV>
 __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
     extern __shared__ __align__(16) uint8_t lds[];
     constexpr int G = FMT == 0 ? 4 : 8;
@@ -123,7 +166,8 @@ __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
     uint8_t* sqs = lds + RG * H * 64;                                // [RG][H][G]
     float* sw = reinterpret_cast<float*>(lds + RG * H * (64 + G));   // [RG][H]
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar math
     const int g = lane >> 4, n = lane & 15;
     const int rb = blockIdx.x / p.n_wgchunks;
     const int wc = (blockIdx.x - rb * p.n_wgchunks) * kWavesPerBlock + wave;
@@ -134,16 +178,78 @@ __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
     const int n_pages_out = (p.out_cols + p.page - 1) / p.page;
     const int lp_begin = wc * p.ppw;
     const int lp_end = min(lp_begin + p.ppw, n_pages_out);
+    const bool has_work = wc < p.n_wchunks;
+    const int halves = p.page / 64;
+    const int slabs_per_page = halves * p.Hkv;
+    const int n_slabs = has_work ? (lp_end - lp_begin) * slabs_per_page : 0;
+    const int t_out = t0 + (g % RG);
+    const int koff = 256 * n + 16 * g;          // lane's byte offset in a slab's keys
+    const int soff = 4 * G * n;                 // and in its scale bytes
 
-    // metadata loads go out before the staging below: the row block's request, the
-    // lanes' row lengths and the block-table entries of the wave's pages (lane i holds
-    // page lp_begin + i; with one request the table row is known without the lookup)
+    // ---- the first segment's metadata and first key slabs go out before the query
+    // staging below, so their round trips overlap it.  Lane i of my_phys holds the
+    // physical page of page lp_begin + i (-1: invisible or invalid); with one request
+    // the block-table row is known without the request lookup.
     RowRequest rq = find_request(p.cu, p.B, t0);
     const int lens_pref = (g % RG) < nrows ? p.lens[t0 + (g % RG)] : 0;
-    const int b_first = p.B == 1 ? 0 : rq.b;
     int bt_pref = -1;
-    if (wc < p.n_wchunks && lane < lp_end - lp_begin && lp_begin + lane < p.W)
-        bt_pref = p.bt[(int64_t)b_first * p.bt_rs + lp_begin + lane];
+    {
+        const int b_first = p.B == 1 ? 0 : rq.b;
+        if (has_work && lane < lp_end - lp_begin && lp_begin + lane < p.W)
+            bt_pref = p.bt[(int64_t)b_first * p.bt_rs + lp_begin + lane];
+    }
+    int b = 0, seg_end = t0, len = 0, my_phys = -1;
+    bool req_ok = false, row_ok = false;
+    auto setup_segment = [&](int t_seg, bool first) {
+        if (!first) rq = find_request(p.cu, p.B, t_seg);
+        b = rq.b;
+        req_ok = rq.ok;
+        seg_end = req_ok ? min(rq.end, t_last + 1) : t_last + 1;
+        row_ok = t_out >= t_seg && t_out < seg_end;
+        len = (row_ok && req_ok) ? min(lens_pref, p.out_cols) : 0;
+        int max_len = len;
+        max_len = max(max_len, __shfl_xor(max_len, 16));
+        max_len = max(max_len, __shfl_xor(max_len, 32));
+        max_len = uniform(max_len);
+        my_phys = -1;
+        const int lp = lp_begin + lane;
+        if (has_work && req_ok && lane < lp_end - lp_begin && lp * p.page < max_len && lp < p.W) {
+            const int v = first ? bt_pref : p.bt[(int64_t)b * p.bt_rs + lp];
+            my_phys = (v >= 0 && v < p.num_pages) ? v : -1;
+        }
+    };
+    // slab s of this wave: page lp_begin + pi, half `half` of it, key head hk (fastest)
+    auto slab_pos = [&](int s, int& pi, int& half, int& hk) {
+        if (slabs_per_page == 1) {
+            pi = s, half = 0, hk = 0;
+        } else {
+            pi = s / slabs_per_page;
+            const int r = s - pi * slabs_per_page;
+            half = MKV ? r / p.Hkv : r;
+            hk = MKV ? r - half * p.Hkv : 0;
+        }
+    };
+    auto issue = [&](int s, Slab<FMT>& dst) {
+        int pi, half, hk;
+        slab_pos(s, pi, half, hk);
+        const int phys = __builtin_amdgcn_readlane(my_phys, pi & 63);
+        const bool ok = s < n_slabs && phys >= 0;
+        const int64_t tok = (int64_t)hk * p.page + half * 64;
+        const uint8_t* kb = ok ? p.k + (int64_t)phys * p.kp_s + tok * 64 : p.k;
+        const uint8_t* sb = ok ? p.ks + (int64_t)phys * p.ksp_s + tok * G : p.ks;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, ok ? 64u * 64u : 0u);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(sb, ok ? 64u * G : 0u);
+#pragma unroll
+        for (int tt = 0; tt < 4; tt++)
+            dst.k[tt] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * tt, 0, 0));
+#pragma unroll
+        for (int c = 0; c < (FMT == 0 ? 1 : 2); c++)
+            dst.s[c] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, soff + 16 * c, 0, 0));
+    };
+    Slab<FMT> b0, b1, b2;
+    setup_segment(t0, true);
+    issue(0, b0);
+    issue(1, b1);
 
     // ---- stage the row block's queries, scales and weights (zeros past T)
     for (int i = threadIdx.x; i < RG * H * 4; i += 256) {
@@ -161,21 +267,17 @@ __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
         sw[i] = r < nrows ? p.w[(int64_t)(t0 + r) * p.w_rs + h] : 0.0f;
     }
     __syncthreads();
-    if (wc >= p.n_wchunks) return;  // uniform per wave, after the only barrier
-
-    const int halves = p.page / 64;
-    const int slabs_per_page = halves * p.Hkv;
-    const int n_slabs = (lp_end - lp_begin) * slabs_per_page;
+    if (!has_work) return;  // uniform per wave, after the only barrier
 
     // The rows of a block may belong to different requests; each pass handles the rows
     // of one request (rows of a request are consecutive).
     int t_seg = t0;
     while (t_seg <= t_last) {
-        if (t_seg != t0) rq = find_request(p.cu, p.B, t_seg);
-        const int b = rq.b;
-        const bool req_ok = rq.ok;
-        const int seg_end = req_ok ? min(rq.end, t_last + 1) : t_last + 1;
-
+        if (t_seg != t0) {
+            setup_segment(t_seg, false);
+            issue(0, b0);
+            issue(1, b1);
+        }
         // ---- A operands and weights of this segment from LDS
         Operand<FMT> a[NT];
         float wv[NT][4];
@@ -206,90 +308,64 @@ __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
                 wv[j][i] = hv ? sw[to * H + hk * p.R + hlo] : 0.0f;
             }
         }
-        const int t_out = t0 + (g % RG);
-        const bool row_ok = t_out >= t_seg && t_out < seg_end;
-        const int len = (row_ok && req_ok) ? min(lens_pref, p.out_cols) : 0;
-        int max_len = len;
-        max_len = max(max_len, __shfl_xor(max_len, 16));
-        max_len = max(max_len, __shfl_xor(max_len, 32));
-        max_len = uniform(max_len);
-
-        // ---- block-table entries of the wave's pages: lane i holds page lp_begin + i
-        int my_phys = -1;
-        {
-            const int lp = lp_begin + lane;
-            if (req_ok && lane < lp_end - lp_begin && lp * p.page < max_len && lp < p.W) {
-                const int v = (t_seg == t0) ? bt_pref : p.bt[(int64_t)b * p.bt_rs + lp];
-                my_phys = (v >= 0 && v < p.num_pages) ? v : -1;
-            }
-        }
-
-        auto issue = [&](int s, RawTile* dst) {
-            const int pi = s / slabs_per_page;
-            const int r = s - pi * slabs_per_page;
-            const int half = r / p.Hkv, hk = r - half * p.Hkv;
-            const int phys = __builtin_amdgcn_readlane(my_phys, pi);
-            if (phys >= 0) {
+        // ---- the wave's slabs: three buffers in a ring keep two slabs of keys in flight
+        // while one is computed (slab s lives in buffer s % 3)
+        float acc[4][4];
 #pragma unroll
-                for (int tt = 0; tt < 4; tt++) {
-                    const int64_t tok = (int64_t)hk * p.page + half * 64 + tt * 16 + n;
-                    dst[tt].v = load16(p.k + (int64_t)phys * p.kp_s + tok * 64 + 16 * g);
-                    dst[tt].s = scale_bytes<FMT>(p.ks + (int64_t)phys * p.ksp_s + tok * G, g);
+        for (int tt = 0; tt < 4; tt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) acc[tt][i] = 0.0f;
+        auto compute = [&](int s, const Slab<FMT>& buf) {
+            int pi, half, hk;
+            slab_pos(s, pi, half, hk);
+#pragma unroll
+            for (int tt = 0; tt < 4; tt++) {
+                RawTile rt;
+                rt.v = buf.k[tt];
+                rt.s = slab_scale<FMT>(buf, tt, g);
+                const Operand<FMT> kb = decode<FMT>(rt);
+#pragma unroll
+                for (int j = 0; j < NT; j++) {
+                    if (MKV && j / p.tiles_per_kv != hk) continue;
+                    const v4f d = tile_dot<FMT>(a[j], kb);
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        acc[tt][i] = __builtin_fmaf(wv[j][i], fmaxf(d[i], 0.0f), acc[tt][i]);
                 }
             }
-        };
-
-        RawTile cur[4], nxt[4];
-        float acc[4][2][4];
-#pragma unroll
-        for (int tt = 0; tt < 4; tt++) {
-            cur[tt].v = nxt[tt].v = v4i{0, 0, 0, 0};
-            cur[tt].s = nxt[tt].s = 0u;
-#pragma unroll
-            for (int u = 0; u < 2; u++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) acc[tt][u][i] = 0.0f;
-        }
-        if (n_slabs > 0) issue(0, cur);
-        for (int s = 0; s < n_slabs; s++) {
-            if (s + 1 < n_slabs) issue(s + 1, nxt);
-            const int pi = s / slabs_per_page;
-            const int r = s - pi * slabs_per_page;
-            const int half = r / p.Hkv, hk = r - half * p.Hkv;
-            const int phys = __builtin_amdgcn_readlane(my_phys, pi);
-            if (phys >= 0) {
+            if (!MKV || hk == p.Hkv - 1) {  // all key heads of these 64 keys are in
+                const int phys = __builtin_amdgcn_readlane(my_phys, pi);
+                const int col0 = (lp_begin + pi) * p.page + half * 64 + 4 * n;
+                float o[4];
 #pragma unroll
                 for (int tt = 0; tt < 4; tt++) {
-                    const Operand<FMT> kb = decode<FMT>(cur[tt]);
+                    float v = (acc[tt][0] + acc[tt][1]) + (acc[tt][2] + acc[tt][3]);
+                    v = group_sum<RG>(v);
+                    o[tt] = (phys >= 0 && col0 + tt < len) ? v : -__builtin_inff();
 #pragma unroll
-                    for (int j = 0; j < NT; j++) {
-                        if (j >= p.n_tiles || j / p.tiles_per_kv != hk) continue;
-                        const v4f d = tile_dot<FMT>(a[j], kb);
+                    for (int i = 0; i < 4; i++) acc[tt][i] = 0.0f;
+                }
+                if (g < RG && row_ok) {
+                    float* dst = p.out + (int64_t)t_out * p.out_rs + col0;
+                    if (p.vec_out && col0 + 3 < p.out_cols) {
+                        *reinterpret_cast<v4f*>(dst) = v4f{o[0], o[1], o[2], o[3]};
+                    } else {
 #pragma unroll
-                        for (int i = 0; i < 4; i++)
-                            acc[tt][j & 1][i] = __builtin_fmaf(wv[j][i], fmaxf(d[i], 0.0f), acc[tt][j & 1][i]);
+                        for (int tt = 0; tt < 4; tt++)
+                            if (col0 + tt < p.out_cols) dst[tt] = o[tt];
                     }
                 }
             }
-            if (hk == p.Hkv - 1) {  // all key heads of these 64 keys are in: finish them
-                const int s_base = (lp_begin + pi) * p.page + half * 64;
-#pragma unroll
-                for (int tt = 0; tt < 4; tt++) {
-                    float v = ((acc[tt][0][0] + acc[tt][0][1]) + (acc[tt][0][2] + acc[tt][0][3])) +
-                              ((acc[tt][1][0] + acc[tt][1][1]) + (acc[tt][1][2] + acc[tt][1][3]));
-                    v = group_sum<RG>(v);
-                    const int col = s_base + tt * 16 + n;
-                    if (g < RG && row_ok && col < p.out_cols)
-                        p.out[(int64_t)t_out * p.out_rs + col] =
-                            (phys >= 0 && col < len) ? v : -__builtin_inff();
-#pragma unroll
-                    for (int u = 0; u < 2; u++)
-#pragma unroll
-                        for (int i = 0; i < 4; i++) acc[tt][u][i] = 0.0f;
-                }
-            }
-#pragma unroll
-            for (int tt = 0; tt < 4; tt++) cur[tt] = nxt[tt];
+        };
+        for (int s = 0; s < n_slabs; s += 3) {
+            issue(s + 2, b2);
+            compute(s, b0);
+            if (s + 1 >= n_slabs) break;
+            issue(s + 3, b0);
+            compute(s + 1, b1);
+            if (s + 2 >= n_slabs) break;
+            issue(s + 4, b1);
+            compute(s + 2, b2);
         }
         t_seg = seg_end;
     }
@@ -301,7 +377,12 @@ hipError_t launch3(const LogitsParams& p, hipStream_t stream) {
     if (blocks <= 0) return hipSuccess;
     const int G = FMT == 0 ? 4 : 8;
     const size_t lds = (size_t)RG * p.H * (64 + G + 4);
-    hipLaunchKernelGGL((k_logits<FMT, RG, NT>), dim3((unsigned)blocks), dim3(256), lds, stream, p);
+    if (p.Hkv == 1)
+        hipLaunchKernelGGL((k_logits<FMT, RG, NT, false>), dim3((unsigned)blocks), dim3(256), lds,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((k_logits<FMT, RG, NT, true>), dim3((unsigned)blocks), dim3(256), lds,
+                           stream, p);
     return hipGetLastError();
 }
 
@@ -342,9 +423,12 @@ hipError_t launch_logits(const LogitsParams& p_in, hipStream_t stream) {
     p.rows_per_block = rg;
     p.n_rowblocks = (p.T + rg - 1) / rg;
     const int n_pages_out = (p.out_cols + p.page - 1) / p.page;
-    // pages per wave: about 2048 busy waves (8 per CU), at most 64 pages each
+    // pages per wave: about FP4IDX_LOGITS_WAVES waves, at most 64 pages each.  Rows of
+    // different lengths leave the waves past a row's end with nothing but -inf to
+    // write, so the grid is cut finer than one pass of the chip: workgroups that end
+    // early free their slots for the rest.
     const int64_t total = (int64_t)p.n_rowblocks * n_pages_out;
-    int64_t ppw = (total + 2047) / 2048;
+    int64_t ppw = (total + FP4IDX_LOGITS_WAVES - 1) / FP4IDX_LOGITS_WAVES;
     ppw = ppw < 1 ? 1 : (ppw > 64 ? 64 : ppw);
     p.ppw = (int)ppw;
     p.n_wchunks = (n_pages_out + p.ppw - 1) / p.ppw;
