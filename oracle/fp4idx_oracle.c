@@ -137,7 +137,8 @@ int orc_dot(const double* q, const double* k, double* out, double* abs_sum) {
  * whatever the query holds ([SGL] Accuracy Tests: invisible positions stay -inf).  A
  * visible key whose page id is negative or >= num_pages, or whose logical page is past
  * the table width, is treated as invisible ([QSA] slot pass).  Query head h reads key
- * head h / (H / Hkv) ([M3] 数学语义).
+ * head h / (H / Hkv) ([M3] 数学语义).  max(x, 0) is C's fmax, so a NaN head dot adds 0
+ * (the pages say nothing about NaN; fmax is the plain C meaning of max).
  *
  * Layouts (element strides in bytes / elements as noted):
  *   q_fp4   [T][H][64]  bytes, row stride q_rs bytes between rows t (heads contiguous)
@@ -210,9 +211,9 @@ long orc_logits_paged(int fmt,
                 double dot, asum;
                 if (!orc_dot(qv + (size_t)h * 128, kv, &dot, &asum)) inexact++;
                 /* the exact dot rounded once to fp32 is the per-head logit; the weighted
-                 * sum uses the exact value */
-                double r = dot > 0.0 ? dot : 0.0;
-                if (isnan(dot)) r = dot;
+                 * sum uses the exact value.  ReLU is C's fmax(x, 0): a NaN dot (only a
+                 * NaN scale code makes one) counts as 0, the pages fix nothing else */
+                double r = fmax(dot, 0.0);
                 double term = (double)w[(int64_t)t * w_rs + h] * r;
                 acc += term;
                 tb += fabs(term);
@@ -237,7 +238,8 @@ long orc_logits_paged(int fmt,
  * offset[b] with offset[b] = qo_offset[b] if given else k_len[b] - q_len[b].  A block
  * with no valid key, or kb >= ceil(k_len[b]/128), is -inf.  Ktiles =
  * ceil(max_seqlen_k / 128).  A physical page id outside [0, num_pages) makes its keys
- * invalid (same reading as for the logits).
+ * invalid (same reading as for the logits).  The max is C's fmax, so a NaN dot (only a
+ * NaN scale code makes one) is skipped, as ReLU skips it in the logits.
  *
  * Layouts: q_fp4 [Tq][Hq][64], q_scale [Tq][Hq][G], k_fp4 [P][Hkv][128][64],
  * k_scale [P][Hkv][128][G], all contiguous; scores [Hq][Ktiles][Tq] float.
@@ -292,13 +294,13 @@ long orc_block_scores(int fmt,
                                         k_scale + (((int64_t)phys * Hkv + hk) * 128 + row) * G, kv);
                         double dot, asum;
                         if (!orc_dot(qv, kv, &dot, &asum)) inexact++;
-                        if (!any || dot > best || isnan(dot)) best = dot;
+                        best = fmax(best, dot);   /* a NaN dot is skipped, as in ReLU */
                         if (asum > ebest) ebest = asum;
                         any = 1;
                     }
                 }
                 int64_t o = ((int64_t)hq * ktiles + kb) * Tq + qg;
-                scores[o] = any ? (float)best : -INFINITY;
+                scores[o] = any ? (float)best : -INFINITY;   /* -inf if only NaN dots */
                 if (errbase) errbase[o] = (float)ebest;
             }
         }

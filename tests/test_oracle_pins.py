@@ -271,11 +271,18 @@ def test_page_permutation_does_not_change_logits():
 
 def test_invisible_positions_stay_neg_inf_with_nan_queries():
     case = _small_logits(seed=5, fmt=wl.NVFP4, ctx=(100, 40), q_per_req=(1, 1))
+    ref, _, _ = _run(case)
     case.q_scale[0, 1, 3] = 0x7F  # NaN scale for one head of row 0
     out, _, _ = _run(case)
-    assert np.all(np.isnan(out[0, :100]))
     assert np.all(out[0, 100:] == -np.inf)
     assert np.all(np.isfinite(out[1, :40])) and np.all(out[1, 40:] == -np.inf)
+    # ReLU is fmax(x, 0): the NaN head adds 0, so row 0 equals the same row with head 1's
+    # weight set to 0 (dot products are exact, so this holds to the last bit)
+    case.q_scale[0, 1, 3] = case.q_scale[0, 1, 2]
+    case.w[0, 1] = 0.0
+    zeroed, _, _ = _run(case)
+    np.testing.assert_array_equal(out[0], zeroed[0])
+    assert not np.array_equal(out[0, :100], ref[0, :100])
 
 
 def test_invalid_page_ids_are_invisible():
