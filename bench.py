@@ -11,8 +11,9 @@ Timing: inputs are resident in HBM before the timed region.  Steps rotate over e
 independent input/output sets that their total (> 512 MiB) exceeds the 256 MiB
 Infinity Cache, so every step reads its keys from HBM.  The K timed steps are
 replayed from HIP graphs (as the pages' bench replays CUDA graphs), bracketed by
-device synchronisation.  Kernel durations for the roofline are measured separately
-with HIP events around single launches on the launch stream.
+device synchronisation.  Kernel durations for the roofline are measured separately:
+a graph of back-to-back launches of one kernel, replayed between HIP events recorded
+on its own stream.
 
 Prints one JSON line.  `--gpus N` with N > 1 is refused: this path runs on one GPU.
 """
@@ -31,8 +32,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD public spec
-KERNEL_SOURCES = {"logits": "sparse_attention_fp4_amd/csrc/logits.hip",
-                  "topk": "sparse_attention_fp4_amd/csrc/topk.hip"}
+CSRC = "sparse_attention_fp4_amd/csrc/"
+COMMON_SOURCES = [CSRC + "device_common.hpp", CSRC + "fp4idx_internal.hpp", CSRC + "fp4idx_api.hip"]
+KERNEL_SOURCES = {"logits": [CSRC + "logits.hip"] + COMMON_SOURCES,
+                  "topk": [CSRC + "topk.hip", CSRC + "topk_long.hip"] + COMMON_SOURCES}
 
 
 def parse():
@@ -46,27 +49,39 @@ def parse():
                          "requests x 1 row, H=64, contexts 4096..131072")
     ap.add_argument("--topk", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel-launches", type=int, default=256,
-                    help="single launches timed per kernel for the roofline")
+    ap.add_argument("--kernel-launches", type=int, default=64,
+                    help="launches per timed graph replay, per kernel, for the roofline")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="also run one plain fp32 copy of this many MiB (read N, write N) so "
+                         "that a counter profile of this run can scale HBM byte counters")
     return ap.parse_args()
 
 
-def source_hash(rel: str) -> str:
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for rel in files:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None if
-    there is none or the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    """HBM bytes per call from the committed rocprofv3 counter summary
+    (profiles/<workload>.md: FETCH_SIZE and WRITE_SIZE scaled by a plain copy), or None
+    if there is none or the kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}.md")
     if not os.path.exists(path):
         return None
+    rec = {}
     with open(path) as f:
-        rec = json.load(f)
+        for line in f:
+            key, sep, val = line.strip().partition(": ")
+            if sep and key.startswith(kernel + "_"):
+                rec[key[len(kernel) + 1:]] = val.strip()
     if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    v = rec.get("hbm_bytes_per_launch")
+    return int(v) if v is not None else None
 
 
 def main():
@@ -183,25 +198,42 @@ def main():
     torch.cuda.synchronize()
     warm_ms = (time.perf_counter() - t1) * 1e3 / 200
 
-    # ---- per-kernel durations: HIP events around single launches on the launch stream
+    # ---- per-kernel durations: a hipGraph of `kernel_launches` launches of one kernel
+    # (cycling over the input sets, so reads stay cache-cold), replayed between two HIP
+    # events recorded on the stream the graph runs on; duration = elapsed / launches.
     def time_kernel(fn):
-        cur = torch.cuda.current_stream()
-        durs = []
-        for i in range(args.kernel_launches):
-            s = sets[i % n_sets]
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(cur)
-            fn(s)
-            e1.record(cur)
-            durs.append((e0, e1))
+        L = args.kernel_launches
+        gk = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(gk, stream=stream):
+                for i in range(L):
+                    fn(sets[i % n_sets])
         torch.cuda.synchronize()
-        us = [a.elapsed_time(b) * 1e3 for a, b in durs]
+        per = []
+        with torch.cuda.stream(stream):
+            gk.replay()                                  # untimed
+            for _ in range(5):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                gk.replay()
+                e1.record(stream)
+                per.append((e0, e1))
+        torch.cuda.synchronize()
+        us = [a.elapsed_time(b) * 1e3 / L for a, b in per]
         return float(np.mean(us)), float(np.median(us))
 
     for s in sets[:4]:
         step(s)
     torch.cuda.synchronize()
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib << 18                   # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)                               # reads N MiB, writes N MiB
+        torch.cuda.synchronize()
+        del src, dst
     logits_us, logits_med = time_kernel(logits)
     topk_us, topk_med = time_kernel(topk)
 

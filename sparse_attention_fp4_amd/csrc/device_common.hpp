@@ -88,7 +88,8 @@ __device__ __forceinline__ v4i load16(const uint8_t* p) {
 // NVFP4 E4M3 scale code -> (power-of-two factor 2^a as fp32, integer factor b) with
 // value = 2^a * b exactly: a normal code (exponent field e > 0, mantissa m) is
 // 2^(e-10) * (8 + m); a subnormal code is 2^-9 * m.  The sign goes into b.
-// NaN codes (0x7F, 0xFF) give a NaN power factor.
+// NaN codes (0x7F, 0xFF) give a NaN integer factor, so every value they scale (zeros
+// included) decodes to NaN.
 __device__ __forceinline__ void e4m3_split(uint32_t code, float& pow2, float& b) {
     uint32_t e = (code >> 3) & 15u, m = code & 7u;
     int a = e ? (int)e - 10 : -9;
@@ -96,7 +97,7 @@ __device__ __forceinline__ void e4m3_split(uint32_t code, float& pow2, float& b)
     b = (code & 0x80u) ? -mag : mag;
     // 2^a built in the exponent field (a in [-10, 5])
     pow2 = __uint_as_float((uint32_t)(a + 127) << 23);
-    if ((code & 0x7Fu) == 0x7Fu) pow2 = __builtin_nanf("");
+    if ((code & 0x7Fu) == 0x7Fu) b = __builtin_nanf("");
 }
 
 // The eight E2M1 values of one dword (bytes 0..3, low nibble first) times 2^a * b, as fp16.

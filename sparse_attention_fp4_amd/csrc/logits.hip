@@ -44,7 +44,7 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 #ifndef FP4IDX_LOGITS_WAVES
-#define FP4IDX_LOGITS_WAVES 8192   // target number of waves of one launch
+#define FP4IDX_LOGITS_WAVES 2048   // target number of waves of one launch
 #endif
 
 // ---------------------------------------------------------------- operand types

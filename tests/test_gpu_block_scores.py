@@ -17,11 +17,13 @@ from .gpu_helpers import gpu_block_scores, oracle_block_scores, say
 pytestmark = pytest.mark.gpu
 
 
-def _check(case, rows=None, exact=False):
-    """exact=True: at least 99% of the visible block maxima are bit-exact."""
+def _check(case, rows=None, exact=False, nan_codes=False):
+    """exact=True: at least 99% of the visible block maxima are bit-exact.
+    nan_codes=True: the case holds NaN scale codes, whose dots the oracle cannot call
+    exact (they are NaN and skipped by the max)."""
     got = gpu_block_scores(case)
     ref, eb, inexact = oracle_block_scores(case, rows=rows)
-    assert inexact == 0
+    assert nan_codes or inexact == 0
     cols = np.arange(case.Tq) if rows is None else np.asarray(rows)
     g, r, e = got[:, :, cols], ref[:, :, cols], eb[:, :, cols]
     inv = r == -np.inf
@@ -68,6 +70,18 @@ def test_ktiles_wider_than_batch_and_bad_pages():
     case.max_seqlen_k = 1000          # more output blocks than any batch item fills
     case.kv_indices[1] = -1           # batch 0, block 1 has no page
     _check(case, exact=True)
+
+
+def test_nvfp4_nan_scale_codes_are_skipped_by_the_max():
+    """A NaN E4M3 code makes every dot it touches NaN; max is C's fmax on both sides, so
+    those dots are skipped (a query head whose dots are all NaN gives -inf blocks)."""
+    case = wl.make_block("nv_nan", fmt=wl.NVFP4, q_lens=[6, 3], k_lens=[300, 129], Hq=4, Hkv=2,
+                         seed=77, causal=False)
+    case.q_scale[2, 1, 3] = 0x7F               # query row 2, head 1: all its dots NaN
+    case.q_scale[7, 3, 0] = 0xFF               # query row 7 (batch 1), head 3
+    p0 = int(case.kv_indices[case.cu_page_offsets[0]])
+    case.k_scale[p0, 0, 5, 2] = 0x7F            # one key of batch 0, key head 0
+    _check(case, nan_codes=True)
 
 
 def test_config3_nvfp4_prefill_sampled_queries():

@@ -112,6 +112,9 @@ def test_nonfinite_queries_leave_invisible_positions_neg_inf():
     assert np.all(got[2, :] == -np.inf)
     assert np.all(got[3, 1:] == -np.inf)
     assert np.all(np.isfinite(got[0, :500])) and np.all(got[0, 500:] == -np.inf)
+    # visible positions too: a NaN head dot counts as 0 in fmax(x, 0) on both sides
+    ref, tb, _ = oracle_logits(case)
+    check_logits(got, ref, tb)
 
 
 def test_noncontiguous_query_rows_and_combined_pages():
