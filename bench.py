@@ -1,19 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of the FP4 paged indexer hot path on one MI355X.
 
-A step is one pass of the decode path over one batch of synthetic input: weighted-ReLU
-logits for 4 verify rows of one request at context 100,000 (H=32, D=128, MXFP4 keys on
-shuffled 64-token pages), then the top-2048 columns of each row.  This is the
-configuration the pages time ("[DSv4.1] Speed up the FP4 indexer scorer...", Speed
-Tests: 4 verify rows, 32 heads, contexts 16,384 / 100,000 / 400,000).
+A step is one pass of the hot path over one batch of synthetic input.  The default
+workload is the headline: weighted-ReLU logits for 4 verify rows of one request at
+context 100,000 (H=32, D=128, MXFP4 keys on shuffled 64-token pages), then the
+top-2048 columns of each row -- the configuration the pages time ("[DSv4.1] Speed up
+the FP4 indexer scorer...", Speed Tests: 4 verify rows, 32 heads, contexts 16,384 /
+100,000 / 400,000).  Other workloads (--workload):
+  batched  64 requests x 1 row, H=64, contexts U[4096, 131072], logits + top-2048;
+  prefill  one request, 32768 causal query rows x 32768 keys, H=64, logits + top-2048;
+  block    NVFP4 per-head 128-token block maxima, varlen batch of 8, Hq=32, Hkv=4,
+           causal ("M3 FP4 Indexer" README shapes).
 
 Timing: inputs are resident in HBM before the timed region.  Steps rotate over enough
 independent input/output sets that their total (> 512 MiB) exceeds the 256 MiB
 Infinity Cache, so every step reads its keys from HBM.  The K timed steps are
 replayed from HIP graphs (as the pages' bench replays CUDA graphs), bracketed by
 device synchronisation.  Kernel durations for the roofline are measured separately:
-a graph of back-to-back launches of one kernel, replayed between HIP events recorded
-on its own stream.
+a graph of back-to-back launches of one entry point, replayed between HIP events
+recorded on its own stream.
 
 Prints one JSON line.  `--gpus N` with N > 1 is refused: this path runs on one GPU.
 """
@@ -31,26 +36,29 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD public spec
+# MI355X published peaks (AMD specification)
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"fp4": 10100.0, "fp16": 2500.0}
+
 CSRC = "sparse_attention_fp4_amd/csrc/"
 COMMON_SOURCES = [CSRC + "device_common.hpp", CSRC + "fp4idx_internal.hpp", CSRC + "fp4idx_api.hip"]
 KERNEL_SOURCES = {"logits": [CSRC + "logits.hip"] + COMMON_SOURCES,
-                  "topk": [CSRC + "topk.hip", CSRC + "topk_long.hip"] + COMMON_SOURCES}
+                  "topk": [CSRC + "topk.hip", CSRC + "topk_long.hip"] + COMMON_SOURCES,
+                  "block_scores": [CSRC + "block_scores.hip"] + COMMON_SOURCES}
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=640)
-    ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--ctx", type=int, default=100_000)
-    ap.add_argument("--workload", choices=["verify", "batched"], default="verify",
-                    help="verify: 4 rows of one request at --ctx (the headline); batched: 64 "
-                         "requests x 1 row, H=64, contexts 4096..131072")
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default per workload)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default per workload)")
+    ap.add_argument("--ctx", type=int, default=100_000, help="context of the verify workload")
+    ap.add_argument("--workload", choices=["verify", "batched", "prefill", "block"],
+                    default="verify")
     ap.add_argument("--topk", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel-launches", type=int, default=64,
-                    help="launches per timed graph replay, per kernel, for the roofline")
+    ap.add_argument("--kernel-launches", type=int, default=None,
+                    help="launches per timed graph replay, per entry point, for the roofline")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one plain fp32 copy of this many MiB (read N, write N) so "
                          "that a counter profile of this run can scale HBM byte counters")
@@ -84,6 +92,178 @@ def load_traffic(kernel: str, workload: str):
     return int(v) if v is not None else None
 
 
+def _timed_oracle(run, sub_pairs):
+    """Run the oracle sample until about 10 s of wall time (at most 8 runs)."""
+    reps, total = 0, 0.0
+    while reps < 8 and total < 10.0:
+        tc = time.perf_counter()
+        run()
+        total += time.perf_counter() - tc
+        reps += 1
+    return sub_pairs * reps / total, reps, total
+
+
+def logits_workload(args, torch, fp4, wl, dev):
+    k = args.topk
+    if args.workload == "verify":
+        case = wl.config1(args.ctx)
+        name = f"decode_ctx{args.ctx}_h32"
+        desc = (f"{name}: 1 request, 4 verify rows seeing ctx-0..3 keys, H=32, D=128, "
+                f"MXFP4, page 64 shuffled, logits + top-{k}")
+        steps, warmup, launches = 640, 64, 64
+    elif args.workload == "batched":
+        case = wl.config2()
+        name = "batched_decode_b64_h64"
+        desc = (f"{name}: 64 requests x 1 row, H=64, D=128, contexts U[4096,131072], MXFP4 "
+                f"E8M0 120..134, page 64 shuffled, logits [64,131072] + top-{k}")
+        steps, warmup, launches = 64, 8, 16
+    else:
+        case = wl.config4()
+        name = "prefill_causal_32768_h64"
+        desc = (f"{name}: 1 request, 32768 query rows x 32768 keys, row t sees t+1 keys, H=64, "
+                f"D=128, MXFP4, page 64 shuffled, logits [32768,32768] + top-{k}")
+        steps, warmup, launches = 8, 2, 4
+    T, H = case.T, case.H
+    out_cols = case.out_cols
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    base = dict(q=up(case.q_fp4), qs=up(case.q_scale), w=up(case.w), k=up(case.k_fp4),
+                ks=up(case.k_scale), bt=up(case.block_table), cu=up(case.cu_seqlens_q),
+                lens=up(case.row_lens))
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + T * out_cols * 4
+
+    def make_set():
+        s = {n: (t if n in ("cu", "lens", "bt") else t.clone()) for n, t in base.items()}
+        s["out"] = torch.empty((T, out_cols), dtype=torch.float32, device=dev)
+        s["idx"] = torch.empty((T, k), dtype=torch.int32, device=dev)
+        s["val"] = torch.empty((T, k), dtype=torch.float32, device=dev)
+        return s
+
+    ws_bytes = fp4.topk_workspace_bytes(T, out_cols, k)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def logits(s):
+        fp4.logits_paged(s["q"], s["qs"], s["w"], s["k"], s["ks"], s["bt"], s["cu"], s["lens"],
+                         fmt="mxfp4", out_cols=out_cols, out=s["out"])
+
+    def topk(s):
+        fp4.topk(s["out"], k, s["lens"], out_idx=s["idx"], out_vals=s["val"], workspace=ws)
+
+    # algorithmic work: each input once, each output once; flops over visible pairs
+    keys = case.unique_keys()
+    pages = -(-keys // case.page_size)
+    pairs = case.visible_pairs()
+    logits_bytes = (keys * 68                        # packed nibbles + E8M0 scales
+                    + T * H * 68 + T * H * 4         # queries, scales, weights
+                    + pages * 4 + (T + 2) * 4        # block table, lengths, cu_seqlens
+                    + T * out_cols * 4)              # logits out
+    topk_bytes = pairs * 4 + T * 4 + T * k * 8
+    work = {
+        "logits": dict(bytes=logits_bytes, flops=2 * H * 128 * pairs,
+                       bound="mfma" if args.workload == "prefill" else "hbm", dtype="fp4"),
+        "topk": dict(bytes=topk_bytes, flops=0, bound="hbm", dtype=None),
+    }
+
+    def cpu_baseline():
+        from oracle import oracle as orc
+        if args.workload == "verify":
+            rows = list(range(T))
+            what = f"one full step (all {T} rows x {out_cols} columns, then top-{k})"
+        elif args.workload == "batched":
+            rows = list(range(8))
+            what = f"logits + top-{k} of 8 of the 64 rows"
+        else:
+            rows = [8191, 16383, 24575, 32767]
+            what = f"logits + top-{k} of 4 rows (t = 8191, 16383, 24575, 32767)"
+        threads = min(len(rows), orc.max_threads())
+        lens = case.row_lens[rows]
+        sub_pairs = int(np.minimum(lens, out_cols).sum())
+
+        def run():
+            ref, _, _ = orc.logits_paged(case.fmt, case.q_fp4, case.q_scale, case.w, case.k_fp4,
+                                         case.k_scale, case.block_table, case.cu_seqlens_q,
+                                         case.row_lens, case.page_size, out_cols, rows=rows,
+                                         n_threads=threads, compact=True)
+            orc.topk(ref, k, lens, n_threads=threads)
+
+        v, reps, total = _timed_oracle(run, sub_pairs)
+        return dict(value=round(v, 1), unit="keys/s", cores=threads, kind="oracle",
+                    sample=f"{what}, {reps} run(s) in {total:.1f} s")
+
+    return dict(name=name, desc=desc, set_bytes=set_bytes, make_set=make_set,
+                calls={"logits": logits, "topk": topk}, work=work, pairs=pairs,
+                steps=steps, warmup=warmup, launches=launches, cpu_baseline=cpu_baseline,
+                config={"ctx": args.ctx if args.workload == "verify" else
+                        ("4096..131072" if args.workload == "batched" else 32768),
+                        "rows": T, "heads": H, "topk": k},
+                dtype="mxfp4 (e2m1 x e8m0, fp32 accumulate)")
+
+
+def block_workload(args, torch, fp4, wl, dev):
+    case = wl.config3()
+    name = "nvfp4_block_prefill_b8"
+    desc = (f"{name}: NVFP4 per-head 128-token block maxima, B=8, q_len U[128,2048], "
+            f"k_len = q_len + U[0,8192], Hq=32, Hkv=4, D=128, causal, 128-token pages shuffled")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    base = dict(q=up(case.q_fp4), qs=up(case.q_scale), k=up(case.k_fp4), ks=up(case.k_scale),
+                cuq=up(case.cu_seqlens_q), cuk=up(case.cu_seqlens_k),
+                cup=up(case.cu_page_offsets), kvi=up(case.kv_indices))
+    out_elems = case.Hq * case.ktiles * case.Tq
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + out_elems * 4
+
+    def make_set():
+        s = {n: (t if n in ("cuq", "cuk", "cup", "kvi") else t.clone()) for n, t in base.items()}
+        s["out"] = torch.empty((case.Hq, case.ktiles, case.Tq), dtype=torch.float32, device=dev)
+        return s
+
+    def blocks(s):
+        fp4.block_scores(s["q"], s["k"], s["qs"], s["ks"], s["cuq"], s["cuk"], s["cup"],
+                         max_seqlen_q=case.max_seqlen_q, max_seqlen_k=case.max_seqlen_k,
+                         kv_indices=s["kvi"], fmt="nvfp4", causal=True, out=s["out"])
+
+    pairs = case.visible_pairs()
+    keys = int(case.cu_seqlens_k[-1])
+    bytes_ = (keys * case.Hkv * 72 + case.Tq * case.Hq * 72 + out_elems * 4
+              + int(case.cu_page_offsets[-1]) * 4 + 3 * (case.B + 1) * 4)
+    work = {"block_scores": dict(bytes=bytes_, flops=2 * case.Hq * 128 * pairs, bound="mfma",
+                                 dtype="fp16")}
+
+    def cpu_baseline():
+        from oracle import oracle as orc
+        rng = np.random.default_rng(7)
+        rows = sorted(rng.choice(case.Tq, 32, replace=False).tolist())
+        threads = min(len(rows), orc.max_threads())
+        sub = 0                                # visible (query, key) pairs of the sample
+        for q in rows:
+            b = int(np.searchsorted(case.cu_seqlens_q, q, side="right") - 1)
+            ql = int(case.cu_seqlens_q[b + 1] - case.cu_seqlens_q[b])
+            kl = int(case.cu_seqlens_k[b + 1] - case.cu_seqlens_k[b])
+            sub += int(np.clip(q - int(case.cu_seqlens_q[b]) + kl - ql + 1, 0, kl))
+
+        def run():
+            orc.block_scores(case.fmt, case.q_fp4, case.q_scale, case.k_fp4, case.k_scale,
+                             case.cu_seqlens_q, case.cu_seqlens_k, case.cu_page_offsets,
+                             case.kv_indices, case.qo_offset, case.max_seqlen_k, case.causal,
+                             rows=rows, n_threads=threads)
+
+        v, reps, total = _timed_oracle(run, sub)
+        return dict(value=round(v, 1), unit="keys/s", cores=threads, kind="oracle",
+                    sample=f"block scores of 32 sampled query tokens (all 32 heads), {reps} "
+                           f"run(s) in {total:.1f} s")
+
+    return dict(name=name, desc=desc, set_bytes=set_bytes, make_set=make_set,
+                calls={"block_scores": blocks}, work=work, pairs=pairs, steps=64, warmup=8,
+                launches=16, cpu_baseline=cpu_baseline,
+                config={"rows": case.Tq, "heads": case.Hq, "kv_heads": case.Hkv,
+                        "ktiles": case.ktiles},
+                dtype="nvfp4 (e2m1 x e4m3, exact fp16 operands, fp32 accumulate)")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -100,52 +280,24 @@ def main():
     assert torch.cuda.is_available(), "no GPU visible"
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    if args.workload == "verify":
-        case = wl.config1(args.ctx)
-        workload = f"decode_ctx{args.ctx}_h32"
-        desc = (f"{workload}: 1 request, 4 verify rows seeing ctx-0..3 keys, H=32, D=128, "
-                f"MXFP4, page 64 shuffled, logits + top-{args.topk}")
-    else:
-        case = wl.config2()
-        workload = "batched_decode_b64_h64"
-        desc = (f"{workload}: 64 requests x 1 row, H=64, D=128, contexts U[4096,131072], MXFP4 "
-                f"E8M0 120..134, page 64 shuffled, logits [64,131072] + top-{args.topk}")
-    T, H, k = case.T, case.H, args.topk
-    out_cols = case.out_cols
+    make = block_workload if args.workload == "block" else logits_workload
+    W = make(args, torch, fp4, wl, dev)
+    steps = args.steps if args.steps is not None else W["steps"]
+    warmup = args.warmup if args.warmup is not None else W["warmup"]
+    launches = args.kernel_launches if args.kernel_launches is not None else W["launches"]
 
-    def up(a):
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    base = dict(q=up(case.q_fp4), qs=up(case.q_scale), w=up(case.w), k=up(case.k_fp4),
-                ks=up(case.k_scale), bt=up(case.block_table), cu=up(case.cu_seqlens_q),
-                lens=up(case.row_lens))
-    set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + T * out_cols * 4
-    n_sets = int(min(256, max(2, -(-(512 << 20) // set_bytes))))
-    if args.steps % n_sets and args.steps < n_sets:
-        n_sets = max(2, args.steps)
-    sets = []
-    for i in range(n_sets):
-        s = {n: (t if n in ("cu", "lens", "bt") else t.clone()) for n, t in base.items()}
-        s["out"] = torch.empty((T, out_cols), dtype=torch.float32, device=dev)
-        s["idx"] = torch.empty((T, k), dtype=torch.int32, device=dev)
-        s["val"] = torch.empty((T, k), dtype=torch.float32, device=dev)
-        sets.append(s)
-    ws_bytes = fp4.topk_workspace_bytes(T, out_cols, k)
-    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-
-    def logits(s):
-        fp4.logits_paged(s["q"], s["qs"], s["w"], s["k"], s["ks"], s["bt"], s["cu"], s["lens"],
-                         fmt="mxfp4", out_cols=out_cols, out=s["out"])
-
-    def topk(s):
-        fp4.topk(s["out"], k, s["lens"], out_idx=s["idx"], out_vals=s["val"], workspace=ws)
+    n_sets = int(min(256, max(2, -(-(512 << 20) // W["set_bytes"]))))
+    if steps % n_sets and steps < n_sets:
+        n_sets = max(2, steps)
+    sets = [W["make_set"]() for _ in range(n_sets)]
+    calls = W["calls"]
 
     def step(s):
-        logits(s)
-        topk(s)
+        for fn in calls.values():
+            fn(s)
 
     # ---- warmup (eager)
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(sets[i % n_sets])
     torch.cuda.synchronize()
 
@@ -154,7 +306,7 @@ def main():
     stream.wait_stream(torch.cuda.current_stream())
     graphs = []
     with torch.cuda.stream(stream):
-        for count in (n_sets, args.steps % n_sets):
+        for count in (n_sets, steps % n_sets):
             if count == 0:
                 graphs.append(None)
                 continue
@@ -171,8 +323,8 @@ def main():
             g.replay()
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly args.steps steps
-    reps = args.steps // n_sets
+    # ---- timed region: exactly `steps` steps
+    reps = steps // n_sets
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(reps):
@@ -181,32 +333,31 @@ def main():
         rem.replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step = elapsed * 1e3 / steps
 
-    # ---- warm-cache reference: the same set every step (eager graph of 20 calls)
+    # ---- warm-cache reference: the same set every step (graph of 4 steps, 3 replays)
     gw = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
         with torch.cuda.graph(gw, stream=stream):
-            for _ in range(20):
+            for _ in range(4):
                 step(sets[0])
     torch.cuda.synchronize()
     gw.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for _ in range(10):
+    for _ in range(3):
         gw.replay()
     torch.cuda.synchronize()
-    warm_ms = (time.perf_counter() - t1) * 1e3 / 200
+    warm_ms = (time.perf_counter() - t1) * 1e3 / 12
 
-    # ---- per-kernel durations: a hipGraph of `kernel_launches` launches of one kernel
-    # (cycling over the input sets, so reads stay cache-cold), replayed between two HIP
-    # events recorded on the stream the graph runs on; duration = elapsed / launches.
-    def time_kernel(fn):
-        L = args.kernel_launches
+    # ---- per-entry-point durations: a hipGraph of `launches` launches (cycling over
+    # the input sets, so reads stay cache-cold), replayed between two HIP events
+    # recorded on the stream the graph runs on; duration = elapsed / launches.
+    def time_calls(fn):
         gk = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
             with torch.cuda.graph(gk, stream=stream):
-                for i in range(L):
+                for i in range(launches):
                     fn(sets[i % n_sets])
         torch.cuda.synchronize()
         per = []
@@ -220,12 +371,8 @@ def main():
                 e1.record(stream)
                 per.append((e0, e1))
         torch.cuda.synchronize()
-        us = [a.elapsed_time(b) * 1e3 / L for a, b in per]
-        return float(np.mean(us)), float(np.median(us))
+        return float(np.mean([a.elapsed_time(b) * 1e3 / launches for a, b in per]))
 
-    for s in sets[:4]:
-        step(s)
-    torch.cuda.synchronize()
     if args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib << 18                   # fp32 elements
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -234,72 +381,53 @@ def main():
         torch.neg(src, out=dst)                               # reads N MiB, writes N MiB
         torch.cuda.synchronize()
         del src, dst
-    logits_us, logits_med = time_kernel(logits)
-    topk_us, topk_med = time_kernel(topk)
+    kern = {name: dict(W["work"][name], us=time_calls(fn)) for name, fn in calls.items()}
 
-    # ---- algorithmic bytes (each input once, each output once)
-    keys = case.unique_keys()                        # distinct keys read
-    G = 4
-    pages = -(-keys // case.page_size)
-    logits_bytes = (keys * (64 + G)                  # packed nibbles + E8M0 scales
-                    + T * H * (64 + G) + T * H * 4   # queries, scales, weights
-                    + pages * 4 + (T + 2) * 4        # block table, lengths, cu_seqlens
-                    + T * out_cols * 4)              # logits out
-    topk_bytes = int(np.minimum(case.row_lens, out_cols).sum()) * 4 + T * 4 + T * k * 8
-    pairs = case.visible_pairs()
-    kern = {
-        "logits": dict(us=logits_us, us_median=logits_med, bytes=logits_bytes),
-        "topk": dict(us=topk_us, us_median=topk_med, bytes=topk_bytes),
-    }
+    # ---- roofline of the entry point that takes the most time
     dom = max(kern, key=lambda n: kern[n]["us"])
     d = kern[dom]
-    achieved = d["bytes"] / (d["us"] * 1e-6) / 1e9
-    traffic = load_traffic(dom, workload)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": dom,
-                "algorithmic_bytes_per_launch": d["bytes"], "avg_launch_us": round(d["us"], 3)}
+    if d["bound"] == "mfma":
+        achieved = d["flops"] / (d["us"] * 1e-6) / 1e12
+        peak, unit = MFMA_PEAK_TFLOPS[d["dtype"]], "TFLOP/s"
+    else:
+        achieved = d["bytes"] / (d["us"] * 1e-6) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+    roofline = {"bound": d["bound"], "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": load_traffic(dom, W["name"]),
+                "kernel": dom, "algorithmic_bytes_per_launch": d["bytes"],
+                "algorithmic_flops_per_launch": d["flops"], "avg_launch_us": round(d["us"], 3)}
 
+    us = {n: round(kv["us"], 3) for n, kv in kern.items()}
+    us["step_cold"] = round(ms_per_step * 1e3, 3)
+    us["step_warm_same_buffers"] = round(warm_ms * 1e3, 3)
+    for name, kv in kern.items():
+        us[name + "_GBps"] = round(kv["bytes"] / (kv["us"] * 1e-6) / 1e9, 1)
+        if kv["flops"]:
+            us[name + "_TFLOPs"] = round(kv["flops"] / (kv["us"] * 1e-6) / 1e12, 1)
+    config = {"workload": W["desc"]}
+    config.update(W["config"])
+    config.update(input_sets_rotated=n_sets, timing="hipGraph replay, cache-cold rotation")
     result = {
         "metric": "keys scored/sec + us/call (FP4 paged indexer) at 100k ctx; % HBM roofline",
-        "value": round(pairs / (ms_per_step * 1e-3), 1),
+        "value": round(W["pairs"] / (ms_per_step * 1e-3), 1),
         "unit": "keys/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4 (e2m1 x e8m0, fp32 accumulate)",
+        "dtype": W["dtype"],
         "data": "synthetic (seeded codes with the pages' distributions)",
-        "config": {"workload": desc,
-                   "ctx": args.ctx if args.workload == "verify" else "4096..131072",
-                   "rows": T, "heads": H, "topk": k,
-                   "input_sets_rotated": n_sets, "timing": "hipGraph replay, cache-cold rotation"},
-        "us_per_call": {"logits": round(logits_us, 3), "topk": round(topk_us, 3),
-                        "step_cold": round(ms_per_step * 1e3, 3),
-                        "step_warm_same_buffers": round(warm_ms * 1e3, 3)},
+        "config": config,
+        "us_per_call": us,
         "roofline": roofline,
         "context": {"pages_sm120_logits_us_at_100k": 59.9,
                     "note": "the pages' SGLang scorer on RTX PRO 6000 (SM120), logits only"},
     }
-    for name, kv in kern.items():
-        result["us_per_call"][name + "_GBps"] = round(kv["bytes"] / (kv["us"] * 1e-6) / 1e9, 1)
-
     if not args.no_cpu_baseline:
-        from oracle import oracle as orc
-        threads = min(T, orc.max_threads())
-        tc = time.perf_counter()
-        ref, _, _ = orc.logits_paged(case.fmt, case.q_fp4, case.q_scale, case.w, case.k_fp4,
-                                     case.k_scale, case.block_table, case.cu_seqlens_q,
-                                     case.row_lens, case.page_size, out_cols, n_threads=threads)
-        orc.topk(ref, k, case.row_lens, n_threads=threads)
-        cpu_s = time.perf_counter() - tc
-        result["cpu_baseline"] = {
-            "value": round(pairs / cpu_s, 1), "unit": "keys/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full step (logits for all {T} rows x {out_cols} columns, then top-{k}), "
-                      f"{cpu_s:.1f} s"}
+        result["cpu_baseline"] = W["cpu_baseline"]()
     print(json.dumps(result), flush=True)
 
 

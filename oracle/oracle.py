@@ -111,9 +111,24 @@ def dot(q: np.ndarray, k: np.ndarray):
 
 def logits_paged(fmt, q_fp4, q_scale, w, k_fp4, k_scale, block_table, cu_seqlens_q, row_lens,
                  page_size, out_cols, num_pages=None, rows=None, n_threads=0,
-                 want_tolbase=False):
+                 want_tolbase=False, compact=False):
     """Weighted-ReLU logits.  Returns (logits [T,out_cols] float32 (only requested rows
-    filled; others NaN), tolbase or None, number of inexact dots)."""
+    filled; others NaN), tolbase or None, number of inexact dots).
+
+    compact=True (with rows): the result holds only the requested rows, in increasing
+    row order ([len(rows), out_cols]); the call then sees just those rows, each still in
+    its own request (cu_seqlens_q is recounted), which changes nothing they compute."""
+    if compact and rows is not None:
+        rows = np.unique(np.asarray(rows, np.int64))
+        cu = np.asarray(cu_seqlens_q, np.int64)
+        assert rows.size and rows[0] >= 0 and rows[-1] < cu[-1]
+        b_of = np.searchsorted(cu, rows, side="right") - 1
+        new_cu = np.zeros(cu.size, np.int32)
+        new_cu[1:] = np.cumsum(np.bincount(b_of, minlength=cu.size - 1))
+        return logits_paged(fmt, np.asarray(q_fp4)[rows], np.asarray(q_scale)[rows],
+                            np.asarray(w)[rows], k_fp4, k_scale, block_table, new_cu,
+                            np.asarray(row_lens)[rows], page_size, out_cols,
+                            num_pages=num_pages, n_threads=n_threads, want_tolbase=want_tolbase)
     q_fp4 = _c(q_fp4, np.uint8)
     q_scale = _c(q_scale, np.uint8)
     w = _c(w, np.float32)

@@ -185,3 +185,57 @@ def test_per_head_dots_through_one_hot_weights(e8):
     say(f"    per-head bit-exact: {total - mism}/{total}")
     if e8 == (123, 131):
         assert mism <= 1e-3 * total
+
+
+# ---- long causal prefill at full size: 32768 x 32768 logits stay on the device; the
+# oracle checks 256 seeded sampled rows plus the boundary rows, in two halves
+_C4_FORCED = [0, 2046, 2047, 2048, 32767]
+
+
+@pytest.fixture(scope="module")
+def config4_gpu():
+    case = wl.config4()
+    rng = np.random.default_rng(1040)
+    sampled = rng.choice(case.T, 256, replace=False)
+    halves = [np.unique(np.concatenate([sampled[:128], _C4_FORCED])), np.unique(sampled[128:])]
+    rows = np.unique(np.concatenate(halves))
+    say(f"[gpu] logits {case.name} T={case.T} H={case.H} out_cols={case.out_cols} (+ top-2048)")
+    out = fp4.logits_paged(dev(case.q_fp4), dev(case.q_scale), dev(case.w), dev(case.k_fp4),
+                           dev(case.k_scale), dev(case.block_table), dev(case.cu_seqlens_q),
+                           dev(case.row_lens), fmt=case.fmt, out_cols=case.out_cols)
+    idx, _ = fp4.topk(out, 2048, dev(case.row_lens))
+    torch.cuda.synchronize()
+    sel = torch.from_numpy(rows).to(out.device)
+    got = dict(zip(rows.tolist(), out.index_select(0, sel).cpu().numpy()))
+    gidx = dict(zip(rows.tolist(), idx.index_select(0, sel).cpu().numpy()))
+    del out, idx
+    torch.cuda.empty_cache()
+    return case, halves, got, gidx
+
+
+@pytest.mark.parametrize("half", [0, 1])
+def test_config4_prefill_sampled_rows_and_topk(config4_gpu, half):
+    case, halves, got, gidx = config4_gpu
+    rows = halves[half]
+    ref, tb, inexact = orc.logits_paged(case.fmt, case.q_fp4, case.q_scale, case.w, case.k_fp4,
+                                        case.k_scale, case.block_table, case.cu_seqlens_q,
+                                        case.row_lens, case.page_size, case.out_cols,
+                                        rows=rows, want_tolbase=True, compact=True)
+    assert inexact == 0
+    g = np.stack([got[t] for t in rows.tolist()])
+    worst = check_logits(g, ref, tb)
+    say(f"    {rows.size} rows, worst error / tolerance = {worst:.3f}")
+    lens = case.row_lens[rows]
+    oi, _ = orc.topk(ref, 2048, lens)
+    ndiff = 0
+    for i, t in enumerate(rows.tolist()):
+        a, b = set(gidx[t][gidx[t] >= 0].tolist()), set(oi[i][oi[i] >= 0].tolist())
+        assert len(a) == len(b) == min(2048, int(lens[i]))
+        assert np.all(gidx[t][len(a):] == -1)
+        sel = np.array(sorted(b))
+        kcol = sel[np.argmin(ref[i][sel])]             # the oracle's k-th largest
+        for c in a ^ b:
+            gap = abs(float(ref[i, c]) - float(ref[i, kcol]))
+            assert gap <= 1e-6 * (float(tb[i, c]) + float(tb[i, kcol])) + 1e-30, (t, c)
+        ndiff += len(a ^ b)
+    say(f"    top-2048 symmetric differences (ties within tolerance): {ndiff}")

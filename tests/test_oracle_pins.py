@@ -355,6 +355,31 @@ def test_block_scores_brute_force_against_library_dot(fmt, causal):
                     assert out[hq, kb, qg] == want
 
 
+def test_block_max_skips_nan_dots():
+    """A NaN E4M3 code (0x7F) on one key makes that key's dots NaN; the block max is C's
+    fmax, so it equals numpy's nanmax over the library-decoded dots of the block, and a
+    query head whose dots are all NaN gets -inf blocks."""
+    case = wl.make_block("nan", fmt=wl.NVFP4, q_lens=[4], k_lens=[200], Hq=2, Hkv=1, seed=19,
+                         causal=False)
+    p0 = int(case.kv_indices[0])
+    case.k_scale[p0, 0, 7, 1] = 0x7F                 # key 7: NaN for every query
+    case.q_scale[3, 1, 0] = 0xFF                     # query 3, head 1: every dot NaN
+    out, _, _ = orc.block_scores(case.fmt, case.q_fp4, case.q_scale, case.k_fp4, case.k_scale,
+                                 case.cu_seqlens_q, case.cu_seqlens_k, case.cu_page_offsets,
+                                 case.kv_indices, None, case.max_seqlen_k, False)
+    K = np.concatenate([lib_dequant(wl.NVFP4, case.k_fp4[p, 0], case.k_scale[p, 0])
+                        for p in case.kv_indices])[:200]
+    for hq in range(2):
+        for q in range(4):
+            with np.errstate(invalid="ignore"):
+                s = K @ lib_dequant(wl.NVFP4, case.q_fp4[q, hq], case.q_scale[q, hq])
+            for kb in range(2):
+                seg = s[128 * kb:min(128 * kb + 128, 200)]
+                want = -np.inf if np.all(np.isnan(seg)) else np.float32(np.nanmax(seg))
+                assert out[hq, kb, q] == want, (hq, q, kb)
+    assert np.all(out[1, :, 3] == -np.inf)
+
+
 def test_block_max_equals_max_of_one_head_logits():
     """Cross-API: H=Hkv=1, w=1 logits on 128-token pages equal max(block score, 0)."""
     bc = wl.make_block("x", fmt=wl.MXFP4, q_lens=[2], k_lens=[300], Hq=1, Hkv=1, seed=17,
@@ -398,3 +423,18 @@ def test_topk_matches_numpy_stable_sort():
         if m and m < len(cand):
             unsel = np.setdiff1d(cand, want)
             assert v[want].min() >= v[unsel].max()
+
+
+def test_compact_rows_match_the_full_call():
+    """The compact form of the logits call (only sampled rows, used where the full
+    [T, out_cols] array would not fit) returns exactly the full call's rows."""
+    case = wl.make_logits("compact", q_per_req=[3, 2, 4], ctx=[150, 90, 200], H=8, seed=12,
+                          row_lens=[150, 149, 3, 90, 0, 200, 199, 64, 1], out_cols=210)
+    rows = [7, 0, 4, 5, 2]
+    full, _, _ = orc.logits_paged(case.fmt, case.q_fp4, case.q_scale, case.w, case.k_fp4,
+                                  case.k_scale, case.block_table, case.cu_seqlens_q, case.row_lens,
+                                  case.page_size, case.out_cols)
+    comp, _, _ = orc.logits_paged(case.fmt, case.q_fp4, case.q_scale, case.w, case.k_fp4,
+                                  case.k_scale, case.block_table, case.cu_seqlens_q, case.row_lens,
+                                  case.page_size, case.out_cols, rows=rows, compact=True)
+    np.testing.assert_array_equal(comp, full[sorted(rows)])
