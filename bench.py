@@ -109,7 +109,7 @@ def logits_workload(args, torch, fp4, wl, dev):
         case = wl.config1(args.ctx)
         name = f"decode_ctx{args.ctx}_h32"
         desc = (f"{name}: 1 request, 4 verify rows seeing ctx-0..3 keys, H=32, D=128, "
-                f"MXFP4, page 64 shuffled, logits + top-{k}")
+                f"MXFP4, page 64 shuffled, logits + top-{k} indices")
         steps, warmup, launches = 640, 64, 64
     elif args.workload == "batched":
         case = wl.config2()
@@ -138,7 +138,6 @@ def logits_workload(args, torch, fp4, wl, dev):
         s = {n: (t if n in ("cu", "lens", "bt") else t.clone()) for n, t in base.items()}
         s["out"] = torch.empty((T, out_cols), dtype=torch.float32, device=dev)
         s["idx"] = torch.empty((T, k), dtype=torch.int32, device=dev)
-        s["val"] = torch.empty((T, k), dtype=torch.float32, device=dev)
         return s
 
     ws_bytes = fp4.topk_workspace_bytes(T, out_cols, k)
@@ -149,7 +148,7 @@ def logits_workload(args, torch, fp4, wl, dev):
                          fmt="mxfp4", out_cols=out_cols, out=s["out"])
 
     def topk(s):
-        fp4.topk(s["out"], k, s["lens"], out_idx=s["idx"], out_vals=s["val"], workspace=ws)
+        fp4.topk(s["out"], k, s["lens"], out_idx=s["idx"], want_vals=False, workspace=ws)
 
     # algorithmic work: each input once, each output once; flops over visible pairs
     keys = case.unique_keys()
@@ -159,7 +158,7 @@ def logits_workload(args, torch, fp4, wl, dev):
                     + T * H * 68 + T * H * 4         # queries, scales, weights
                     + pages * 4 + (T + 2) * 4        # block table, lengths, cu_seqlens
                     + T * out_cols * 4)              # logits out
-    topk_bytes = pairs * 4 + T * 4 + T * k * 8
+    topk_bytes = pairs * 4 + T * 4 + T * k * 4       # scores in, int32 indices out
     work = {
         "logits": dict(bytes=logits_bytes, flops=2 * H * 128 * pairs,
                        bound="mfma" if args.workload == "prefill" else "hbm", dtype="fp4"),

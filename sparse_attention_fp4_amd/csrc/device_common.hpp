@@ -114,34 +114,45 @@ __device__ __forceinline__ v8h decode8_f16(uint32_t packed, float pow2, float b)
     return r;
 }
 
-// Exclusive prefix sum of x over the NT threads of a workgroup (wave scans, then the
-// wave totals through LDS).  wtot: LDS scratch of NT/64 ints.  Ends with a barrier.
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS): three
+// row_shr steps and two masked ones give each 16-lane row its scan, then row_bcast:15
+// and row_bcast:31 carry row totals into the rows above (GCN/CDNA cross-lane scan).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    int v = x;
+    v += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, x, 0x113, 0xf, 0xf, true);   // row_shr:3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xe, false);  // row_shr:4, lanes 4..15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xc, false);  // row_shr:8, lanes 8..15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+    return v;
+}
+
+// Exclusive prefix sum of x over the NT threads of a workgroup (wave scans, then a scan
+// of the wave totals in every wave).  wtot: LDS scratch of NT/64 ints.  Ends with a
+// barrier.
 template <int NT>
 __device__ __forceinline__ void block_excl_scan(int x, int* wtot, int& excl, int& total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int s = x;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(s, d);
-        if (lane >= d) s += y;
-    }
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int s = wave_incl_scan(x);
     if (lane == 63) wtot[wave] = s;
     __syncthreads();
-    int before = 0;
-    total = 0;
-    for (int w = 0; w < NT / 64; w++) {
-        const int t = wtot[w];
-        if (w < wave) before += t;
-        total += t;
-    }
+    const int t = lane < NW ? wtot[lane] : 0;
+    const int ts = wave_incl_scan(t);
+    const int before = wave > 0 ? __builtin_amdgcn_readlane(ts, wave - 1) : 0;
+    total = __builtin_amdgcn_readlane(ts, NW - 1);
     excl = before + s - x;
     __syncthreads();
 }
 
 // Thread-parallel bin pick: thread t owns PER bins listed in "before" order (c[b] =
 // count, bin[b] = bin index).  Finds the bin that holds the kk-th element of that
-// order; out[0] = bin, out[1] = elements before it, out[2] = total.  out[0] is left
-// untouched when total < kk.  Ends with a barrier.
+// order; out[0] = bin, out[1] = elements before it, out[2] = total, out[3] = the bin's
+// own count.  out[0], out[1] and out[3] are left untouched when total < kk.  Ends with
+// a barrier.
 template <int NT, int PER>
 __device__ __forceinline__ void pick_bin(const int (&c)[PER], const int (&bin)[PER], int kk, int* wtot,
                                          int* out) {
@@ -157,6 +168,7 @@ __device__ __forceinline__ void pick_bin(const int (&c)[PER], const int (&bin)[P
             if (excl + c[b] >= kk) {
                 out[0] = bin[b];
                 out[1] = excl;
+                out[3] = c[b];
                 break;
             }
             excl += c[b];

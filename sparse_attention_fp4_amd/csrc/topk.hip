@@ -52,7 +52,7 @@ struct Shared {
     uint32_t wave_max[kWaves];
     int wave_cnt[kWaves];
     int wtot[kWaves];
-    int pick[3];
+    int pick[4];
     int total;
 };
 

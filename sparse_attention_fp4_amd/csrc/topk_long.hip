@@ -5,25 +5,29 @@
 // target)": a wave-level (ballot) top-k instead of a serial shared-memory heap merge.)
 //
 // Same order and output as topk.hip (larger first, ties to the smaller column, -inf
-// and NaN never selected, result in increasing column order, -1 padded).  A row is cut
-// into chunks of 4096 columns.  Workgroups exchange data only across kernel
-// boundaries (a device-wide fence inside a kernel costs microseconds on this
+// and NaN never selected, result in increasing column order, -1 padded).  Scores map
+// to order-preserving 32-bit keys; digit 1 is key bits [31:20], digit 2 bits [19:8].
+// A row is cut into chunks of 4096 columns.  Workgroups exchange data only across
+// kernel boundaries (a device-wide fence inside a kernel costs microseconds on this
 // multi-die part):
-//   1. hist:    each chunk builds the histogram of the top 12 key bits of its elements
-//               in LDS and adds its nonzero bins to the row's histogram (global
-//               atomics that nothing waits for).
-//   2. collect: each chunk reads the row's histogram, finds the bin d1 that holds the
-//               row's k-th largest key, and stores a bitmap of its columns above d1
-//               (all selected) and, in column order, the keys and columns in d1 (the
-//               candidates).
-//   3. finish:  one workgroup per row narrows the candidates to the exact threshold key
-//               T (two more digit passes over candidates kept in registers), finds the
-//               column cut among ties at T, ORs the selected candidates into an LDS copy
-//               of the row's bitmap, writes the columns in order from a popcount scan,
-//               gathers their scores, and clears the row's histogram for the next call.
-// Every phase issues its global loads together: a round trip costs about a
-// microsecond here.  The workspace must be zero-filled before its first use; every
-// call leaves the histograms zero-filled again.
+//   1. hist:    each chunk builds the histogram of digit 1 of its keys in LDS and adds
+//               its nonzero bins to the row's histogram (global atomics).
+//   2. collect: each chunk reads the row's histogram, finds the bin d1 holding the
+//               row's k-th largest key, stores a bitmap of its columns above d1 (all
+//               selected) and its keys in d1 (the candidates, with their columns and
+//               count), and adds the digit-2 histogram of those candidates to the
+//               row's second histogram.
+//   3. finish:  one workgroup per row reads the second histogram, the candidate counts,
+//               the bitmap and the first slots of every chunk's candidates in one
+//               round of loads (a chunk with more candidates sends the workgroup
+//               through a slower path that reloads them), finds the digit-2 bin d2 holding
+//               the k-th key, selects every candidate above prefix (d1, d2), ranks the
+//               few candidates inside it by direct comparison (a digit-pass fallback
+//               handles more than 1024 of them), writes the columns in order from
+//               popcount scans of the bitmap, and clears its histograms and counter
+//               for the next call.
+// The workspace must be zero-filled before its first use; every call leaves the
+// histograms zero-filled again.
 #include "device_common.hpp"
 #include "fp4idx_internal.hpp"
 
@@ -41,17 +45,17 @@ constexpr int kMaxWords = kMaxChunks * kWords;
 constexpr int kMaxK = 8192;
 
 struct RowState {
-    int d1;         // bin of the k-th largest key, or -1 when every valid key is kept
+    int d1;         // digit-1 bin of the k-th largest key, or -1 when every valid key is kept
     int kk;         // wanted keys inside bin d1
 };
 
 struct LongWs {
     RowState* st;        // [rows]
-    uint32_t* hist;      // [rows][kBins]            zero between calls
+    uint32_t* hist;      // [rows][kBins]            digit 1 of the keys; zero between calls
+    uint32_t* hist2;     // [rows][kBins]            digit 2 of the candidates; zero between calls
     uint32_t* bitmap;    // [rows][n_chunks * kWords] columns above bin d1 (+ selected candidates)
-    uint32_t* ckey;      // [rows][n_chunks][kChunk] candidates (bin d1): keys, in column order
-    int32_t* ccol;       // [rows][n_chunks][kChunk] candidates: columns
-    int32_t* cnum;       // [rows][n_chunks]         candidates per chunk
+    uint2* cand;         // [rows][n_chunks][kChunk]  candidates (bin d1): (key, column), column order
+    int32_t* cnum;       // [rows][n_chunks]          candidates per chunk
     int n_chunks;
 };
 
@@ -108,8 +112,10 @@ __global__ __launch_bounds__(kCT) void k_hist(const TopkParams p, LongWs ws) {
 
 // ---------------------------------------------------------------- 2. collect
 struct CollectShared {
+    uint32_t h2[kBins];
     int wtot[kCT / 64];
-    int pick[3];
+    int pick[4];
+    int total;
     uint32_t bits[kWords];
     int cnt[kPer * (kCT / 64)];
     int off[kPer * (kCT / 64)];
@@ -145,15 +151,12 @@ __global__ __launch_bounds__(kCT) void k_collect(const TopkParams p, LongWs ws) 
     const int nch = ws.n_chunks;
     uint32_t key[kPer];
     load_chunk(p, row, chunk, key);  // in flight with the histogram loads
+    for (int i = threadIdx.x; i < kBins; i += kCT) sh.h2[i] = 0u;
     int d1, kk;
-    row_threshold_bin(sh, p, ws, row, d1, kk);
-    if (chunk == 0 && threadIdx.x == 0) {
-        ws.st[row].d1 = d1;
-        ws.st[row].kk = kk;
-    }
+    row_threshold_bin(sh, p, ws, row, d1, kk);  // ends with a barrier
     const int c0 = chunk * kChunk;
 
-    // ---- bitmap of the columns above bin d1; candidates of bin d1 in column order
+    // ---- bitmap of the columns above bin d1; candidates of bin d1 and their digit 2
     bool cand[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; j++) {
@@ -168,47 +171,70 @@ __global__ __launch_bounds__(kCT) void k_collect(const TopkParams p, LongWs ws) 
         cand[j] = d1 >= 0 && kj != 0u && dig == d1;
         const unsigned long long mc = __ballot(cand[j]);
         if (lane == 0) sh.cnt[j * (kCT / 64) + wave] = __popcll(mc);
+        if (cand[j]) atomicAdd(&sh.h2[(kj >> 8) & 0xfffu], 1u);
     }
     __syncthreads();
-    uint32_t* gbits = ws.bitmap + (int64_t)row * nch * kWords + chunk * kWords;
-    for (int i = threadIdx.x; i < kWords; i += kCT) gbits[i] = sh.bits[i];
     if (wave == 0) {  // exclusive scan over the kPer * 4 = 64 (step, wave) blocks
         const int x = sh.cnt[lane];
-        int s = x;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int y = __shfl_up(s, d);
-            if (lane >= d) s += y;
-        }
+        const int s = wave_incl_scan(x);
         sh.off[lane] = s - x;
-        if (lane == 63) ws.cnum[(int64_t)row * nch + chunk] = s;
+        if (lane == 63) sh.total = s;
     }
     __syncthreads();
-    const int64_t base = ((int64_t)row * nch + chunk) * kChunk;
+    // Global writes come last: a barrier after them would wait for their completion.
+    uint2* dst = ws.cand + ((int64_t)row * nch + chunk) * kChunk;
 #pragma unroll
     for (int j = 0; j < kPer; j++) {
         const unsigned long long mc = __ballot(cand[j]);
         if (cand[j]) {
             const int pos = sh.off[j * (kCT / 64) + wave] + lanes_below(mc);
-            ws.ckey[base + pos] = key[j];
-            ws.ccol[base + pos] = c0 + threadIdx.x + kCT * j;
+            dst[pos] = make_uint2(key[j], (uint32_t)(c0 + threadIdx.x + kCT * j));
         }
+    }
+    uint32_t* gbits = ws.bitmap + (int64_t)row * nch * kWords + chunk * kWords;
+    for (int i = threadIdx.x; i < kWords; i += kCT) gbits[i] = sh.bits[i];
+    if (threadIdx.x == 0) {
+        ws.cnum[(int64_t)row * nch + chunk] = sh.total;
+        if (chunk == 0) {
+            ws.st[row].d1 = d1;
+            ws.st[row].kk = kk;
+        }
+    }
+    // the chunk's digit-2 counts join the row's second histogram
+    uint32_t* gh2 = ws.hist2 + (int64_t)row * kBins;
+    for (int i = threadIdx.x; i < kBins; i += kCT) {
+        const uint32_t v = sh.h2[i];
+        if (v) atomicAdd(&gh2[i], v);
     }
 }
 
 // ---------------------------------------------------------------- 3. finish
-constexpr int kFT = 1024;  // threads of the finishing workgroup
+constexpr int kFT = 1024;    // threads of the finishing workgroup
+constexpr int kCR = 8;       // candidates per thread per round
+constexpr int kRankMax = 1024;  // candidates at the threshold prefix ranked by comparison
 
 struct FinishShared {
     uint32_t h[kBins];
     uint32_t bits[kMaxWords];  // the row's bitmap
-    int sel[kMaxK];            // selected columns in order
+    uint32_t mkey[kRankMax];   // candidates with the threshold prefix (d1, d2)
+    int mcol[kRankMax];
+    int cnum[kMaxChunks];
     int coff[kMaxChunks + 1];  // candidate prefix over chunks
     int wtot[kFT / 64];
-    int pick[3];
+    int pick[4];
+    int nm;
 };
 
-// Candidate i of the row lives in chunk c with coff[c] <= i < coff[c+1].
+// Candidate registers: kCR per thread.  In the common case they hold every candidate
+// of the row (slot i = threadIdx.x + kFT * j is slot i % spec of chunk i / spec);
+// otherwise ("flat" mode) they hold candidates [round * kFT * kCR, +kFT * kCR) of the
+// row in chunk order, reloaded round by round.
+struct CandRegs {
+    uint32_t key[kCR];
+    int col[kCR];  // -1: no candidate
+};
+
+// Candidate i of the row (flat order) lives in chunk c with coff[c] <= i < coff[c+1].
 __device__ __forceinline__ int64_t cand_slot(const FinishShared& sh, int row, int nch, int i) {
     int lo = 0, hi = nch;
     while (hi - lo > 1) {
@@ -219,28 +245,18 @@ __device__ __forceinline__ int64_t cand_slot(const FinishShared& sh, int row, in
     return ((int64_t)row * nch + lo) * kChunk + (i - sh.coff[lo]);
 }
 
-// The candidates of the row, kCR per thread per round (candidate i = round * kFT * kCR
-// + threadIdx.x + kFT * j); a row with at most kFT * kCR candidates keeps them in
-// registers for all passes, a larger one reloads them round by round.
-constexpr int kCR = 8;
-
-struct CandRegs {
-    uint32_t key[kCR];
-    int col[kCR];  // -1: no candidate
-};
-
-__device__ __forceinline__ void load_round(CandRegs& r, const FinishShared& sh, const LongWs& ws, int row,
-                                           int nch, int m, int round) {
+__device__ __forceinline__ void load_flat(CandRegs& r, const FinishShared& sh, const LongWs& ws, int row,
+                                          int nch, int m, int round) {
+    uint2 v[kCR];
 #pragma unroll
     for (int j = 0; j < kCR; j++) {
         const int i = round * kFT * kCR + threadIdx.x + kFT * j;
-        r.key[j] = 0u;
-        r.col[j] = -1;
-        if (i < m) {
-            const int64_t at = cand_slot(sh, row, nch, i);
-            r.key[j] = ws.ckey[at];
-            r.col[j] = ws.ccol[at];
-        }
+        v[j] = i < m ? ws.cand[cand_slot(sh, row, nch, i)] : make_uint2(0u, 0xffffffffu);
+    }
+#pragma unroll
+    for (int j = 0; j < kCR; j++) {
+        r.key[j] = v[j].x;
+        r.col[j] = (int)v[j].y;
     }
 }
 
@@ -248,18 +264,15 @@ __device__ __forceinline__ void load_round(CandRegs& r, const FinishShared& sh, 
 // and the bin holding the kk-th element in the given order.
 template <typename Keep, typename Digit>
 __device__ __forceinline__ void cand_pass(FinishShared& sh, CandRegs& r, const LongWs& ws, int row, int nch,
-                                          int m, int rounds, int kk, bool descending, Keep keep, Digit digit) {
+                                          int m, int rounds, bool flat, int kk, bool descending, Keep keep,
+                                          Digit digit) {
     for (int i = threadIdx.x; i < kBins; i += kFT) sh.h[i] = 0u;
     __syncthreads();
     for (int round = 0; round < rounds; round++) {
-        if (rounds > 1) load_round(r, sh, ws, row, nch, m, round);
-        const int left = m - round * kFT * kCR;  // candidates of this round
+        if (flat) load_flat(r, sh, ws, row, nch, m, round);
 #pragma unroll
-        for (int j = 0; j < kCR; j++) {
-            // slot j holds candidates only below `left` (a uniform test)
-            if (kFT * j < left && r.col[j] >= 0 && keep(r.key[j], r.col[j]))
-                atomicAdd(&sh.h[digit(r.key[j], r.col[j])], 1u);
-        }
+        for (int j = 0; j < kCR; j++)
+            if (r.col[j] >= 0 && keep(r.key[j], r.col[j])) atomicAdd(&sh.h[digit(r.key[j], r.col[j])], 1u);
     }
     __syncthreads();
     constexpr int per = kBins / kFT;
@@ -280,108 +293,171 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws) {
     const int k = p.k;
     const int nwords = nch * kWords;
     const uint32_t* rbits = ws.bitmap + (int64_t)row * nch * kWords;
-    // ---- the row's bitmap into LDS (loads in flight together)
-    for (int w = threadIdx.x; w < nwords; w += kFT * 16) {
-        uint32_t x[16];
-#pragma unroll
-        for (int j = 0; j < 16; j++) x[j] = w + kFT * j < nwords ? rbits[w + kFT * j] : 0u;
-#pragma unroll
-        for (int j = 0; j < 16; j++)
-            if (w + kFT * j < nwords) sh.bits[w + kFT * j] = x[j];
-    }
+    uint32_t* gh = ws.hist + (int64_t)row * kBins;
+    uint32_t* gh2 = ws.hist2 + (int64_t)row * kBins;
+    constexpr int lspec = 6;            // candidate slots read per chunk up front: 64
+    constexpr int spec = 1 << lspec;    // (kMaxChunks * spec = kFT * kCR)
+
+    // ---- one round of loads: state, candidate counts, second histogram, bitmap, and the
+    // first `spec` candidate slots of every chunk (read before the counts are known;
+    // slots past a count are ignored)
     const int d1 = ws.st[row].d1;
     int kk = ws.st[row].kk;
+    const int my_cnum = threadIdx.x < nch ? ws.cnum[(int64_t)row * nch + threadIdx.x] : 0;
+    constexpr int per = kBins / kFT;
+    int c2[per], bin2[per];
+#pragma unroll
+    for (int b = 0; b < per; b++) {
+        bin2[b] = kBins - 1 - (threadIdx.x * per + b);
+        c2[b] = (int)gh2[bin2[b]];
+    }
+    uint32_t x[16];
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        const int w = threadIdx.x + kFT * j;
+        x[j] = w < nwords ? rbits[w] : 0u;
+    }
+    uint2 sv[kCR];
+#pragma unroll
+    for (int j = 0; j < kCR; j++) {
+        const int i = threadIdx.x + kFT * j;
+        const int c = i >> lspec, slot = i & (spec - 1);
+        sv[j] = c < nch ? ws.cand[((int64_t)row * nch + c) * kChunk + slot] : make_uint2(0u, 0xffffffffu);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        const int w = threadIdx.x + kFT * j;
+        if (w < nwords) sh.bits[w] = x[j];
+    }
+    if (threadIdx.x < nch) sh.cnum[threadIdx.x] = my_cnum;
+    if (threadIdx.x == 0) sh.nm = 0;
     {
-        const int c = threadIdx.x;  // nch <= kMaxChunks <= kFT
-        const int v = c < nch ? ws.cnum[(int64_t)row * nch + c] : 0;
         int before, total;
-        block_excl_scan<kFT>(v, sh.wtot, before, total);
-        if (c < nch) sh.coff[c] = before;
+        block_excl_scan<kFT>(my_cnum, sh.wtot, before, total);  // barriers inside
+        if (threadIdx.x < nch) sh.coff[threadIdx.x] = before;
         if (threadIdx.x == 0) sh.coff[nch] = total;
     }
-    __syncthreads();
+    const bool flat = __syncthreads_or(my_cnum > spec) != 0;  // also publishes coff
     const int m = sh.coff[nch];
+    const int rounds = flat ? (m + kFT * kCR - 1) / (kFT * kCR) : 1;
+    CandRegs r;
+#pragma unroll
+    for (int j = 0; j < kCR; j++) {
+        const int i = threadIdx.x + kFT * j;
+        const int c = i >> lspec, slot = i & (spec - 1);
+        const bool ok = c < nch && slot < sh.cnum[c < nch ? c : 0];
+        r.key[j] = sv[j].x;
+        r.col[j] = ok ? (int)sv[j].y : -1;
+    }
+
     if (d1 >= 0) {
-        const int rounds = (m + kFT * kCR - 1) / (kFT * kCR);
-        CandRegs r;
-        load_round(r, sh, ws, row, nch, m, 0);
-        cand_pass(sh, r, ws, row, nch, m, rounds, kk, true, [&](uint32_t, int) { return true; },
-                  [&](uint32_t kx, int) { return (int)((kx >> 8) & 0xfffu); });
+        // ---- digit 2 from the row's second histogram (pick_bin ends with a barrier)
+        pick_bin<kFT, per>(c2, bin2, kk, sh.wtot, sh.pick);
         const uint32_t preA = ((uint32_t)d1 << 12) | (uint32_t)sh.pick[0];
-        kk -= sh.pick[1];
-        cand_pass(sh, r, ws, row, nch, m, rounds, kk, true, [&](uint32_t kx, int) { return (kx >> 8) == preA; },
-                  [&](uint32_t kx, int) { return (int)(kx & 0xffu); });
-        const uint32_t T = (preA << 8) | (uint32_t)sh.pick[0];
-        kk -= sh.pick[1];  // ties at T to keep, >= 1
-        const int ties = (int)sh.h[sh.pick[0]];
-        __syncthreads();
-        int c_cut = 0x7fffffff;
-        if (kk < ties) {
-            // the kk-th smallest column among the ties at T: bits [30:20], [19:8], [7:0]
-            cand_pass(sh, r, ws, row, nch, m, rounds, kk, false, [&](uint32_t kx, int) { return kx == T; },
-                      [&](uint32_t, int col) { return (int)(((uint32_t)col >> 20) & 0x7ffu); });
-            const uint32_t c1 = (uint32_t)sh.pick[0];
-            kk -= sh.pick[1];
-            cand_pass(sh, r, ws, row, nch, m, rounds, kk, false,
-                      [&](uint32_t kx, int col) { return kx == T && ((uint32_t)col >> 20) == c1; },
-                      [&](uint32_t, int col) { return (int)(((uint32_t)col >> 8) & 0xfffu); });
-            const uint32_t c2 = (c1 << 12) | (uint32_t)sh.pick[0];
-            kk -= sh.pick[1];
-            cand_pass(sh, r, ws, row, nch, m, rounds, kk, false,
-                      [&](uint32_t kx, int col) { return kx == T && ((uint32_t)col >> 8) == c2; },
-                      [&](uint32_t, int col) { return (int)((uint32_t)col & 0xffu); });
-            c_cut = (int)((c2 << 8) | (uint32_t)sh.pick[0]);
-        }
-        // selected candidates join the bitmap
+        kk -= sh.pick[1];                      // keys wanted with prefix preA, >= 1
+        const int n_pre = sh.pick[3];          // candidates with prefix preA
+        // ---- candidates above the prefix are selected; those at it are collected
         for (int round = 0; round < rounds; round++) {
-            if (rounds > 1) load_round(r, sh, ws, row, nch, m, round);
+            if (flat) load_flat(r, sh, ws, row, nch, m, round);
 #pragma unroll
             for (int j = 0; j < kCR; j++) {
-                const uint32_t kx = r.key[j];
+                const uint32_t pre = r.key[j] >> 8;
                 const int col = r.col[j];
-                if (col >= 0 && (kx > T || (kx == T && col <= c_cut))) atomicOr(&sh.bits[col >> 5], 1u << (col & 31));
+                if (col < 0) continue;
+                if (pre > preA) {
+                    atomicOr(&sh.bits[col >> 5], 1u << (col & 31));
+                } else if (pre == preA && n_pre <= kRankMax) {
+                    const int at = atomicAdd(&sh.nm, 1);
+                    if (at < kRankMax) {   // n_pre bounds it; the test keeps LDS safe
+                        sh.mkey[at] = r.key[j];
+                        sh.mcol[at] = col;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (n_pre <= kRankMax) {
+            // ---- rank each collected candidate by direct comparison
+            const int nm = min(sh.nm, kRankMax);
+            for (int t = threadIdx.x; t < nm; t += kFT) {
+                const uint32_t kt = sh.mkey[t];
+                const int ct = sh.mcol[t];
+                int rank = 0;
+                for (int u = 0; u < nm; u++) {
+                    const uint32_t ku = sh.mkey[u];
+                    rank += (ku > kt || (ku == kt && sh.mcol[u] < ct)) ? 1 : 0;
+                }
+                if (rank < kk) atomicOr(&sh.bits[ct >> 5], 1u << (ct & 31));
+            }
+        } else {
+            // ---- many candidates share the prefix: digit passes over them
+            cand_pass(sh, r, ws, row, nch, m, rounds, flat, kk, true,
+                      [&](uint32_t kx, int) { return (kx >> 8) == preA; },
+                      [&](uint32_t kx, int) { return (int)(kx & 0xffu); });
+            const uint32_t T = (preA << 8) | (uint32_t)sh.pick[0];
+            kk -= sh.pick[1];  // ties at T to keep, >= 1
+            const int ties = sh.pick[3];
+            int c_cut = 0x7fffffff;
+            if (kk < ties) {
+                // the kk-th smallest column among the ties at T: bits [30:20], [19:8], [7:0]
+                cand_pass(sh, r, ws, row, nch, m, rounds, flat, kk, false, [&](uint32_t kx, int) { return kx == T; },
+                          [&](uint32_t, int col) { return (int)(((uint32_t)col >> 20) & 0x7ffu); });
+                const uint32_t c1 = (uint32_t)sh.pick[0];
+                kk -= sh.pick[1];
+                cand_pass(sh, r, ws, row, nch, m, rounds, flat, kk, false,
+                          [&](uint32_t kx, int col) { return kx == T && ((uint32_t)col >> 20) == c1; },
+                          [&](uint32_t, int col) { return (int)(((uint32_t)col >> 8) & 0xfffu); });
+                const uint32_t c2 = (c1 << 12) | (uint32_t)sh.pick[0];
+                kk -= sh.pick[1];
+                cand_pass(sh, r, ws, row, nch, m, rounds, flat, kk, false,
+                          [&](uint32_t kx, int col) { return kx == T && ((uint32_t)col >> 8) == c2; },
+                          [&](uint32_t, int col) { return (int)((uint32_t)col & 0xffu); });
+                c_cut = (int)((c2 << 8) | (uint32_t)sh.pick[0]);
+            }
+            for (int round = 0; round < rounds; round++) {
+                if (flat) load_flat(r, sh, ws, row, nch, m, round);
+#pragma unroll
+                for (int j = 0; j < kCR; j++) {
+                    const uint32_t kx = r.key[j];
+                    const int col = r.col[j];
+                    if (col >= 0 && (kx >> 8) == preA && (kx > T || (kx == T && col <= c_cut)))
+                        atomicOr(&sh.bits[col >> 5], 1u << (col & 31));
+                }
             }
         }
     }
     __syncthreads();
 
-    // ---- columns in order: thread t scans words [t*wpt, (t+1)*wpt) of the LDS bitmap
+    // ---- columns in order: thread t owns words [t*wpt, (t+1)*wpt) of the bitmap; a
+    // block scan of their popcounts gives each thread its output offset
+    const float* srow = p.scores + (int64_t)row * p.row_stride;
+    int32_t* oidx = p.out_idx + (int64_t)row * k;
+    float* oval = p.out_vals ? p.out_vals + (int64_t)row * k : nullptr;
     const int wpt = (nwords + kFT - 1) / kFT;
-    const int w0 = threadIdx.x * wpt, w1 = min(w0 + wpt, nwords);
-    int s = 0;
-    for (int w = w0; w < w1; w++) s += __popc(sh.bits[w]);
-    int pos, total;
-    block_excl_scan<kFT>(s, sh.wtot, pos, total);
-    for (int w = w0; w < w1 && pos < k; w++) {
+    const int wa = threadIdx.x * wpt, wb = min(wa + wpt, nwords);
+    int cnt = 0;
+    for (int w = wa; w < wb; w++) cnt += __popc(sh.bits[w]);
+    int pos, done;
+    block_excl_scan<kFT>(cnt, sh.wtot, pos, done);
+    for (int w = wa; w < wb && pos < k; w++) {
         uint32_t bits = sh.bits[w];
         while (bits && pos < k) {
-            sh.sel[pos++] = w * 32 + __ffs((int)bits) - 1;
+            const int col = w * 32 + __ffs((int)bits) - 1;
+            oidx[pos] = col;
+            if (oval) oval[pos] = srow[col];
+            pos++;
             bits &= bits - 1u;
         }
     }
-    __syncthreads();
-    // ---- output, coalesced; the scores come in with all loads in flight
-    const int n_out = min(total, k);
-    const float* srow = p.scores + (int64_t)row * p.row_stride;
-    for (int base = 0; base < k; base += kFT * 8) {
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const int i = base + threadIdx.x + kFT * j;
-            v[j] = (p.out_vals && i < n_out) ? srow[sh.sel[i]] : -__builtin_inff();
-        }
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const int i = base + threadIdx.x + kFT * j;
-            if (i < k) {
-                p.out_idx[(int64_t)row * k + i] = i < n_out ? sh.sel[i] : -1;
-                if (p.out_vals) p.out_vals[(int64_t)row * k + i] = v[j];
-            }
-        }
+    for (int i = min(done, k) + threadIdx.x; i < k; i += kFT) {
+        oidx[i] = -1;
+        if (oval) oval[i] = -__builtin_inff();
     }
-    // ---- leave the row's histogram zero-filled for the next call
-    uint32_t* gh = ws.hist + (int64_t)row * kBins;
-    for (int i = threadIdx.x; i < kBins; i += kFT) gh[i] = 0u;
+    // ---- leave the row's histograms zero for the next call
+    for (int i = threadIdx.x; i < kBins; i += kFT) {
+        gh[i] = 0u;
+        gh2[i] = 0u;
+    }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -396,12 +472,12 @@ LongWs carve(void* base, int rows, int cols, size_t* bytes) {
     o = align256(o + (size_t)rows * sizeof(RowState));
     w.hist = reinterpret_cast<uint32_t*>(b + o);
     o = align256(o + (size_t)rows * kBins * 4);
+    w.hist2 = reinterpret_cast<uint32_t*>(b + o);
+    o = align256(o + (size_t)rows * kBins * 4);
     w.bitmap = reinterpret_cast<uint32_t*>(b + o);
     o = align256(o + rc * kWords * 4);
-    w.ckey = reinterpret_cast<uint32_t*>(b + o);
-    o = align256(o + rc * kChunk * 4);
-    w.ccol = reinterpret_cast<int32_t*>(b + o);
-    o = align256(o + rc * kChunk * 4);
+    w.cand = reinterpret_cast<uint2*>(b + o);
+    o = align256(o + rc * kChunk * sizeof(uint2));
     w.cnum = reinterpret_cast<int32_t*>(b + o);
     o = align256(o + rc * 4);
     if (bytes) *bytes = o;

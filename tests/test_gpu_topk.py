@@ -34,6 +34,22 @@ def test_same_scores_exact(rows, cols, k):
     _same(s, k)
 
 
+@pytest.mark.parametrize("rows,cols", [(4, 100_000), (3, 20_000)])
+def test_indices_only(rows, cols):
+    """out_vals NULL: the same indices, and no value is read back."""
+    import sparse_attention_fp4_amd as fp4
+    from .gpu_helpers import dev
+
+    rng = np.random.default_rng(cols)
+    s = rng.standard_normal((rows, cols)).astype(np.float32)
+    lens = np.array([cols - 3 * i for i in range(rows)], np.int32)
+    say(f"[gpu] topk indices only rows={rows} cols={cols}")
+    idx, vals = fp4.topk(dev(s), 2048, dev(lens), want_vals=False)
+    assert vals is None
+    oi, _ = orc.topk(s, 2048, lens)
+    assert np.array_equal(idx.cpu().numpy(), oi)
+
+
 def test_ties_zeros_and_lengths():
     rng = np.random.default_rng(4)
     rows, cols, k = 6, 40000, 2048
