@@ -27,8 +27,11 @@ def hipcc() -> str:
 
 
 def flags():
+    # MFMA results in ordinary VGPRs: the epilogues read every result with VALU
+    # instructions, which accumulation registers would make copy out first.
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-I", INCLUDE, "-I", CSRC]
 
 

@@ -184,8 +184,8 @@ __global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
 #pragma unroll
                 for (int hb = 0; hb < NB; hb++) {
                     float v = run[hb];
-                    v = fmaxf(v, __shfl_xor(v, 16));
-                    v = fmaxf(v, __shfl_xor(v, 32));
+                    v = max_lane_xor16(v);
+                    v = max_lane_xor32(v);
                     if (g == 0 && col_ok && hb < nh)
                         p.scores[((int64_t)(h0 + hb) * p.ktiles + kb) * p.Tq + qg] = v;
                     run[hb] = -__builtin_inff();

@@ -81,6 +81,27 @@ __device__ __forceinline__ RowRequest find_request(const int32_t* __restrict__ c
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// v[l] + v[l ^ 32] and v[l] + v[l ^ 16] with the gfx950 lane-swap instructions (plain
+// VALU operations, no LDS round trip).  Called with the same value in both operands,
+// v_permlane32_swap returns (v[l & 31], v[l | 32]) and v_permlane16_swap returns the
+// matching pair for 16-lane rows, so the two halves hold both addends.
+__device__ __forceinline__ float add_lane_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_lane_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_lane_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_lane_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ v4i load16(const uint8_t* p) {
     return *reinterpret_cast<const v4i*>(p);
 }

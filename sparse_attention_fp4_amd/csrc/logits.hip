@@ -34,7 +34,7 @@
 // in fp32.  Head sums use four accumulators per lane (chains of at most 8 fused
 // multiply-adds: one per A tile) and a tree, so each term meets at most 8 + 2 (+ 2
 // cross-lane) roundings, about 7e-7 of sum_h |w_h ReLU(dot_h)| in the worst case,
-// inside the 1e-6 bound.  ReLU is fmaxf (IEEE maxNum: a NaN dot counts as 0).
+// inside the 1e-6 bound.
 #include "device_common.hpp"
 #include "fp4idx_internal.hpp"
 
@@ -104,14 +104,25 @@ __device__ __forceinline__ uint32_t scale_bytes(const uint8_t* s, int g) {
     else return (uint32_t)s[2 * g] | ((uint32_t)s[2 * g + 1] << 8);
 }
 
+// ReLU of a per-head dot.  NVFP4: fmaxf (IEEE maxNum: a NaN dot, which only a NaN E4M3
+// scale code can make, counts as 0).  MXFP4: one integer max on the bit pattern (every
+// negative value, -0 included, becomes +0; positive values pass), which saves the
+// quieting step fmaxf needs on a matrix-core result.  An MXFP4 dot is NaN only for
+// E8M0 scale code 255, which the format never stores; such a NaN passes through.
+template <int FMT>
+__device__ __forceinline__ float relu(float d) {
+    if constexpr (FMT == 0) return __int_as_float(max(__float_as_int(d), 0));
+    else return fmaxf(d, 0.0f);
+}
+
 // Cross-lane sum of the 4/RG lane groups that share a row.
 template <int RG>
 __device__ __forceinline__ float group_sum(float v) {
     if constexpr (RG == 1) {
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
+        v = add_lane_xor16(v);
+        v = add_lane_xor32(v);
     } else if constexpr (RG == 2) {
-        v += __shfl_xor(v, 32);
+        v = add_lane_xor32(v);
     }
     return v;
 }
@@ -318,23 +329,43 @@ __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
         auto compute = [&](int s, const Slab<FMT>& buf) {
             int pi, half, hk;
             slab_pos(s, pi, half, hk);
+            const int phys = __builtin_amdgcn_readlane(my_phys, pi);
+            // an invisible page (past every row's length, or invalid) only gets -inf
+            if (phys >= 0) {
+                Operand<FMT> kb[4];
 #pragma unroll
-            for (int tt = 0; tt < 4; tt++) {
-                RawTile rt;
-                rt.v = buf.k[tt];
-                rt.s = slab_scale<FMT>(buf, tt, g);
-                const Operand<FMT> kb = decode<FMT>(rt);
+                for (int tt = 0; tt < 4; tt++) {
+                    RawTile rt;
+                    rt.v = buf.k[tt];
+                    rt.s = slab_scale<FMT>(buf, tt, g);
+                    kb[tt] = decode<FMT>(rt);
+                }
+                // (tile, key tile) products in a two-deep software pipeline: the matrix
+                // core computes product q while the vector ALU applies ReLU and the head
+                // weights to product q-1.  Scheduling barriers keep that order (left
+                // alone, the compiler puts each product's epilogue right behind it and
+                // the wave waits for every product in turn).
+                constexpr int NP = 4 * NT;
+                v4f dprev = tile_dot<FMT>(a[0], kb[0]);
 #pragma unroll
-                for (int j = 0; j < NT; j++) {
-                    if (MKV && j / p.tiles_per_kv != hk) continue;
-                    const v4f d = tile_dot<FMT>(a[j], kb);
+                for (int q = 1; q <= NP; q++) {
+                    v4f dcur = dprev;
+                    if (q < NP) {
+                        const int tt = q / NT, j = q % NT;
+                        if (!MKV || j / p.tiles_per_kv == hk) dcur = tile_dot<FMT>(a[j], kb[tt]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int tp = (q - 1) / NT, jp = (q - 1) % NT;
+                    if (!MKV || jp / p.tiles_per_kv == hk) {
 #pragma unroll
-                    for (int i = 0; i < 4; i++)
-                        acc[tt][i] = __builtin_fmaf(wv[j][i], fmaxf(d[i], 0.0f), acc[tt][i]);
+                        for (int i = 0; i < 4; i++)
+                            acc[tp][i] = __builtin_fmaf(wv[jp][i], relu<FMT>(dprev[i]), acc[tp][i]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    dprev = dcur;
                 }
             }
             if (!MKV || hk == p.Hkv - 1) {  // all key heads of these 64 keys are in
-                const int phys = __builtin_amdgcn_readlane(my_phys, pi);
                 const int col0 = (lp_begin + pi) * p.page + half * 64 + 4 * n;
                 float o[4];
 #pragma unroll
@@ -347,12 +378,15 @@ __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
                 }
                 if (g < RG && row_ok) {
                     float* dst = p.out + (int64_t)t_out * p.out_rs + col0;
+                    // streaming stores: the logits are not read again by this kernel,
+                    // and keeping them out of L2 leaves room for the keys
                     if (p.vec_out && col0 + 3 < p.out_cols) {
-                        *reinterpret_cast<v4f*>(dst) = v4f{o[0], o[1], o[2], o[3]};
+                        __builtin_nontemporal_store(v4f{o[0], o[1], o[2], o[3]},
+                                                    reinterpret_cast<v4f*>(dst));
                     } else {
 #pragma unroll
                         for (int tt = 0; tt < 4; tt++)
-                            if (col0 + tt < p.out_cols) dst[tt] = o[tt];
+                            if (col0 + tt < p.out_cols) __builtin_nontemporal_store(o[tt], dst + tt);
                     }
                 }
             }

@@ -58,6 +58,11 @@ SMALL = [
     dict(name="h128", q_per_req=[2], ctx=[100], H=128),
     dict(name="nvfp4_decode", q_per_req=[4, 1], ctx=[333, 64], H=32, fmt=wl.NVFP4),
     dict(name="nvfp4_gqa", q_per_req=[2], ctx=[150], H=8, Hkv=4, fmt=wl.NVFP4),
+    # many rows per request: workgroups of four row blocks, a partial last group and
+    # row blocks that straddle two requests
+    dict(name="prefill_rows_major", q_per_req=[71, 60], ctx=[700, 260], H=64),
+    dict(name="prefill_rows_major_h32", q_per_req=[130], ctx=[1000], H=32),
+    dict(name="prefill_rows_major_nvfp4", q_per_req=[9, 67], ctx=[90, 400], H=16, fmt=wl.NVFP4),
 ]
 
 
