@@ -81,6 +81,15 @@ __device__ __forceinline__ RowRequest find_request(const int32_t* __restrict__ c
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Workgroup barrier that orders LDS only.  Every barrier in this library guards data in
+// LDS; __syncthreads() would also wait for each wave's outstanding global loads and
+// stores, which keeps prefetched data from staying in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // v[l] + v[l ^ 32] and v[l] + v[l ^ 16] with the gfx950 lane-swap instructions (plain
 // VALU operations, no LDS round trip).  Called with the same value in both operands,
 // v_permlane32_swap returns (v[l & 31], v[l | 32]) and v_permlane16_swap returns the
@@ -96,6 +105,14 @@ __device__ __forceinline__ float add_lane_xor16(float v) {
 __device__ __forceinline__ float max_lane_xor32(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ int max_lane_xor32i(int v) {
+    const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    return max((int)r[0], (int)r[1]);
+}
+__device__ __forceinline__ int max_lane_xor16i(int v) {
+    const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    return max((int)r[0], (int)r[1]);
 }
 __device__ __forceinline__ float max_lane_xor16(float v) {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -160,13 +177,13 @@ __device__ __forceinline__ void block_excl_scan(int x, int* wtot, int& excl, int
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int s = wave_incl_scan(x);
     if (lane == 63) wtot[wave] = s;
-    __syncthreads();
+    lds_barrier();
     const int t = lane < NW ? wtot[lane] : 0;
     const int ts = wave_incl_scan(t);
     const int before = wave > 0 ? __builtin_amdgcn_readlane(ts, wave - 1) : 0;
     total = __builtin_amdgcn_readlane(ts, NW - 1);
     excl = before + s - x;
-    __syncthreads();
+    lds_barrier();
 }
 
 // Thread-parallel bin pick: thread t owns PER bins listed in "before" order (c[b] =
@@ -195,7 +212,7 @@ __device__ __forceinline__ void pick_bin(const int (&c)[PER], const int (&bin)[P
             excl += c[b];
         }
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 }  // namespace fp4idx

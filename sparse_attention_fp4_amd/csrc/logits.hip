@@ -46,6 +46,9 @@ constexpr int kWavesPerBlock = 4;
 #ifndef FP4IDX_LOGITS_WAVES
 #define FP4IDX_LOGITS_WAVES 2048   // target number of waves of one launch
 #endif
+#ifndef FP4IDX_LOGITS_MAX_PPW
+#define FP4IDX_LOGITS_MAX_PPW 64   // at most this many pages per wave
+#endif
 
 // ---------------------------------------------------------------- operand types
 template <int FMT>
@@ -197,18 +200,51 @@ __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
     const int koff = 256 * n + 16 * g;          // lane's byte offset in a slab's keys
     const int soff = 4 * G * n;                 // and in its scale bytes
 
-    // ---- the first segment's metadata and first key slabs go out before the query
-    // staging below, so their round trips overlap it.  Lane i of my_phys holds the
-    // physical page of page lp_begin + i (-1: invisible or invalid); with one request
-    // the block-table row is known without the request lookup.
+    // ---- prologue.  Loads go out in the order their results are needed: the first
+    // segment's metadata (request, row lengths, block-table entries), then the
+    // workgroup's query staging, then the first two key slabs.  The LDS stores of the
+    // staged queries wait only for the staging loads and the barrier only for LDS, so the
+    // key loads stay in flight across both.  Lane i of my_phys holds the physical page of
+    // page lp_begin + i (-1: invisible or invalid); with one request the block-table
+    // row is known without the request lookup.
+    // Every prologue load reads a valid address (indices are clamped into range) and the
+    // unwanted values are replaced afterwards, so no branch separates a load from its use
+    // and each wait covers just the loads it needs.
     RowRequest rq = find_request(p.cu, p.B, t0);
-    const int lens_pref = (g % RG) < nrows ? p.lens[t0 + (g % RG)] : 0;
-    int bt_pref = -1;
-    {
+    const int nr1 = max(nrows, 1);  // a row block always holds at least one row
+    const int lens_raw = p.lens[t0 + min(g % RG, nr1 - 1)];
+    int bt_raw = -1;  // the block-table entry of page lp_begin + lane (clamped)
+    if (has_work && p.W > 0) {
         const int b_first = p.B == 1 ? 0 : rq.b;
-        if (has_work && lane < lp_end - lp_begin && lp_begin + lane < p.W)
-            bt_pref = p.bt[(int64_t)b_first * p.bt_rs + lp_begin + lane];
+        bt_raw = p.bt[(int64_t)b_first * p.bt_rs + min(lp_begin + lane, p.W - 1)];
     }
+    // staging loads into registers (RG * H <= 512: at most 8, 16 and 2 per thread)
+    constexpr int kSQ = 8, kSS = 16, kSW = 2;
+    v4i st_q[kSQ];
+    uint32_t st_s[kSS];
+    float st_w[kSW];
+#pragma unroll
+    for (int k = 0; k < kSQ; k++) {
+        const int i = threadIdx.x + 256 * k;
+        const int ic = min(i, RG * H * 4 - 1);
+        const int r = ic / (H * 4), rest = ic - r * (H * 4);
+        st_q[k] = load16(p.q + (int64_t)(t0 + min(r, nr1 - 1)) * p.q_rs + rest * 16);
+    }
+#pragma unroll
+    for (int k = 0; k < kSS; k++) {
+        const int i = threadIdx.x + 256 * k;
+        const int ic = min(i, RG * H * G - 1);
+        const int r = ic / (H * G), rest = ic - r * (H * G);
+        st_s[k] = p.qs[(int64_t)(t0 + min(r, nr1 - 1)) * p.qs_rs + rest];
+    }
+#pragma unroll
+    for (int k = 0; k < kSW; k++) {
+        const int i = threadIdx.x + 256 * k;
+        const int ic = min(i, RG * H - 1);
+        const int r = ic / H, h = ic - r * H;
+        st_w[k] = p.w[(int64_t)(t0 + min(r, nr1 - 1)) * p.w_rs + h];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     int b = 0, seg_end = t0, len = 0, my_phys = -1;
     bool req_ok = false, row_ok = false;
     auto setup_segment = [&](int t_seg, bool first) {
@@ -217,15 +253,13 @@ __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
         req_ok = rq.ok;
         seg_end = req_ok ? min(rq.end, t_last + 1) : t_last + 1;
         row_ok = t_out >= t_seg && t_out < seg_end;
+        const int lens_pref = (g % RG) < nrows ? lens_raw : 0;
         len = (row_ok && req_ok) ? min(lens_pref, p.out_cols) : 0;
-        int max_len = len;
-        max_len = max(max_len, __shfl_xor(max_len, 16));
-        max_len = max(max_len, __shfl_xor(max_len, 32));
-        max_len = uniform(max_len);
+        const int max_len = uniform(max_lane_xor32i(max_lane_xor16i(len)));
         my_phys = -1;
         const int lp = lp_begin + lane;
         if (has_work && req_ok && lane < lp_end - lp_begin && lp * p.page < max_len && lp < p.W) {
-            const int v = first ? bt_pref : p.bt[(int64_t)b * p.bt_rs + lp];
+            const int v = first ? bt_raw : p.bt[(int64_t)b * p.bt_rs + lp];
             my_phys = (v >= 0 && v < p.num_pages) ? v : -1;
         }
     };
@@ -261,23 +295,26 @@ __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
     setup_segment(t0, true);
     issue(0, b0);
     issue(1, b1);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- stage the row block's queries, scales and weights (zeros past T)
-    for (int i = threadIdx.x; i < RG * H * 4; i += 256) {
-        const int r = i / (H * 4), rest = i - r * (H * 4);
-        v4i v = v4i{0, 0, 0, 0};
-        if (r < nrows) v = load16(p.q + (int64_t)(t0 + r) * p.q_rs + rest * 16);
-        *reinterpret_cast<v4i*>(sq + (int64_t)i * 16) = v;
+    // ---- the staged queries, scales and weights into LDS (zeros past T)
+#pragma unroll
+    for (int k = 0; k < kSQ; k++) {
+        const int i = threadIdx.x + 256 * k;
+        if (i < RG * H * 4)
+            *reinterpret_cast<v4i*>(sq + (int64_t)i * 16) = i / (H * 4) < nrows ? st_q[k] : v4i{0, 0, 0, 0};
     }
-    for (int i = threadIdx.x; i < RG * H * G; i += 256) {
-        const int r = i / (H * G), rest = i - r * (H * G);
-        sqs[i] = r < nrows ? p.qs[(int64_t)(t0 + r) * p.qs_rs + rest] : (uint8_t)(FMT == 0 ? 127 : 0);
+#pragma unroll
+    for (int k = 0; k < kSS; k++) {
+        const int i = threadIdx.x + 256 * k;
+        if (i < RG * H * G) sqs[i] = (uint8_t)(i / (H * G) < nrows ? st_s[k] : (FMT == 0 ? 127u : 0u));
     }
-    for (int i = threadIdx.x; i < RG * H; i += 256) {
-        const int r = i / H, h = i - r * H;
-        sw[i] = r < nrows ? p.w[(int64_t)(t0 + r) * p.w_rs + h] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < kSW; k++) {
+        const int i = threadIdx.x + 256 * k;
+        if (i < RG * H) sw[i] = i / H < nrows ? st_w[k] : 0.0f;
     }
-    __syncthreads();
+    lds_barrier();
     if (!has_work) return;  // uniform per wave, after the only barrier
 
     // The rows of a block may belong to different requests; each pass handles the rows
@@ -357,9 +394,13 @@ __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
                     __builtin_amdgcn_sched_barrier(0);
                     const int tp = (q - 1) / NT, jp = (q - 1) % NT;
                     if (!MKV || jp / p.tiles_per_kv == hk) {
+                        // four independent ReLUs first, then the four multiply-adds, so
+                        // no instruction waits on the one just before it
+                        float r[4];
 #pragma unroll
-                        for (int i = 0; i < 4; i++)
-                            acc[tp][i] = __builtin_fmaf(wv[jp][i], relu<FMT>(dprev[i]), acc[tp][i]);
+                        for (int i = 0; i < 4; i++) r[i] = relu<FMT>(dprev[i]);
+#pragma unroll
+                        for (int i = 0; i < 4; i++) acc[tp][i] = __builtin_fmaf(wv[jp][i], r[i], acc[tp][i]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                     dprev = dcur;
@@ -463,7 +504,7 @@ hipError_t launch_logits(const LogitsParams& p_in, hipStream_t stream) {
     // early free their slots for the rest.
     const int64_t total = (int64_t)p.n_rowblocks * n_pages_out;
     int64_t ppw = (total + FP4IDX_LOGITS_WAVES - 1) / FP4IDX_LOGITS_WAVES;
-    ppw = ppw < 1 ? 1 : (ppw > 64 ? 64 : ppw);
+    ppw = ppw < 1 ? 1 : (ppw > FP4IDX_LOGITS_MAX_PPW ? FP4IDX_LOGITS_MAX_PPW : ppw);
     p.ppw = (int)ppw;
     p.n_wchunks = (n_pages_out + p.ppw - 1) / p.ppw;
     p.n_wgchunks = (p.n_wchunks + kWavesPerBlock - 1) / kWavesPerBlock;

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(const TopkParams p) {
             sh.wave_cnt[wave] = cnt;
         }
     }
-    __syncthreads();
+    lds_barrier();
     uint32_t lo = 0xffffffffu, hi = 0u;
     int n_valid = 0;
     for (int w = 0; w < kWaves; w++) {
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(const TopkParams p) {
                 const uint32_t kj = key[j];
                 if (kj != 0u && kj >= lo && kj <= hi) atomicAdd(&sh.hist[(kj - lo) >> shift], 1u);
             }
-            __syncthreads();
+            lds_barrier();
             {
                 constexpr int per = kBins / kThreads;  // bins per thread, walked from the top
                 int c[per], bin[per];
@@ -158,9 +158,9 @@ __global__ __launch_bounds__(kThreads) void k_topk(const TopkParams p) {
             const uint32_t nhi_raw = nlo + width_m1;
             hi = min(hi, nhi_raw < nlo ? 0xffffffffu : nhi_raw);
             lo = nlo;
-            __syncthreads();
+            lds_barrier();
             clear_hist(sh);
-            __syncthreads();
+            lds_barrier();
         }
         T = lo;
         need = kk;  // >= 1 keys equal to T are kept
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(const TopkParams p) {
             sh.cnt_eq[j * kWaves + wave] = __popcll(me);
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
         // exclusive scans over the kPer * kWaves blocks in index order: ties first (the
         // first `need` ties are kept), then selected = gt + kept ties
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(const TopkParams p) {
         }
         if (lane == 63) sh.total = sel_before;
     }
-    __syncthreads();
+    lds_barrier();
     const int total = sh.total;
     const float* srow = p.scores + (int64_t)row * p.row_stride;
 #pragma unroll

@@ -100,11 +100,11 @@ __global__ __launch_bounds__(kCT) void k_hist(const TopkParams p, LongWs ws) {
     for (int i = threadIdx.x; i < kBins; i += kCT) h[i] = 0u;
     uint32_t key[kPer];
     load_chunk(p, row, chunk, key);
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int j = 0; j < kPer; j++)
         if (key[j]) atomicAdd(&h[key[j] >> 20], 1u);
-    __syncthreads();
+    lds_barrier();
     uint32_t* gh = ws.hist + (int64_t)row * kBins;
     for (int i = threadIdx.x; i < kBins; i += kCT)
         if (h[i]) atomicAdd(&gh[i], h[i]);
@@ -173,14 +173,14 @@ __global__ __launch_bounds__(kCT) void k_collect(const TopkParams p, LongWs ws) 
         if (lane == 0) sh.cnt[j * (kCT / 64) + wave] = __popcll(mc);
         if (cand[j]) atomicAdd(&sh.h2[(kj >> 8) & 0xfffu], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {  // exclusive scan over the kPer * 4 = 64 (step, wave) blocks
         const int x = sh.cnt[lane];
         const int s = wave_incl_scan(x);
         sh.off[lane] = s - x;
         if (lane == 63) sh.total = s;
     }
-    __syncthreads();
+    lds_barrier();
     // Global writes come last: a barrier after them would wait for their completion.
     uint2* dst = ws.cand + ((int64_t)row * nch + chunk) * kChunk;
 #pragma unroll
@@ -267,14 +267,14 @@ __device__ __forceinline__ void cand_pass(FinishShared& sh, CandRegs& r, const L
                                           int m, int rounds, bool flat, int kk, bool descending, Keep keep,
                                           Digit digit) {
     for (int i = threadIdx.x; i < kBins; i += kFT) sh.h[i] = 0u;
-    __syncthreads();
+    lds_barrier();
     for (int round = 0; round < rounds; round++) {
         if (flat) load_flat(r, sh, ws, row, nch, m, round);
 #pragma unroll
         for (int j = 0; j < kCR; j++)
             if (r.col[j] >= 0 && keep(r.key[j], r.col[j])) atomicAdd(&sh.h[digit(r.key[j], r.col[j])], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     constexpr int per = kBins / kFT;
     int c[per], bin[per];
 #pragma unroll
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (n_pre <= kRankMax) {
             // ---- rank each collected candidate by direct comparison
             const int nm = min(sh.nm, kRankMax);
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- columns in order: thread t owns words [t*wpt, (t+1)*wpt) of the bitmap; a
     // block scan of their popcounts gives each thread its output offset
