@@ -152,6 +152,30 @@ __device__ __forceinline__ v8h decode8_f16(uint32_t packed, float pow2, float b)
     return r;
 }
 
+// Reduction over the 64 lanes of a wave without LDS: DPP quad permutations and row
+// mirrors combine the 16 lanes of each row, then the two lane-swap instructions combine
+// rows and halves.  Every lane receives the result.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xf, 0xf, false));   // lane ^ 1
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xf, 0xf, false));   // lane ^ 2
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xf, 0xf, false));  // 7 - lane%8
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xf, 0xf, false));  // 15 - lane%16
+    const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = op((uint32_t)r16[0], (uint32_t)r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return op((uint32_t)r32[0], (uint32_t)r32[1]);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    return wave_reduce(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    return wave_reduce(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+    return (int)wave_reduce((uint32_t)v, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS): three
 // row_shr steps and two masked ones give each 16-lane row its scan, then row_bcast:15
 // and row_bcast:31 carry row totals into the rows above (GCN/CDNA cross-lane scan).

@@ -42,8 +42,21 @@ __device__ __forceinline__ uint32_t to_key(float v) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of to_key for selectable keys.
+__device__ __forceinline__ float from_key(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+constexpr int kRankMax = 1024;  // threshold-bin candidates ranked by direct comparison
+
 struct Shared {
     uint32_t hist[kBins];
+    uint32_t mkey[kRankMax];     // candidates in the threshold bin of the value pass
+    int midx[kRankMax];
+    int nm;
+    uint32_t T;
+    int need;
+    uint32_t blo, bhi;
     int cnt_gt[kPer * kWaves];   // per (step j, wave w), index e = j * kWaves + w
     int cnt_eq[kPer * kWaves];
     int off_sel[kPer * kWaves];
@@ -101,12 +114,9 @@ __global__ __launch_bounds__(kThreads) void k_topk(const TopkParams p) {
                 cnt++;
             }
         }
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) {
-            mn = min(mn, (uint32_t)__shfl_xor((int)mn, d));
-            mx = max(mx, (uint32_t)__shfl_xor((int)mx, d));
-            cnt += __shfl_xor(cnt, d);
-        }
+        mn = wave_min_u32(mn);
+        mx = wave_max_u32(mx);
+        cnt = wave_sum_i32(cnt);
         if (lane == 0) {
             sh.wave_min[wave] = mn;
             sh.wave_max[wave] = mx;
@@ -131,7 +141,89 @@ __global__ __launch_bounds__(kThreads) void k_topk(const TopkParams p) {
         // invariant: the k-th largest key is in [lo, hi] and kk of the wanted keys are
         // in [lo, hi] (the rest are above hi)
         int kk = k;
-        while (lo < hi) {
+        bool resolved = false;
+        // ---- first pass in value space: 4096 equal-width bins between the smallest and
+        // the largest value.  The bin index is a monotone function of the value, so the
+        // bins above the one holding the k-th value hold only selected keys; scores that
+        // crowd a few octaves (as logits do) spread over many bins instead of a handful
+        // of key-prefix bins.  The few keys of that bin are then ranked by comparison.
+        const float vlo = from_key(lo), vhi = from_key(hi);
+        const float scale = (float)kBins / (vhi - vlo);
+        if (vhi > vlo && __builtin_isfinite(vlo) && __builtin_isfinite(vhi) && __builtin_isfinite(scale)) {
+            auto vbin = [&](uint32_t kx) {
+                const int b = (int)((from_key(kx) - vlo) * scale);
+                return b < kBins - 1 ? b : kBins - 1;
+            };
+#pragma unroll
+            for (int j = 0; j < PER; j++)
+                if (key[j] != 0u) atomicAdd(&sh.hist[vbin(key[j])], 1u);
+            if (tid == 0) {
+                sh.nm = 0;
+                sh.blo = 0xffffffffu;
+                sh.bhi = 0u;
+            }
+            lds_barrier();
+            {
+                constexpr int per = kBins / kThreads;
+                int c[per], bin[per];
+#pragma unroll
+                for (int b = 0; b < per; b++) {
+                    bin[b] = kBins - 1 - (tid * per + b);
+                    c[b] = (int)sh.hist[bin[b]];
+                }
+                pick_bin<kThreads, per>(c, bin, kk, sh.wtot, sh.pick);
+            }
+            const int d = sh.pick[0];
+            const int nd = sh.pick[3];
+            kk -= sh.pick[1];  // wanted keys inside bin d, >= 1
+            if (nd <= kRankMax) {
+#pragma unroll
+                for (int j = 0; j < PER; j++) {
+                    if (key[j] != 0u && vbin(key[j]) == d) {
+                        const int at = atomicAdd(&sh.nm, 1);
+                        if (at < kRankMax) {
+                            sh.mkey[at] = key[j];
+                            sh.midx[at] = tid + kThreads * j;
+                        }
+                    }
+                }
+                lds_barrier();
+                const int nm = min(sh.nm, kRankMax);
+                for (int t = tid; t < nm; t += kThreads) {
+                    const uint32_t kt = sh.mkey[t];
+                    const int it = sh.midx[t];
+                    int gt = 0, rank = 0;
+                    for (int u = 0; u < nm; u++) {
+                        const uint32_t ku = sh.mkey[u];
+                        gt += ku > kt ? 1 : 0;
+                        rank += (ku > kt || (ku == kt && sh.midx[u] < it)) ? 1 : 0;
+                    }
+                    if (rank == kk - 1) {  // the k-th selected key: T and the ties to keep
+                        sh.T = kt;
+                        sh.need = kk - gt;
+                    }
+                }
+                lds_barrier();
+                lo = hi = sh.T;
+                kk = sh.need;
+                resolved = true;
+            } else {
+                // many keys in bin d (heavy ties): continue in key space on its key range
+#pragma unroll
+                for (int j = 0; j < PER; j++) {
+                    if (key[j] != 0u && vbin(key[j]) == d) {
+                        atomicMin(&sh.blo, key[j]);
+                        atomicMax(&sh.bhi, key[j]);
+                    }
+                }
+                lds_barrier();
+                lo = sh.blo;
+                hi = sh.bhi;
+            }
+            clear_hist(sh);
+            lds_barrier();
+        }
+        while (!resolved && lo < hi) {
             const uint32_t span_m1 = hi - lo;
             const int bits = 32 - __clz((int)span_m1);
             const int shift = bits > kBinBits ? bits - kBinBits : 0;
@@ -166,14 +258,19 @@ __global__ __launch_bounds__(kThreads) void k_topk(const TopkParams p) {
         need = kk;  // >= 1 keys equal to T are kept
     }
 
-    // ---- ordered compaction over index order (j, wave, lane)
+    // ---- ordered compaction over index order (j, wave, lane); steps past the row's
+    // length hold no key and are skipped (their counts are zero)
+    const int nsteps = (n + kThreads - 1) / kThreads;
 #pragma unroll
     for (int j = 0; j < PER; j++) {
-        const unsigned long long mg = __ballot(key[j] > T);
-        const unsigned long long me = __ballot(need > 0 && key[j] == T);
+        int cg = 0, ce = 0;
+        if (j < nsteps) {
+            cg = __popcll(__ballot(key[j] > T));
+            ce = __popcll(__ballot(need > 0 && key[j] == T));
+        }
         if (lane == 0) {
-            sh.cnt_gt[j * kWaves + wave] = __popcll(mg);
-            sh.cnt_eq[j * kWaves + wave] = __popcll(me);
+            sh.cnt_gt[j * kWaves + wave] = cg;
+            sh.cnt_eq[j * kWaves + wave] = ce;
         }
     }
     lds_barrier();
@@ -190,12 +287,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(const TopkParams p) {
             gt[u] = sh.cnt_gt[lane * per + u];
             se += eq[u];
         }
-        int ie = se;  // inclusive prefix over lanes
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            int y = __shfl_up(ie, d);
-            if (lane >= d) ie += y;
-        }
+        const int ie = wave_incl_scan(se);  // inclusive prefix over lanes
         int tie_before = ie - se;
         int sel[per];
         int ss = 0;
@@ -207,12 +299,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(const TopkParams p) {
             sel[u] = gt[u] + take;
             ss += sel[u];
         }
-        int is = ss;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            int y = __shfl_up(is, d);
-            if (lane >= d) is += y;
-        }
+        const int is = wave_incl_scan(ss);
         int sel_before = is - ss;
 #pragma unroll
         for (int u = 0; u < per; u++) {
@@ -226,6 +313,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(const TopkParams p) {
     const float* srow = p.scores + (int64_t)row * p.row_stride;
 #pragma unroll
     for (int j = 0; j < PER; j++) {
+        if (j >= nsteps) continue;
         const int e = j * kWaves + wave;
         const bool is_gt = key[j] > T;
         const bool is_eq = need > 0 && key[j] == T;

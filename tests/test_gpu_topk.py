@@ -50,16 +50,31 @@ def test_indices_only(rows, cols):
     assert np.array_equal(idx.cpu().numpy(), oi)
 
 
-def test_ties_zeros_and_lengths():
+@pytest.mark.parametrize("cols", [40000, 20000, 3000])
+def test_ties_zeros_and_lengths(cols):
     rng = np.random.default_rng(4)
-    rows, cols, k = 6, 40000, 2048
+    rows, k = 6, 2048
     s = (rng.integers(-20, 20, (rows, cols)) / 4).astype(np.float32)  # heavy ties
     s[1, ::3] = -0.0
     s[2, :] = 1.5                                                     # all equal
     s[3, :] = -np.inf                                                 # nothing valid
     s[4, 100:] = -np.inf                                              # fewer than k valid
-    lens = np.array([40000, 39999, 1, 20000, 40000, 0], np.int32)
+    lens = np.array([cols, cols - 1, 1, cols // 2, cols, 0], np.int32)
     _same(s, k, lens)
+
+
+@pytest.mark.parametrize("cols", [16384, 100_000])
+def test_clustered_values_with_outliers(cols):
+    """Most scores in a narrow band, a few far away (value-space bins put nearly all in
+    one bin), plus +inf entries."""
+    rng = np.random.default_rng(cols + 1)
+    s = (1.0 + rng.standard_normal((3, cols)) * 1e-6).astype(np.float32)
+    s[0, 7] = 1e30
+    s[0, 9] = -1e30
+    s[1, 100] = np.inf
+    s[2, :] = np.float32(1.0)
+    s[2, ::17] = np.float32(1.0000001)
+    _same(s, 2048)
 
 
 def test_on_config1_logits_within_tie_tolerance():
