@@ -371,6 +371,76 @@ void orc_topk(const float* scores, int64_t row_stride, int rows, int cols,
 }
 
 /* Threads an OpenMP region would use (for reporting). */
+/* ---------------------------------------------------------------------------------
+ * MXFP4 quantize-and-store of index keys into the paged cache.
+ *
+ * [SGL] bench and Modifications: keys [N][128] in bf16 are written into 64-byte
+ * nibble rows and 4 E8M0 codes per token of a paged cache, at the page and token a
+ * slot names (page = slot / page_size, token = slot % page_size); rounding is to
+ * nearest even ("rne=True"); stored exponent codes are clamped to 1..254.  [ISS] "Why
+ * it's wrong": the stored nibble is the index into {0, 0.5, 1, 1.5, 2, 3, 4, 6} with
+ * the sign in bit 3.
+ *
+ * Reading (the pages do not say how a block's exponent is chosen): the OCP
+ * microscaling rule -- the scale of a 32-value block is 2^(floor(log2(amax)) - 2),
+ * with 2 the exponent of E2M1's largest value 6, so amax / scale lies in [4, 8); the
+ * code is that exponent + 127 clamped to 1..254 (an all-zero block gets code 1).  Each
+ * value is divided by the scale and mapped to the nearest of the eight magnitudes,
+ * ties going to the even index (mantissa bit 0); magnitudes above 6 take 6; the sign
+ * bit is copied (so -0 and small negatives that round to zero store code 8).
+ * Parity pinned by closed forms, a hand-worked fixture and properties in the tests.
+ * ------------------------------------------------------------------------------- */
+
+/* One block of 32 values -> 16 packed bytes (element 2j in the low nibble of byte j)
+ * and its E8M0 code. */
+void orc_quantize_mx_block(const double* x, uint8_t* packed, uint8_t* code_out) {
+    static const double level[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    double amax = 0.0;
+    for (int i = 0; i < 32; i++)
+        if (fabs(x[i]) > amax) amax = fabs(x[i]);
+    int code = 1;
+    if (amax > 0.0) {
+        int e;
+        frexp(amax, &e);             /* amax = f * 2^e with f in [0.5, 1) */
+        int shared = (e - 1) - 2;    /* floor(log2(amax)) - 2 */
+        code = shared + 127;
+        if (code < 1) code = 1;
+        if (code > 254) code = 254;
+    }
+    double scale = ldexp(1.0, code - 127);
+    for (int i = 0; i < 32; i++) {
+        double m = fabs(x[i]) / scale;
+        int best = 0;
+        for (int c = 1; c < 8; c++) {
+            double d = fabs(m - level[c]), db = fabs(m - level[best]);
+            if (d < db || (d == db && (c & 1) == 0)) best = c;
+        }
+        unsigned nib = (unsigned)best | (signbit(x[i]) ? 8u : 0u);
+        if (i & 1) packed[i >> 1] = (uint8_t)(packed[i >> 1] | (nib << 4));
+        else packed[i >> 1] = (uint8_t)nib;
+    }
+    *code_out = (uint8_t)code;
+}
+
+/* Keys [N][128] (as doubles) into the cache: token n goes to slot slots[n]; a slot
+ * outside [0, num_pages * page) is skipped.  Layouts as in orc_logits_paged (one key
+ * head): k_fp4 pages k_page_stride bytes apart holding [page][64], k_scale pages
+ * ks_page_stride bytes apart holding [page][4]. */
+void orc_quantize_store(const double* keys, const int64_t* slots, int N,
+                        uint8_t* k_fp4, int64_t k_page_stride,
+                        uint8_t* k_scale, int64_t ks_page_stride,
+                        int page, int num_pages) {
+    for (int n = 0; n < N; n++) {
+        int64_t slot = slots[n];
+        if (slot < 0 || slot >= (int64_t)num_pages * page) continue;
+        int64_t pg = slot / page, tok = slot % page;
+        for (int g = 0; g < 4; g++)
+            orc_quantize_mx_block(keys + (int64_t)n * 128 + 32 * g,
+                                  k_fp4 + pg * k_page_stride + tok * 64 + 16 * g,
+                                  k_scale + pg * ks_page_stride + tok * 4 + g);
+    }
+}
+
 int orc_max_threads(int n_threads) {
 #ifdef _OPENMP
     if (n_threads > 0) return n_threads;

@@ -56,6 +56,10 @@ def lib():
         L.orc_topk.argtypes = [P, i64, i32, i32, P, i32, P, P, i32]
         L.orc_max_threads.restype = i32
         L.orc_max_threads.argtypes = [i32]
+        L.orc_quantize_mx_block.restype = None
+        L.orc_quantize_mx_block.argtypes = [P, P, P]
+        L.orc_quantize_store.restype = None
+        L.orc_quantize_store.argtypes = [P, P, i32, P, i64, P, i64, i32, i32]
         _lib = L
     return _lib
 
@@ -203,3 +207,27 @@ def topk(scores, k, row_lens=None, n_threads=0):
 
 def max_threads(n_threads=0) -> int:
     return int(lib().orc_max_threads(n_threads))
+
+
+def quantize_mx_block(x):
+    """32 real values -> (16 packed bytes, E8M0 code)."""
+    x = _c(x, np.float64)
+    assert x.shape == (32,)
+    packed = np.zeros(16, np.uint8)
+    code = np.zeros(1, np.uint8)
+    lib().orc_quantize_mx_block(_p(x), _p(packed), _p(code))
+    return packed, int(code[0])
+
+
+def quantize_store(keys, slots, k_fp4, k_scale):
+    """Keys [N,128] (real values) into copies of the cache arrays k_fp4 [P,1,page,64] and
+    k_scale [P,1,page,4] at the given slots (others untouched) -> (k_fp4, k_scale)."""
+    keys = _c(keys, np.float64)
+    slots = _c(slots, np.int64)
+    kf = np.array(k_fp4, dtype=np.uint8, copy=True, order="C")
+    ks = np.array(k_scale, dtype=np.uint8, copy=True, order="C")
+    P, hkv, page = kf.shape[0], kf.shape[1], kf.shape[2]
+    assert hkv == 1 and ks.shape == (P, 1, page, 4) and keys.shape[1] == 128
+    lib().orc_quantize_store(_p(keys), _p(slots), keys.shape[0], _p(kf), page * 64, _p(ks),
+                             page * 4, page, P)
+    return kf, ks

@@ -438,3 +438,88 @@ def test_compact_rows_match_the_full_call():
                                   case.k_scale, case.block_table, case.cu_seqlens_q, case.row_lens,
                                   case.page_size, case.out_cols, rows=rows, compact=True)
     np.testing.assert_array_equal(comp, full[sorted(rows)])
+
+
+# ---------------------------------------------------------------- quantizer pins
+def _golden_blocks():
+    blocks, cur = [], None
+    with open(os.path.join(GOLDEN, "quantize_blocks.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            parts = line.split()
+            if parts[0] == "block":
+                cur = dict(name=parts[1], code=int(parts[3]), x=np.zeros(32), nib=np.zeros(32, int))
+                blocks.append(cur)
+            else:
+                i = int(parts[0])
+                cur["x"][i] = float(parts[1])
+                cur["nib"][i] = int(parts[2])
+    return blocks
+
+
+@pytest.mark.parametrize("blk", _golden_blocks(), ids=lambda b: b["name"])
+def test_quantize_block_matches_hand_worked_fixture(blk):
+    packed, code = orc.quantize_mx_block(blk["x"])
+    assert code == blk["code"]
+    nib = np.empty(32, int)
+    nib[0::2] = packed & 15
+    nib[1::2] = packed >> 4
+    assert np.array_equal(nib, blk["nib"])
+
+
+def _nearest_even_level(m):
+    """numpy reference of the rounding rule: nearest of the eight magnitudes, ties to
+    the even index."""
+    lv = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    d = np.abs(m[:, None] - lv[None, :])
+    dmin = d.min(axis=1, keepdims=True)
+    cand = np.where(np.isclose(d, dmin, rtol=0, atol=0), np.arange(8)[None, :], 99)
+    even = np.where(cand % 2 == 0, cand, 99).min(axis=1)
+    return np.where(even < 99, even, cand.min(axis=1))
+
+
+def test_quantize_random_blocks_against_numpy_rounding_and_exponent_rule():
+    rng = np.random.default_rng(21)
+    for t in range(400):
+        mag = 2.0 ** rng.integers(-20, 20)
+        x = (rng.standard_normal(32) * mag).astype(np.float32).astype(np.float64)
+        if t % 7 == 0:
+            x[rng.integers(0, 32, 5)] = 0.0
+        packed, code = orc.quantize_mx_block(x)
+        amax = np.abs(x).max()
+        assert code == int(np.clip(np.floor(np.log2(amax)) - 2 + 127, 1, 254))
+        scale = 2.0 ** (code - 127)
+        want = _nearest_even_level(np.abs(x) / scale)
+        nib = np.empty(32, int)
+        nib[0::2] = packed & 15
+        nib[1::2] = packed >> 4
+        assert np.array_equal(nib & 7, want)
+        assert np.array_equal(nib >> 3, np.signbit(x).astype(int))
+        # decoding with the library E2M1 / E8M0 decoders stays within half a grid step
+        dec = lib_dequant(wl.MXFP4, np.concatenate([packed, np.zeros(48, np.uint8)]),
+                          np.array([code, 127, 127, 127], np.uint8))[:32]
+        step = np.where(np.abs(x) / scale >= 4, 2.0, np.where(np.abs(x) / scale >= 2, 1.0, 0.5))
+        assert np.all(np.abs(dec - np.clip(x, -6 * scale, 6 * scale)) <= 0.5 * step * scale)
+
+
+def test_quantize_store_scatters_by_slot():
+    rng = np.random.default_rng(22)
+    P, page = 5, 64
+    kf = rng.integers(0, 256, (P, 1, page, 64), dtype=np.uint8)
+    ks = rng.integers(0, 256, (P, 1, page, 4), dtype=np.uint8)
+    keys = rng.standard_normal((7, 128))
+    slots = np.array([3, 200, -1, 319, 64, 320, 0], np.int64)   # -1 and 320 are skipped
+    of, os_ = orc.quantize_store(keys, slots, kf, ks)
+    touched = np.zeros((P, page), bool)
+    for n, s in enumerate(slots):
+        if 0 <= s < P * page:
+            pg, tok = divmod(int(s), page)
+            touched[pg, tok] = True
+            for g in range(4):
+                pk, c = orc.quantize_mx_block(keys[n, 32 * g:32 * g + 32])
+                assert np.array_equal(of[pg, 0, tok, 16 * g:16 * g + 16], pk)
+                assert os_[pg, 0, tok, g] == c
+    assert np.array_equal(of[:, 0][~touched], kf[:, 0][~touched])
+    assert np.array_equal(os_[:, 0][~touched], ks[:, 0][~touched])
