@@ -156,6 +156,34 @@ int fp4idx_topk(const float* scores, int64_t row_stride, int rows, int cols,
                 int32_t* out_idx, float* out_vals,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* MXFP4 quantize-and-store of index keys into the paged cache ([SGL] Modifications and
+ * bench: bf16 keys become E2M1 nibbles plus one E8M0 code per 32 values, rounded to
+ * nearest even, written at the page and token their slot names; stored exponent codes
+ * are clamped to 1..254; [ISS] "Why it's wrong": nibble = index into the level set,
+ * sign in bit 3):
+ *
+ *     token n (keys row n, 128 values) -> page slots[n] / page_size,
+ *                                         token slots[n] % page_size
+ *
+ * Each block of 32 values gets the scale 2^(floor(log2(amax)) - 2), with amax its
+ * largest magnitude (the OCP microscaling rule; the pages do not say how the exponent
+ * is chosen); its E8M0 code is that exponent + 127 clamped to 1..254 (an all-zero or
+ * subnormal block gets 1).  Each value divided by the scale is stored as the nearest
+ * level, ties to the even index, magnitudes above 6 as 6, with its sign bit copied
+ * (so -0 stores 8).  Keys must be finite (NaN and Inf give unspecified codes).
+ *
+ * Layouts: keys [N][key_row_stride] bf16 bit patterns (row stride in elements, even;
+ * keys 4-byte aligned, else EALIGN); slots [N] int64 -- a slot outside
+ * [0, num_pages * page_size) leaves its token unwritten; k_fp4 / k_scale: the cache of
+ * fp4idx_logits_paged with Hkv = 1 (MXFP4: [P][page_size][64] nibbles and [P][page_size][4]
+ * codes, pages k_page_stride / ks_page_stride bytes apart).  Two tokens with the same
+ * slot race.  Limits: page_size in {64, 128} (else EUNSUPPORTED). */
+int fp4idx_quantize_store_k(const uint16_t* keys, int64_t key_row_stride,
+                            const int64_t* slots, int N,
+                            uint8_t* k_fp4, int64_t k_page_stride,
+                            uint8_t* k_scale, int64_t ks_page_stride,
+                            int page_size, int num_pages, void* stream);
+
 /* Static string naming a status code. */
 const char* fp4idx_strerror(int code);
 

@@ -6,9 +6,12 @@ this package is its Python binding:
     logits_paged(...)   weighted-ReLU logits over a paged FP4 key cache
     block_scores(...)   per-head 128-token block-max scores
     topk(...)           exact top-k column selection per row
+    quantize_store_k(...)  MXFP4 quantize-and-store of keys into the paged cache
 
 ``workloads`` holds seeded synthetic inputs for the benchmark shapes.
 """
-from .ops import MXFP4, NVFP4, block_scores, logits_paged, topk, topk_workspace_bytes  # noqa: F401
+from .ops import (MXFP4, NVFP4, block_scores, logits_paged, quantize_store_k, topk,  # noqa: F401
+                  topk_workspace_bytes)
 
-__all__ = ["MXFP4", "NVFP4", "logits_paged", "block_scores", "topk", "topk_workspace_bytes"]
+__all__ = ["MXFP4", "NVFP4", "logits_paged", "block_scores", "topk", "topk_workspace_bytes",
+           "quantize_store_k"]

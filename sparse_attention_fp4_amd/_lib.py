@@ -18,6 +18,7 @@ EXPORTS = (
     "fp4idx_block_scores",
     "fp4idx_topk_workspace_bytes",
     "fp4idx_topk",
+    "fp4idx_quantize_store_k",
     "fp4idx_strerror",
     "fp4idx_version",
 )
@@ -52,6 +53,8 @@ def lib() -> ctypes.CDLL:
     L.fp4idx_topk_workspace_bytes.argtypes = [i32, i32, i32]
     L.fp4idx_topk.restype = i32
     L.fp4idx_topk.argtypes = [P, i64, i32, i32, P, i32, P, P, P, ctypes.c_size_t, P]
+    L.fp4idx_quantize_store_k.restype = i32
+    L.fp4idx_quantize_store_k.argtypes = [P, i64, P, i32, P, i64, P, i64, i32, i32, P]
     L.fp4idx_strerror.restype = ctypes.c_char_p
     L.fp4idx_strerror.argtypes = [i32]
     L.fp4idx_version.restype = i32

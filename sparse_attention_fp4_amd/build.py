@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libfp4idx.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["fp4idx_api.hip", "logits.hip", "block_scores.hip", "topk.hip", "topk_long.hip"]
+SOURCES = ["fp4idx_api.hip", "logits.hip", "block_scores.hip", "topk.hip", "topk_long.hip",
+           "quantize.hip"]
 ARCH = "gfx950"
 
 

@@ -142,6 +142,31 @@ int fp4idx_block_scores(int fmt,
     return hip_status(fp4idx::launch_block_scores(p, (hipStream_t)stream));
 }
 
+int fp4idx_quantize_store_k(const uint16_t* keys, int64_t key_row_stride, const int64_t* slots, int N,
+                            uint8_t* k_fp4, int64_t k_page_stride, uint8_t* k_scale,
+                            int64_t ks_page_stride, int page_size, int num_pages, void* stream) {
+    if (N < 0 || num_pages < 0) return FP4IDX_EINVAL;
+    if (page_size != 64 && page_size != 128) return FP4IDX_EUNSUPPORTED;
+    if (N == 0 || num_pages == 0) return FP4IDX_OK;
+    if (!keys || !slots || !k_fp4 || !k_scale) return FP4IDX_EINVAL;
+    if (key_row_stride < 128 || k_page_stride < (int64_t)page_size * 64 ||
+        ks_page_stride < (int64_t)page_size * 4)
+        return FP4IDX_EINVAL;
+    if (((uintptr_t)keys & 3u) || (key_row_stride & 1)) return FP4IDX_EALIGN;
+    fp4idx::QuantParams p{};
+    p.keys = keys;
+    p.key_rs = key_row_stride;
+    p.slots = slots;
+    p.k = k_fp4;
+    p.kp_s = k_page_stride;
+    p.ks = k_scale;
+    p.ksp_s = ks_page_stride;
+    p.N = N;
+    p.page = page_size;
+    p.num_pages = num_pages;
+    return hip_status(fp4idx::launch_quantize_store(p, (hipStream_t)stream));
+}
+
 size_t fp4idx_topk_workspace_bytes(int rows, int cols, int k) {
     if (rows <= 0 || cols <= 0 || k <= 0) return 0;
     return fp4idx::topk_workspace_bytes(rows, cols, k);

@@ -69,6 +69,19 @@ struct TopkParams {
 hipError_t launch_logits(const LogitsParams& p, hipStream_t stream);
 hipError_t launch_block_scores(const BlockParams& p, hipStream_t stream);
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
+
+struct QuantParams {
+    const uint16_t* keys;  // [N][key_rs] bf16 bit patterns
+    int64_t key_rs;        // elements between key rows
+    const int64_t* slots;  // [N]
+    uint8_t* k;            // key pages, kp_s bytes apart: [page][64]
+    int64_t kp_s;
+    uint8_t* ks;           // scale pages, ksp_s bytes apart: [page][4]
+    int64_t ksp_s;
+    int N, page, num_pages;
+};
+
+hipError_t launch_quantize_store(const QuantParams& p, hipStream_t stream);
 size_t topk_workspace_bytes(int rows, int cols, int k);
 
 }  // namespace fp4idx

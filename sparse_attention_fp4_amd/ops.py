@@ -196,3 +196,29 @@ def topk(scores, k: int, row_lens=None, *, out_idx=None, out_vals=None, want_val
                            0 if workspace is None else workspace.numel(), _stream())
     check("fp4idx_topk", rc)
     return out_idx, out_vals
+
+
+def quantize_store_k(keys, slots, k_fp4, k_scale):
+    """MXFP4 quantize-and-store of keys [N, 128] (bf16) into the paged cache k_fp4
+    [P, 1, page, 64] / k_scale [P, 1, page, 4] (uint8, modified in place) at the given
+    slots [N] (int64; slots outside the cache are skipped)."""
+    _need(keys, "keys", torch.bfloat16, 2)
+    dev = keys.device
+    k_fp4, k_scale = _u8(k_fp4), _u8(k_scale)
+    _need(slots, "slots", torch.int64, 1, dev)
+    _need(k_fp4, "k_fp4", torch.uint8, 4, dev)
+    _need(k_scale, "k_scale", torch.uint8, 4, dev)
+    N, D = keys.shape
+    P, hkv, page, _ = k_fp4.shape
+    if D != 128 or keys.stride(1) != 1:
+        raise ValueError("keys must be [N, 128] with unit column stride")
+    if hkv != 1 or k_fp4.shape != (P, 1, page, 64) or k_scale.shape != (P, 1, page, 4):
+        raise ValueError("cache must be k_fp4 [P,1,page,64] and k_scale [P,1,page,4]")
+    if slots.numel() != N or not slots.is_contiguous():
+        raise ValueError("slots must be a contiguous [N] tensor")
+    if not (k_fp4.is_contiguous() and k_scale.is_contiguous()):
+        raise ValueError("cache tensors must be contiguous")
+    rc = lib().fp4idx_quantize_store_k(_ptr(keys), keys.stride(0), _ptr(slots), N, _ptr(k_fp4),
+                                       page * 64, _ptr(k_scale), page * 4, page, P, _stream())
+    check("fp4idx_quantize_store_k", rc)
+    return k_fp4, k_scale

@@ -93,3 +93,15 @@ def test_topk_argument_errors_and_workspace():
     assert L.fp4idx_topk(256, 100_000, 4, 100_000, None, 2048, 256, None, None, 0, None) == 5
     assert L.fp4idx_topk(256, 100_000, 4, 100_000, None, 2048, 256, None, 512 + 8, need,
                          None) == 5                                                  # misaligned
+
+
+def test_quantize_store_argument_errors():
+    L = _lib.lib()
+    f = L.fp4idx_quantize_store_k
+    assert f(256, 128, 256, -1, 256, 4096, 256, 256, 64, 4, None) == 1       # N < 0
+    assert f(256, 128, 256, 4, 256, 4096, 256, 256, 32, 4, None) == 2        # page size
+    assert f(256, 128, 256, 0, 256, 4096, 256, 256, 64, 4, None) == 0        # nothing to do
+    assert f(None, 128, 256, 4, 256, 4096, 256, 256, 64, 4, None) == 1       # null keys
+    assert f(256, 100, 256, 4, 256, 4096, 256, 256, 64, 4, None) == 1        # short rows
+    assert f(258, 128, 256, 4, 256, 4096, 256, 256, 64, 4, None) == 3        # misaligned
+    assert f(256, 129, 256, 4, 256, 4096, 256, 256, 64, 4, None) == 3        # odd stride
