@@ -122,7 +122,7 @@ int fp4idx_logits_paged(int fmt,
  * Caller guarantees [M3 输入 shape 和类型]: every q_len[b] <= max_seqlen_q and every
  * k_len[b] <= max_seqlen_k.
  * Errors: EINVAL for max_seqlen_q <= 0, Hq % Hkv != 0, qo_offset given with causal == 0,
- * or a bad fmt; EALIGN for q_fp4 / k_fp4 not 16-byte aligned. */
+ * or a bad fmt; EALIGN for q_fp4 / k_fp4 / k_scale not 16-byte aligned. */
 int fp4idx_block_scores(int fmt,
                         const uint8_t* q_fp4, const uint8_t* q_scale,
                         const uint8_t* k_fp4, const uint8_t* k_scale,

@@ -17,6 +17,11 @@
 // max over tiles in each lane, then two cross-lane steps (over the four lane groups)
 // at each 128-key block boundary; lane group 0 stores 16 consecutive tokens (64 B).
 //
+// Key tiles are fetched two ahead of the one being computed, through buffer
+// descriptors built per tile (an invalid page gets a zero-byte descriptor, so the
+// loads stay unconditional); the block-table entries of 64 blocks come in with one
+// load.
+//
 // MXFP4 uses the scaled FP4 MFMA (one instruction per 16x16 tile covers all 128
 // products).  NVFP4 decodes both operands exactly to fp16 (E2M1 * 2^a * b, b the E4M3
 // significand as an integer) and accumulates four 16x16x32 fp16 MFMAs in fp32.
@@ -132,51 +137,74 @@ __global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
 #pragma unroll
         for (int hb = 0; hb < NB; hb++) run[hb] = -__builtin_inff();
 
-        for (int kt = 0; kt < n_kt; kt++) {
+        // Block-table entries of 64 blocks at a time: lane i holds the page of block
+        // win + i (-1 when invalid).  Key tiles are fetched two ahead of the one being
+        // computed, through buffer descriptors that read zeros for invalid pages.
+        int win = -64, my_phys = -1;
+        auto window = [&](int kb) {
+            if (kb - win >= 64) {
+                win = kb & ~63;
+                const int i = win + lane;
+                int v = -1;
+                if (p.kv_indices && i < kb_done) v = p.kv_indices[page0 + i];
+                my_phys = (v >= 0 && v < p.num_pages) ? v : -1;
+            }
+            return __builtin_amdgcn_readlane(my_phys, kb - win);
+        };
+        struct KTile {
+            v4i k;
+            uint32_t s;
+            int phys;
+        };
+        auto fetch = [&](int kt, KTile& t) {
+            t.phys = kt < n_kt ? window(kt >> 3) : -1;
+            const bool ok = t.phys >= 0;
+            const int64_t tok0 = ((int64_t)(ok ? t.phys : 0) * p.Hkv + hk) * 128 + (kt & 7) * 16;
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(ok ? p.k + tok0 * 64 : p.k, ok ? 16u * 64u : 0u);
+            t.k = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rk, n * 64 + 16 * g, 0, 0));
+            constexpr int G = FMT == 0 ? 4 : 8;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(ok ? p.ks + tok0 * G : p.ks, ok ? 16u * G : 0u);
+            if constexpr (FMT == 0)
+                t.s = __builtin_amdgcn_raw_buffer_load_b8(rs, n * 4 + g, 0, 0);
+            else
+                t.s = __builtin_amdgcn_raw_buffer_load_b16(rs, n * 8 + 2 * g, 0, 0);
+        };
+        auto process = [&](int kt, const KTile& t) {
             const int kb = kt >> 3;
-            const int32_t phys = p.kv_indices ? uniform(p.kv_indices[page0 + kb]) : -1;
-            const bool page_ok = phys >= 0 && phys < p.num_pages;
-            if (page_ok) {
-                const int64_t tok = ((int64_t)phys * p.Hkv + hk) * 128 + (kt & 7) * 16 + n;
-                const v4i kr = load16(p.k + tok * 64 + 16 * g);
-                // keys of this lane's output rows: kt*16 + 4g + i
+            if (t.phys >= 0) {
+                // keys of this lane's output rows: kt*16 + 4g + i.  Heads past nh have
+                // zero query operands and are computed but never stored, so the head
+                // loop has no branch; the products of all heads are independent.
                 const int kbase = kt * 16 + 4 * g;
-                const bool full = kbase + 3 < kv_min;  // every element of the lane visible
+                const bool full = __ballot(kbase + 3 >= kv_min) == 0;  // whole tile visible
+                v4f d[NB];
                 if constexpr (FMT == 0) {
-                    const int sk = p.ks[tok * 4 + g];
 #pragma unroll
-                    for (int hb = 0; hb < NB; hb++) {
-                        if (hb >= nh) continue;
-                        v4f d = mfma_fp4_16x16x128(kr, sk, qop[hb].v, qop[hb].s, v4f{0.f, 0.f, 0.f, 0.f});
-                        if (!full) {
-#pragma unroll
-                            for (int i = 0; i < 4; i++)
-                                if (kbase + i >= kv_lim) d[i] = -__builtin_inff();
-                        }
-                        run[hb] = fmaxf(run[hb], max4(d[0], d[1], d[2], d[3]));
-                    }
+                    for (int hb = 0; hb < NB; hb++)
+                        d[hb] = mfma_fp4_16x16x128(t.k, (int)t.s, qop[hb].v, qop[hb].s, v4f{0.f, 0.f, 0.f, 0.f});
                 } else {
-                    const uint32_t sc = (uint32_t)p.ks[tok * 8 + 2 * g] | ((uint32_t)p.ks[tok * 8 + 2 * g + 1] << 8);
                     v8h kd[4];
 #pragma unroll
                     for (int c = 0; c < 4; c++) {
                         float pw, bb;
-                        e4m3_split((sc >> (8 * (c >> 1))) & 0xffu, pw, bb);
-                        kd[c] = decode8_f16((uint32_t)kr[c], pw, bb);
+                        e4m3_split((t.s >> (8 * (c >> 1))) & 0xffu, pw, bb);
+                        kd[c] = decode8_f16((uint32_t)t.k[c], pw, bb);
                     }
 #pragma unroll
-                    for (int hb = 0; hb < NB; hb++) {
-                        if (hb >= nh) continue;
-                        v4f d = v4f{0.f, 0.f, 0.f, 0.f};
+                    for (int hb = 0; hb < NB; hb++) d[hb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int c = 0; c < 4; c++) d = mfma_f16_16x16x32(kd[c], qop[hb].v[c], d);
-                        if (!full) {
+                    for (int c = 0; c < 4; c++)
 #pragma unroll
-                            for (int i = 0; i < 4; i++)
-                                if (kbase + i >= kv_lim) d[i] = -__builtin_inff();
-                        }
-                        run[hb] = fmaxf(run[hb], max4(d[0], d[1], d[2], d[3]));
+                        for (int hb = 0; hb < NB; hb++) d[hb] = mfma_f16_16x16x32(kd[c], qop[hb].v[c], d[hb]);
+                }
+#pragma unroll
+                for (int hb = 0; hb < NB; hb++) {
+                    v4f e = d[hb];
+                    if (!full) {
+#pragma unroll
+                        for (int i = 0; i < 4; i++) e[i] = kbase + i < kv_lim ? e[i] : -__builtin_inff();
                     }
+                    run[hb] = fmaxf(fmaxf(run[hb], fmaxf(e[0], e[1])), fmaxf(e[2], e[3]));
                 }
             }
             // block boundary: reduce over the four lane groups and store
@@ -191,6 +219,19 @@ __global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
                     run[hb] = -__builtin_inff();
                 }
             }
+        };
+        KTile t0, t1, t2;
+        fetch(0, t0);
+        fetch(1, t1);
+        for (int kt = 0; kt < n_kt; kt += 3) {
+            fetch(kt + 2, t2);
+            process(kt, t0);
+            if (kt + 1 >= n_kt) break;
+            fetch(kt + 3, t0);
+            process(kt + 1, t1);
+            if (kt + 2 >= n_kt) break;
+            fetch(kt + 4, t1);
+            process(kt + 2, t2);
         }
         // blocks never reached: -inf
         for (int kb = kb_done; kb < p.ktiles; kb++) {
@@ -223,8 +264,9 @@ hipError_t launch_block_scores(const BlockParams& p, hipStream_t stream) {
         if (p.R <= 8) return launch_fmt_nb<0, 8>(p, stream);
         return launch_fmt_nb<0, 16>(p, stream);
     }
-    if (p.R <= 4) return launch_fmt_nb<1, 4>(p, stream);
-    return launch_fmt_nb<1, 8>(p, stream);
+    // NVFP4 keeps its query operands decoded to fp16 (16 registers per head): four
+    // heads per wave leave room for three waves per SIMD
+    return launch_fmt_nb<1, 4>(p, stream);
 }
 
 }  // namespace fp4idx

@@ -79,6 +79,15 @@ __device__ __forceinline__ RowRequest find_request(const int32_t* __restrict__ c
     return r;
 }
 
+// Raw buffer descriptor over [base, base + bytes): loads past the end return zeros
+// without touching memory (a zero-byte descriptor makes every load return zeros).
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 raw-buffer descriptor, word 3
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             (int)kRsrcWord3);
+}
+
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Workgroup barrier that orders LDS only.  Every barrier in this library guards data in

@@ -115,7 +115,8 @@ int fp4idx_block_scores(int fmt,
     if (!q_fp4 || !q_scale || !cu_seqlens_q || !cu_seqlens_k || !cu_page_offsets || !scores)
         return FP4IDX_EINVAL;
     if (num_pages > 0 && (!k_fp4 || !k_scale || !kv_indices)) return FP4IDX_EINVAL;
-    if (!aligned16(q_fp4) || (k_fp4 && !aligned16(k_fp4))) return FP4IDX_EALIGN;
+    if (!aligned16(q_fp4) || (k_fp4 && !aligned16(k_fp4)) || (k_scale && !aligned16(k_scale)))
+        return FP4IDX_EALIGN;
     fp4idx::BlockParams p{};
     p.q = q_fp4;
     p.qs = q_scale;

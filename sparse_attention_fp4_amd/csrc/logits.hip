@@ -142,13 +142,6 @@ __device__ __forceinline__ float group_sum(float v) {
 // invalid gets a descriptor of zero bytes: its loads return zeros without touching
 // memory, so every slab issues the same instructions and no branch separates a load
 // from its use.
-constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 raw-buffer descriptor, word 3
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             (int)kRsrcWord3);
-}
-
 template <int FMT>
 struct Slab {
     v4i k[4];                    // tile tt: bytes [16g, +16) of token 4n + tt
