@@ -11,9 +11,10 @@
 // or 1); the columns [0, out_cols) are cut into chunks of `ppw` key pages.  A
 // workgroup takes one row block and four consecutive column chunks (one per wave), so
 // the grid covers the whole [T, out_cols] output exactly once.  The workgroup first
-// copies the row block's packed queries, query scales and head weights into LDS (one
-// coalesced read instead of one per wave); each wave then keeps its A operands and
-// weights in registers for all its pages.
+// copies the row block's A operands (packed queries and their scale codes, or the
+// decoded NVFP4 values) into LDS in the order the lanes read them, and the head weights
+// next to them; each wave keeps its weights in registers and reads one A tile at a
+// time from LDS, so a wave holds few registers and three waves share each SIMD.
 //
 // MFMA mapping.  The contraction is [rows*heads x 128] x [128 x 16 keys].  A-tile j
 // holds 16 (row, head) pairs arranged so that output lane group g = l/16 always sees
@@ -42,9 +43,19 @@ namespace fp4idx {
 
 namespace {
 
-constexpr int kWavesPerBlock = 4;
+#ifndef FP4IDX_LOGITS_WPB
+#define FP4IDX_LOGITS_WPB 4
+#endif
+constexpr int kWavesPerBlock = FP4IDX_LOGITS_WPB;
+constexpr int kThreads = 64 * kWavesPerBlock;
 #ifndef FP4IDX_LOGITS_WAVES
 #define FP4IDX_LOGITS_WAVES 2048   // target number of waves of one launch
+#endif
+#ifndef FP4IDX_LOGITS_PIPE
+#define FP4IDX_LOGITS_PIPE 2       // products in flight in the epilogue pipeline
+#endif
+#ifndef FP4IDX_LOGITS_RING
+#define FP4IDX_LOGITS_RING 3       // key slabs in the ring (in flight + computing)
 #endif
 #ifndef FP4IDX_LOGITS_MAX_PPW
 #define FP4IDX_LOGITS_MAX_PPW 64   // at most this many pages per wave
@@ -162,16 +173,62 @@ __device__ __forceinline__ uint32_t slab_scale(const Slab<FMT>& b, int tt, int g
     }
 }
 
+// ---------------------------------------------------------------- A operands in LDS
+// The workgroup's A operands live in LDS for the whole kernel, stored in the order the
+// lanes read them, so a tile costs one conflict-free read per lane and no registers
+// between uses:
+//   MXFP4: slot (j, l) = lane l's 16 bytes of nibbles of A tile j ([NT][64] x 16 B), and
+//          the E8M0 codes of all tiles of lane l side by side ([64][NT] bytes), so one
+//          read gives a lane every code; the MFMA takes tile j's byte through its
+//          operand-select field.
+//   NVFP4: the decoded fp16 operand in four 16-byte chunks ([NT][4][64] x 16 B).
+// The head weights follow in their natural [RG][H] order.
+template <int FMT, int NT>
+struct ALayout {
+    static constexpr int kOpBytes = FMT == 0 ? 16 : 64;
+    static constexpr int kScaleOff = NT * 64 * kOpBytes;
+    static constexpr int kWOff = kScaleOff + (FMT == 0 ? NT * 64 : 0);
+    static size_t bytes(int rg, int h) { return (size_t)kWOff + (size_t)rg * h * 4; }
+};
+
+// A row held by slot (j, l): row offset `toff` in the row block and head `h`, with the
+// 16 bytes it needs at [16 * (l / 16), +16).  False for padding slots (heads past the
+// key head's count or tiles past n_tiles).
+template <int RG>
+__device__ __forceinline__ bool slot_row(const LogitsParams& p, int j, int l, int& toff, int& h) {
+    const int m = l & 15, gp = m >> 2, i0 = m & 3;
+    const int hk = j / p.tiles_per_kv, jj = j - hk * p.tiles_per_kv;
+    const int hl = (16 / RG) * jj + 4 * (gp / RG) + i0;
+    toff = gp % RG;
+    h = hk * p.R + hl;
+    return j < p.n_tiles && hl < p.R;
+}
+
+template <int FMT, int SEL>
+__device__ __forceinline__ v4f tile_dot_sel(const Operand<FMT>& a, uint32_t a_codes,
+                                            const Operand<FMT>& b) {
+    if constexpr (FMT == 0) {
+        const v8i A = {a.v[0], a.v[1], a.v[2], a.v[3], 0, 0, 0, 0};
+        const v8i B = {b.v[0], b.v[1], b.v[2], b.v[3], 0, 0, 0, 0};
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, v4f{0.f, 0.f, 0.f, 0.f}, 4, 4,
+                                                                SEL, (int)a_codes, 0, b.s);
+    } else {
+        (void)a_codes;
+        return tile_dot<FMT>(a, b);
+    }
+}
+
 // ---------------------------------------------------------------- the kernel
 // MKV: more than one key head (the tiles of key head hk only meet that head's slabs).
 template <int FMT, int RG, int NT, bool MKV>
-__global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
+__global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
     extern __shared__ __align__(16) uint8_t lds[];
+    using L = ALayout<FMT, NT>;
     constexpr int G = FMT == 0 ? 4 : 8;
     const int H = p.H;
-    uint8_t* sq = lds;                                               // [RG][H][64]
-    uint8_t* sqs = lds + RG * H * 64;                                // [RG][H][G]
-    float* sw = reinterpret_cast<float*>(lds + RG * H * (64 + G));   // [RG][H]
+    uint8_t* sa = lds;                                          // operands, lane order
+    uint8_t* sac = lds + L::kScaleOff;                          // MXFP4 codes [64][NT]
+    float* sw = reinterpret_cast<float*>(lds + L::kWOff);       // weights [RG][H]
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar math
@@ -195,9 +252,9 @@ __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
 
     // ---- prologue.  Loads go out in the order their results are needed: the first
     // segment's metadata (request, row lengths, block-table entries), then the
-    // workgroup's query staging, then the first two key slabs.  The LDS stores of the
-    // staged queries wait only for the staging loads and the barrier only for LDS, so the
-    // key loads stay in flight across both.  Lane i of my_phys holds the physical page of
+    // workgroup's A operands and weights, then the first two key slabs.  The LDS stores
+    // of the operands wait only for their loads and the barrier only for LDS, so the key
+    // loads stay in flight across both.  Lane i of my_phys holds the physical page of
     // page lp_begin + i (-1: invisible or invalid); with one request the block-table
     // row is known without the request lookup.
     // Every prologue load reads a valid address (indices are clamped into range) and the
@@ -211,39 +268,38 @@ __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
         const int b_first = p.B == 1 ? 0 : rq.b;
         bt_raw = p.bt[(int64_t)b_first * p.bt_rs + min(lp_begin + lane, p.W - 1)];
     }
-    // staging loads into registers (RG * H <= 512: at most 8, 16 and 2 per thread)
-    constexpr int kSQ = 8, kSS = 16, kSW = 2;
-    v4i st_q[kSQ];
-    uint32_t st_s[kSS];
+    // operand slots of this thread: the query bytes and scale codes of each
+    constexpr int kSlots = (NT * 64 + kThreads - 1) / kThreads;
+    constexpr int kSW = (128 + kThreads - 1) / kThreads;  // RG * H <= 128 weights
+    v4i st_q[kSlots];
+    uint32_t st_s[kSlots];
+    bool st_ok[kSlots];
     float st_w[kSW];
 #pragma unroll
-    for (int k = 0; k < kSQ; k++) {
-        const int i = threadIdx.x + 256 * k;
-        const int ic = min(i, RG * H * 4 - 1);
-        const int r = ic / (H * 4), rest = ic - r * (H * 4);
-        st_q[k] = load16(p.q + (int64_t)(t0 + min(r, nr1 - 1)) * p.q_rs + rest * 16);
-    }
-#pragma unroll
-    for (int k = 0; k < kSS; k++) {
-        const int i = threadIdx.x + 256 * k;
-        const int ic = min(i, RG * H * G - 1);
-        const int r = ic / (H * G), rest = ic - r * (H * G);
-        st_s[k] = p.qs[(int64_t)(t0 + min(r, nr1 - 1)) * p.qs_rs + rest];
+    for (int k = 0; k < kSlots; k++) {
+        const int slot = threadIdx.x + kThreads * k;
+        const int j = slot >> 6, l = slot & 63;
+        int toff, h;
+        const bool ok = slot < NT * 64 && slot_row<RG>(p, j, l, toff, h) && toff < nrows;
+        st_ok[k] = ok;
+        const int t = t0 + (ok ? toff : 0), hh = ok ? h : 0, c = l >> 4;
+        st_q[k] = load16(p.q + (int64_t)t * p.q_rs + hh * 64 + 16 * c);
+        st_s[k] = scale_bytes<FMT>(p.qs + (int64_t)t * p.qs_rs + hh * G, c);
     }
 #pragma unroll
     for (int k = 0; k < kSW; k++) {
-        const int i = threadIdx.x + 256 * k;
+        const int i = threadIdx.x + kThreads * k;
         const int ic = min(i, RG * H - 1);
         const int r = ic / H, h = ic - r * H;
         st_w[k] = p.w[(int64_t)(t0 + min(r, nr1 - 1)) * p.w_rs + h];
     }
     __builtin_amdgcn_sched_barrier(0);
     int b = 0, seg_end = t0, len = 0, my_phys = -1;
-    bool req_ok = false, row_ok = false;
+    bool row_ok = false;
     auto setup_segment = [&](int t_seg, bool first) {
         if (!first) rq = find_request(p.cu, p.B, t_seg);
         b = rq.b;
-        req_ok = rq.ok;
+        const bool req_ok = rq.ok;
         seg_end = req_ok ? min(rq.end, t_last + 1) : t_last + 1;
         row_ok = t_out >= t_seg && t_out < seg_end;
         const int lens_pref = (g % RG) < nrows ? lens_raw : 0;
@@ -284,31 +340,84 @@ __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
         for (int c = 0; c < (FMT == 0 ? 1 : 2); c++)
             dst.s[c] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, soff + 16 * c, 0, 0));
     };
-    Slab<FMT> b0, b1, b2;
+    Slab<FMT> b0, b1;
+#if FP4IDX_LOGITS_RING != 2
+    Slab<FMT> b2;
+#endif
     setup_segment(t0, true);
     issue(0, b0);
     issue(1, b1);
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- the staged queries, scales and weights into LDS (zeros past T)
+    // ---- operands and weights into LDS (zeros in padding slots and past T)
 #pragma unroll
-    for (int k = 0; k < kSQ; k++) {
-        const int i = threadIdx.x + 256 * k;
-        if (i < RG * H * 4)
-            *reinterpret_cast<v4i*>(sq + (int64_t)i * 16) = i / (H * 4) < nrows ? st_q[k] : v4i{0, 0, 0, 0};
-    }
+    for (int k = 0; k < kSlots; k++) {
+        const int slot = threadIdx.x + kThreads * k;
+        if (slot < NT * 64) {
+            const int j = slot >> 6, l = slot & 63;
+            RawTile r;
+            r.v = st_ok[k] ? st_q[k] : v4i{0, 0, 0, 0};
+            r.s = st_ok[k] ? st_s[k] : (FMT == 0 ? 127u : 0u);
+            if constexpr (FMT == 0) {
+                *reinterpret_cast<v4i*>(sa + (size_t)slot * 16) = r.v;
+                sac[l * NT + j] = (uint8_t)r.s;
+            } else {
+                const Operand<1> o = decode<1>(r);
 #pragma unroll
-    for (int k = 0; k < kSS; k++) {
-        const int i = threadIdx.x + 256 * k;
-        if (i < RG * H * G) sqs[i] = (uint8_t)(i / (H * G) < nrows ? st_s[k] : (FMT == 0 ? 127u : 0u));
+                for (int c = 0; c < 4; c++)
+                    *reinterpret_cast<v8h*>(sa + ((size_t)(j * 4 + c) * 64 + l) * 16) = o.v[c];
+            }
+        }
     }
 #pragma unroll
     for (int k = 0; k < kSW; k++) {
-        const int i = threadIdx.x + 256 * k;
+        const int i = threadIdx.x + kThreads * k;
         if (i < RG * H) sw[i] = i / H < nrows ? st_w[k] : 0.0f;
     }
     lds_barrier();
     if (!has_work) return;  // uniform per wave, after the only barrier
+
+    // ---- per-lane head weights (lane group g sums rows 4g .. 4g+3 of each tile) and
+    // MXFP4 scale codes; neither depends on the request segment: a lane only ever adds
+    // products of its own query row
+    float wv[NT][4];
+#pragma unroll
+    for (int j = 0; j < NT; j++) {
+        const int hk = j / p.tiles_per_kv, jj = j - hk * p.tiles_per_kv;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int hlo = (16 / RG) * jj + 4 * (g / RG) + i;
+            const bool hv = j < p.n_tiles && hlo < p.R;
+            wv[j][i] = hv ? sw[(g % RG) * H + hk * p.R + hlo] : 0.0f;
+        }
+    }
+    uint32_t acodes[(NT + 3) / 4];
+    if constexpr (FMT == 0) {
+        if constexpr (NT == 8) {
+            const uint2 c2 = *reinterpret_cast<const uint2*>(sac + lane * NT);
+            acodes[0] = c2.x, acodes[1] = c2.y;
+        } else if constexpr (NT == 4) {
+            acodes[0] = *reinterpret_cast<const uint32_t*>(sac + lane * NT);
+        } else {
+            acodes[0] = *reinterpret_cast<const uint16_t*>(sac + lane * NT);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < (NT + 3) / 4; i++) acodes[i] = 0;
+    }
+    auto a_op = [&](int j) {
+        Operand<FMT> o;
+        if constexpr (FMT == 0) {
+            o.v = *reinterpret_cast<const v4i*>(sa + ((size_t)j * 64 + lane) * 16);
+            o.s = 0;
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; c++)
+                o.v[c] = *reinterpret_cast<const v8h*>(sa + ((size_t)(j * 4 + c) * 64 + lane) * 16);
+        }
+        return o;
+    };
+    const bool lane_stores = g < RG;
 
     // The rows of a block may belong to different requests; each pass handles the rows
     // of one request (rows of a request are consecutive).
@@ -319,36 +428,7 @@ __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
             issue(0, b0);
             issue(1, b1);
         }
-        // ---- A operands and weights of this segment from LDS
-        Operand<FMT> a[NT];
-        float wv[NT][4];
-#pragma unroll
-        for (int j = 0; j < NT; j++) {
-            const int m = lane & 15;
-            const int gp = m >> 2, i0 = m & 3;
-            const int hk = j / p.tiles_per_kv, jj = j - hk * p.tiles_per_kv;
-            const int hl = (16 / RG) * jj + 4 * (gp / RG) + i0;
-            const int toff = gp % RG;
-            const bool ok = j < p.n_tiles && hl < p.R && req_ok && t0 + toff >= t_seg &&
-                            t0 + toff < seg_end;
-            RawTile r;
-            r.v = v4i{0, 0, 0, 0};
-            r.s = FMT == 0 ? 127u : 0u;
-            if (ok) {
-                const int row = toff * H + hk * p.R + hl;
-                r.v = *reinterpret_cast<const v4i*>(sq + row * 64 + 16 * g);
-                r.s = scale_bytes<FMT>(sqs + row * G, g);
-            }
-            a[j] = decode<FMT>(r);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int hlo = (16 / RG) * jj + 4 * (g / RG) + i;
-                const int to = g % RG;
-                const bool hv = j < p.n_tiles && hlo < p.R && req_ok && t0 + to >= t_seg &&
-                                t0 + to < seg_end;
-                wv[j][i] = hv ? sw[to * H + hk * p.R + hlo] : 0.0f;
-            }
-        }
+        const bool st_lane = lane_stores && row_ok;
         // ---- the wave's slabs: three buffers in a ring keep two slabs of keys in flight
         // while one is computed (slab s lives in buffer s % 3)
         float acc[4][4];
@@ -356,11 +436,14 @@ __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
         for (int tt = 0; tt < 4; tt++)
 #pragma unroll
             for (int i = 0; i < 4; i++) acc[tt][i] = 0.0f;
+        Operand<FMT> acur = a_op(0);  // the A tile the next product needs
         auto compute = [&](int s, const Slab<FMT>& buf) {
             int pi, half, hk;
             slab_pos(s, pi, half, hk);
             const int phys = __builtin_amdgcn_readlane(my_phys, pi);
-            // an invisible page (past every row's length, or invalid) only gets -inf
+            const bool last_kv = !MKV || hk == p.Hkv - 1;  // all key heads of these keys are in
+            const int col0 = (lp_begin + pi) * p.page + half * 64 + 4 * n;
+            float o[4];
             if (phys >= 0) {
                 Operand<FMT> kb[4];
 #pragma unroll
@@ -370,61 +453,97 @@ __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
                     rt.s = slab_scale<FMT>(buf, tt, g);
                     kb[tt] = decode<FMT>(rt);
                 }
-                // (tile, key tile) products in a two-deep software pipeline: the matrix
-                // core computes product q while the vector ALU applies ReLU and the head
-                // weights to product q-1.  Scheduling barriers keep that order (left
-                // alone, the compiler puts each product's epilogue right behind it and
-                // the wave waits for every product in turn).
+                // Products q = 4j + tt (A tile j outer, key tile tt inner), software
+                // pipelined: the matrix core computes product q while the vector ALU
+                // applies ReLU and the head weights to product q-(DEPTH-1).  A tile
+                // j+1 (wrapping to tile 0 of the next slab) is read from LDS while tile
+                // j is in use.  Scheduling barriers keep that order (left alone, the
+                // compiler puts each product's epilogue right behind it and the wave
+                // waits for every product in turn).
                 constexpr int NP = 4 * NT;
-                v4f dprev = tile_dot<FMT>(a[0], kb[0]);
+                constexpr int DEPTH = FP4IDX_LOGITS_PIPE;  // products in flight
+                v4f dq[DEPTH];
+                Operand<FMT> anext = acur;
 #pragma unroll
-                for (int q = 1; q <= NP; q++) {
-                    v4f dcur = dprev;
+                for (int q = 0; q < NP + DEPTH - 1; q++) {
                     if (q < NP) {
-                        const int tt = q / NT, j = q % NT;
-                        if (!MKV || j / p.tiles_per_kv == hk) dcur = tile_dot<FMT>(a[j], kb[tt]);
+                        const int j = q >> 2, tt = q & 3;
+                        if (tt == 0) anext = a_op(j + 1 < NT ? j + 1 : 0);
+                        v4f d = v4f{0.f, 0.f, 0.f, 0.f};
+                        if (!MKV || j / p.tiles_per_kv == hk) {
+                            switch (j & 3) {
+                                case 0: d = tile_dot_sel<FMT, 0>(acur, acodes[j >> 2], kb[tt]); break;
+                                case 1: d = tile_dot_sel<FMT, 1>(acur, acodes[j >> 2], kb[tt]); break;
+                                case 2: d = tile_dot_sel<FMT, 2>(acur, acodes[j >> 2], kb[tt]); break;
+                                default: d = tile_dot_sel<FMT, 3>(acur, acodes[j >> 2], kb[tt]); break;
+                            }
+                        }
+                        dq[q % DEPTH] = d;
+                        if (tt == 3) acur = anext;
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                    const int tp = (q - 1) / NT, jp = (q - 1) % NT;
-                    if (!MKV || jp / p.tiles_per_kv == hk) {
-                        // four independent ReLUs first, then the four multiply-adds, so
-                        // no instruction waits on the one just before it
-                        float r[4];
+                    const int qp = q - (DEPTH - 1);
+                    if (qp >= 0) {
+                        const int jp = qp >> 2, tp = qp & 3;
+                        if (!MKV || jp / p.tiles_per_kv == hk) {
+                            // four independent ReLUs first, then the four multiply-adds,
+                            // so no instruction waits on the one just before it; without
+                            // key heads the first tile starts the sums (one multiply
+                            // instead of zeroing them after every store)
+                            const v4f d = dq[qp % DEPTH];
+                            float r[4];
 #pragma unroll
-                        for (int i = 0; i < 4; i++) r[i] = relu<FMT>(dprev[i]);
+                            for (int i = 0; i < 4; i++) r[i] = relu<FMT>(d[i]);
 #pragma unroll
-                        for (int i = 0; i < 4; i++) acc[tp][i] = __builtin_fmaf(wv[jp][i], r[i], acc[tp][i]);
+                            for (int i = 0; i < 4; i++)
+                                acc[tp][i] = (!MKV && jp == 0) ? wv[0][i] * r[i]
+                                                               : __builtin_fmaf(wv[jp][i], r[i], acc[tp][i]);
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                    dprev = dcur;
                 }
-            }
-            if (!MKV || hk == p.Hkv - 1) {  // all key heads of these 64 keys are in
-                const int col0 = (lp_begin + pi) * p.page + half * 64 + 4 * n;
-                float o[4];
+                if (!last_kv) return;
 #pragma unroll
                 for (int tt = 0; tt < 4; tt++) {
                     float v = (acc[tt][0] + acc[tt][1]) + (acc[tt][2] + acc[tt][3]);
                     v = group_sum<RG>(v);
-                    o[tt] = (phys >= 0 && col0 + tt < len) ? v : -__builtin_inff();
-#pragma unroll
-                    for (int i = 0; i < 4; i++) acc[tt][i] = 0.0f;
+                    o[tt] = col0 + tt < len ? v : -__builtin_inff();
                 }
-                if (g < RG && row_ok) {
-                    float* dst = p.out + (int64_t)t_out * p.out_rs + col0;
-                    // streaming stores: the logits are not read again by this kernel,
-                    // and keeping them out of L2 leaves room for the keys
-                    if (p.vec_out && col0 + 3 < p.out_cols) {
-                        __builtin_nontemporal_store(v4f{o[0], o[1], o[2], o[3]},
-                                                    reinterpret_cast<v4f*>(dst));
-                    } else {
+                if constexpr (MKV) {
 #pragma unroll
-                        for (int tt = 0; tt < 4; tt++)
-                            if (col0 + tt < p.out_cols) __builtin_nontemporal_store(o[tt], dst + tt);
-                    }
+                    for (int tt = 0; tt < 4; tt++)
+#pragma unroll
+                        for (int i = 0; i < 4; i++) acc[tt][i] = 0.0f;
+                }
+            } else {
+                // an invisible page (past every row's length, or invalid) only gets -inf
+                if (!last_kv) return;
+#pragma unroll
+                for (int tt = 0; tt < 4; tt++) o[tt] = -__builtin_inff();
+            }
+            if (st_lane) {
+                float* dst = p.out + (int64_t)t_out * p.out_rs + col0;
+                // streaming stores: the logits are not read again by this kernel,
+                // and keeping them out of L2 leaves room for the keys
+                if (p.vec_out && col0 + 3 < p.out_cols) {
+                    __builtin_nontemporal_store(v4f{o[0], o[1], o[2], o[3]},
+                                                reinterpret_cast<v4f*>(dst));
+                } else {
+#pragma unroll
+                    for (int tt = 0; tt < 4; tt++)
+                        if (col0 + tt < p.out_cols) __builtin_nontemporal_store(o[tt], dst + tt);
                 }
             }
         };
+#if FP4IDX_LOGITS_RING == 2
+        for (int s = 0; s < n_slabs; s += 2) {
+            compute(s, b0);
+            issue(s + 2, b0);
+            if (s + 1 >= n_slabs) break;
+            compute(s + 1, b1);
+            issue(s + 3, b1);
+        }
+#else
         for (int s = 0; s < n_slabs; s += 3) {
             issue(s + 2, b2);
             compute(s, b0);
@@ -435,21 +554,20 @@ __global__ __launch_bounds__(256) void k_logits(const LogitsParams p) {
             issue(s + 4, b1);
             compute(s + 2, b2);
         }
+#endif
         t_seg = seg_end;
     }
 }
-
 template <int FMT, int RG, int NT>
 hipError_t launch3(const LogitsParams& p, hipStream_t stream) {
     const int64_t blocks = (int64_t)p.n_rowblocks * p.n_wgchunks;
     if (blocks <= 0) return hipSuccess;
-    const int G = FMT == 0 ? 4 : 8;
-    const size_t lds = (size_t)RG * p.H * (64 + G + 4);
+    const size_t lds = ALayout<FMT, NT>::bytes(RG, p.H);
     if (p.Hkv == 1)
-        hipLaunchKernelGGL((k_logits<FMT, RG, NT, false>), dim3((unsigned)blocks), dim3(256), lds,
+        hipLaunchKernelGGL((k_logits<FMT, RG, NT, false>), dim3((unsigned)blocks), dim3(kThreads), lds,
                            stream, p);
     else
-        hipLaunchKernelGGL((k_logits<FMT, RG, NT, true>), dim3((unsigned)blocks), dim3(256), lds,
+        hipLaunchKernelGGL((k_logits<FMT, RG, NT, true>), dim3((unsigned)blocks), dim3(kThreads), lds,
                            stream, p);
     return hipGetLastError();
 }
