@@ -86,7 +86,8 @@ enum {
  *   logits [T][out_cols] float, rows out_row_stride floats apart
  * Alignment: q_fp4, k_fp4, k_scale and their row/page strides must be multiples of 16
  * bytes (EALIGN).
- * Limits: H % Hkv == 0, page_size in {64, 128} (else EUNSUPPORTED), 1 <= H <= 128.
+ * Limits: H % Hkv == 0, page_size in {64, 128} (else EUNSUPPORTED), 1 <= H <= 128,
+ * out_row_stride <= 2^27 floats (else EUNSUPPORTED).
  * fmt = FP4IDX_MXFP4 or FP4IDX_NVFP4. */
 int fp4idx_logits_paged(int fmt,
                         const uint8_t* q_fp4, int64_t q_row_stride,

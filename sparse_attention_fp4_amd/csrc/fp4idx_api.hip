@@ -57,6 +57,8 @@ int fp4idx_logits_paged(int fmt,
     if (q_row_stride < (int64_t)H * 64 || qs_row_stride < (int64_t)H * G || w_row_stride < H ||
         out_row_stride < out_cols || bt_row_stride < table_width)
         return FP4IDX_EINVAL;
+    // output rows of one row block are addressed with 32-bit offsets
+    if (out_row_stride > ((int64_t)1 << 27)) return FP4IDX_EUNSUPPORTED;
     if (k_page_stride < (int64_t)Hkv * page_size * 64 || ks_page_stride < (int64_t)Hkv * page_size * G)
         return FP4IDX_EINVAL;
     if (!aligned16(q_fp4) || (q_row_stride & 15) || !aligned16(k_fp4) || (k_page_stride & 15))
@@ -92,7 +94,6 @@ int fp4idx_logits_paged(int fmt,
     p.fmt = fmt;
     p.G = G;
     p.R = H / Hkv;
-    p.vec_out = aligned16(logits) && (out_row_stride & 3) == 0;
     return hip_status(fp4idx::launch_logits(p, (hipStream_t)stream));
 }
 

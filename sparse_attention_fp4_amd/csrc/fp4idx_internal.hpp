@@ -36,7 +36,6 @@ struct LogitsParams {
     int n_wgchunks;      // workgroups per row block (four chunks each)
     int n_rowblocks;
     int rows_per_block;  // RG: query rows sharing one A tile
-    int vec_out;         // logits rows 16-byte aligned: four columns per store
 };
 
 struct BlockParams {

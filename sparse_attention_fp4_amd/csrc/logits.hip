@@ -204,6 +204,9 @@ __device__ __forceinline__ bool slot_row(const LogitsParams& p, int j, int l, in
     return j < p.n_tiles && hl < p.R;
 }
 
+constexpr uint32_t kOffNone = 0x80000000u;  // buffer offset past every output range
+constexpr int kNonTemporal = 2;              // cache-policy bit of a streaming store
+
 template <int FMT, int SEL>
 __device__ __forceinline__ v4f tile_dot_sel(const Operand<FMT>& a, uint32_t a_codes,
                                             const Operand<FMT>& b) {
@@ -313,24 +316,28 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
         }
     };
     // slab s of this wave: page lp_begin + pi, half `half` of it, key head hk (fastest)
+    // (one key head: a page holds one or two slabs, so shifts replace the division)
     auto slab_pos = [&](int s, int& pi, int& half, int& hk) {
-        if (slabs_per_page == 1) {
-            pi = s, half = 0, hk = 0;
+        if constexpr (!MKV) {
+            const int sh = halves - 1;
+            pi = s >> sh, half = s & sh, hk = 0;
         } else {
             pi = s / slabs_per_page;
             const int r = s - pi * slabs_per_page;
-            half = MKV ? r / p.Hkv : r;
-            hk = MKV ? r - half * p.Hkv : 0;
+            half = r / p.Hkv;
+            hk = r - half * p.Hkv;
         }
     };
+    // Branch-free: a slab that is not there reads page 0 through a zero-byte descriptor.
     auto issue = [&](int s, Slab<FMT>& dst) {
         int pi, half, hk;
         slab_pos(s, pi, half, hk);
         const int phys = __builtin_amdgcn_readlane(my_phys, pi & 63);
         const bool ok = s < n_slabs && phys >= 0;
+        const int64_t pg = ok ? phys : 0;
         const int64_t tok = (int64_t)hk * p.page + half * 64;
-        const uint8_t* kb = ok ? p.k + (int64_t)phys * p.kp_s + tok * 64 : p.k;
-        const uint8_t* sb = ok ? p.ks + (int64_t)phys * p.ksp_s + tok * G : p.ks;
+        const uint8_t* kb = p.k + pg * p.kp_s + tok * 64;
+        const uint8_t* sb = p.ks + pg * p.ksp_s + tok * G;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, ok ? 64u * 64u : 0u);
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(sb, ok ? 64u * G : 0u);
 #pragma unroll
@@ -418,6 +425,11 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
         return o;
     };
     const bool lane_stores = g < RG;
+    // output addressing: row t0 + (g % RG), column col0, relative to the slab's first
+    // column of row t0 (the host keeps (RG-1) rows + 64 columns within 2^31 bytes)
+    const int64_t row_base = (int64_t)t0 * p.out_rs;
+    const uint32_t lane_off = (uint32_t)(((int64_t)(g % RG) * p.out_rs + 4 * n) * 4);
+    const uint32_t out_range = (uint32_t)(((int64_t)(RG - 1) * p.out_rs + 64) * 4);
 
     // The rows of a block may belong to different requests; each pass handles the rows
     // of one request (rows of a request are consecutive).
@@ -521,39 +533,51 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
 #pragma unroll
                 for (int tt = 0; tt < 4; tt++) o[tt] = -__builtin_inff();
             }
-            if (st_lane) {
-                float* dst = p.out + (int64_t)t_out * p.out_rs + col0;
-                // streaming stores: the logits are not read again by this kernel,
-                // and keeping them out of L2 leaves room for the keys
-                if (p.vec_out && col0 + 3 < p.out_cols) {
-                    __builtin_nontemporal_store(v4f{o[0], o[1], o[2], o[3]},
-                                                reinterpret_cast<v4f*>(dst));
-                } else {
+            // Stores go through a descriptor based at the slab's first column of row
+            // t0; lanes that must not store get an offset past its range, so every
+            // slab issues the same store instructions without a branch.  Streaming
+            // (non-temporal): the logits are not read again by this kernel, and
+            // keeping them out of L2 leaves room for the keys.  A slab inside the
+            // output takes one 16-byte store per lane, the last one of a row four
+            // 4-byte stores.
+            const int colb = col0 - 4 * n;
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + row_base + colb, out_range);
+            if (colb + 64 <= p.out_cols) {
+                const v4f ov = v4f{o[0], o[1], o[2], o[3]};
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, ov), ro,
+                                                       st_lane ? lane_off : kOffNone, 0, kNonTemporal);
+            } else {
 #pragma unroll
-                    for (int tt = 0; tt < 4; tt++)
-                        if (col0 + tt < p.out_cols) __builtin_nontemporal_store(o[tt], dst + tt);
-                }
+                for (int tt = 0; tt < 4; tt++)
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        __float_as_uint(o[tt]), ro,
+                        st_lane && col0 + tt < p.out_cols ? lane_off + 4u * tt : kOffNone, 0, kNonTemporal);
             }
         };
+        // The loop body has no early exit: the last one or two slabs are computed
+        // after it.  (An exit taken in the middle of the body would join the loop
+        // head and make the wait counters there assume that the latest slab must be
+        // in, which drains the ring once per pass.)
+        int s = 0;
 #if FP4IDX_LOGITS_RING == 2
-        for (int s = 0; s < n_slabs; s += 2) {
+        for (; s + 2 <= n_slabs; s += 2) {
             compute(s, b0);
             issue(s + 2, b0);
-            if (s + 1 >= n_slabs) break;
             compute(s + 1, b1);
             issue(s + 3, b1);
         }
+        if (s < n_slabs) compute(s, b0);
 #else
-        for (int s = 0; s < n_slabs; s += 3) {
+        for (; s + 3 <= n_slabs; s += 3) {
             issue(s + 2, b2);
             compute(s, b0);
-            if (s + 1 >= n_slabs) break;
             issue(s + 3, b0);
             compute(s + 1, b1);
-            if (s + 2 >= n_slabs) break;
             issue(s + 4, b1);
             compute(s + 2, b2);
         }
+        if (s < n_slabs) compute(s, b0);
+        if (s + 1 < n_slabs) compute(s + 1, b1);
 #endif
         t_seg = seg_end;
     }

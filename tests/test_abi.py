@@ -53,6 +53,7 @@ def _logits(**kw):
     (dict(fmt=2), 1), (dict(H=6, Hkv=4), 1), (dict(page=32), 2), (dict(H=256, qrs=256 * 64,
      qsrs=256 * 4, wrs=256), 2), (dict(q=None), 1), (dict(B=0), 1), (dict(qrs=100), 1),
     (dict(qrs=32 * 64 + 8), 3), (dict(out_cols=300), 1), (dict(kps=100), 1),
+    (dict(ors=(1 << 27) + 4), 2),
 ])
 def test_logits_argument_errors(kw, code):
     assert _logits(**kw) == code
