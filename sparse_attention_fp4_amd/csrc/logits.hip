@@ -27,7 +27,9 @@
 // section below for which lane reads which bytes); each key byte is used by exactly one
 // wave, so keys skip LDS on this path.  A wave walks its pages slab by slab with the
 // loads of the next two slabs in flight while it computes one; the block-table entries
-// of all its pages come in with a single load.
+// of its pages come in with one load per 64 pages.  Pages past the end of every row
+// of the block get -inf without any key traffic, and a workgroup that has no visible
+// page at all skips the operand staging.
 //
 // Rounding.  MXFP4: one scaled MFMA per (tile, key head) covers all 128 products.
 // NVFP4: E2M1 x E4M3 is not an MX operand, so both sides are decoded exactly to fp16
@@ -57,8 +59,17 @@ constexpr int kThreads = 64 * kWavesPerBlock;
 #ifndef FP4IDX_LOGITS_RING
 #define FP4IDX_LOGITS_RING 3       // key slabs in the ring (in flight + computing)
 #endif
+#ifndef FP4IDX_LOGITS_WLDS
+#define FP4IDX_LOGITS_WLDS 0       // head weights read from LDS per tile (else registers)
+#endif
+#ifndef FP4IDX_LOGITS_MAX_NT
+#define FP4IDX_LOGITS_MAX_NT 16    // A tiles per block at most (8 or 16)
+#endif
+#ifndef FP4IDX_LOGITS_REVERSE
+#define FP4IDX_LOGITS_REVERSE 0
+#endif
 #ifndef FP4IDX_LOGITS_MAX_PPW
-#define FP4IDX_LOGITS_MAX_PPW 64   // at most this many pages per wave
+#define FP4IDX_LOGITS_MAX_PPW 128  // at most this many pages per wave (a multiple of 64)
 #endif
 
 // ---------------------------------------------------------------- operand types
@@ -182,13 +193,15 @@ __device__ __forceinline__ uint32_t slab_scale(const Slab<FMT>& b, int tt, int g
 //          read gives a lane every code; the MFMA takes tile j's byte through its
 //          operand-select field.
 //   NVFP4: the decoded fp16 operand in four 16-byte chunks ([NT][4][64] x 16 B).
-// The head weights follow in their natural [RG][H] order.
+// The head weights follow in the order the epilogue applies them: [NT][4][4] floats,
+// entry (j, g, i) = the weight of tile row 4g + i of A tile j (0 for padding rows), so
+// lane group g reads its four weights of a tile as one 16-byte broadcast.
 template <int FMT, int NT>
 struct ALayout {
     static constexpr int kOpBytes = FMT == 0 ? 16 : 64;
     static constexpr int kScaleOff = NT * 64 * kOpBytes;
     static constexpr int kWOff = kScaleOff + (FMT == 0 ? NT * 64 : 0);
-    static size_t bytes(int rg, int h) { return (size_t)kWOff + (size_t)rg * h * 4; }
+    static constexpr size_t kBytes = (size_t)kWOff + NT * 64;
 };
 
 // A row held by slot (j, l): row offset `toff` in the row block and head `h`, with the
@@ -228,16 +241,20 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
     extern __shared__ __align__(16) uint8_t lds[];
     using L = ALayout<FMT, NT>;
     constexpr int G = FMT == 0 ? 4 : 8;
-    const int H = p.H;
     uint8_t* sa = lds;                                          // operands, lane order
     uint8_t* sac = lds + L::kScaleOff;                          // MXFP4 codes [64][NT]
-    float* sw = reinterpret_cast<float*>(lds + L::kWOff);       // weights [RG][H]
+    float* sw = reinterpret_cast<float*>(lds + L::kWOff);       // weights [NT][4][4]
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar math
     const int g = lane >> 4, n = lane & 15;
-    const int rb = blockIdx.x / p.n_wgchunks;
-    const int wc = (blockIdx.x - rb * p.n_wgchunks) * kWavesPerBlock + wave;
+    const int bq = blockIdx.x / p.n_wgchunks;
+    const int wc = (blockIdx.x - bq * p.n_wgchunks) * kWavesPerBlock + wave;
+#if FP4IDX_LOGITS_REVERSE
+    const int rb = p.n_rowblocks - 1 - bq;
+#else
+    const int rb = bq;
+#endif
     const int t0 = rb * RG;
     const int nrows = min(RG, p.T - t0);
     const int t_last = t0 + nrows - 1;
@@ -248,36 +265,75 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
     const bool has_work = wc < p.n_wchunks;
     const int halves = p.page / 64;
     const int slabs_per_page = halves * p.Hkv;
-    const int n_slabs = has_work ? (lp_end - lp_begin) * slabs_per_page : 0;
     const int t_out = t0 + (g % RG);
     const int koff = 256 * n + 16 * g;          // lane's byte offset in a slab's keys
     const int soff = 4 * G * n;                 // and in its scale bytes
+    const bool lane_stores = g < RG;            // lane groups that hold a row's final sums
+
+    // ---- output.  Lane (g, n) with g < RG writes columns col0 .. col0+3 (col0 = the
+    // slab's first column + 4n) of row t0 + g.  Stores go through a descriptor based at
+    // the slab's first column of row t0 (the host keeps (RG-1) rows + 64 columns within
+    // 2^31 bytes); lanes that must not store get an offset past its range, so every
+    // slab issues the same store instructions without a branch.  Streaming
+    // (non-temporal): the logits are not read again by this kernel, and keeping them
+    // out of L2 leaves room for the keys.  A slab inside the output takes one 16-byte
+    // store per lane, the last one of a row four 4-byte stores.
+    const int64_t row_base = (int64_t)t0 * p.out_rs;
+    const uint32_t lane_off = (uint32_t)(((int64_t)(g % RG) * p.out_rs + 4 * n) * 4);
+    const uint32_t out_range = (uint32_t)(((int64_t)(RG - 1) * p.out_rs + 64) * 4);
+    auto store_slab = [&](int colb, const float (&o)[4], bool st) {
+        const int col0 = colb + 4 * n;
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + row_base + colb, out_range);
+        if (colb + 64 <= p.out_cols) {
+            const v4f ov = v4f{o[0], o[1], o[2], o[3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, ov), ro,
+                                                   st ? lane_off : kOffNone, 0, kNonTemporal);
+        } else {
+#pragma unroll
+            for (int tt = 0; tt < 4; tt++)
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __float_as_uint(o[tt]), ro, st && col0 + tt < p.out_cols ? lane_off + 4u * tt : kOffNone,
+                    0, kNonTemporal);
+        }
+    };
+    // -inf over the wave's pages [pi0, lp_end - lp_begin): no keys are read there
+    auto fill = [&](int pi0, bool st) {
+        const float ninf[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+        for (int pi = pi0; pi < lp_end - lp_begin; pi++)
+            for (int hf = 0; hf < halves; hf++) store_slab((lp_begin + pi) * p.page + hf * 64, ninf, st);
+    };
 
     // ---- prologue.  Loads go out in the order their results are needed: the first
     // segment's metadata (request, row lengths, block-table entries), then the
     // workgroup's A operands and weights, then the first two key slabs.  The LDS stores
     // of the operands wait only for their loads and the barrier only for LDS, so the key
-    // loads stay in flight across both.  Lane i of my_phys holds the physical page of
-    // page lp_begin + i (-1: invisible or invalid); with one request the block-table
-    // row is known without the request lookup.
+    // loads stay in flight across both.  Lane i of my_phys[w] holds the physical page of
+    // page lp_begin + 64w + i (-1: invisible or invalid); with one request the
+    // block-table row is known without the request lookup.
     // Every prologue load reads a valid address (indices are clamped into range) and the
     // unwanted values are replaced afterwards, so no branch separates a load from its use
     // and each wait covers just the loads it needs.
     RowRequest rq = find_request(p.cu, p.B, t0);
     const int nr1 = max(nrows, 1);  // a row block always holds at least one row
     const int lens_raw = p.lens[t0 + min(g % RG, nr1 - 1)];
-    int bt_raw = -1;  // the block-table entry of page lp_begin + lane (clamped)
-    if (has_work && p.W > 0) {
-        const int b_first = p.B == 1 ? 0 : rq.b;
-        bt_raw = p.bt[(int64_t)b_first * p.bt_rs + min(lp_begin + lane, p.W - 1)];
+    constexpr int kWin = (FP4IDX_LOGITS_MAX_PPW + 63) / 64;  // 64-page windows per wave
+    int bt_raw[kWin];  // the block-table entry of page lp_begin + 64w + lane (clamped)
+#pragma unroll
+    for (int w = 0; w < kWin; w++) {
+        bt_raw[w] = -1;
+        if (has_work && p.W > 0) {
+            const int b_first = p.B == 1 ? 0 : rq.b;
+            bt_raw[w] = p.bt[(int64_t)b_first * p.bt_rs + min(lp_begin + 64 * w + lane, p.W - 1)];
+        }
     }
     // operand slots of this thread: the query bytes and scale codes of each
     constexpr int kSlots = (NT * 64 + kThreads - 1) / kThreads;
-    constexpr int kSW = (128 + kThreads - 1) / kThreads;  // RG * H <= 128 weights
+    constexpr int kSW = (NT * 16 + kThreads - 1) / kThreads;  // NT * 16 weights
     v4i st_q[kSlots];
     uint32_t st_s[kSlots];
     bool st_ok[kSlots];
     float st_w[kSW];
+    bool stw_ok[kSW];
 #pragma unroll
     for (int k = 0; k < kSlots; k++) {
         const int slot = threadIdx.x + kThreads * k;
@@ -291,13 +347,29 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
     }
 #pragma unroll
     for (int k = 0; k < kSW; k++) {
+        // weight entry (j, gg, ii): row t0 + gg % RG, head of tile row 4 gg + ii
         const int i = threadIdx.x + kThreads * k;
-        const int ic = min(i, RG * H - 1);
-        const int r = ic / H, h = ic - r * H;
-        st_w[k] = p.w[(int64_t)(t0 + min(r, nr1 - 1)) * p.w_rs + h];
+        const int j = i >> 4, gg = (i >> 2) & 3, ii = i & 3;
+        const int hk = j / p.tiles_per_kv, jj = j - hk * p.tiles_per_kv;
+        const int hlo = (16 / RG) * jj + 4 * (gg / RG) + ii, to = gg % RG;
+        const bool ok = i < NT * 16 && j < p.n_tiles && hlo < p.R && to < nrows;
+        stw_ok[k] = ok;
+        st_w[k] = p.w[(int64_t)(t0 + (ok ? to : 0)) * p.w_rs + (ok ? hk * p.R + hlo : 0)];
     }
     __builtin_amdgcn_sched_barrier(0);
-    int b = 0, seg_end = t0, len = 0, my_phys = -1;
+    // A workgroup whose columns all lie past every row's end only writes -inf (all its
+    // waves see the same rows, so they all leave here or none does).
+    {
+        const int lr = (g % RG) < nrows ? min(lens_raw, p.out_cols) : 0;
+        const int wg_max = uniform(max_lane_xor32i(max_lane_xor16i(lr)));
+        const int wg_col0 = (blockIdx.x - bq * p.n_wgchunks) * kWavesPerBlock * p.ppw * p.page;
+        if (wg_col0 >= wg_max) {
+            if (has_work) fill(0, lane_stores && g < nrows);
+            return;
+        }
+    }
+    int b = 0, seg_end = t0, len = 0, my_phys[kWin];
+    int vis_pages = 0, n_vis = 0;  // the wave's pages (slabs) before every row's end
     bool row_ok = false;
     auto setup_segment = [&](int t_seg, bool first) {
         if (!first) rq = find_request(p.cu, p.B, t_seg);
@@ -308,12 +380,25 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
         const int lens_pref = (g % RG) < nrows ? lens_raw : 0;
         len = (row_ok && req_ok) ? min(lens_pref, p.out_cols) : 0;
         const int max_len = uniform(max_lane_xor32i(max_lane_xor16i(len)));
-        my_phys = -1;
-        const int lp = lp_begin + lane;
-        if (has_work && req_ok && lane < lp_end - lp_begin && lp * p.page < max_len && lp < p.W) {
-            const int v = first ? bt_raw : p.bt[(int64_t)b * p.bt_rs + lp];
-            my_phys = (v >= 0 && v < p.num_pages) ? v : -1;
+#pragma unroll
+        for (int w = 0; w < kWin; w++) {
+            my_phys[w] = -1;
+            const int lp = lp_begin + 64 * w + lane;
+            if (has_work && req_ok && lp < lp_end && lp * p.page < max_len && lp < p.W) {
+                const int v = first ? bt_raw[w] : p.bt[(int64_t)b * p.bt_rs + lp];
+                my_phys[w] = (v >= 0 && v < p.num_pages) ? v : -1;
+            }
         }
+        vis_pages = has_work ? min(max((max_len + p.page - 1) / p.page - lp_begin, 0), lp_end - lp_begin) : 0;
+        n_vis = vis_pages * slabs_per_page;
+    };
+    // physical page of the wave's page pi (wave-uniform)
+    auto phys_of = [&](int pi) {
+        int ph = __builtin_amdgcn_readlane(my_phys[0], pi & 63);
+#pragma unroll
+        for (int w = 1; w < kWin; w++)
+            if ((pi >> 6) == w) ph = __builtin_amdgcn_readlane(my_phys[w], pi & 63);
+        return ph;
     };
     // slab s of this wave: page lp_begin + pi, half `half` of it, key head hk (fastest)
     // (one key head: a page holds one or two slabs, so shifts replace the division)
@@ -332,8 +417,8 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
     auto issue = [&](int s, Slab<FMT>& dst) {
         int pi, half, hk;
         slab_pos(s, pi, half, hk);
-        const int phys = __builtin_amdgcn_readlane(my_phys, pi & 63);
-        const bool ok = s < n_slabs && phys >= 0;
+        const int phys = phys_of(pi);
+        const bool ok = s < n_vis && phys >= 0;
         const int64_t pg = ok ? phys : 0;
         const int64_t tok = (int64_t)hk * p.page + half * 64;
         const uint8_t* kb = p.k + pg * p.kp_s + tok * 64;
@@ -379,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
 #pragma unroll
     for (int k = 0; k < kSW; k++) {
         const int i = threadIdx.x + kThreads * k;
-        if (i < RG * H) sw[i] = i / H < nrows ? st_w[k] : 0.0f;
+        if (i < NT * 16) sw[i] = stw_ok[k] ? st_w[k] : 0.0f;
     }
     lds_barrier();
     if (!has_work) return;  // uniform per wave, after the only barrier
@@ -387,20 +472,20 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
     // ---- per-lane head weights (lane group g sums rows 4g .. 4g+3 of each tile) and
     // MXFP4 scale codes; neither depends on the request segment: a lane only ever adds
     // products of its own query row
-    float wv[NT][4];
+    auto w_tile = [&](int j) { return *reinterpret_cast<const v4f*>(sw + (j * 4 + g) * 4); };
+    // more than 8 tiles: the weights are read from LDS a tile at a time
+    constexpr bool kWLds = FP4IDX_LOGITS_WLDS || NT > 8;
+    v4f wv[kWLds ? 1 : NT];
+    if constexpr (!kWLds) {
 #pragma unroll
-    for (int j = 0; j < NT; j++) {
-        const int hk = j / p.tiles_per_kv, jj = j - hk * p.tiles_per_kv;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int hlo = (16 / RG) * jj + 4 * (g / RG) + i;
-            const bool hv = j < p.n_tiles && hlo < p.R;
-            wv[j][i] = hv ? sw[(g % RG) * H + hk * p.R + hlo] : 0.0f;
-        }
+        for (int j = 0; j < NT; j++) wv[j] = w_tile(j);
     }
     uint32_t acodes[(NT + 3) / 4];
     if constexpr (FMT == 0) {
-        if constexpr (NT == 8) {
+        if constexpr (NT == 16) {
+            const uint4 c4 = *reinterpret_cast<const uint4*>(sac + lane * NT);
+            acodes[0] = c4.x, acodes[1] = c4.y, acodes[2] = c4.z, acodes[3] = c4.w;
+        } else if constexpr (NT == 8) {
             const uint2 c2 = *reinterpret_cast<const uint2*>(sac + lane * NT);
             acodes[0] = c2.x, acodes[1] = c2.y;
         } else if constexpr (NT == 4) {
@@ -424,12 +509,6 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
         }
         return o;
     };
-    const bool lane_stores = g < RG;
-    // output addressing: row t0 + (g % RG), column col0, relative to the slab's first
-    // column of row t0 (the host keeps (RG-1) rows + 64 columns within 2^31 bytes)
-    const int64_t row_base = (int64_t)t0 * p.out_rs;
-    const uint32_t lane_off = (uint32_t)(((int64_t)(g % RG) * p.out_rs + 4 * n) * 4);
-    const uint32_t out_range = (uint32_t)(((int64_t)(RG - 1) * p.out_rs + 64) * 4);
 
     // The rows of a block may belong to different requests; each pass handles the rows
     // of one request (rows of a request are consecutive).
@@ -443,16 +522,23 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
         const bool st_lane = lane_stores && row_ok;
         // ---- the wave's slabs: three buffers in a ring keep two slabs of keys in flight
         // while one is computed (slab s lives in buffer s % 3)
-        float acc[4][4];
+        // head sums: acc[set][key tile][i]; tiles 8*set .. 8*set+7 go to one set, so
+        // no accumulation chain is longer than 8 multiply-adds
+        constexpr int kSets = NT > 8 ? 2 : 1;
+        float acc[kSets][4][4];
 #pragma unroll
-        for (int tt = 0; tt < 4; tt++)
+        for (int c = 0; c < kSets; c++)
 #pragma unroll
-            for (int i = 0; i < 4; i++) acc[tt][i] = 0.0f;
+            for (int tt = 0; tt < 4; tt++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) acc[c][tt][i] = 0.0f;
         Operand<FMT> acur = a_op(0);  // the A tile the next product needs
+        v4f wcur = v4f{0.f, 0.f, 0.f, 0.f}, wnext = v4f{0.f, 0.f, 0.f, 0.f};
+        if constexpr (kWLds) wnext = w_tile(0);  // weights of the epilogue's tile, the next
         auto compute = [&](int s, const Slab<FMT>& buf) {
             int pi, half, hk;
             slab_pos(s, pi, half, hk);
-            const int phys = __builtin_amdgcn_readlane(my_phys, pi);
+            const int phys = phys_of(pi);
             const bool last_kv = !MKV || hk == p.Hkv - 1;  // all key heads of these keys are in
             const int col0 = (lp_begin + pi) * p.page + half * 64 + 4 * n;
             float o[4];
@@ -497,6 +583,18 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
                     const int qp = q - (DEPTH - 1);
                     if (qp >= 0) {
                         const int jp = qp >> 2, tp = qp & 3;
+                        v4f wj;
+                        if constexpr (kWLds) {
+                            // tile jp's weights were read four products ago; read the
+                            // next tile's (wrapping to the next slab's first) now
+                            if (tp == 0) {
+                                wcur = wnext;
+                                wnext = w_tile(jp + 1 < NT ? jp + 1 : 0);
+                            }
+                            wj = wcur;
+                        } else {
+                            wj = wv[kWLds ? 0 : jp];
+                        }
                         if (!MKV || jp / p.tiles_per_kv == hk) {
                             // four independent ReLUs first, then the four multiply-adds,
                             // so no instruction waits on the one just before it; without
@@ -508,8 +606,9 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
                             for (int i = 0; i < 4; i++) r[i] = relu<FMT>(d[i]);
 #pragma unroll
                             for (int i = 0; i < 4; i++)
-                                acc[tp][i] = (!MKV && jp == 0) ? wv[0][i] * r[i]
-                                                               : __builtin_fmaf(wv[jp][i], r[i], acc[tp][i]);
+                                acc[jp >> 3][tp][i] = (!MKV && (jp & 7) == 0)
+                                                          ? wj[i] * r[i]
+                                                          : __builtin_fmaf(wj[i], r[i], acc[jp >> 3][tp][i]);
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);
@@ -517,15 +616,19 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
                 if (!last_kv) return;
 #pragma unroll
                 for (int tt = 0; tt < 4; tt++) {
-                    float v = (acc[tt][0] + acc[tt][1]) + (acc[tt][2] + acc[tt][3]);
+                    float v = (acc[0][tt][0] + acc[0][tt][1]) + (acc[0][tt][2] + acc[0][tt][3]);
+                    if constexpr (kSets == 2)
+                        v += (acc[1][tt][0] + acc[1][tt][1]) + (acc[1][tt][2] + acc[1][tt][3]);
                     v = group_sum<RG>(v);
                     o[tt] = col0 + tt < len ? v : -__builtin_inff();
                 }
                 if constexpr (MKV) {
 #pragma unroll
-                    for (int tt = 0; tt < 4; tt++)
+                    for (int c = 0; c < kSets; c++)
 #pragma unroll
-                        for (int i = 0; i < 4; i++) acc[tt][i] = 0.0f;
+                        for (int tt = 0; tt < 4; tt++)
+#pragma unroll
+                            for (int i = 0; i < 4; i++) acc[c][tt][i] = 0.0f;
                 }
             } else {
                 // an invisible page (past every row's length, or invalid) only gets -inf
@@ -533,26 +636,7 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
 #pragma unroll
                 for (int tt = 0; tt < 4; tt++) o[tt] = -__builtin_inff();
             }
-            // Stores go through a descriptor based at the slab's first column of row
-            // t0; lanes that must not store get an offset past its range, so every
-            // slab issues the same store instructions without a branch.  Streaming
-            // (non-temporal): the logits are not read again by this kernel, and
-            // keeping them out of L2 leaves room for the keys.  A slab inside the
-            // output takes one 16-byte store per lane, the last one of a row four
-            // 4-byte stores.
-            const int colb = col0 - 4 * n;
-            const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + row_base + colb, out_range);
-            if (colb + 64 <= p.out_cols) {
-                const v4f ov = v4f{o[0], o[1], o[2], o[3]};
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, ov), ro,
-                                                       st_lane ? lane_off : kOffNone, 0, kNonTemporal);
-            } else {
-#pragma unroll
-                for (int tt = 0; tt < 4; tt++)
-                    __builtin_amdgcn_raw_buffer_store_b32(
-                        __float_as_uint(o[tt]), ro,
-                        st_lane && col0 + tt < p.out_cols ? lane_off + 4u * tt : kOffNone, 0, kNonTemporal);
-            }
+            store_slab(col0 - 4 * n, o, st_lane);
         };
         // The loop body has no early exit: the last one or two slabs are computed
         // after it.  (An exit taken in the middle of the body would join the loop
@@ -560,15 +644,15 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
         // in, which drains the ring once per pass.)
         int s = 0;
 #if FP4IDX_LOGITS_RING == 2
-        for (; s + 2 <= n_slabs; s += 2) {
+        for (; s + 2 <= n_vis; s += 2) {
             compute(s, b0);
             issue(s + 2, b0);
             compute(s + 1, b1);
             issue(s + 3, b1);
         }
-        if (s < n_slabs) compute(s, b0);
+        if (s < n_vis) compute(s, b0);
 #else
-        for (; s + 3 <= n_slabs; s += 3) {
+        for (; s + 3 <= n_vis; s += 3) {
             issue(s + 2, b2);
             compute(s, b0);
             issue(s + 3, b0);
@@ -576,9 +660,10 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
             issue(s + 4, b1);
             compute(s + 2, b2);
         }
-        if (s < n_slabs) compute(s, b0);
-        if (s + 1 < n_slabs) compute(s + 1, b1);
+        if (s < n_vis) compute(s, b0);
+        if (s + 1 < n_vis) compute(s + 1, b1);
 #endif
+        fill(vis_pages, st_lane);
         t_seg = seg_end;
     }
 }
@@ -586,7 +671,7 @@ template <int FMT, int RG, int NT>
 hipError_t launch3(const LogitsParams& p, hipStream_t stream) {
     const int64_t blocks = (int64_t)p.n_rowblocks * p.n_wgchunks;
     if (blocks <= 0) return hipSuccess;
-    const size_t lds = ALayout<FMT, NT>::bytes(RG, p.H);
+    const size_t lds = ALayout<FMT, NT>::kBytes;
     if (p.Hkv == 1)
         hipLaunchKernelGGL((k_logits<FMT, RG, NT, false>), dim3((unsigned)blocks), dim3(kThreads), lds,
                            stream, p);
@@ -600,6 +685,9 @@ template <int FMT, int RG>
 hipError_t launch2(const LogitsParams& p, hipStream_t stream) {
     if (p.n_tiles <= 2) return launch3<FMT, RG, 2>(p, stream);
     if (p.n_tiles <= 4) return launch3<FMT, RG, 4>(p, stream);
+    if constexpr (RG > 1) {  // one row per block never needs more than 8 tiles (H <= 128)
+        if (p.n_tiles > 8) return launch3<FMT, RG, 16>(p, stream);
+    }
     return launch3<FMT, RG, 8>(p, stream);
 }
 
@@ -617,8 +705,9 @@ hipError_t launch1(const LogitsParams& p, hipStream_t stream) {
 hipError_t launch_logits(const LogitsParams& p_in, hipStream_t stream) {
     LogitsParams p = p_in;
     // Rows per A-tile group: as many as the average request holds (up to 4), reduced
-    // while the A tiles would not fit the register budget (8 tiles).  Any choice is
-    // correct; rows of different requests in one block are handled in separate passes.
+    // while the block would need more than FP4IDX_LOGITS_MAX_NT A tiles (at most 16;
+    // they live in LDS).  Any choice is correct; rows of different requests in one block
+    // are handled in separate passes.
     int rg = 1;
     if (p.T >= 4 * p.B) rg = 4;
     else if (p.T >= 2 * p.B) rg = 2;
@@ -626,17 +715,17 @@ hipError_t launch_logits(const LogitsParams& p_in, hipStream_t stream) {
         const int hpt = 16 / rg;  // heads per A tile per row
         p.tiles_per_kv = (p.R + hpt - 1) / hpt;
         p.n_tiles = p.Hkv * p.tiles_per_kv;
-        if (p.n_tiles <= 8 || rg == 1) break;
+        if (p.n_tiles <= FP4IDX_LOGITS_MAX_NT || rg == 1) break;
         rg >>= 1;
     }
-    if (p.n_tiles > 8) return hipErrorInvalidValue;  // H <= 128 is checked by the caller
+    if (p.n_tiles > 8 * (rg == 1 ? 1 : 2)) return hipErrorInvalidValue;  // H <= 128 is checked by the caller
     p.rows_per_block = rg;
     p.n_rowblocks = (p.T + rg - 1) / rg;
     const int n_pages_out = (p.out_cols + p.page - 1) / p.page;
-    // pages per wave: about FP4IDX_LOGITS_WAVES waves, at most 64 pages each.  Rows of
-    // different lengths leave the waves past a row's end with nothing but -inf to
-    // write, so the grid is cut finer than one pass of the chip: workgroups that end
-    // early free their slots for the rest.
+    // pages per wave: about FP4IDX_LOGITS_WAVES waves, at most FP4IDX_LOGITS_MAX_PPW
+    // pages each.  Long waves spread the per-workgroup set-up (operand staging, the
+    // first key loads) over more work; enough of them keep every SIMD busy.  Pages past
+    // every row's end only get -inf, from a loop that reads no keys.
     const int64_t total = (int64_t)p.n_rowblocks * n_pages_out;
     int64_t ppw = (total + FP4IDX_LOGITS_WAVES - 1) / FP4IDX_LOGITS_WAVES;
     ppw = ppw < 1 ? 1 : (ppw > FP4IDX_LOGITS_MAX_PPW ? FP4IDX_LOGITS_MAX_PPW : ppw);
