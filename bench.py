@@ -43,7 +43,7 @@ MFMA_PEAK_TFLOPS = {"fp4": 10100.0, "fp16": 2500.0}
 CSRC = "sparse_attention_fp4_amd/csrc/"
 COMMON_SOURCES = [CSRC + "device_common.hpp", CSRC + "fp4idx_internal.hpp", CSRC + "fp4idx_api.hip"]
 KERNEL_SOURCES = {"logits": [CSRC + "logits.hip"] + COMMON_SOURCES,
-                  "topk": [CSRC + "topk.hip", CSRC + "topk_long.hip"] + COMMON_SOURCES,
+                  "topk": [CSRC + "topk.hip", CSRC + "topk_long.hip", CSRC + "topk_stream.hip"] + COMMON_SOURCES,
                   "block_scores": [CSRC + "block_scores.hip"] + COMMON_SOURCES}
 
 

@@ -68,6 +68,8 @@ struct TopkParams {
 hipError_t launch_logits(const LogitsParams& p, hipStream_t stream);
 hipError_t launch_block_scores(const BlockParams& p, hipStream_t stream);
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
+hipError_t launch_topk_stream(const TopkParams& p, hipStream_t stream);
+int topk_stream_cap(int cols, int k);
 
 struct QuantParams {
     const uint16_t* keys;  // [N][key_rs] bf16 bit patterns

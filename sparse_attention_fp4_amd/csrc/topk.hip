@@ -344,8 +344,21 @@ size_t topk_workspace_bytes(int rows, int cols, int k) {
     return topk_long_rows(cols) ? topk_long_workspace_bytes(rows, cols, k) : 0;
 }
 
+#ifndef FP4IDX_TOPK_STREAM
+#define FP4IDX_TOPK_STREAM 0
+#endif
+
+// Many rows of at most 32768 columns (prefill): one streaming workgroup per row (see
+// topk_stream.hip) keeps the whole chip busy and reads each row once.  Few rows: the
+// per-row work is spread over many workgroups (topk_long.hip) or held in LDS here.
+bool topk_use_stream(const TopkParams& p) {
+    if (FP4IDX_TOPK_STREAM == 2) return true;
+    return p.rows >= 512 && p.cols <= kMaxElems && topk_stream_cap(p.cols, p.k) >= 0;
+}
+
 hipError_t launch_topk(const TopkParams& p_in, hipStream_t stream) {
     TopkParams p = p_in;
+    if (topk_use_stream(p)) return launch_topk_stream(p, stream);
     if (topk_long_rows(p.cols)) return launch_topk_long(p, p.workspace, stream);
     hipLaunchKernelGGL(k_topk, dim3(p.rows), dim3(kThreads), 0, stream, p);
     return hipGetLastError();

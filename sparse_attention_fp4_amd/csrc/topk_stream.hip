@@ -1,0 +1,415 @@
+// topk_stream.hip -- exact top-k of score rows, one workgroup per row streaming the
+// row from memory, gfx950.
+//
+// ("ISSUE -- Lightning Indexer FP4 dequant decodes E2M1 wrong", "Fix (production
+// target)": a wave-level (ballot) top-k instead of a serial shared-memory heap merge.)
+//
+// Same order and output as topk.hip: larger first, ties to the smaller column, -inf
+// and NaN never selected, the chosen columns in increasing order, -1 padded (values
+// -inf).  Scores map to order-preserving 32-bit keys; digit 1 is key bits [31:20],
+// digit 2 bits [19:8], digit 3 bits [7:0].
+//
+// One workgroup per row, no workspace and no exchange between workgroups:
+//   1. sample: evenly spaced columns, about 64 of them above the k-th largest key in
+//      expectation; two digit levels of their keys give the 97th largest sample key
+//      (24 bits of it), `lo`, so about 1.5 k keys of the row are >= lo.
+//   2. stream: one pass over the row keeps every key >= lo in LDS (key and column,
+//      appended in any order) and builds the exact digit-1 histogram of those keys.
+//   3. the histogram and two more digit levels over the kept keys give the k-th
+//      largest key K* and how many keys equal to K* are taken; every kept key above
+//      K* is marked in a column bitmap, and the ties when all of them are taken.
+//   4. the bitmap is read out in column order (a popcount scan) into the output row.
+// Rare cases take extra passes over the row and stay exact: fewer than k keys >= lo
+// (the sample overestimated lo: stream again from the lowest key), more keys >= lo
+// than LDS holds (stream again keeping only keys from the k-th one's digit-1 bin, then
+// its digit-2 bin, then only keys above K*), and more ties at K* than needed (two
+// passes over contiguous column ranges mark the first ones in column order).
+#include "device_common.hpp"
+#include "fp4idx_internal.hpp"
+
+namespace fp4idx {
+
+namespace {
+
+#ifndef FP4IDX_TOPK_U
+#define FP4IDX_TOPK_U 4
+#endif
+constexpr int kSBins = 4096;
+constexpr int kU = FP4IDX_TOPK_U;  // 16-byte loads per thread in one chunk of the row
+
+__device__ __forceinline__ uint32_t skey(float v) {
+    if (!(v > -__builtin_inff())) return 0u;
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of skey for selectable keys (>= skey(-FLT_MAX)).
+__device__ __forceinline__ float from_skey(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// LDS layout (uint32 words): histogram, candidate keys, candidate columns, bitmap,
+// then a small area for scan totals and shared scalars.
+struct StreamLds {
+    uint32_t* hist;
+    uint32_t* ckey;
+    uint32_t* ccol;
+    uint32_t* bmap;
+    int* wtot;   // [16] wave totals of block scans
+    int* pick;   // [4] pick_bin results
+    int* ctr;    // [4] candidate count
+};
+
+__device__ __forceinline__ StreamLds carve(uint32_t* lds, int cap, int words) {
+    StreamLds s;
+    s.hist = lds;
+    s.ckey = s.hist + kSBins;
+    s.ccol = s.ckey + cap;
+    s.bmap = s.ccol + cap;
+    s.wtot = reinterpret_cast<int*>(s.bmap + words);
+    s.pick = s.wtot + 16;
+    s.ctr = s.pick + 4;
+    return s;
+}
+
+}  // namespace
+
+size_t topk_stream_lds_bytes(int cols, int cap) {
+    const int words = (cols + 31) / 32;
+    return 4 * ((size_t)kSBins + 2 * (size_t)cap + words + 24);
+}
+
+namespace {
+
+template <int NT>
+__global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap) {
+    extern __shared__ __align__(16) uint32_t lds_words[];
+    constexpr int NW = NT / 64;
+    constexpr int PB = kSBins / NT;  // histogram bins per thread
+    const int words = (p.cols + 31) / 32;
+    const StreamLds L = carve(lds_words, cap, words);
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int k = p.k;
+    int len = p.cols;
+    if (p.row_lens) len = min(max(p.row_lens[row], 0), p.cols);
+    const float* src = p.scores + (int64_t)row * p.row_stride;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)p.cols * 4u);
+    const int rwords = (len + 31) / 32;  // bitmap words that cover the row
+
+    auto clear_hist = [&]() {
+#pragma unroll
+        for (int b = 0; b < PB; b++) L.hist[tid + NT * b] = 0u;
+    };
+    // The bin holding the kk-th largest of the histogrammed keys: thread t owns bins
+    // kSBins-1-PB*t .. kSBins-PB*t-PB (descending).  pick[0] = bin, [1] = keys in
+    // higher bins, [2] = total, [3] = keys in the bin.  Ends with a barrier.
+    auto pick_desc = [&](int kk) {
+        int c[PB], bin[PB];
+#pragma unroll
+        for (int b = 0; b < PB; b++) {
+            bin[b] = kSBins - 1 - (PB * tid + b);
+            c[b] = (int)L.hist[bin[b]];
+        }
+        pick_bin<NT, PB>(c, bin, kk, L.wtot, L.pick);
+    };
+
+    // ---- clear the histogram, the counter and the row's bitmap words
+    clear_hist();
+    for (int w = tid; w < rwords; w += NT) L.bmap[w] = 0u;
+    if (tid == 0) L.ctr[0] = 0;
+    lds_barrier();
+
+    // ---- 1. sample: S evenly spaced columns, about 64 of them expected above the
+    // k-th largest key; lo = the first 24 bits of the rho-th largest sample key with
+    // rho = 64 + 32 + 1 (four standard deviations of the sample count), so about
+    // 1.5 k keys of the row are >= lo and fewer than k only with probability ~1e-4.
+    // Short rows (len <= 2k) keep every valid key.
+    constexpr int kSPer = NT >= 1024 ? 16 : 4;  // samples per thread at most
+    uint32_t lo = 1u;
+    if (len > 2 * k) {
+        const int S = (int)min((int64_t)NT * kSPer, max((int64_t)1, ((int64_t)len * 64 + k - 1) / k));
+        const int rho = 97;
+        uint32_t sk[kSPer];
+#pragma unroll
+        for (int j = 0; j < kSPer; j++) {
+            const int i = tid + NT * j;
+            sk[j] = i < S ? skey(src[(int)(((int64_t)i * len) / S)]) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kSPer; j++)
+            if (sk[j]) atomicAdd(&L.hist[sk[j] >> 20], 1u);
+        lds_barrier();
+        pick_desc(rho);
+        if (L.pick[2] >= rho) {
+            const uint32_t d1 = (uint32_t)L.pick[0];
+            const int r2 = rho - L.pick[1];
+            lds_barrier();
+            clear_hist();
+            lds_barrier();
+#pragma unroll
+            for (int j = 0; j < kSPer; j++)
+                if (sk[j] && (sk[j] >> 20) == d1) atomicAdd(&L.hist[(sk[j] >> 8) & 0xfffu], 1u);
+            lds_barrier();
+            pick_desc(r2);
+            lo = (d1 << 20) | ((uint32_t)L.pick[0] << 8);
+        }
+        lds_barrier();
+    }
+
+    // ---- 2./3. stream passes until the kept keys settle K*
+    // level 0: keep keys >= lo, histogram digit 1 of the kept keys
+    // level 1: keep keys >= d1:0:0, histogram digit 2 of keys in bin d1
+    // level 2: keep keys >= d1:d2:0, histogram digit 3 of keys in bin (d1, d2)
+    // level 3: keep keys > K* only (fewer than k: they always fit)
+    int level = 0;
+    uint32_t kstar = 0u;   // K* once known
+    int need = 0;          // keys equal to K* that are taken
+    int ties = 0;          // keys equal to K* in the row
+    int kk = k;            // rank of K* among the keys matching the current prefix
+    int n_kept = 0;
+    bool all_valid = false;  // fewer valid keys than k: every valid key is taken
+    const int n_ch = (len + 4 * NT * kU - 1) / (4 * NT * kU);
+    for (;;) {
+        clear_hist();
+        if (tid == 0) L.ctr[0] = 0;
+        lds_barrier();
+        const int hshift = level == 0 ? 20 : (level == 1 ? 8 : 0);
+        const uint32_t hmask = level == 2 ? 0xffu : 0xfffu;
+        const int pshift = level == 0 ? 32 : (level == 1 ? 20 : 8);  // prefix bits above the digit
+        const uint32_t prefix = pshift == 32 ? 0u : (lo >> pshift);
+        // The row streams through in chunks of kU 16-byte loads per thread (4 * NT * kU
+        // columns), the next chunk's loads in flight while one is processed.  Column
+        // 4 * (tid + NT * u) + e of a chunk is element e of load u.  A chunk that
+        // reaches past the row end reads dwords, so no 16-byte load straddles the
+        // buffer's end.  Kept keys go to LDS with one counter update per wave and chunk.
+        auto load_chunk = [&](int ch, v4f (&buf)[kU]) {
+            const int cb = ch * 4 * NT * kU;
+            // per-thread part of the address in a VGPR, the rest in the scalar offset
+            if (cb + 4 * NT * kU <= len) {
+#pragma unroll
+                for (int u = 0; u < kU; u++)
+                    buf[u] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         rs, 16 * tid, 4 * cb + 16 * NT * u, 0));
+            } else {
+#pragma unroll
+                for (int u = 0; u < kU; u++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        buf[u][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                                  rs, 16 * tid + 4 * e, 4 * cb + 16 * NT * u, 0));
+            }
+        };
+        // keep test in float space: key(v) >= keep_min, or key(v) > K* in level 3
+        // (NaN compares false; -0 and +0 are one key and compare equal)
+        const bool keep_all = level < 3 && lo <= 0x00800000u;  // every valid key
+        const bool strict = level == 3 || keep_all;
+        const float thr = keep_all ? -__builtin_inff() : from_skey(level == 3 ? kstar : lo);
+        auto kept = [&](float v) { return strict ? v > thr : v >= thr; };
+        auto process = [&](int ch, const v4f (&buf)[kU]) {
+            const int cb = ch * 4 * NT * kU;
+            const bool full = cb + 4 * NT * kU <= len;
+            int nkeep = 0;
+#pragma unroll
+            for (int u = 0; u < kU; u++)
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    nkeep += (kept(buf[u][e]) && (full || cb + 4 * (tid + NT * u) + e < len)) ? 1 : 0;
+            const int incl = wave_incl_scan(nkeep);
+            const int tot = __builtin_amdgcn_readlane(incl, 63);
+            if (tot == 0) return;
+            int base = 0;
+            if (lane == 63) base = atomicAdd(L.ctr, tot);
+            base = __builtin_amdgcn_readlane(base, 63);
+            int pos = base + incl - nkeep;
+#pragma unroll
+            for (int u = 0; u < kU; u++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int c = cb + 4 * (tid + NT * u) + e;
+                    if (kept(buf[u][e]) && (full || c < len)) {
+                        const uint32_t kv = skey(buf[u][e]);
+                        if (level < 3 && (pshift == 32 || (kv >> pshift) == prefix))
+                            atomicAdd(&L.hist[(kv >> hshift) & hmask], 1u);
+                        if (pos < cap) {
+                            L.ckey[pos] = kv;
+                            L.ccol[pos] = (uint32_t)c;
+                        }
+                        pos++;
+                    }
+                }
+        };
+        // pairs of chunks alternate between two buffers; the loop body has no exit
+        v4f ba[kU], bb[kU];
+        int ch = 0;
+        if (n_ch > 0) load_chunk(0, ba);
+        for (; ch + 2 <= n_ch; ch += 2) {
+            load_chunk(ch + 1, bb);
+            process(ch, ba);
+            if (ch + 2 < n_ch) load_chunk(ch + 2, ba);
+            process(ch + 1, bb);
+        }
+        if (ch < n_ch) process(ch, ba);
+        lds_barrier();
+        n_kept = L.ctr[0];
+        const bool overflow = n_kept > cap;
+        if (level == 3) break;  // keys above K* are all kept (fewer than k <= cap)
+        pick_desc(kk);
+        const int total = L.pick[2];
+        if (level == 0 && total < k) {
+            if (lo > 1u) {  // the sample overestimated lo: keep every valid key
+                lo = 1u;
+                lds_barrier();
+                continue;
+            }
+            all_valid = true;  // fewer valid keys than k, all kept (n_kept < k <= cap)
+            lds_barrier();
+            break;
+        }
+        const uint32_t d = (uint32_t)L.pick[0];
+        const int above = L.pick[1], inbin = L.pick[3];
+        lds_barrier();
+        if (!overflow) {
+            // settle the remaining digits over the kept keys in LDS
+            uint32_t pre = level == 0 ? (d << 20) : (level == 1 ? ((lo & 0xfff00000u) | (d << 8)) : ((lo & 0xffffff00u) | d));
+            int lvl = level + 1;
+            kk -= above;
+            ties = inbin;
+            const int nk = n_kept;
+            while (lvl < 3) {
+                clear_hist();
+                lds_barrier();
+                const int sh = lvl == 1 ? 8 : 0;
+                const uint32_t msk = lvl == 1 ? 0xfffu : 0xffu;
+                const int ps = lvl == 1 ? 20 : 8;
+                for (int i = tid; i < nk; i += NT) {
+                    const uint32_t key = L.ckey[i];
+                    if ((key >> ps) == (pre >> ps)) atomicAdd(&L.hist[(key >> sh) & msk], 1u);
+                }
+                lds_barrier();
+                pick_desc(kk);
+                const uint32_t dd = (uint32_t)L.pick[0];
+                kk -= L.pick[1];
+                ties = L.pick[3];
+                pre |= lvl == 1 ? (dd << 8) : dd;
+                lds_barrier();
+                lvl++;
+            }
+            kstar = pre;
+            need = kk;
+            break;
+        }
+        // overflow: narrow what the next pass keeps
+        kk -= above;
+        if (level == 0) lo = d << 20;
+        else if (level == 1) lo = (lo & 0xfff00000u) | (d << 8);
+        else {
+            kstar = (lo & 0xffffff00u) | d;
+            need = kk;
+            ties = inbin;
+        }
+        level++;
+    }
+
+    // ---- mark the selected columns
+    // keys equal to K* are in LDS unless the last pass kept only keys above it
+    const bool ties_kept = level < 3;
+    const int nk = min(n_kept, cap);
+    for (int i = tid; i < nk; i += NT) {
+        const uint32_t key = L.ckey[i];
+        const bool take = all_valid || key > kstar || (key == kstar && ties == need && ties_kept);
+        if (take) {
+            const uint32_t col = L.ccol[i];
+            atomicOr(&L.bmap[col >> 5], 1u << (col & 31));
+        }
+    }
+    if (!all_valid && (ties > need || !ties_kept)) {
+        // the first `need` keys equal to K* in column order: wave w scans columns
+        // [w*span, (w+1)*span) twice (count, then mark)
+        const int span = ((len + NW - 1) / NW + 63) & ~63;
+        const int cbeg = wave * span, cend = min(len, cbeg + span);
+        const int steps = max(cend - cbeg + 63, 0) / 64;
+        int mine = 0;
+        for (int st = 0; st < steps; st++) {
+            const int c = cbeg + 64 * st + lane;
+            const bool eq = c < cend && skey(src[c]) == kstar;
+            mine += __popcll(__ballot(eq));
+        }
+        if (lane == 0) L.wtot[wave] = mine;
+        lds_barrier();
+        int before = 0;
+        for (int w = 0; w < wave; w++) before += L.wtot[w];
+        for (int st = 0; st < steps; st++) {
+            const int c = cbeg + 64 * st + lane;
+            const bool eq = c < cend && skey(src[c]) == kstar;
+            const unsigned long long m = __ballot(eq);
+            const int r = before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (eq && r < need) atomicOr(&L.bmap[c >> 5], 1u << (c & 31));
+            before += __popcll(m);
+        }
+    }
+    lds_barrier();
+
+    // ---- 4. the bitmap in column order: thread t owns words [t*WPT, (t+1)*WPT)
+    const int wpt = (rwords + NT - 1) / NT;
+    int cnt = 0;
+    for (int j = 0; j < wpt; j++) {
+        const int w = tid * wpt + j;
+        if (w < rwords) cnt += __popc(L.bmap[w]);
+    }
+    int excl, total;
+    block_excl_scan<NT>(cnt, L.wtot, excl, total);
+    int32_t* oi = p.out_idx + (int64_t)row * k;
+    float* ov = p.out_vals ? p.out_vals + (int64_t)row * k : nullptr;
+    int pos = excl;
+    for (int j = 0; j < wpt; j++) {
+        const int w = tid * wpt + j;
+        if (w >= rwords) break;
+        uint32_t bits = L.bmap[w];
+        while (bits) {
+            const int b = __builtin_ctz(bits);
+            bits &= bits - 1u;
+            const int col = 32 * w + b;
+            if (pos < k) {
+                oi[pos] = col;
+                if (ov) ov[pos] = src[col];
+            }
+            pos++;
+        }
+    }
+    for (int i = total + tid; i < k; i += NT) {
+        oi[i] = -1;
+        if (ov) ov[i] = -__builtin_inff();
+    }
+}
+
+}  // namespace
+
+// Candidates kept in LDS: k plus slack, within the LDS left after the histogram and
+// the bitmap (at least k, which the exact fallbacks need).
+int topk_stream_cap(int cols, int k) {
+    const size_t budget = 150u * 1024u;
+    const size_t fixed = topk_stream_lds_bytes(cols, 0);
+    size_t room = budget > fixed ? (budget - fixed) / 8 : 0;
+    const size_t want = (size_t)k + 2048;
+    const int cap = (int)(room < want ? room : want);
+    return cap < k ? -1 : cap;
+}
+
+hipError_t launch_topk_stream(const TopkParams& p, hipStream_t stream) {
+    const int cap = topk_stream_cap(p.cols, p.k);
+    if (cap < 0) return hipErrorInvalidValue;
+    const size_t lds = topk_stream_lds_bytes(p.cols, cap);
+    // many short rows: 256 threads a row (several rows share a CU); otherwise 1024
+    if (p.rows >= 512 && p.cols <= 32768)
+        hipLaunchKernelGGL(k_topk_stream<256>, dim3(p.rows), dim3(256), lds, stream, p, cap);
+    else
+        hipLaunchKernelGGL(k_topk_stream<1024>, dim3(p.rows), dim3(1024), lds, stream, p, cap);
+    return hipGetLastError();
+}
+
+}  // namespace fp4idx

@@ -112,3 +112,23 @@ def test_workspace_reused_across_calls_without_clearing():
         oi, ov = orc.topk(s, k, lens)
         assert np.array_equal(idx.cpu().numpy(), oi)
         assert np.array_equal(vals.cpu().numpy().view(np.uint32), ov.view(np.uint32))
+
+
+@pytest.mark.parametrize("rows,cols,k,kind", [(600, 4096, 2048, "normal"), (520, 32768, 2048, "ties"),
+                                              (512, 20000, 100, "clustered"), (700, 3000, 2048, "normal")])
+def test_many_short_rows(rows, cols, k, kind):
+    """Many rows of <= 32768 columns take one streaming workgroup per row."""
+    rng = np.random.default_rng(rows + cols + k)
+    say(f"[gpu] topk many rows rows={rows} cols={cols} k={k} {kind}")
+    if kind == "ties":
+        s = (rng.integers(-20, 20, (rows, cols)) / 4).astype(np.float32)
+    elif kind == "clustered":
+        s = (1.0 + rng.standard_normal((rows, cols)) * 1e-6).astype(np.float32)
+    else:
+        s = rng.standard_normal((rows, cols)).astype(np.float32)
+    s[0, rng.integers(0, cols, 50)] = -np.inf
+    s[1, rng.integers(0, cols, 50)] = np.nan
+    s[2, :] = -np.inf
+    lens = rng.integers(0, cols + 1, rows).astype(np.int32)
+    lens[:6] = [cols, cols, cols, 0, 1, min(cols, k)]
+    _same(s, k, lens)
