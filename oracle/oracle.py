@@ -205,6 +205,25 @@ def topk(scores, k, row_lens=None, n_threads=0):
     return idx, vals
 
 
+def block_topk(scores, k, n_threads=0):
+    """Top-k 128-token blocks of each (head, query) from block scores [Hq, Ktiles, Tq].
+
+    [M3] The block-score interface returns scores only; a caller that wants TopK takes
+    it along the Ktiles dimension (dim 1).  This is that TopK, with the same rule as
+    ``topk``: the k largest finite scores (-inf and NaN never chosen, ties to the
+    smaller block), listed in increasing block order and -1 padded.  The number of
+    chosen blocks per (head, query) is the sparse metadata a block-sparse consumer
+    needs next to the list.
+    -> (idx [Hq, Tq, k] int32, count [Hq, Tq] int32)."""
+    scores = _c(scores, np.float32)
+    Hq, Kt, Tq = scores.shape
+    rows = np.ascontiguousarray(np.transpose(scores, (0, 2, 1))).reshape(Hq * Tq, Kt)
+    idx, _ = topk(rows, k, None, n_threads)
+    idx = idx.reshape(Hq, Tq, k)
+    count = (idx >= 0).sum(axis=2).astype(np.int32)
+    return idx, count
+
+
 def max_threads(n_threads=0) -> int:
     return int(lib().orc_max_threads(n_threads))
 

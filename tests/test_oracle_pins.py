@@ -523,3 +523,37 @@ def test_quantize_store_scatters_by_slot():
                 assert os_[pg, 0, tok, g] == c
     assert np.array_equal(of[:, 0][~touched], kf[:, 0][~touched])
     assert np.array_equal(os_[:, 0][~touched], ks[:, 0][~touched])
+
+
+def test_block_topk_hand_worked():
+    # Hq=1, Ktiles=5, Tq=2.  Query 0 sees blocks [3, 7, -inf, 7, 1]: top-2 = blocks 1 and
+    # 3 (both 7; the tie keeps the smaller block first, and both fit); top-3 adds block 0.
+    # Query 1 sees [nan, -inf, 2, -inf, -inf]: one finite block.
+    s = np.array([[[3, np.nan], [7, -np.inf], [-np.inf, 2], [7, -np.inf], [1, -np.inf]]], np.float32)
+    idx, cnt = orc.block_topk(s, 2)
+    np.testing.assert_array_equal(idx[0], [[1, 3], [2, -1]])
+    np.testing.assert_array_equal(cnt[0], [2, 1])
+    idx, cnt = orc.block_topk(s, 3)
+    np.testing.assert_array_equal(idx[0], [[0, 1, 3], [2, -1, -1]])
+    np.testing.assert_array_equal(cnt[0], [3, 1])
+    # a tie at the k-th place goes to the smaller block
+    t = np.array([[[5], [4], [4], [4]]], np.float32)
+    idx, cnt = orc.block_topk(t, 2)
+    np.testing.assert_array_equal(idx[0, 0], [0, 1])
+
+
+def test_block_topk_brute_force():
+    rng = np.random.default_rng(9)
+    Hq, Kt, Tq, k = 3, 40, 17, 6
+    s = (rng.integers(-8, 8, (Hq, Kt, Tq)) / 2).astype(np.float32)
+    s[rng.random(s.shape) < 0.3] = -np.inf
+    s[0, :, 0] = -np.inf
+    idx, cnt = orc.block_topk(s, k)
+    for h in range(Hq):
+        for q in range(Tq):
+            col = s[h, :, q].astype(np.float64)
+            fin = [b for b in range(Kt) if col[b] > -np.inf]
+            best = sorted(fin, key=lambda b: (-col[b], b))[:k]
+            want = sorted(best) + [-1] * (k - len(best))
+            assert idx[h, q].tolist() == want
+            assert cnt[h, q] == len(best)
