@@ -134,6 +134,21 @@ int fp4idx_block_scores(int fmt,
                         int max_seqlen_q, int max_seqlen_k, int causal,
                         float* scores, void* stream);
 
+/* Top-k 128-token blocks of every (head, query) from block scores [M3 public API: the
+ * block-score interface returns no TopK; a caller takes it along the Ktiles dimension]:
+ * for head h and query q, the candidates are the blocks kb < Ktiles whose score
+ * scores[h][kb][q] is greater than -inf (-inf and NaN are never chosen); the k largest
+ * are chosen, ties toward the smaller block (-0 equals +0).
+ * out_idx[h][q][0..m) receives the chosen blocks in increasing order, m = min(k,
+ * #candidates), and out_idx[h][q][m..k) = -1; out_count[h][q] (nullable) receives m.
+ * scores: [Hq][Ktiles][Tq] float, contiguous (the layout fp4idx_block_scores writes);
+ * out_idx: [Hq][Tq][k] int32; out_count: [Hq][Tq] int32; all caller-owned device
+ * memory.  Asynchronous on `stream`; nothing is allocated.
+ * Limits: 1 <= k <= 64 (else EUNSUPPORTED); EINVAL for Hq < 1, Ktiles < 0, Tq < 0,
+ * k < 1 or a missing pointer. */
+int fp4idx_block_topk(const float* scores, int Hq, int Ktiles, int Tq, int k,
+                      int32_t* out_idx, int32_t* out_count, void* stream);
+
 /* Bytes of device workspace fp4idx_topk needs for these sizes (0 if none). */
 size_t fp4idx_topk_workspace_bytes(int rows, int cols, int k);
 

@@ -5,13 +5,14 @@ this package is its Python binding:
 
     logits_paged(...)   weighted-ReLU logits over a paged FP4 key cache
     block_scores(...)   per-head 128-token block-max scores
+    block_topk(...)     top-k blocks per (head, query) along the block scores' Ktiles
     topk(...)           exact top-k column selection per row
     quantize_store_k(...)  MXFP4 quantize-and-store of keys into the paged cache
 
 ``workloads`` holds seeded synthetic inputs for the benchmark shapes.
 """
-from .ops import (MXFP4, NVFP4, block_scores, logits_paged, quantize_store_k, topk,  # noqa: F401
-                  topk_workspace_bytes)
+from .ops import (MXFP4, NVFP4, block_scores, block_topk, logits_paged,  # noqa: F401
+                  quantize_store_k, topk, topk_workspace_bytes)
 
-__all__ = ["MXFP4", "NVFP4", "logits_paged", "block_scores", "topk", "topk_workspace_bytes",
-           "quantize_store_k"]
+__all__ = ["MXFP4", "NVFP4", "logits_paged", "block_scores", "block_topk", "topk",
+           "topk_workspace_bytes", "quantize_store_k"]

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libfp4idx.so")
 EXPORTS = (
     "fp4idx_logits_paged",
     "fp4idx_block_scores",
+    "fp4idx_block_topk",
     "fp4idx_topk_workspace_bytes",
     "fp4idx_topk",
     "fp4idx_quantize_store_k",
@@ -49,6 +50,8 @@ def lib() -> ctypes.CDLL:
     L.fp4idx_block_scores.restype = i32
     L.fp4idx_block_scores.argtypes = [i32, P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                       i32, i32, i32, P, P]
+    L.fp4idx_block_topk.restype = i32
+    L.fp4idx_block_topk.argtypes = [P, i32, i32, i32, i32, P, P, P]
     L.fp4idx_topk_workspace_bytes.restype = ctypes.c_size_t
     L.fp4idx_topk_workspace_bytes.argtypes = [i32, i32, i32]
     L.fp4idx_topk.restype = i32

@@ -169,6 +169,24 @@ int fp4idx_quantize_store_k(const uint16_t* keys, int64_t key_row_stride, const 
     return hip_status(fp4idx::launch_quantize_store(p, (hipStream_t)stream));
 }
 
+int fp4idx_block_topk(const float* scores, int Hq, int Ktiles, int Tq, int k,
+                      int32_t* out_idx, int32_t* out_count, void* stream) {
+    if (Hq < 1 || Ktiles < 0 || Tq < 0 || k < 1) return FP4IDX_EINVAL;
+    if (k > 64) return FP4IDX_EUNSUPPORTED;
+    if (Tq == 0) return FP4IDX_OK;
+    if (!out_idx || (Ktiles > 0 && !scores)) return FP4IDX_EINVAL;
+    if ((int64_t)Hq * Ktiles * Tq > ((int64_t)1 << 40)) return FP4IDX_EUNSUPPORTED;
+    fp4idx::BlockTopkParams p{};
+    p.scores = scores;
+    p.Hq = Hq;
+    p.Kt = Ktiles;
+    p.Tq = Tq;
+    p.k = k;
+    p.out_idx = out_idx;
+    p.out_count = out_count;
+    return hip_status(fp4idx::launch_block_topk(p, (hipStream_t)stream));
+}
+
 size_t fp4idx_topk_workspace_bytes(int rows, int cols, int k) {
     if (rows <= 0 || cols <= 0 || k <= 0) return 0;
     return fp4idx::topk_workspace_bytes(rows, cols, k);

@@ -65,7 +65,15 @@ struct TopkParams {
     void* workspace;          // long rows only (see topk_workspace_bytes)
 };
 
+struct BlockTopkParams {
+    const float* scores;  // [Hq][Kt][Tq]
+    int Hq, Kt, Tq, k;
+    int32_t* out_idx;     // [Hq][Tq][k]
+    int32_t* out_count;   // [Hq][Tq], nullable
+};
+
 hipError_t launch_logits(const LogitsParams& p, hipStream_t stream);
+hipError_t launch_block_topk(const BlockTopkParams& p, hipStream_t stream);
 hipError_t launch_block_scores(const BlockParams& p, hipStream_t stream);
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
 hipError_t launch_topk_stream(const TopkParams& p, hipStream_t stream);

@@ -198,6 +198,25 @@ def topk(scores, k: int, row_lens=None, *, out_idx=None, out_vals=None, want_val
     return out_idx, out_vals
 
 
+def block_topk(scores, k: int, *, out_idx=None, out_count=None):
+    """Top-k 128-token blocks per (head, query) along Ktiles of block scores
+    [Hq, Ktiles, Tq] -> (idx [Hq, Tq, k] int32 in increasing block order, -1 padded,
+    count [Hq, Tq] int32)."""
+    _need(scores, "scores", torch.float32, 3)
+    if not scores.is_contiguous():
+        raise ValueError("scores must be contiguous [Hq, Ktiles, Tq]")
+    dev = scores.device
+    Hq, Kt, Tq = scores.shape
+    if out_idx is None:
+        out_idx = torch.empty((Hq, Tq, k), dtype=torch.int32, device=dev)
+    if out_count is None:
+        out_count = torch.empty((Hq, Tq), dtype=torch.int32, device=dev)
+    rc = lib().fp4idx_block_topk(_ptr(scores), Hq, Kt, Tq, k, _ptr(out_idx), _ptr(out_count),
+                                 _stream())
+    check("fp4idx_block_topk", rc)
+    return out_idx, out_count
+
+
 def quantize_store_k(keys, slots, k_fp4, k_scale):
     """MXFP4 quantize-and-store of keys [N, 128] (bf16) into the paged cache k_fp4
     [P, 1, page, 64] / k_scale [P, 1, page, 4] (uint8, modified in place) at the given

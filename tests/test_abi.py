@@ -106,3 +106,15 @@ def test_quantize_store_argument_errors():
     assert f(256, 100, 256, 4, 256, 4096, 256, 256, 64, 4, None) == 1        # short rows
     assert f(258, 128, 256, 4, 256, 4096, 256, 256, 64, 4, None) == 3        # misaligned
     assert f(256, 129, 256, 4, 256, 4096, 256, 256, 64, 4, None) == 3        # odd stride
+
+
+def test_block_topk_argument_errors():
+    L = _lib.lib()
+    f = L.fp4idx_block_topk
+    assert f(256, 0, 4, 8, 2, 256, None, None) == 1        # Hq < 1
+    assert f(256, 2, -1, 8, 2, 256, None, None) == 1       # Ktiles < 0
+    assert f(256, 2, 4, 8, 0, 256, None, None) == 1        # k < 1
+    assert f(256, 2, 4, 8, 65, 256, None, None) == 2       # k > 64
+    assert f(256, 2, 4, 0, 2, 256, None, None) == 0        # no queries: nothing to do
+    assert f(None, 2, 4, 8, 2, 256, None, None) == 1       # missing scores
+    assert f(256, 2, 4, 8, 2, None, None, None) == 1       # missing output
