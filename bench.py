@@ -10,7 +10,8 @@ the FP4 indexer scorer...", Speed Tests: 4 verify rows, 32 heads, contexts 16,38
   batched  64 requests x 1 row, H=64, contexts U[4096, 131072], logits + top-2048;
   prefill  one request, 32768 causal query rows x 32768 keys, H=64, logits + top-2048;
   block    NVFP4 per-head 128-token block maxima, varlen batch of 8, Hq=32, Hkv=4,
-           causal ("M3 FP4 Indexer" README shapes).
+           causal ("M3 FP4 Indexer" README shapes), then the top-16 blocks of every
+           (head, query) along Ktiles.
 
 Timing: inputs are resident in HBM before the timed region.  Steps rotate over enough
 independent input/output sets that their total (> 512 MiB) exceeds the 256 MiB
@@ -44,7 +45,8 @@ CSRC = "sparse_attention_fp4_amd/csrc/"
 COMMON_SOURCES = [CSRC + "device_common.hpp", CSRC + "fp4idx_internal.hpp", CSRC + "fp4idx_api.hip"]
 KERNEL_SOURCES = {"logits": [CSRC + "logits.hip"] + COMMON_SOURCES,
                   "topk": [CSRC + "topk.hip", CSRC + "topk_long.hip", CSRC + "topk_stream.hip"] + COMMON_SOURCES,
-                  "block_scores": [CSRC + "block_scores.hip"] + COMMON_SOURCES}
+                  "block_scores": [CSRC + "block_scores.hip"] + COMMON_SOURCES,
+                  "block_topk": [CSRC + "block_topk.hip"] + COMMON_SOURCES}
 
 
 def parse():
@@ -204,7 +206,8 @@ def block_workload(args, torch, fp4, wl, dev):
     case = wl.config3()
     name = "nvfp4_block_prefill_b8"
     desc = (f"{name}: NVFP4 per-head 128-token block maxima, B=8, q_len U[128,2048], "
-            f"k_len = q_len + U[0,8192], Hq=32, Hkv=4, D=128, causal, 128-token pages shuffled")
+            f"k_len = q_len + U[0,8192], Hq=32, Hkv=4, D=128, causal, 128-token pages shuffled, "
+            f"then the top-16 blocks per (head, query)")
 
     def up(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -215,9 +218,13 @@ def block_workload(args, torch, fp4, wl, dev):
     out_elems = case.Hq * case.ktiles * case.Tq
     set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + out_elems * 4
 
+    bk = 16  # blocks chosen per (head, query): 2048 tokens of 128-token blocks
+
     def make_set():
         s = {n: (t if n in ("cuq", "cuk", "cup", "kvi") else t.clone()) for n, t in base.items()}
         s["out"] = torch.empty((case.Hq, case.ktiles, case.Tq), dtype=torch.float32, device=dev)
+        s["bidx"] = torch.empty((case.Hq, case.Tq, bk), dtype=torch.int32, device=dev)
+        s["bcnt"] = torch.empty((case.Hq, case.Tq), dtype=torch.int32, device=dev)
         return s
 
     def blocks(s):
@@ -225,12 +232,17 @@ def block_workload(args, torch, fp4, wl, dev):
                          max_seqlen_q=case.max_seqlen_q, max_seqlen_k=case.max_seqlen_k,
                          kv_indices=s["kvi"], fmt="nvfp4", causal=True, out=s["out"])
 
+    def btopk(s):
+        fp4.block_topk(s["out"], bk, out_idx=s["bidx"], out_count=s["bcnt"])
+
     pairs = case.visible_pairs()
     keys = int(case.cu_seqlens_k[-1])
     bytes_ = (keys * case.Hkv * 72 + case.Tq * case.Hq * 72 + out_elems * 4
               + int(case.cu_page_offsets[-1]) * 4 + 3 * (case.B + 1) * 4)
     work = {"block_scores": dict(bytes=bytes_, flops=2 * case.Hq * 128 * pairs, bound="mfma",
-                                 dtype="fp16")}
+                                 dtype="fp16"),
+            "block_topk": dict(bytes=out_elems * 4 + case.Hq * case.Tq * (bk + 1) * 4, flops=0,
+                               bound="hbm", dtype=None)}
 
     def cpu_baseline():
         from oracle import oracle as orc
@@ -256,10 +268,11 @@ def block_workload(args, torch, fp4, wl, dev):
                            f"run(s) in {total:.1f} s")
 
     return dict(name=name, desc=desc, set_bytes=set_bytes, make_set=make_set,
-                calls={"block_scores": blocks}, work=work, pairs=pairs, steps=64, warmup=8,
+                calls={"block_scores": blocks, "block_topk": btopk}, work=work, pairs=pairs,
+                steps=64, warmup=8,
                 launches=16, cpu_baseline=cpu_baseline,
                 config={"rows": case.Tq, "heads": case.Hq, "kv_heads": case.Hkv,
-                        "ktiles": case.ktiles},
+                        "ktiles": case.ktiles, "block_topk": bk},
                 dtype="nvfp4 (e2m1 x e4m3, exact fp16 operands, fp32 accumulate)")
 
 
