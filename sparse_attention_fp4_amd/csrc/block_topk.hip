@@ -10,13 +10,11 @@
 //
 // One lane per (head, query): a wave holds 64 consecutive queries of one head, so each
 // step reads 64 consecutive floats of one block row of [Hq][Ktiles][Tq] (coalesced).
-//   pass 1: each lane keeps its KMAX best (key, block) pairs sorted in registers (an
-//           insertion network; a step that would change no lane's list is skipped).
-//           Strict comparison keeps the earlier block ahead among equal keys, so the
-//           list's k-th key T and the number of list entries equal to T ("need")
-//           settle the choice.
-//   pass 2: the lane walks its blocks again in order and writes every block above T
-//           and the first `need` blocks equal to T.
+// Each lane keeps its KMAX best (key, block) pairs sorted in registers (an insertion
+// network; a step that would change no lane's list is skipped).  Strict comparison
+// keeps the earlier block ahead among equal keys, so the list's first k entries are
+// exactly the chosen blocks; a sorting network puts them in block order for the
+// output.  Every score is read once.
 #include "device_common.hpp"
 #include "fp4idx_internal.hpp"
 
@@ -47,46 +45,51 @@ __global__ __launch_bounds__(256) void k_block_topk(const BlockTopkParams p) {
     for (int kb = 0; kb < p.Kt; kb++) {
         const float v = nxt;
         if (kb + 1 < p.Kt) nxt = col[(kb + 1) * step];
-        uint32_t key = active ? bkey(v) : 0u;
+        const uint32_t key = active ? bkey(v) : 0u;
         if (__ballot(key > lk[KMAX - 1]) == 0ull) continue;
-        int b = kb;
+        // insert at the first slot holding a smaller key and shift the rest down one
+        // (the list is sorted, so c[i] is false up to that slot and true after it;
+        // equal keys stay in block order)
+        bool c[KMAX];
 #pragma unroll
-        for (int i = 0; i < KMAX; i++) {
-            const bool gt = key > lk[i];
-            const uint32_t tk = lk[i];
-            const int tb = lb[i];
-            lk[i] = gt ? key : tk;
-            lb[i] = gt ? b : tb;
-            key = gt ? tk : key;
-            b = gt ? tb : b;
+        for (int i = 0; i < KMAX; i++) c[i] = key > lk[i];
+#pragma unroll
+        for (int i = KMAX - 1; i > 0; i--) {
+            lk[i] = c[i] ? (c[i - 1] ? lk[i - 1] : key) : lk[i];
+            lb[i] = c[i] ? (c[i - 1] ? lb[i - 1] : kb) : lb[i];
         }
+        lk[0] = c[0] ? key : lk[0];
+        lb[0] = c[0] ? kb : lb[0];
     }
     if (!active) return;
-    // T = the k-th key (0: fewer than k valid blocks, all of them are chosen)
-    uint32_t T = 0u;
+    // The list's first k entries are the chosen blocks: put them in block order (a
+    // sorting network on the block indices; entries past k or empty sort last).
+    int m = 0;
 #pragma unroll
-    for (int i = 0; i < KMAX; i++)
-        if (i == p.k - 1) T = lk[i];
-    int need = 0;
-#pragma unroll
-    for (int i = 0; i < KMAX; i++)
-        if (i < p.k && lk[i] == T && T != 0u) need++;
-
-    int32_t* out = p.out_idx + ((int64_t)hq * p.Tq + q) * p.k;
-    int pos = 0, seen = 0;
-    for (int kb = 0; kb < p.Kt; kb++) {
-        const uint32_t key = bkey(col[kb * step]);
-        bool take;
-        if (T == 0u) {
-            take = key != 0u;
-        } else {
-            take = key > T || (key == T && seen < need);
-            seen += key == T ? 1 : 0;
-        }
-        if (take) out[pos++] = kb;
+    for (int i = 0; i < KMAX; i++) {
+        const bool use = i < p.k && lk[i] != 0u;
+        m += use ? 1 : 0;
+        lb[i] = use ? lb[i] : INT32_MAX;
     }
-    for (int i = pos; i < p.k; i++) out[i] = -1;
-    if (p.out_count) p.out_count[(int64_t)hq * p.Tq + q] = pos;
+#pragma unroll
+    for (int size = 2; size <= KMAX; size <<= 1)
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+            for (int i = 0; i < KMAX; i++) {
+                const int j = i ^ stride;
+                if (j > i) {
+                    const bool up = (i & size) == 0;
+                    const int a = lb[i], b = lb[j];
+                    lb[i] = up ? min(a, b) : max(a, b);
+                    lb[j] = up ? max(a, b) : min(a, b);
+                }
+            }
+    int32_t* out = p.out_idx + ((int64_t)hq * p.Tq + q) * p.k;
+#pragma unroll
+    for (int i = 0; i < KMAX; i++)
+        if (i < p.k) out[i] = i < m ? lb[i] : -1;
+    if (p.out_count) p.out_count[(int64_t)hq * p.Tq + q] = m;
 }
 
 template <int KMAX>

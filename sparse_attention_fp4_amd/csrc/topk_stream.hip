@@ -10,9 +10,10 @@
 // digit 2 bits [19:8], digit 3 bits [7:0].
 //
 // One workgroup per row, no workspace and no exchange between workgroups:
-//   1. sample: evenly spaced columns, about 64 of them above the k-th largest key in
-//      expectation; two digit levels of their keys give the 97th largest sample key
-//      (24 bits of it), `lo`, so about 1.5 k keys of the row are >= lo.
+//   1. sample: runs of 32 adjacent columns at evenly spaced starts, about 64 sampled
+//      keys above the k-th largest key in expectation; two digit levels of their keys
+//      give the 97th largest sample key (24 bits of it), `lo`, so about 1.5 k keys of
+//      the row are >= lo.
 //   2. stream: one pass over the row keeps every key >= lo in LDS (key and column,
 //      appended in any order) and builds the exact digit-1 histogram of those keys.
 //   3. the histogram and two more digit levels over the kept keys give the k-th
@@ -134,10 +135,13 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
         const int S = (int)min((int64_t)NT * kSPer, max((int64_t)1, ((int64_t)len * 64 + k - 1) / k));
         const int rho = 97;
         uint32_t sk[kSPer];
+        // runs of 32 adjacent columns (one 128-byte line each) at evenly spaced starts
+        const int runs = (S + 31) / 32;
 #pragma unroll
         for (int j = 0; j < kSPer; j++) {
             const int i = tid + NT * j;
-            sk[j] = i < S ? skey(src[(int)(((int64_t)i * len) / S)]) : 0u;
+            const int c = (int)(((int64_t)(i >> 5) * len) / runs) + (i & 31);
+            sk[j] = i < S ? skey(src[min(c, len - 1)]) : 0u;
         }
 #pragma unroll
         for (int j = 0; j < kSPer; j++)
