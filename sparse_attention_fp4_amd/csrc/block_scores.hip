@@ -6,11 +6,13 @@
 // causal offset k_len - q_len unless qo_offset is given; keys past k_len never count;
 // an empty block is -inf.)
 //
-// Work split: one wave owns 16 consecutive query tokens (a query tile) and up to NB
-// query heads of one key-head group, walks the key tiles the tile can see in 16-key
-// steps and writes every score block of its (heads, tokens), including the -inf
-// blocks it never reaches.  Query tiles that straddle two batch items are handled one
-// item at a time.
+// Work split: one wave owns 16 consecutive query tokens (a query tile), up to NB query
+// heads of one key-head group and a chunk of kb_chunk consecutive 128-key blocks; it
+// walks the key tiles of its chunk that the tile can see in 16-key steps and writes
+// every score block of its chunk for its (heads, tokens), including the -inf blocks it
+// never reaches.  Cutting the key range keeps the waves' work even under the causal
+// mask (late query tiles see many more keys) and the grid many times the chip's size.
+// Query tiles that straddle two batch items are handled one item at a time.
 //
 // MFMA mapping: A = 16 keys x 128, B = 128 x 16 query tokens of one head, so output
 // lane (g, n) holds keys 4g..4g+3 of the tile for token n.  The block max is a running
@@ -33,6 +35,9 @@ namespace fp4idx {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
+#ifndef FP4IDX_BLOCK_CHUNK
+#define FP4IDX_BLOCK_CHUNK 16  // 128-key blocks per wave
+#endif
 
 template <int FMT>
 struct QOperand;
@@ -58,14 +63,20 @@ __global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
     const int g = lane >> 4, n = lane & 15;
     const int n_qtiles = (p.Tq + 15) / 16;
     const int n_hgrp = (p.R + NB - 1) / NB;
-    // block index -> (kv head, head group, 4 consecutive query tiles)
+    // block index -> (kv head, key chunk, head group, 4 consecutive query tiles); the
+    // query tiles of one key chunk are neighbours, so their key reads meet in L2
     const int qt_blocks = (n_qtiles + kWavesPerBlock - 1) / kWavesPerBlock;
     const int bx = blockIdx.x;
-    const int hk = bx / (n_hgrp * qt_blocks);
-    const int rem = bx - hk * n_hgrp * qt_blocks;
+    const int per_hk = p.n_kchunks * n_hgrp * qt_blocks;
+    const int hk = bx / per_hk;
+    int rem = bx - hk * per_hk;
+    const int kc = rem / (n_hgrp * qt_blocks);
+    rem -= kc * n_hgrp * qt_blocks;
     const int hgrp = rem / qt_blocks;
     const int qt = (rem - hgrp * qt_blocks) * kWavesPerBlock + (threadIdx.x >> 6);
     if (hk >= p.Hkv || qt >= n_qtiles) return;  // uniform per wave
+    const int kb_lo = kc * p.kb_chunk;                       // this wave's blocks
+    const int kb_hi = min(kb_lo + p.kb_chunk, p.ktiles);
     const int h0 = hk * p.R + hgrp * NB;         // first query head of this wave
     const int nh = min(NB, p.R - hgrp * NB);
     const int q_first = qt * 16;
@@ -132,7 +143,9 @@ __global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
         }
 
         const int n_kt = (kv_max + 15) / 16;      // key tiles with any visible key
-        const int kb_done = (n_kt + 7) / 8;        // blocks this wave computes
+        const int kb_done = (n_kt + 7) / 8;        // blocks with a visible key
+        const int kt_lo = min(kb_lo * 8, n_kt);    // this wave's key tiles
+        const int kt_hi = min(kb_hi * 8, n_kt);
         float run[NB];
 #pragma unroll
         for (int hb = 0; hb < NB; hb++) run[hb] = -__builtin_inff();
@@ -140,9 +153,9 @@ __global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
         // Block-table entries of 64 blocks at a time: lane i holds the page of block
         // win + i (-1 when invalid).  Key tiles are fetched two ahead of the one being
         // computed, through buffer descriptors that read zeros for invalid pages.
-        int win = -64, my_phys = -1;
+        int win = -64 - 64, my_phys = -1;
         auto window = [&](int kb) {
-            if (kb - win >= 64) {
+            if (kb - win >= 64 || kb < win) {
                 win = kb & ~63;
                 const int i = win + lane;
                 int v = -1;
@@ -157,7 +170,7 @@ __global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
             int phys;
         };
         auto fetch = [&](int kt, KTile& t) {
-            t.phys = kt < n_kt ? window(kt >> 3) : -1;
+            t.phys = kt < kt_hi ? window(kt >> 3) : -1;
             const bool ok = t.phys >= 0;
             const int64_t tok0 = ((int64_t)(ok ? t.phys : 0) * p.Hkv + hk) * 128 + (kt & 7) * 16;
             const __amdgpu_buffer_rsrc_t rk = make_rsrc(ok ? p.k + tok0 * 64 : p.k, ok ? 16u * 64u : 0u);
@@ -221,20 +234,20 @@ __global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
             }
         };
         KTile t0, t1, t2;
-        fetch(0, t0);
-        fetch(1, t1);
-        for (int kt = 0; kt < n_kt; kt += 3) {
+        fetch(kt_lo, t0);
+        fetch(kt_lo + 1, t1);
+        for (int kt = kt_lo; kt < kt_hi; kt += 3) {
             fetch(kt + 2, t2);
             process(kt, t0);
-            if (kt + 1 >= n_kt) break;
+            if (kt + 1 >= kt_hi) break;
             fetch(kt + 3, t0);
             process(kt + 1, t1);
-            if (kt + 2 >= n_kt) break;
+            if (kt + 2 >= kt_hi) break;
             fetch(kt + 4, t1);
             process(kt + 2, t2);
         }
-        // blocks never reached: -inf
-        for (int kb = kb_done; kb < p.ktiles; kb++) {
+        // blocks of the chunk never reached: -inf
+        for (int kb = max(kb_done, kb_lo); kb < kb_hi; kb++) {
             if (g == 0 && col_ok) {
 #pragma unroll
                 for (int hb = 0; hb < NB; hb++)
@@ -250,7 +263,7 @@ hipError_t launch_fmt_nb(const BlockParams& p, hipStream_t stream) {
     const int n_qtiles = (p.Tq + 15) / 16;
     const int n_hgrp = (p.R + NB - 1) / NB;
     const int qt_blocks = (n_qtiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t blocks = (int64_t)p.Hkv * n_hgrp * qt_blocks;
+    const int64_t blocks = (int64_t)p.Hkv * p.n_kchunks * n_hgrp * qt_blocks;
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL((k_block_scores<FMT, NB>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
@@ -258,7 +271,11 @@ hipError_t launch_fmt_nb(const BlockParams& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_block_scores(const BlockParams& p, hipStream_t stream) {
+hipError_t launch_block_scores(const BlockParams& p_in, hipStream_t stream) {
+    BlockParams p = p_in;
+    p.kb_chunk = FP4IDX_BLOCK_CHUNK;
+    p.n_kchunks = (p.ktiles + p.kb_chunk - 1) / p.kb_chunk;
+    if (p.n_kchunks == 0) p.n_kchunks = 1;  // no blocks: the grid still runs its (empty) chunk
     if (p.fmt == 0) {
         if (p.R <= 4) return launch_fmt_nb<0, 4>(p, stream);
         if (p.R <= 8) return launch_fmt_nb<0, 8>(p, stream);

@@ -53,6 +53,8 @@ struct BlockParams {
     int fmt, G, R;
     int ktiles;
     int q_tiles;         // query tiles of 16 tokens in the grid's y dimension
+    int kb_chunk;        // 128-key blocks per wave (the key range is cut in chunks)
+    int n_kchunks;       // chunks of kb_chunk blocks over Ktiles
 };
 
 struct TopkParams {
