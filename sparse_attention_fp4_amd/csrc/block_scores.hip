@@ -53,8 +53,14 @@ struct QOperand<1> {
     v8h v[4];
 };
 
-__device__ __forceinline__ float max4(float a, float b, float c, float d) {
-    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+// max of three floats in one instruction.  The hardware max skips a NaN operand (the
+// block max's reading of fmax); written out because the compiler would first quiet
+// every matrix-core result (a no-op here: those are never signalling NaNs), which costs
+// as much as the max itself.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
 }
 
 template <int FMT, int NB>
@@ -210,14 +216,18 @@ __global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
 #pragma unroll
                         for (int hb = 0; hb < NB; hb++) d[hb] = mfma_f16_16x16x32(kd[c], qop[hb].v[c], d[hb]);
                 }
+                if (__builtin_expect(full, 1)) {
 #pragma unroll
-                for (int hb = 0; hb < NB; hb++) {
-                    v4f e = d[hb];
-                    if (!full) {
+                    for (int hb = 0; hb < NB; hb++)
+                        run[hb] = max3_raw(max3_raw(run[hb], d[hb][0], d[hb][1]), d[hb][2], d[hb][3]);
+                } else {
+#pragma unroll
+                    for (int hb = 0; hb < NB; hb++) {
+                        v4f e = d[hb];
 #pragma unroll
                         for (int i = 0; i < 4; i++) e[i] = kbase + i < kv_lim ? e[i] : -__builtin_inff();
+                        run[hb] = max3_raw(max3_raw(run[hb], e[0], e[1]), e[2], e[3]);
                     }
-                    run[hb] = fmaxf(fmaxf(run[hb], fmaxf(e[0], e[1])), fmaxf(e[2], e[3]));
                 }
             }
             // block boundary: reduce over the four lane groups and store
