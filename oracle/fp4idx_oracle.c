@@ -17,7 +17,9 @@
  *          semantics) and the causal paragraph that follows it.
  *   [ISS]  "ISSUE -- Lightning Indexer FP4 dequant decodes E2M1 wrong", sections
  *          "Why it's wrong" and "Fix (interim, correct FP32 base)".
- *   [QSA]  vLLM qsa_fp8 API page, _qsa_physical_slots_kernel (invalid pages -> masked).
+ *   [QSA]  vLLM qsa_fp8 API page: _qsa_physical_slots_kernel (invalid pages -> masked),
+ *          _decode_slot_layout, _qsa_sparse_paged_decode_kernel and
+ *          qsa_sparse_paged_decode (sparse attention over the selected tokens).
  *
  * Precision: every real value is a double.  A per-head dot product of dequantized FP4
  * values is a sum of 128 dyadic terms; orc_dot() adds them in double and reports
@@ -449,4 +451,156 @@ int orc_max_threads(int n_threads) {
     (void)n_threads;
     return 1;
 #endif
+}
+
+/* ---------------------------------------------------------------------------------
+ * Sparse paged attention over the selected tokens ([QSA] vLLM qsa_fp8 API page):
+ * the consumer of a top-k token selection.  Two steps: the slot pass turns each
+ * row's logical token indices into physical cache slots; the decode step attends
+ * from every query head over the selected tokens of its KV head.
+ * ------------------------------------------------------------------------------- */
+
+/* Bits that hold a token's place inside its page in a slot: the bit length of
+ * page_size - 1, and at least 1 ([QSA] _decode_slot_layout).  Pinned by closed forms
+ * in the tests. */
+int orc_qsa_offset_bits(int page_size) {
+    int b = 0;
+    while (b < 31 && ((int64_t)1 << b) < (int64_t)page_size) b++;
+    return b < 1 ? 1 : b;
+}
+
+/* Slot pass ([QSA] _qsa_physical_slots_kernel and qsa_sparse_paged_decode).
+ *
+ * Row r belongs to request b = token_to_req[r].  For column c < topk, the logical
+ * token x = indices[r][c] sits at place x % page_size of logical page x / page_size,
+ * whose physical page p is block_table[b][x / page_size].  The slot is
+ * (p << offset_bits) | (x % page_size) when 0 <= b < num_requests, x >= 0,
+ * x / page_size < table_width and 0 <= p < num_cache_blocks; otherwise it is -1.
+ * Columns topk .. slot_cols-1 are -1 (padding).  The valid count stored in column
+ * topk of indices is not read here (the decode step reads it).
+ * Layouts: indices [rows][>= topk] int32 (row stride ind_rs), block_table
+ * [num_requests][table_width] int32 (row stride bt_rs), slots [rows][slot_cols] int32
+ * (row stride slots_rs).  Parity pinned by a hand-worked table in the tests. */
+void orc_qsa_slots(const int32_t* indices, int64_t ind_rs, int rows, int topk,
+                   const int32_t* block_table, int64_t bt_rs, int num_requests,
+                   int table_width, const int32_t* token_to_req, int num_cache_blocks,
+                   int page_size, int32_t* slots, int64_t slots_rs, int slot_cols) {
+    int ob = orc_qsa_offset_bits(page_size);
+    for (int r = 0; r < rows; r++) {
+        int b = token_to_req[r];
+        for (int c = 0; c < slot_cols; c++) {
+            int32_t slot = -1;
+            if (c < topk && b >= 0 && b < num_requests) {
+                int32_t x = indices[(int64_t)r * ind_rs + c];
+                if (x >= 0 && x / page_size < table_width) {
+                    int32_t p = block_table[(int64_t)b * bt_rs + x / page_size];
+                    if (p >= 0 && p < num_cache_blocks)
+                        slot = (int32_t)(((uint32_t)p << ob) | (uint32_t)(x % page_size));
+                }
+            }
+            slots[(int64_t)r * slots_rs + c] = slot;
+        }
+    }
+}
+
+/* bf16 bit pattern -> value (the 16 bits are the top half of an IEEE binary32). */
+static double bf16_value(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Decode step ([QSA] _qsa_sparse_paged_decode_kernel, qsa_sparse_paged_decode):
+ * grouped-query attention of each row over its selected tokens.
+ *
+ * Row r selects the columns c < min(count, topk), count = indices[r][topk], whose slot
+ * is not negative (reading: a column at or past the valid count is not selected even
+ * when its slot is valid; a negative count selects nothing).  Selected token j lives at
+ * place slot & (2^offset_bits - 1) of cache page slot >> offset_bits.  Query head h
+ * uses KV head g = h / (Hq / Hkv).  With K_j, V_j the e4m3fn codes of token j, head g
+ * decoded exactly (orc_e4m3) and q, gate the bf16 values:
+ *
+ *   s_j      = softmax_scale * sum_d q[r][h][d] * K_j[d]
+ *   a_j      = exp(s_j - max_i s_i) / sum_i exp(s_i - max_i s_i)
+ *   out[r][h][d] = output_scale * (sum_j a_j V_j[d]) * sigmoid(gate[r][h][d])
+ *
+ * and out = 0 when nothing is selected ([QSA] epilogue: rows with no probability mass
+ * output zero).  A token selected twice counts twice.  Everything is computed in double
+ * from exact decodes; the page's own kernel rounds the probabilities to fp16 and the
+ * output to bf16, which the tests allow for in their tolerance.
+ * Layouts: q and gate [rows][Hq][D] bf16 bits with row / head strides in elements;
+ * K and V cache token (page p, place t, head g) at byte p*block_stride +
+ * t*token_stride + g*head_stride (separate head strides for K and V); out [rows][Hq][D]
+ * double, contiguous.  tolbase (optional, same layout as out): output_scale *
+ * sum_j a_j |V_j[d]| * sigmoid(gate), the size of the terms the output sums.
+ * Parity pinned in the tests by closed forms (one token, equal keys, a two-token
+ * case with weights 3/4 and 1/4), invariants (order, masking, duplicates) and by
+ * torch's scaled_dot_product_attention in double on the gathered tokens. */
+void orc_qsa_decode(const uint16_t* q, int64_t q_rs, int64_t q_hs,
+                    const uint8_t* k_cache, const uint8_t* v_cache, int64_t block_stride,
+                    int64_t token_stride, int64_t k_head_stride, int64_t v_head_stride,
+                    const int32_t* slots, int64_t slots_rs,
+                    const int32_t* indices, int64_t ind_rs, int topk,
+                    int rows, int Hq, int Hkv, int D, int offset_bits,
+                    double softmax_scale, double output_scale,
+                    const uint16_t* gate, int64_t gate_rs, int64_t gate_hs,
+                    double* out, double* tolbase, int n_threads) {
+    int G = Hq / Hkv;
+    int32_t mask = (int32_t)((1u << offset_bits) - 1u);
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < rows; r++) {
+        int n = indices[(int64_t)r * ind_rs + topk];
+        if (n > topk) n = topk;
+        if (n < 0) n = 0;
+        double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        int* sel = (int*)malloc(sizeof(int) * (size_t)(n > 0 ? n : 1));
+        int m = 0;
+        for (int c = 0; c < n; c++)
+            if (slots[(int64_t)r * slots_rs + c] >= 0) sel[m++] = c;
+        for (int h = 0; h < Hq; h++) {
+            int g = h / G;
+            const uint16_t* qh = q + (int64_t)r * q_rs + (int64_t)h * q_hs;
+            double smax = -INFINITY;
+            for (int j = 0; j < m; j++) {
+                int32_t slot = slots[(int64_t)r * slots_rs + sel[j]];
+                const uint8_t* kr = k_cache + (int64_t)(slot >> offset_bits) * block_stride +
+                                    (int64_t)(slot & mask) * token_stride +
+                                    (int64_t)g * k_head_stride;
+                double acc = 0.0;
+                for (int d = 0; d < D; d++) acc += bf16_value(qh[d]) * orc_e4m3(kr[d]);
+                s[j] = softmax_scale * acc;
+                if (s[j] > smax) smax = s[j];
+            }
+            double z = 0.0;
+            for (int j = 0; j < m; j++) {
+                s[j] = exp(s[j] - smax);
+                z += s[j];
+            }
+            for (int d = 0; d < D; d++) {
+                double o = 0.0, a = 0.0;
+                for (int j = 0; j < m; j++) {
+                    int32_t slot = slots[(int64_t)r * slots_rs + sel[j]];
+                    const uint8_t* vr = v_cache + (int64_t)(slot >> offset_bits) * block_stride +
+                                        (int64_t)(slot & mask) * token_stride +
+                                        (int64_t)g * v_head_stride;
+                    double v = orc_e4m3(vr[d]);
+                    o += s[j] * v;
+                    a += s[j] * fabs(v);
+                }
+                double gv = bf16_value(gate[(int64_t)r * gate_rs + (int64_t)h * gate_hs + d]);
+                double sig = 1.0 / (1.0 + exp(-gv));
+                int64_t at = ((int64_t)r * Hq + h) * D + d;
+                out[at] = m > 0 ? output_scale * (o / z) * sig : 0.0;
+                if (tolbase) tolbase[at] = m > 0 ? fabs(output_scale) * (a / z) * sig : 0.0;
+            }
+        }
+        free(sel);
+        free(s);
+    }
 }

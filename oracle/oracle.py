@@ -60,6 +60,15 @@ def lib():
         L.orc_quantize_mx_block.argtypes = [P, P, P]
         L.orc_quantize_store.restype = None
         L.orc_quantize_store.argtypes = [P, P, i32, P, i64, P, i64, i32, i32]
+        L.orc_qsa_offset_bits.restype = i32
+        L.orc_qsa_offset_bits.argtypes = [i32]
+        L.orc_qsa_slots.restype = None
+        L.orc_qsa_slots.argtypes = [P, i64, i32, i32, P, i64, i32, i32, P, i32, i32, P, i64,
+                                    i32]
+        L.orc_qsa_decode.restype = None
+        L.orc_qsa_decode.argtypes = [P, i64, i64, P, P, i64, i64, i64, i64, P, i64, P, i64,
+                                     i32, i32, i32, i32, i32, i32, ctypes.c_double,
+                                     ctypes.c_double, P, i64, i64, P, P, i32]
         _lib = L
     return _lib
 
@@ -250,3 +259,61 @@ def quantize_store(keys, slots, k_fp4, k_scale):
     lib().orc_quantize_store(_p(keys), _p(slots), keys.shape[0], _p(kf), page * 64, _p(ks),
                              page * 4, page, P)
     return kf, ks
+
+
+def qsa_offset_bits(page_size: int) -> int:
+    """Bits of a slot that hold the place inside a page ([QSA] _decode_slot_layout)."""
+    return int(lib().orc_qsa_offset_bits(page_size))
+
+
+def qsa_slots(indices, block_table, token_to_req, num_cache_blocks, page_size, slot_cols=None):
+    """[QSA] slot pass.  indices [rows, topk + 1] int32 (the last column is the valid
+    count, not read here), block_table [num_requests, width] int32, token_to_req [rows]
+    int32 -> slots [rows, slot_cols] int32 (slot_cols defaults to topk)."""
+    ind = _c(indices, np.int32)
+    bt = _c(block_table, np.int32)
+    t2r = _c(token_to_req, np.int32)
+    rows, topk = ind.shape[0], ind.shape[1] - 1
+    slot_cols = topk if slot_cols is None else slot_cols
+    out = np.empty((rows, slot_cols), np.int32)
+    lib().orc_qsa_slots(_p(ind), ind.shape[1], rows, topk, _p(bt), bt.shape[1], bt.shape[0],
+                        bt.shape[1], _p(t2r), num_cache_blocks, page_size, _p(out), slot_cols,
+                        slot_cols)
+    return out
+
+
+def qsa_decode(q_bits, k_cache, v_cache, slots, indices, offset_bits, softmax_scale,
+               output_scale, gate_bits, rows=None, n_threads=0, want_tolbase=False):
+    """[QSA] sparse decode step in double.
+
+    q_bits, gate_bits: [R, Hq, D] uint16 bf16 bit patterns.  k_cache, v_cache:
+    [num_blocks, page, Hkv, D] uint8 e4m3fn codes (any byte strides; numpy views of one
+    combined cache are fine).  slots [R, >= topk] int32, indices [R, topk + 1] int32.
+    rows: optional subset of row ids (the result then holds just those rows, in the
+    given order).  -> (out [n, Hq, D] float64, tolbase or None)."""
+    q = np.asarray(q_bits)
+    g = np.asarray(gate_bits)
+    sl = np.asarray(slots)
+    ind = np.asarray(indices)
+    if rows is not None:
+        rows = np.asarray(rows, np.int64)
+        q, g, sl, ind = q[rows], g[rows], sl[rows], ind[rows]
+    q = _c(q, np.uint16)
+    g = _c(g, np.uint16)
+    sl = _c(sl, np.int32)
+    ind = _c(ind, np.int32)
+    kc = np.asarray(k_cache)
+    vc = np.asarray(v_cache)
+    assert kc.dtype == np.uint8 and vc.dtype == np.uint8
+    assert kc.strides[3] == 1 and vc.strides[3] == 1 and kc.strides[:2] == vc.strides[:2]
+    n, Hq, D = q.shape
+    Hkv = kc.shape[2]
+    topk = ind.shape[1] - 1
+    out = np.zeros((n, Hq, D), np.float64)
+    tb = np.zeros((n, Hq, D), np.float64) if want_tolbase else None
+    lib().orc_qsa_decode(_p(q), Hq * D, D, kc.ctypes.data, vc.ctypes.data, kc.strides[0],
+                         kc.strides[1], kc.strides[2], vc.strides[2], _p(sl), sl.shape[1],
+                         _p(ind), ind.shape[1], topk, n, Hq, Hkv, D, offset_bits,
+                         float(softmax_scale), float(output_scale), _p(g), Hq * D, D,
+                         _p(out), _p(tb), n_threads)
+    return out, tb

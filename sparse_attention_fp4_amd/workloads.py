@@ -261,3 +261,143 @@ def config3(seed=1030):
     k_lens = q_lens + rng.integers(0, 8192 + 1, size=8)
     return make_block("nvfp4_block_prefill_b8", fmt=NVFP4, q_lens=q_lens, k_lens=k_lens, Hq=32,
                       Hkv=4, seed=seed, causal=True)
+
+
+# ---------------------------------------------------------------------------------------
+# Sparse paged attention over the selected tokens (vLLM qsa_fp8 API page): an fp8 e4m3fn
+# K/V cache, bf16 queries and output gates, and per-row lists of selected logical tokens.
+# ---------------------------------------------------------------------------------------
+
+@dataclass
+class QsaCase:
+    """Inputs of one sparse decode over selected tokens (host arrays)."""
+    name: str
+    kv: np.ndarray             # [blocks, Hkv, page, 2D] uint8: per token and head, D K codes
+                               # then D V codes (one combined cache)
+    block_table: np.ndarray    # [R, W] int32, -1 padded
+    token_to_req: np.ndarray   # [rows] int32
+    indices: np.ndarray        # [rows, topk + 1] int32: selected logical tokens, -1 padded,
+                               # the valid count in the last column
+    q: np.ndarray              # [rows, Hq, D] uint16 bf16 bit patterns
+    gate: np.ndarray           # [rows, Hq, D] uint16 bf16 bit patterns
+    page_size: int
+    softmax_scale: float
+    output_scale: float
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def rows(self):
+        return self.q.shape[0]
+
+    @property
+    def Hq(self):
+        return self.q.shape[1]
+
+    @property
+    def D(self):
+        return self.q.shape[2]
+
+    @property
+    def Hkv(self):
+        return self.kv.shape[1]
+
+    @property
+    def topk(self):
+        return self.indices.shape[1] - 1
+
+    @property
+    def num_cache_blocks(self):
+        return self.kv.shape[0]
+
+    @property
+    def k_cache(self):
+        """[blocks, page, Hkv, D] view of the K codes."""
+        return self.kv.transpose(0, 2, 1, 3)[..., :self.D]
+
+    @property
+    def v_cache(self):
+        return self.kv.transpose(0, 2, 1, 3)[..., self.D:]
+
+    def selected(self) -> int:
+        """Selected (row, token) pairs with a valid entry before the count."""
+        n = 0
+        for r in range(self.rows):
+            c = int(np.clip(self.indices[r, -1], 0, self.topk))
+            n += int((self.indices[r, :c] >= 0).sum())
+        return n
+
+
+def e4m3_codes(rng, shape, exp_lo=4, exp_hi=7):
+    """Uniform e4m3fn codes (sign << 7 | exponent field << 3 | mantissa) with exponent
+    field in [exp_lo, exp_hi] (values 2^(e-7) * (1 + m/8); field 0 gives the subnormals
+    m/8 * 2^-6), sign uniform, the NaN codes 0x7F / 0xFF never drawn."""
+    size = int(np.prod(shape))
+    if (exp_lo, exp_hi) == (4, 7):
+        # fields 4..7 are 0b01xx: a random byte with bit 6 cleared and bit 5 set is a
+        # uniform draw over these 64 codes
+        words = rng.integers(0, 2**64 - 1, size=-(-size // 8), dtype=np.uint64, endpoint=True)
+        raw = words.view(np.uint8)[:size]
+        np.bitwise_and(raw, 0x9F, out=raw)
+        np.bitwise_or(raw, 0x20, out=raw)
+        return raw.reshape(shape)
+    allowed = np.array([(s << 7) | (e << 3) | m for s in (0, 1)
+                        for e in range(exp_lo, exp_hi + 1) for m in range(8)
+                        if not (e == 15 and m == 7)], np.uint8)
+    return allowed[rng.integers(0, allowed.size, size=size)].reshape(shape)
+
+
+def bf16_bits(rng, shape, exp_lo=-3, exp_hi=1):
+    """bf16 bit patterns 2^e * (1 + m/128), e uniform in [exp_lo, exp_hi], m uniform in
+    [0, 127], sign uniform."""
+    s = rng.integers(0, 2, size=shape, dtype=np.uint16)
+    e = rng.integers(127 + exp_lo, 127 + exp_hi + 1, size=shape).astype(np.uint16)
+    m = rng.integers(0, 128, size=shape, dtype=np.uint16)
+    return (s << 15) | (e << 7) | m
+
+
+def make_qsa(name, *, ctx, rows_per_req=1, Hq, Hkv, D=128, page=64, topk=2048, seed,
+             k_exp=(4, 7), q_exp=(-3, 1), gate_exp=(-3, 2), softmax_scale=None,
+             output_scale=1.0, extra_pages=0, drop_frac=0.0) -> QsaCase:
+    """Requests with contexts `ctx` on pages of a shuffled pool; each request's rows select
+    min(topk, ctx) distinct tokens in increasing order (the indexer's top-k output
+    order), -1 padded, count in the last column.  drop_frac of the selected entries
+    before the count are replaced by -1 (masked entries)."""
+    rng = np.random.default_rng(seed)
+    ctx = [int(c) for c in ctx]
+    R = len(ctx)
+    npg = [-(-c // page) for c in ctx]
+    P = sum(npg) + extra_pages
+    W = max(npg) if npg else 1
+    kv = e4m3_codes(rng, (P, Hkv, page, 2 * D), *k_exp)
+    perm = rng.permutation(P).astype(np.int32)
+    table = np.full((R, W), -1, np.int32)
+    at = 0
+    for b in range(R):
+        table[b, :npg[b]] = perm[at:at + npg[b]]
+        at += npg[b]
+    rows = R * rows_per_req
+    t2r = np.repeat(np.arange(R, dtype=np.int32), rows_per_req)
+    ind = np.full((rows, topk + 1), -1, np.int32)
+    for r in range(rows):
+        c = ctx[t2r[r]]
+        n = min(topk, c)
+        sel = np.sort(rng.choice(c, size=n, replace=False)).astype(np.int32)
+        if drop_frac > 0 and n:
+            sel[rng.random(n) < drop_frac] = -1
+        ind[r, :n] = sel
+        ind[r, topk] = n
+    q = bf16_bits(rng, (rows, Hq, D), *q_exp)
+    gate = bf16_bits(rng, (rows, Hq, D), *gate_exp)
+    scale = float(D) ** -0.5 if softmax_scale is None else float(softmax_scale)
+    return QsaCase(name, kv, table, t2r, ind, q, gate, page, scale, float(output_scale),
+                   {"seed": seed, "ctx": ctx})
+
+
+def qsa_decode_case(seed=1050, requests=128):
+    """Large-batch sparse decode: 128 requests x 1 row, contexts U[8192, 32768], Hq=32,
+    Hkv=4, D=128, 64-token pages, top-2048 selected tokens per row, softmax scale
+    1/sqrt(128)."""
+    rng = np.random.default_rng(seed + 5)
+    ctx = rng.integers(8192, 32768 + 1, size=requests)
+    return make_qsa("qsa_fp8_decode_b128", ctx=ctx, Hq=32, Hkv=4, D=128, page=64, topk=2048,
+                    seed=seed)

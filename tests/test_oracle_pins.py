@@ -557,3 +557,224 @@ def test_block_topk_brute_force():
             want = sorted(best) + [-1] * (k - len(best))
             assert idx[h, q].tolist() == want
             assert cnt[h, q] == len(best)
+
+
+# ---------------------------------------------------------------------------------------
+# Sparse paged attention over the selected tokens (vLLM qsa_fp8 API page).
+# ---------------------------------------------------------------------------------------
+
+def test_qsa_offset_bits_is_the_least_width_that_holds_every_place():
+    for page in range(1, 1025):
+        b = orc.qsa_offset_bits(page)
+        assert b >= 1 and (1 << b) >= page          # every place 0..page-1 fits in b bits
+        assert b == 1 or (1 << (b - 1)) < page      # and b - 1 bits would not do
+
+
+def _golden_slots():
+    meta, table, rows = {}, [], []
+    with open(os.path.join(GOLDEN, "qsa_slots.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, rest = line.split(None, 1)
+            if key == "table":
+                table.append([int(x) for x in rest.split()])
+            elif key == "row":
+                req, toks, want = rest.split("|")
+                rows.append((int(req), [int(x) for x in toks.split()],
+                             [int(x) for x in want.split()]))
+            else:
+                meta[key] = int(rest)
+    return meta, np.array(table, np.int32), rows
+
+
+def test_qsa_slots_match_hand_worked_fixture():
+    meta, table, rows = _golden_slots()
+    ind = np.array([r[1] for r in rows], np.int32)
+    t2r = np.array([r[0] for r in rows], np.int32)
+    assert ind.shape[1] == meta["topk"] + 1
+    got = orc.qsa_slots(ind, table, t2r, meta["num_cache_blocks"], meta["page"],
+                        meta["slot_cols"])
+    np.testing.assert_array_equal(got, np.array([r[2] for r in rows], np.int32))
+
+
+def _bf16_bits(x):
+    return torch.as_tensor(x, dtype=torch.float64).to(torch.bfloat16).view(torch.int16) \
+        .numpy().view(np.uint16)
+
+
+def _bf16_values(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16) \
+        .to(torch.float64).numpy()
+
+
+def _e4m3_values(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn) \
+        .to(torch.float64).numpy()
+
+
+def _qsa_case(rng, rows=3, Hq=8, Hkv=2, D=16, page=8, blocks=12, topk=10, combined=True):
+    """Random small case: per-request block tables over a shuffled page pool, finite
+    e4m3fn K/V codes (0x7F/0xFF excluded), bf16 q and gate."""
+    codes = rng.integers(0, 256, size=(blocks, Hkv, page, 2 * D), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38                       # no NaN codes
+    if combined:   # one cache [blocks, Hkv, page, 2D] seen as [blocks, page, Hkv, D] twice
+        kv = codes.transpose(0, 2, 1, 3)
+        k, v = kv[..., :D], kv[..., D:]
+    else:          # separate caches; V's heads stored in reverse order (head stride -D)
+        k = np.ascontiguousarray(codes[..., :D].transpose(0, 2, 1, 3))
+        vbuf = np.ascontiguousarray(codes[..., D:].transpose(0, 2, 1, 3)[:, :, ::-1])
+        v = vbuf[:, :, ::-1]
+    width = blocks // rows
+    perm = rng.permutation(blocks).astype(np.int32)
+    table = perm[: rows * width].reshape(rows, width)
+    ctx = width * page
+    ind = np.full((rows, topk + 1), -1, np.int32)
+    for r in range(rows):
+        sel = np.sort(rng.choice(ctx, size=topk - 2, replace=False))
+        ind[r, : topk - 2] = sel
+        ind[r, topk] = topk - 2
+    q = _bf16_bits(rng.standard_normal((rows, Hq, D)))
+    gate = _bf16_bits(rng.standard_normal((rows, Hq, D)) * 2)
+    t2r = np.arange(rows, dtype=np.int32)
+    return dict(k=k, v=v, table=table, ind=ind, q=q, gate=gate, t2r=t2r, page=page,
+                blocks=blocks, D=D, Hq=Hq, Hkv=Hkv)
+
+
+def _run(c, softmax_scale=0.3, output_scale=1.0, slots=None, ind=None):
+    ind = c["ind"] if ind is None else ind
+    if slots is None:
+        slots = orc.qsa_slots(ind, c["table"], c["t2r"], c["blocks"], c["page"])
+    out, tb = orc.qsa_decode(c["q"], c["k"], c["v"], slots, ind,
+                             orc.qsa_offset_bits(c["page"]), softmax_scale, output_scale,
+                             c["gate"], want_tolbase=True)
+    return out, tb
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def test_qsa_single_selected_token_outputs_its_value_row_gated():
+    """One selected token takes all the probability: out = output_scale * V * sigmoid(gate)
+    (V decoded by torch's float8_e4m3fn, not by the oracle's decoder)."""
+    rng = np.random.default_rng(11)
+    c = _qsa_case(rng)
+    ind = c["ind"].copy()
+    ind[:, 1:] = -1
+    ind[:, -1] = 1
+    out, _ = _run(c, output_scale=0.75, ind=ind)
+    G = c["Hq"] // c["Hkv"]
+    for r in range(ind.shape[0]):
+        x = ind[r, 0]
+        pg, place = c["table"][r, x // c["page"]], x % c["page"]
+        for h in range(c["Hq"]):
+            vrow = _e4m3_values(c["v"][pg, place, h // G])
+            want = 0.75 * vrow * _sigmoid(_bf16_values(c["gate"][r, h]))
+            np.testing.assert_allclose(out[r, h], want, rtol=1e-14, atol=0)
+
+
+def test_qsa_equal_keys_average_the_values():
+    """Every selected token of a row holds the same key: the weights are all 1/n and the
+    output is the mean of the value rows."""
+    rng = np.random.default_rng(12)
+    c = _qsa_case(rng, combined=False)
+    k = np.array(c["k"])          # writable copy, same strides as the separate V cache
+    k[...] = k[0, 0, :, :][None, None]
+    c["k"] = k
+    out, _ = _run(c, softmax_scale=1.7)
+    G = c["Hq"] // c["Hkv"]
+    for r in range(c["ind"].shape[0]):
+        n = c["ind"][r, -1]
+        toks = c["ind"][r, :n]
+        for h in range(c["Hq"]):
+            vals = np.stack([_e4m3_values(c["v"][c["table"][r, x // c["page"]], x % c["page"],
+                                                 h // G]) for x in toks])
+            want = vals.mean(axis=0) * _sigmoid(_bf16_values(c["gate"][r, h]))
+            np.testing.assert_allclose(out[r, h], want, rtol=1e-13, atol=1e-300)
+
+
+def test_qsa_two_tokens_with_score_gap_ln3_weigh_three_to_one():
+    """q = e_0, K_a[0] = 1, K_b[0] = 0 and softmax_scale = ln 3: scores ln 3 and 0, so the
+    weights are 3/4 and 1/4; gate 0 halves the output."""
+    D, page = 16, 4
+    k = np.zeros((2, page, 1, D), np.uint8)
+    v = np.zeros((2, page, 1, D), np.uint8)
+    k[0, 1, 0, 0] = 0x38                                   # 1.0
+    v[0, 1, 0, :] = 0x40                                   # 2.0
+    v[1, 2, 0, :] = 0x48                                   # 4.0
+    table = np.array([[0, 1]], np.int32)
+    ind = np.array([[1, 6, 2]], np.int32)                  # token 1 (page 0), 6 (page 1)
+    q = np.zeros((1, 2, D), np.uint16)
+    q[0, :, 0] = _bf16_bits(np.array([1.0]))[0]
+    gate = np.zeros((1, 2, D), np.uint16)
+    slots = orc.qsa_slots(ind, table, np.zeros(1, np.int32), 2, page)
+    out, _ = orc.qsa_decode(q, k, v, slots, ind, orc.qsa_offset_bits(page), math.log(3.0),
+                            1.0, gate)
+    np.testing.assert_allclose(out, np.full((1, 2, D), 0.5 * (0.75 * 2.0 + 0.25 * 4.0)),
+                               rtol=1e-15)
+
+
+@pytest.mark.parametrize("combined", [True, False])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (6, 3), (4, 4), (8, 1)])
+def test_qsa_matches_torch_sdpa_on_tokens_gathered_from_logical_indices(Hq, Hkv, combined):
+    """Grouped-query attention of torch.nn.functional.scaled_dot_product_attention in
+    float64 on K/V rows gathered straight from the logical indices and the block table
+    (not through the slots), times output_scale and sigmoid(gate).  Duplicated and -1
+    entries, and entries past the valid count, are in the selection."""
+    rng = np.random.default_rng(100 + Hq * 7 + Hkv + (50 if combined else 0))
+    c = _qsa_case(rng, Hq=Hq, Hkv=Hkv, combined=combined)
+    ind = c["ind"].copy()
+    ind[:, 3] = ind[:, 1]                                   # a duplicate
+    ind[:, 4] = -1                                          # a masked entry
+    ind[:, -2] = ind[:, 0]                                  # past the count: ignored
+    out, _ = _run(c, softmax_scale=0.21, output_scale=1.3, ind=ind)
+    for r in range(ind.shape[0]):
+        n = ind[r, -1]
+        toks = [x for x in ind[r, :n] if x >= 0]
+        pages = c["table"][r, [x // c["page"] for x in toks]]
+        places = [x % c["page"] for x in toks]
+        kk = _e4m3_values(c["k"][pages, places])           # [n, Hkv, D]
+        vv = _e4m3_values(c["v"][pages, places])
+        qq = torch.from_numpy(_bf16_values(c["q"][r]))[:, None, :]          # [Hq, 1, D]
+        att = torch.nn.functional.scaled_dot_product_attention(
+            qq, torch.from_numpy(kk).transpose(0, 1), torch.from_numpy(vv).transpose(0, 1),
+            scale=0.21, enable_gqa=True)[:, 0, :].numpy()
+        want = 1.3 * att * _sigmoid(_bf16_values(c["gate"][r]))
+        np.testing.assert_allclose(out[r], want, rtol=1e-12, atol=1e-14)
+
+
+def test_qsa_selection_invariants():
+    """Reordering the selected columns changes nothing (up to double rounding); a row with
+    count 0, a negative count or only -1 entries outputs zeros; a count above topk is
+    clipped to topk."""
+    rng = np.random.default_rng(13)
+    c = _qsa_case(rng)
+    base, _ = _run(c)
+    ind = c["ind"].copy()
+    for r in range(ind.shape[0]):
+        n = ind[r, -1]
+        ind[r, :n] = ind[r, :n][rng.permutation(n)]
+    perm, _ = _run(c, ind=ind)
+    np.testing.assert_allclose(perm, base, rtol=1e-13, atol=1e-15)
+    ind = c["ind"].copy()
+    ind[0, -1] = 0
+    ind[1, -1] = -3
+    ind[2, :-1] = -1
+    z, _ = _run(c, ind=ind)
+    assert not z.any()
+    ind = c["ind"].copy()
+    big = ind.copy()
+    big[:, -1] = 1000                      # clipped to topk: the -1 padding is masked anyway
+    a, _ = _run(c, ind=big)
+    b, _ = _run(c, ind=ind)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_qsa_tolbase_bounds_the_output():
+    rng = np.random.default_rng(14)
+    c = _qsa_case(rng)
+    out, tb = _run(c, output_scale=-0.5)
+    assert np.all(np.abs(out) <= tb * (1 + 1e-12))
+    assert np.all(tb > 0)
