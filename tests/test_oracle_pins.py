@@ -642,7 +642,7 @@ def _qsa_case(rng, rows=3, Hq=8, Hkv=2, D=16, page=8, blocks=12, topk=10, combin
                 blocks=blocks, D=D, Hq=Hq, Hkv=Hkv)
 
 
-def _run(c, softmax_scale=0.3, output_scale=1.0, slots=None, ind=None):
+def _qsa_run(c, softmax_scale=0.3, output_scale=1.0, slots=None, ind=None):
     ind = c["ind"] if ind is None else ind
     if slots is None:
         slots = orc.qsa_slots(ind, c["table"], c["t2r"], c["blocks"], c["page"])
@@ -664,7 +664,7 @@ def test_qsa_single_selected_token_outputs_its_value_row_gated():
     ind = c["ind"].copy()
     ind[:, 1:] = -1
     ind[:, -1] = 1
-    out, _ = _run(c, output_scale=0.75, ind=ind)
+    out, _ = _qsa_run(c, output_scale=0.75, ind=ind)
     G = c["Hq"] // c["Hkv"]
     for r in range(ind.shape[0]):
         x = ind[r, 0]
@@ -683,7 +683,7 @@ def test_qsa_equal_keys_average_the_values():
     k = np.array(c["k"])          # writable copy, same strides as the separate V cache
     k[...] = k[0, 0, :, :][None, None]
     c["k"] = k
-    out, _ = _run(c, softmax_scale=1.7)
+    out, _ = _qsa_run(c, softmax_scale=1.7)
     G = c["Hq"] // c["Hkv"]
     for r in range(c["ind"].shape[0]):
         n = c["ind"][r, -1]
@@ -729,7 +729,7 @@ def test_qsa_matches_torch_sdpa_on_tokens_gathered_from_logical_indices(Hq, Hkv,
     ind[:, 3] = ind[:, 1]                                   # a duplicate
     ind[:, 4] = -1                                          # a masked entry
     ind[:, -2] = ind[:, 0]                                  # past the count: ignored
-    out, _ = _run(c, softmax_scale=0.21, output_scale=1.3, ind=ind)
+    out, _ = _qsa_run(c, softmax_scale=0.21, output_scale=1.3, ind=ind)
     for r in range(ind.shape[0]):
         n = ind[r, -1]
         toks = [x for x in ind[r, :n] if x >= 0]
@@ -751,30 +751,30 @@ def test_qsa_selection_invariants():
     clipped to topk."""
     rng = np.random.default_rng(13)
     c = _qsa_case(rng)
-    base, _ = _run(c)
+    base, _ = _qsa_run(c)
     ind = c["ind"].copy()
     for r in range(ind.shape[0]):
         n = ind[r, -1]
         ind[r, :n] = ind[r, :n][rng.permutation(n)]
-    perm, _ = _run(c, ind=ind)
+    perm, _ = _qsa_run(c, ind=ind)
     np.testing.assert_allclose(perm, base, rtol=1e-13, atol=1e-15)
     ind = c["ind"].copy()
     ind[0, -1] = 0
     ind[1, -1] = -3
     ind[2, :-1] = -1
-    z, _ = _run(c, ind=ind)
+    z, _ = _qsa_run(c, ind=ind)
     assert not z.any()
     ind = c["ind"].copy()
     big = ind.copy()
     big[:, -1] = 1000                      # clipped to topk: the -1 padding is masked anyway
-    a, _ = _run(c, ind=big)
-    b, _ = _run(c, ind=ind)
+    a, _ = _qsa_run(c, ind=big)
+    b, _ = _qsa_run(c, ind=ind)
     np.testing.assert_array_equal(a, b)
 
 
 def test_qsa_tolbase_bounds_the_output():
     rng = np.random.default_rng(14)
     c = _qsa_case(rng)
-    out, tb = _run(c, output_scale=-0.5)
+    out, tb = _qsa_run(c, output_scale=-0.5)
     assert np.all(np.abs(out) <= tb * (1 + 1e-12))
     assert np.all(tb > 0)
