@@ -14,7 +14,9 @@
  *         I[t,s]), "Fix (interim...)" (E2M1 level set, low nibble first), "Fix
  *         (production target)" (ReLU and head weights in the epilogue, wave-level top-k).
  *   [QSA] vLLM qsa_fp8 API page, _qsa_physical_slots_kernel: an entry that names no valid
- *         page is masked; -1 pads a selection.
+ *         page is masked; -1 pads a selection.  _decode_slot_layout,
+ *         _qsa_sparse_paged_decode_kernel and qsa_sparse_paged_decode: the slot pass and
+ *         the sparse attention over the selected tokens of an fp8 e4m3fn K/V cache.
  *
  * Conventions for every entry point
  *   - Every pointer is device memory owned by the caller, except where a parameter says
@@ -199,6 +201,64 @@ int fp4idx_quantize_store_k(const uint16_t* keys, int64_t key_row_stride,
                             uint8_t* k_fp4, int64_t k_page_stride,
                             uint8_t* k_scale, int64_t ks_page_stride,
                             int page_size, int num_pages, void* stream);
+
+/* Slot pass of the sparse attention over selected tokens [QSA _qsa_physical_slots_kernel,
+ * _decode_slot_layout]: row r of request b = token_to_req[r]; for column c < topk the
+ * logical token x = indices[r][c] sits at place x % page_size of logical page
+ * x / page_size, whose physical page is p = block_table[b][x / page_size];
+ *   slots[r][c] = (p << offset_bits) | (x % page_size),
+ * offset_bits = the bit length of page_size - 1, at least 1, when 0 <= b < num_requests,
+ * x >= 0, x / page_size < table_width and 0 <= p < num_cache_blocks; otherwise -1.
+ * Columns topk .. slot_cols-1 are -1.  The slots serve every KV head.
+ * Layouts: indices [rows][>= topk] int32 (row stride in elements; the valid count that
+ * fp4idx_qsa_decode reads sits at column topk), block_table [num_requests][table_width]
+ * int32 (row stride in elements), token_to_req [rows] int32, slots [rows][slot_cols]
+ * int32 (row stride in elements); all caller-owned device memory.
+ * Errors: EINVAL for rows < 0, topk < 1, slot_cols < topk, page_size < 1,
+ * num_requests < 1, table_width < 1, num_cache_blocks < 1, strides shorter than a row,
+ * a missing pointer, or (num_cache_blocks << offset_bits) >= 2^31 (a slot must fit in
+ * int32). */
+int fp4idx_qsa_slots(const int32_t* indices, int64_t indices_row_stride, int rows, int topk,
+                     const int32_t* block_table, int64_t block_table_row_stride,
+                     int num_requests, int table_width, const int32_t* token_to_req,
+                     int num_cache_blocks, int page_size,
+                     int32_t* slots, int64_t slots_row_stride, int slot_cols, void* stream);
+
+/* Sparse grouped-query attention over the selected tokens [QSA
+ * _qsa_sparse_paged_decode_kernel, qsa_sparse_paged_decode].  Row r selects the columns
+ * c < min(max(indices[r][topk], 0), topk) whose slot is not -1 and names a page below
+ * num_cache_blocks (a column at or past the valid count is never selected).  Query head
+ * h reads KV head g = h / (Hq / Hkv).  With K_j, V_j the e4m3fn codes of selected token j
+ * (page slot >> offset_bits, place slot & (2^offset_bits - 1)) and q, gate bf16:
+ *   s_j = softmax_scale * q[r][h] . K_j          (bf16 x e4m3 products, fp32 sums)
+ *   a_j = softmax over the selected j            (probabilities rounded to fp16 for the
+ *                                                  product with V, fp32 normalizer)
+ *   out[r][h][d] = bf16(bf16(output_scale * sum_j a_j V_j[d]) * sigmoid(gate[r][h][d]))
+ * and out = 0 for a row with nothing selected.  A token selected twice counts twice.
+ * Layouts: q, gate, out [rows][Hq][head_dim] bf16 (uint16 bit patterns) with row and head
+ * strides in elements, dims contiguous; the caches hold token (page p, place t, head g) at
+ * byte p * block_stride + t * token_stride + g * k_head_stride (v_head_stride for V), dims
+ * contiguous (one combined cache with V at k_cache + head_dim is fine); slots as written
+ * by fp4idx_qsa_slots (>= min(count, topk) columns per row); indices as above.  All
+ * caller-owned device memory; asynchronous on `stream`; nothing is allocated.
+ * Limits: head_dim == 128 and 1 <= Hq / Hkv <= 16 (else EUNSUPPORTED); block_stride and
+ * token_stride below 2^32 (else EUNSUPPORTED); EALIGN unless q, gate, out, k_cache and
+ * v_cache are 16-byte aligned, the bf16 strides are multiples of 8 elements and the
+ * cache strides multiples of 16 bytes; EINVAL for rows < 0, topk < 1, Hkv < 1,
+ * Hq % Hkv != 0, page_size < 1, num_cache_blocks < 1, a missing pointer, or
+ * (num_cache_blocks << offset_bits) >= 2^31. */
+int fp4idx_qsa_decode(const uint16_t* q, int64_t q_row_stride, int64_t q_head_stride,
+                      const uint8_t* k_cache, const uint8_t* v_cache,
+                      int64_t block_stride, int64_t token_stride,
+                      int64_t k_head_stride, int64_t v_head_stride,
+                      int num_cache_blocks, int page_size,
+                      const int32_t* slots, int64_t slots_row_stride,
+                      const int32_t* indices, int64_t indices_row_stride, int topk,
+                      int rows, int Hq, int Hkv, int head_dim,
+                      float softmax_scale, float output_scale,
+                      const uint16_t* gate, int64_t gate_row_stride, int64_t gate_head_stride,
+                      uint16_t* out, int64_t out_row_stride, int64_t out_head_stride,
+                      void* stream);
 
 /* Static string naming a status code. */
 const char* fp4idx_strerror(int code);

@@ -8,11 +8,15 @@ this package is its Python binding:
     block_topk(...)     top-k blocks per (head, query) along the block scores' Ktiles
     topk(...)           exact top-k column selection per row
     quantize_store_k(...)  MXFP4 quantize-and-store of keys into the paged cache
+    qsa_sparse_paged_decode(...)  sparse attention over the selected tokens of an fp8
+                        K/V cache (slot pass ``qsa_slots`` + ``qsa_decode``)
 
 ``workloads`` holds seeded synthetic inputs for the benchmark shapes.
 """
 from .ops import (MXFP4, NVFP4, block_scores, block_topk, logits_paged,  # noqa: F401
-                  quantize_store_k, topk, topk_workspace_bytes)
+                  qsa_decode, qsa_slots, qsa_sparse_paged_decode, quantize_store_k, topk,
+                  topk_workspace_bytes)
 
 __all__ = ["MXFP4", "NVFP4", "logits_paged", "block_scores", "block_topk", "topk",
-           "topk_workspace_bytes", "quantize_store_k"]
+           "topk_workspace_bytes", "quantize_store_k", "qsa_slots", "qsa_decode",
+           "qsa_sparse_paged_decode"]

@@ -20,6 +20,8 @@ EXPORTS = (
     "fp4idx_topk_workspace_bytes",
     "fp4idx_topk",
     "fp4idx_quantize_store_k",
+    "fp4idx_qsa_slots",
+    "fp4idx_qsa_decode",
     "fp4idx_strerror",
     "fp4idx_version",
 )
@@ -58,6 +60,14 @@ def lib() -> ctypes.CDLL:
     L.fp4idx_topk.argtypes = [P, i64, i32, i32, P, i32, P, P, P, ctypes.c_size_t, P]
     L.fp4idx_quantize_store_k.restype = i32
     L.fp4idx_quantize_store_k.argtypes = [P, i64, P, i32, P, i64, P, i64, i32, i32, P]
+    L.fp4idx_qsa_slots.restype = i32
+    L.fp4idx_qsa_slots.argtypes = [P, i64, i32, i32, P, i64, i32, i32, P, i32, i32, P, i64, i32,
+                                   P]
+    f32 = ctypes.c_float
+    L.fp4idx_qsa_decode.restype = i32
+    L.fp4idx_qsa_decode.argtypes = [P, i64, i64, P, P, i64, i64, i64, i64, i32, i32, P, i64, P,
+                                    i64, i32, i32, i32, i32, i32, f32, f32, P, i64, i64, P, i64,
+                                    i64, P]
     L.fp4idx_strerror.restype = ctypes.c_char_p
     L.fp4idx_strerror.argtypes = [i32]
     L.fp4idx_version.restype = i32

@@ -187,6 +187,120 @@ int fp4idx_block_topk(const float* scores, int Hq, int Ktiles, int Tq, int k,
     return hip_status(fp4idx::launch_block_topk(p, (hipStream_t)stream));
 }
 
+namespace {
+
+// bit length of page_size - 1, at least 1 (slot layout of the sparse attention)
+int qsa_offset_bits(int page_size) {
+    int b = 1;
+    while (b < 31 && ((int64_t)1 << b) < (int64_t)page_size) b++;
+    return b;
+}
+
+bool qsa_slot_fits(int num_cache_blocks, int ob) {
+    return ((int64_t)num_cache_blocks << ob) < ((int64_t)1 << 31);
+}
+
+}  // namespace
+
+int fp4idx_qsa_slots(const int32_t* indices, int64_t indices_row_stride, int rows, int topk,
+                     const int32_t* block_table, int64_t block_table_row_stride,
+                     int num_requests, int table_width, const int32_t* token_to_req,
+                     int num_cache_blocks, int page_size,
+                     int32_t* slots, int64_t slots_row_stride, int slot_cols, void* stream) {
+    if (rows < 0 || topk < 1 || slot_cols < topk || page_size < 1 || num_requests < 1 ||
+        table_width < 1 || num_cache_blocks < 1)
+        return FP4IDX_EINVAL;
+    if (indices_row_stride < topk || block_table_row_stride < table_width ||
+        slots_row_stride < slot_cols)
+        return FP4IDX_EINVAL;
+    const int ob = qsa_offset_bits(page_size);
+    if (!qsa_slot_fits(num_cache_blocks, ob)) return FP4IDX_EINVAL;
+    if (rows == 0) return FP4IDX_OK;
+    if (!indices || !block_table || !token_to_req || !slots) return FP4IDX_EINVAL;
+    if ((int64_t)rows * ((slot_cols + 255) / 256) > 0x7fffffff) return FP4IDX_EUNSUPPORTED;
+    fp4idx::QsaSlotParams p{};
+    p.ind = indices;
+    p.ind_rs = indices_row_stride;
+    p.rows = rows;
+    p.topk = topk;
+    p.bt = block_table;
+    p.bt_rs = block_table_row_stride;
+    p.num_req = num_requests;
+    p.width = table_width;
+    p.t2r = token_to_req;
+    p.num_blocks = num_cache_blocks;
+    p.page = page_size;
+    p.ob = ob;
+    p.slots = slots;
+    p.slots_rs = slots_row_stride;
+    p.slot_cols = slot_cols;
+    return hip_status(fp4idx::launch_qsa_slots(p, (hipStream_t)stream));
+}
+
+int fp4idx_qsa_decode(const uint16_t* q, int64_t q_row_stride, int64_t q_head_stride,
+                      const uint8_t* k_cache, const uint8_t* v_cache,
+                      int64_t block_stride, int64_t token_stride,
+                      int64_t k_head_stride, int64_t v_head_stride,
+                      int num_cache_blocks, int page_size,
+                      const int32_t* slots, int64_t slots_row_stride,
+                      const int32_t* indices, int64_t indices_row_stride, int topk,
+                      int rows, int Hq, int Hkv, int head_dim,
+                      float softmax_scale, float output_scale,
+                      const uint16_t* gate, int64_t gate_row_stride, int64_t gate_head_stride,
+                      uint16_t* out, int64_t out_row_stride, int64_t out_head_stride,
+                      void* stream) {
+    if (rows < 0 || topk < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || page_size < 1 ||
+        num_cache_blocks < 1)
+        return FP4IDX_EINVAL;
+    const int ob = qsa_offset_bits(page_size);
+    if (!qsa_slot_fits(num_cache_blocks, ob)) return FP4IDX_EINVAL;
+    if (head_dim != 128 || Hq / Hkv > 16) return FP4IDX_EUNSUPPORTED;
+    if (block_stride < 0 || token_stride < 0 || block_stride >= ((int64_t)1 << 32) ||
+        token_stride >= ((int64_t)1 << 32))
+        return FP4IDX_EUNSUPPORTED;
+    if (rows == 0) return FP4IDX_OK;
+    if (!q || !k_cache || !v_cache || !slots || !indices || !gate || !out) return FP4IDX_EINVAL;
+    if (indices_row_stride <= topk || slots_row_stride < 0) return FP4IDX_EINVAL;
+    if ((int64_t)rows * Hkv > 0x7fffffff) return FP4IDX_EUNSUPPORTED;
+    if (!aligned16(q) || !aligned16(gate) || !aligned16(out) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(slots))
+        return FP4IDX_EALIGN;
+    if ((q_row_stride | q_head_stride | gate_row_stride | gate_head_stride | out_row_stride |
+         out_head_stride) & 7)
+        return FP4IDX_EALIGN;
+    if ((block_stride | token_stride | k_head_stride | v_head_stride) & 15) return FP4IDX_EALIGN;
+    fp4idx::QsaDecodeParams p{};
+    p.q = q;
+    p.q_rs = q_row_stride;
+    p.q_hs = q_head_stride;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.bs = block_stride;
+    p.ts = token_stride;
+    p.khs = k_head_stride;
+    p.vhs = v_head_stride;
+    p.slots = slots;
+    p.slots_rs = slots_row_stride;
+    p.ind = indices;
+    p.ind_rs = indices_row_stride;
+    p.topk = topk;
+    p.rows = rows;
+    p.Hkv = Hkv;
+    p.G = Hq / Hkv;
+    p.ob = ob;
+    p.num_blocks = num_cache_blocks;
+    p.page = page_size;
+    p.score_scale = (float)((double)softmax_scale * 1.4426950408889634);
+    p.out_scale = output_scale;
+    p.gate = gate;
+    p.gate_rs = gate_row_stride;
+    p.gate_hs = gate_head_stride;
+    p.out = out;
+    p.out_rs = out_row_stride;
+    p.out_hs = out_head_stride;
+    return hip_status(fp4idx::launch_qsa_decode(p, (hipStream_t)stream));
+}
+
 size_t fp4idx_topk_workspace_bytes(int rows, int cols, int k) {
     if (rows <= 0 || cols <= 0 || k <= 0) return 0;
     return fp4idx::topk_workspace_bytes(rows, cols, k);

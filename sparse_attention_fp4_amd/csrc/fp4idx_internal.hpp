@@ -93,6 +93,44 @@ struct QuantParams {
 };
 
 hipError_t launch_quantize_store(const QuantParams& p, hipStream_t stream);
+
+// Sparse attention over selected tokens: slot pass.
+struct QsaSlotParams {
+    const int32_t* ind;     // [rows][ind_rs] logical tokens
+    int64_t ind_rs;
+    int rows, topk;
+    const int32_t* bt;      // [num_req][bt_rs] physical pages
+    int64_t bt_rs;
+    int num_req, width;
+    const int32_t* t2r;     // [rows] request of each row
+    int num_blocks, page, ob;
+    int32_t* slots;         // [rows][slots_rs]
+    int64_t slots_rs;
+    int slot_cols;
+};
+
+// Sparse attention over selected tokens: decode step.
+struct QsaDecodeParams {
+    const uint16_t* q;      // bf16 [rows][Hq][128], strides in elements
+    int64_t q_rs, q_hs;
+    const uint8_t* k;       // e4m3fn cache, byte strides
+    const uint8_t* v;
+    int64_t bs, ts, khs, vhs;
+    const int32_t* slots;
+    int64_t slots_rs;
+    const int32_t* ind;     // valid count at column topk
+    int64_t ind_rs;
+    int topk, rows, Hkv, G, ob, num_blocks, page;
+    float score_scale;      // softmax_scale * log2(e)
+    float out_scale;
+    const uint16_t* gate;   // bf16 [rows][Hq][128]
+    int64_t gate_rs, gate_hs;
+    uint16_t* out;          // bf16 [rows][Hq][128]
+    int64_t out_rs, out_hs;
+};
+
+hipError_t launch_qsa_slots(const QsaSlotParams& p, hipStream_t stream);
+hipError_t launch_qsa_decode(const QsaDecodeParams& p, hipStream_t stream);
 size_t topk_workspace_bytes(int rows, int cols, int k);
 
 }  // namespace fp4idx

@@ -241,3 +241,96 @@ def quantize_store_k(keys, slots, k_fp4, k_scale):
                                        page * 64, _ptr(k_scale), page * 4, page, P, _stream())
     check("fp4idx_quantize_store_k", rc)
     return k_fp4, k_scale
+
+
+def qsa_slots(logical_indices, block_table, token_to_req, num_cache_blocks: int, page_size: int,
+              *, out=None, slot_cols: Optional[int] = None):
+    """Slot pass of the sparse attention over selected tokens (vLLM qsa_fp8 page,
+    _qsa_physical_slots_kernel): logical_indices [rows, topk + 1] int32 (the valid count
+    in the last column), block_table [num_requests, width] int32, token_to_req [rows]
+    int32 -> slots [rows, slot_cols] int32, (page << offset_bits) | place or -1."""
+    _need(logical_indices, "logical_indices", torch.int32, 2)
+    dev = logical_indices.device
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(token_to_req, "token_to_req", torch.int32, 1, dev)
+    rows, cols = logical_indices.shape
+    topk = cols - 1
+    slot_cols = topk if slot_cols is None else int(slot_cols)
+    for t, name in ((logical_indices, "logical_indices"), (block_table, "block_table")):
+        if t.stride(1) != 1:
+            raise ValueError(f"{name} must have unit column stride")
+    if token_to_req.numel() != rows or not token_to_req.is_contiguous():
+        raise ValueError("token_to_req must be a contiguous [rows] tensor")
+    if out is None:
+        out = torch.empty((rows, slot_cols), dtype=torch.int32, device=dev)
+    _need(out, "out", torch.int32, 2, dev)
+    if out.stride(1) != 1 or out.shape != (rows, slot_cols):
+        raise ValueError("out must be [rows, slot_cols] with unit column stride")
+    rc = lib().fp4idx_qsa_slots(_ptr(logical_indices), logical_indices.stride(0), rows, topk,
+                                _ptr(block_table), block_table.stride(0), block_table.shape[0],
+                                block_table.shape[1], _ptr(token_to_req), num_cache_blocks,
+                                page_size, _ptr(out), out.stride(0), slot_cols, _stream())
+    check("fp4idx_qsa_slots", rc)
+    return out
+
+
+def _cache_view(t, name):
+    t = _u8(t)
+    _need(t, name, torch.uint8, 4)
+    if t.stride(3) != 1:
+        raise ValueError(f"{name} must have contiguous head dims")
+    return t
+
+
+def qsa_decode(q, k_cache, v_cache, slots, logical_indices, out, output_gate,
+               softmax_scale: float, output_scale: float):
+    """Sparse grouped-query attention over the selected tokens (vLLM qsa_fp8 page,
+    _qsa_sparse_paged_decode_kernel) given the slots of ``qsa_slots``.
+    q, output_gate, out: [rows, Hq, 128] bf16; k_cache, v_cache: [num_blocks, page, Hkv,
+    128] e4m3fn codes (uint8 or float8_e4m3fn views, equal block and token strides)."""
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    k_cache, v_cache = _cache_view(k_cache, "k_cache"), _cache_view(v_cache, "v_cache")
+    _need(slots, "slots", torch.int32, 2, dev)
+    _need(logical_indices, "logical_indices", torch.int32, 2, dev)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    _need(output_gate, "output_gate", torch.bfloat16, 3, dev)
+    rows, Hq, D = q.shape
+    nb, page, Hkv, Dk = k_cache.shape
+    if v_cache.shape != k_cache.shape or v_cache.stride()[:2] != k_cache.stride()[:2]:
+        raise ValueError("k_cache and v_cache must have the same shape and block/token strides")
+    if Dk != D or out.shape != q.shape or output_gate.shape != q.shape:
+        raise ValueError("q, out, output_gate must be [rows, Hq, D] with the cache's D")
+    for t, name in ((q, "q"), (out, "out"), (output_gate, "output_gate")):
+        if t.stride(2) != 1:
+            raise ValueError(f"{name} must have unit dim stride")
+    if slots.shape[0] != rows or slots.stride(1) != 1 or logical_indices.shape[0] != rows \
+            or logical_indices.stride(1) != 1:
+        raise ValueError("slots and logical_indices must have one row per query row")
+    topk = logical_indices.shape[1] - 1
+    if slots.shape[1] < topk:
+        raise ValueError("slots must have at least topk columns")
+    rc = lib().fp4idx_qsa_decode(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), _ptr(v_cache), k_cache.stride(0),
+        k_cache.stride(1), k_cache.stride(2), v_cache.stride(2), nb, page, _ptr(slots),
+        slots.stride(0), _ptr(logical_indices), logical_indices.stride(0), topk, rows, Hq, Hkv,
+        D, float(softmax_scale), float(output_scale), _ptr(output_gate), output_gate.stride(0),
+        output_gate.stride(1), _ptr(out), out.stride(0), out.stride(1), _stream())
+    check("fp4idx_qsa_decode", rc)
+    return out
+
+
+def qsa_sparse_paged_decode(q, k_cache, v_cache, logical_indices, block_table, token_to_req,
+                            out, output_gate, softmax_scale: float, output_scale: float,
+                            *, slots=None):
+    """The slot pass then the sparse decode (vLLM qsa_fp8 page, qsa_sparse_paged_decode).
+    slots: optional preallocated [rows, >= topk] int32 buffer."""
+    k8 = _cache_view(k_cache, "k_cache")
+    rows = q.shape[0]
+    topk = logical_indices.shape[1] - 1
+    if slots is None:
+        slots = torch.empty((rows, topk), dtype=torch.int32, device=q.device)
+    qsa_slots(logical_indices, block_table, token_to_req, k8.shape[0], k8.shape[1], out=slots,
+              slot_cols=slots.shape[1])
+    return qsa_decode(q, k_cache, v_cache, slots, logical_indices, out, output_gate,
+                      softmax_scale, output_scale)

@@ -118,3 +118,52 @@ def test_block_topk_argument_errors():
     assert f(256, 2, 4, 0, 2, 256, None, None) == 0        # no queries: nothing to do
     assert f(None, 2, 4, 8, 2, 256, None, None) == 1       # missing scores
     assert f(256, 2, 4, 8, 2, None, None, None) == 1       # missing output
+
+
+def _qsa_slots(**kw):
+    L = _lib.lib()
+    a = dict(ind=256, irs=9, rows=4, topk=8, bt=256, btrs=4, nreq=2, width=4, t2r=256, nb=16,
+             page=64, slots=256, srs=8, cols=8)
+    a.update(kw)
+    return L.fp4idx_qsa_slots(a["ind"], a["irs"], a["rows"], a["topk"], a["bt"], a["btrs"],
+                              a["nreq"], a["width"], a["t2r"], a["nb"], a["page"], a["slots"],
+                              a["srs"], a["cols"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=-1), 1), (dict(topk=0), 1), (dict(cols=7), 1), (dict(page=0), 1),
+    (dict(nreq=0), 1), (dict(width=0), 1), (dict(nb=0), 1), (dict(irs=7), 1),
+    (dict(btrs=3), 1), (dict(srs=7), 1), (dict(ind=None), 1), (dict(slots=None), 1),
+    (dict(nb=1 << 25, page=64), 1),          # 2^25 pages << 6 bits does not fit in int32
+    (dict(rows=0, ind=None), 0),             # nothing to do
+])
+def test_qsa_slots_argument_errors(kw, code):
+    assert _qsa_slots(**kw) == code
+
+
+def _qsa_decode(**kw):
+    L = _lib.lib()
+    a = dict(q=256, qrs=32 * 128, qhs=128, k=256, v=256 + 128, bs=4 * 64 * 256, ts=256,
+             khs=64 * 256, vhs=64 * 256, nb=16, page=64, slots=256, srs=8, ind=256, irs=9,
+             topk=8, rows=4, Hq=32, Hkv=4, D=128, ss=0.1, os=1.0, gate=256, grs=32 * 128,
+             ghs=128, out=256, ors=32 * 128, ohs=128)
+    a.update(kw)
+    return L.fp4idx_qsa_decode(a["q"], a["qrs"], a["qhs"], a["k"], a["v"], a["bs"], a["ts"],
+                               a["khs"], a["vhs"], a["nb"], a["page"], a["slots"], a["srs"],
+                               a["ind"], a["irs"], a["topk"], a["rows"], a["Hq"], a["Hkv"],
+                               a["D"], a["ss"], a["os"], a["gate"], a["grs"], a["ghs"],
+                               a["out"], a["ors"], a["ohs"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=-1), 1), (dict(topk=0), 1), (dict(Hkv=0), 1), (dict(Hq=30), 1),
+    (dict(Hq=2), 1), (dict(page=0), 1), (dict(nb=0), 1), (dict(irs=8), 1),
+    (dict(q=None), 1), (dict(gate=None), 1), (dict(out=None), 1), (dict(slots=None), 1),
+    (dict(nb=1 << 25), 1),
+    (dict(D=64), 2), (dict(Hq=68, Hkv=4), 2), (dict(bs=1 << 32), 2), (dict(ts=1 << 32), 2),
+    (dict(q=264), 3), (dict(k=264), 3), (dict(v=256 + 136), 3), (dict(out=258), 3),
+    (dict(qhs=132), 3), (dict(ors=32 * 128 + 4), 3), (dict(ts=264), 3), (dict(vhs=8), 3),
+    (dict(rows=0, q=None), 0),               # nothing to do
+])
+def test_qsa_decode_argument_errors(kw, code):
+    assert _qsa_decode(**kw) == code
