@@ -45,6 +45,7 @@ constexpr int kChunk = 32;
 constexpr int kDim = 128;
 constexpr int kORow = kDim + 4;  // LDS row of a wave's partial output (padded)
 constexpr float kMaskedMax = -1e30f;
+constexpr int kSeg = 4096;       // columns whose token offsets are staged in LDS at a time
 
 __global__ __launch_bounds__(256) void k_qsa_slots(const QsaSlotParams p, int col_blocks) {
     const int r = blockIdx.x / col_blocks;
@@ -108,7 +109,13 @@ struct QsaRaw {
 };
 
 __global__ __launch_bounds__(kQsaThreads) void k_qsa_decode(const QsaDecodeParams p) {
-    __shared__ float s_o[kQsaWaves][16][kORow];
+    // LDS: the byte offsets of one segment of columns while the chunks run (bit 0 set
+    // for a selected token), the waves' partial outputs for the final merge
+    union QsaLds {
+        uint64_t off[kSeg];
+        float o[kQsaWaves][16][kORow];
+    };
+    __shared__ QsaLds lds;
     __shared__ float s_m[kQsaWaves][16];
     __shared__ float s_l[kQsaWaves][16];
 
@@ -121,7 +128,6 @@ __global__ __launch_bounds__(kQsaThreads) void k_qsa_decode(const QsaDecodeParam
 
     int n = p.ind[(int64_t)r * p.ind_rs + p.topk];
     n = __builtin_amdgcn_readfirstlane(min(max(n, 0), p.topk));
-    const int nch = (n + kChunk - 1) / kChunk;
 
     // q operand of k-step s: dims 32*qg + 8*s .. +8 of head g*G + hn (zero past the group)
     v8bf qop[4];
@@ -141,34 +147,23 @@ __global__ __launch_bounds__(kQsaThreads) void k_qsa_decode(const QsaDecodeParam
     const uint32_t omask = (1u << p.ob) - 1u;
     const uint32_t bs = (uint32_t)p.bs, ts = (uint32_t)p.ts;
 
-    // byte offset of a selected token's row (0 = page 0, place 0 when not selected); a
-    // slot whose page or place is outside the cache is not selected (-1 gives a page
-    // past the cache)
-    auto token_off = [&](int c, bool& ok) -> uint64_t {
-        const uint32_t s = (uint32_t)srow[min(c, n - 1)];
-        const uint32_t pg = s >> p.ob, pl = s & omask;
-        ok = c < n && pg < (uint32_t)p.num_blocks && pl < (uint32_t)p.page;
-        const uint64_t off = (uint64_t)pg * bs + (uint64_t)pl * ts;
-        return ok ? off : 0ull;
-    };
-
+    // gather the chunk's K and V pieces of this lane; a token that is not selected
+    // (offset 0, bit 0 clear) reads page 0, place 0
     auto fetch = [&](int ch, QsaRaw& raw) {
-        const int c0 = ch * kChunk;
+        const uint64_t* so = lds.off + ch * kChunk;
         raw.valid = 0;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            bool ok;
-            const uint64_t off = token_off(c0 + 8 * qg + i, ok);
-            raw.v[i] = *(const uint2*)(vbase + off);
-            raw.valid |= ok ? (1u << i) : 0u;
+            const uint64_t off = so[8 * qg + i];
+            raw.v[i] = *(const uint2*)(vbase + (off & ~(uint64_t)1));
+            raw.valid |= ((uint32_t)off & 1u) << i;
         }
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            bool ok;
             // tile j row hn holds token 8*(hn/4) + 4*j + hn%4: its scores land in lane
             // group hn/4 as that group's tokens 4*j .. 4*j+3
-            const uint64_t off = token_off(c0 + 8 * (hn >> 2) + 4 * j + (hn & 3), ok);
-            const uint4* kp = (const uint4*)(kbase + off);
+            const uint64_t off = so[8 * (hn >> 2) + 4 * j + (hn & 3)];
+            const uint4* kp = (const uint4*)(kbase + (off & ~(uint64_t)1));
             raw.k[j][0] = kp[0];
             raw.k[j][1] = kp[1];
         }
@@ -179,84 +174,119 @@ __global__ __launch_bounds__(kQsaThreads) void k_qsa_decode(const QsaDecodeParam
 #pragma unroll
     for (int c = 0; c < 8; c++) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    if (wave < nch) {
-        QsaRaw cur;
-        fetch(wave, cur);
-        for (int ch = wave; ch < nch; ch += kQsaWaves) {
-            QsaRaw nxt;
-            fetch(min(ch + kQsaWaves, nch - 1), nxt);  // the last one re-reads a chunk
-
-            // scores of tokens 8*qg + 4*j + i for head hn
-            float x[8];
+    // one chunk: scores, online softmax, P V
+    auto process = [&](const QsaRaw& cur) {
+        // scores of tokens 8*qg + 4*j + i for head hn
+        float x[8];
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const uint32_t* kw = (const uint32_t*)&cur.k[j][0];
-                v4f sc = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2; j++) {
+            const uint32_t* kw = (const uint32_t*)&cur.k[j][0];
+            v4f sc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < 4; s++)
-                    sc = mfma_bf16_16x16x32(e4m3x8_to_bf16(kw[2 * s], kw[2 * s + 1]), qop[s], sc);
+            for (int s = 0; s < 4; s++)
+                sc = mfma_bf16_16x16x32(e4m3x8_to_bf16(kw[2 * s], kw[2 * s + 1]), qop[s], sc);
 #pragma unroll
-                for (int i = 0; i < 4; i++) x[4 * j + i] = sc[i] * p.score_scale;
-            }
-            float cm = kMaskedMax;
-#pragma unroll
-            for (int t = 0; t < 8; t++) {
-                x[t] = (cur.valid >> t) & 1u ? x[t] : kMaskedMax;
-                cm = fmaxf(cm, x[t]);
-            }
-            cm = fmaxf(cm, __shfl_xor(cm, 16));
-            cm = fmaxf(cm, __shfl_xor(cm, 32));
-            const float mn = fmaxf(m, cm);
-            const float alpha = __builtin_amdgcn_exp2f(m - mn);
-            float pr[8], ps = 0.f;
-#pragma unroll
-            for (int t = 0; t < 8; t++) {
-                pr[t] = (cur.valid >> t) & 1u ? __builtin_amdgcn_exp2f(x[t] - mn) : 0.f;
-                ps += pr[t];
-            }
-            l = l * alpha + ps;
-            m = mn;
-            if (__ballot(alpha != 1.f)) {
-#pragma unroll
-                for (int c = 0; c < 8; c++) acc[c] *= alpha;
-            }
-            v4u pop;
-#pragma unroll
-            for (int k = 0; k < 4; k++) pop[k] = pack_f16x2(pr[2 * k], pr[2 * k + 1]);
-            const v8h pB = __builtin_bit_cast(v8h, pop);
-
-            // V of unselected tokens is zeroed (its bytes may be anything)
-            uint2 vv[8];
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const bool ok = (cur.valid >> i) & 1u;
-                vv[i].x = ok ? cur.v[i].x : 0u;
-                vv[i].y = ok ? cur.v[i].y : 0u;
-            }
-#pragma unroll
-            for (int cp = 0; cp < 4; cp++) {
-                // dims 8*hn + 2*cp and + 1: byte (2*cp) % 4 and the next of word cp / 2
-                const uint32_t sel = (cp & 1) ? 0x07030602u : 0x05010400u;
-                v4u a0, a1;
-#pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    const uint32_t w0 = (cp >> 1) ? vv[2 * k].y : vv[2 * k].x;
-                    const uint32_t w1 = (cp >> 1) ? vv[2 * k + 1].y : vv[2 * k + 1].x;
-                    // bytes: [w0.b, w1.b, w0.b+1, w1.b+1]
-                    const uint32_t w = __builtin_amdgcn_perm(w1, w0, sel);
-                    a0[k] = e4m3x2_to_f16x2<false>(w);
-                    a1[k] = e4m3x2_to_f16x2<true>(w);
-                }
-                acc[2 * cp] = mfma_f16_16x16x32(__builtin_bit_cast(v8h, a0), pB, acc[2 * cp]);
-                acc[2 * cp + 1] = mfma_f16_16x16x32(__builtin_bit_cast(v8h, a1), pB, acc[2 * cp + 1]);
-            }
-            cur = nxt;
+            for (int i = 0; i < 4; i++) x[4 * j + i] = sc[i] * p.score_scale;
         }
+        float cm = kMaskedMax;
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+            x[t] = (cur.valid >> t) & 1u ? x[t] : kMaskedMax;
+            cm = fmaxf(cm, x[t]);
+        }
+        cm = fmaxf(cm, __shfl_xor(cm, 16));
+        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        const float mn = fmaxf(m, cm);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        float pr[8], ps = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+            pr[t] = (cur.valid >> t) & 1u ? __builtin_amdgcn_exp2f(x[t] - mn) : 0.f;
+            ps += pr[t];
+        }
+        l = l * alpha + ps;
+        m = mn;
+        if (__ballot(alpha != 1.f)) {
+#pragma unroll
+            for (int c = 0; c < 8; c++) acc[c] *= alpha;
+        }
+        v4u pop;
+#pragma unroll
+        for (int k = 0; k < 4; k++) pop[k] = pack_f16x2(pr[2 * k], pr[2 * k + 1]);
+        const v8h pB = __builtin_bit_cast(v8h, pop);
+
+        // V of unselected tokens is zeroed (its bytes may be anything)
+        uint2 vv[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const bool ok = (cur.valid >> i) & 1u;
+            vv[i].x = ok ? cur.v[i].x : 0u;
+            vv[i].y = ok ? cur.v[i].y : 0u;
+        }
+#pragma unroll
+        for (int cp = 0; cp < 4; cp++) {
+            // dims 8*hn + 2*cp and + 1: byte (2*cp) % 4 and the next of word cp / 2
+            const uint32_t sel = (cp & 1) ? 0x07030602u : 0x05010400u;
+            v4u a0, a1;
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const uint32_t w0 = (cp >> 1) ? vv[2 * k].y : vv[2 * k].x;
+                const uint32_t w1 = (cp >> 1) ? vv[2 * k + 1].y : vv[2 * k + 1].x;
+                // bytes: [w0.b, w1.b, w0.b+1, w1.b+1]
+                const uint32_t w = __builtin_amdgcn_perm(w1, w0, sel);
+                a0[k] = e4m3x2_to_f16x2<false>(w);
+                a1[k] = e4m3x2_to_f16x2<true>(w);
+            }
+            acc[2 * cp] = mfma_f16_16x16x32(__builtin_bit_cast(v8h, a0), pB, acc[2 * cp]);
+            acc[2 * cp + 1] = mfma_f16_16x16x32(__builtin_bit_cast(v8h, a1), pB, acc[2 * cp + 1]);
+        }
+    };
+
+    for (int seg0 = 0; seg0 < n; seg0 += kSeg) {
+        const int ns = min(kSeg, n - seg0);
+        const int nch = (ns + kChunk - 1) / kChunk;
+        __syncthreads();  // the previous segment's offsets are no longer read
+        // byte offset of each column's token row, bit 0 set when it is selected: the
+        // slot is not -1 and its page and place lie inside the cache (-1 gives a page
+        // past the cache); columns past the segment's count are not selected
+        // (loads clamped to the last column so that they all issue before the first wait)
+        constexpr int kPer = kSeg / kQsaThreads;
+        uint32_t sl[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; u++)
+            sl[u] = (uint32_t)srow[seg0 + min((int)threadIdx.x + u * kQsaThreads, ns - 1)];
+#pragma unroll
+        for (int u = 0; u < kPer; u++) {
+            const int c = threadIdx.x + u * kQsaThreads;
+            const uint32_t pg = sl[u] >> p.ob, pl = sl[u] & omask;
+            const bool ok = c < ns && pg < (uint32_t)p.num_blocks && pl < (uint32_t)p.page;
+            const uint64_t o = ((uint64_t)pg * bs + (uint64_t)pl * ts) | 1u;
+            if (c < nch * kChunk) lds.off[c] = ok ? o : 0ull;
+        }
+        __syncthreads();
+        if (wave >= nch) continue;
+        // this wave's chunks wave, wave+4, ...: two buffers in turn, the next chunk's
+        // gathers in flight while one is processed (no copies between them, no exit
+        // inside the loop body)
+        const int K = (nch - wave + kQsaWaves - 1) / kQsaWaves;
+        QsaRaw A, B;
+        fetch(wave, A);
+        int k = 0;
+        for (; k + 2 <= K; k += 2) {
+            fetch(wave + (k + 1) * kQsaWaves, B);
+            __builtin_amdgcn_sched_barrier(0);  // B's gathers go out before A is waited on
+            process(A);
+            fetch(wave + min(k + 2, K - 1) * kQsaWaves, A);  // the last one re-reads a chunk
+            __builtin_amdgcn_sched_barrier(0);
+            process(B);
+        }
+        if (k < K) process(A);
     }
 
     // merge the four waves' states
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
+    __syncthreads();  // the offsets are no longer read: the LDS takes the partial outputs
     if (qg == 0) {
         s_m[wave][hn] = m;
         s_l[wave][hn] = l;
@@ -264,7 +294,7 @@ __global__ __launch_bounds__(kQsaThreads) void k_qsa_decode(const QsaDecodeParam
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         // accumulator c, element i: dim 8*(4*qg + i) + c of head hn
-        float* o = &s_o[wave][hn][32 * qg + 8 * i];
+        float* o = &lds.o[wave][hn][32 * qg + 8 * i];
         *(float4*)o = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
         *(float4*)(o + 4) = make_float4(acc[4][i], acc[5][i], acc[6][i], acc[7][i]);
     }
@@ -281,8 +311,8 @@ __global__ __launch_bounds__(kQsaThreads) void k_qsa_decode(const QsaDecodeParam
     for (int w = 0; w < kQsaWaves; w++) {
         const float f = __builtin_amdgcn_exp2f(s_m[w][h] - M);
         L += s_l[w][h] * f;
-        const float4 a = *(const float4*)&s_o[w][h][d0];
-        const float4 b = *(const float4*)&s_o[w][h][d0 + 4];
+        const float4 a = *(const float4*)&lds.o[w][h][d0];
+        const float4 b = *(const float4*)&lds.o[w][h][d0 + 4];
         o[0] += a.x * f; o[1] += a.y * f; o[2] += a.z * f; o[3] += a.w * f;
         o[4] += b.x * f; o[5] += b.y * f; o[6] += b.z * f; o[7] += b.w * f;
     }
