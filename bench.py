@@ -12,6 +12,9 @@ the FP4 indexer scorer...", Speed Tests: 4 verify rows, 32 heads, contexts 16,38
   block    NVFP4 per-head 128-token block maxima, varlen batch of 8, Hq=32, Hkv=4,
            causal ("M3 FP4 Indexer" README shapes), then the top-16 blocks of every
            (head, query) along Ktiles.
+  qsa      the consumer of the top-k selection (vLLM qsa_fp8 API page): slot pass and
+           sparse grouped-query attention over the top-2048 tokens of 128 decode rows,
+           fp8 e4m3fn K/V cache (contexts U[8192, 32768], 64-token pages), Hq=32, Hkv=4.
 
 Timing: inputs are resident in HBM before the timed region.  Steps rotate over enough
 independent input/output sets that their total (> 512 MiB) exceeds the 256 MiB
@@ -46,7 +49,9 @@ COMMON_SOURCES = [CSRC + "device_common.hpp", CSRC + "fp4idx_internal.hpp", CSRC
 KERNEL_SOURCES = {"logits": [CSRC + "logits.hip"] + COMMON_SOURCES,
                   "topk": [CSRC + "topk.hip", CSRC + "topk_long.hip", CSRC + "topk_stream.hip"] + COMMON_SOURCES,
                   "block_scores": [CSRC + "block_scores.hip"] + COMMON_SOURCES,
-                  "block_topk": [CSRC + "block_topk.hip"] + COMMON_SOURCES}
+                  "block_topk": [CSRC + "block_topk.hip"] + COMMON_SOURCES,
+                  "qsa_slots": [CSRC + "qsa.hip"] + COMMON_SOURCES,
+                  "qsa_decode": [CSRC + "qsa.hip"] + COMMON_SOURCES}
 
 
 def parse():
@@ -55,7 +60,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default per workload)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default per workload)")
     ap.add_argument("--ctx", type=int, default=100_000, help="context of the verify workload")
-    ap.add_argument("--workload", choices=["verify", "batched", "prefill", "block"],
+    ap.add_argument("--workload", choices=["verify", "batched", "prefill", "block", "qsa"],
                     default="verify")
     ap.add_argument("--topk", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -276,6 +281,78 @@ def block_workload(args, torch, fp4, wl, dev):
                 dtype="nvfp4 (e2m1 x e4m3, exact fp16 operands, fp32 accumulate)")
 
 
+def qsa_workload(args, torch, fp4, wl, dev):
+    case = wl.qsa_decode_case()
+    name = case.name
+    desc = (f"{name}: sparse attention over the top-2048 selected tokens, 128 decode rows "
+            f"(1 per request, contexts U[8192,32768]), Hq=32, Hkv=4, D=128, fp8 e4m3fn K/V "
+            f"cache on shuffled 64-token pages, bf16 q / gate / out; slot pass + decode")
+    D = case.D
+    kv = torch.from_numpy(case.kv).to(dev)          # shared by every input set
+    kc = kv.permute(0, 2, 1, 3)[..., :D]
+    vc = kv.permute(0, 2, 1, 3)[..., D:]
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    bt = torch.from_numpy(case.block_table).to(dev)
+    t2r = torch.from_numpy(case.token_to_req).to(dev)
+    selected = case.selected()
+    kv_bytes = selected * case.Hkv * 2 * D
+    row_bytes = case.rows * case.Hq * D * 2
+    ind_bytes = case.indices.nbytes
+    slot_bytes = case.rows * case.topk * 4
+    set_bytes = kv_bytes + 3 * row_bytes + ind_bytes + 2 * slot_bytes
+    made = [0]
+
+    def make_set():
+        i = made[0]
+        made[0] += 1
+        ind = case.indices if i == 0 else wl.qsa_selection(case, 7000 + i)
+        return dict(q=bf16(case.q), gate=bf16(case.gate), out=torch.empty_like(bf16(case.q)),
+                    ind=torch.from_numpy(ind).to(dev),
+                    slots=torch.empty((case.rows, case.topk), dtype=torch.int32, device=dev))
+
+    def slots(s):
+        fp4.qsa_slots(s["ind"], bt, t2r, case.num_cache_blocks, case.page_size, out=s["slots"])
+
+    def decode(s):
+        fp4.qsa_decode(s["q"], kc, vc, s["slots"], s["ind"], s["out"], s["gate"],
+                       case.softmax_scale, case.output_scale)
+
+    work = {"qsa_slots": dict(bytes=ind_bytes + selected * 4 + case.rows * 4 + slot_bytes,
+                              flops=0, bound="hbm", dtype=None),
+            "qsa_decode": dict(bytes=kv_bytes + 3 * row_bytes + slot_bytes + case.rows * 4,
+                               flops=4 * selected * case.Hq * D, bound="hbm", dtype=None)}
+
+    def cpu_baseline():
+        from oracle import oracle as orc
+        rows = list(range(0, case.rows, case.rows // 8))
+        threads = min(len(rows), orc.max_threads())
+        so = orc.qsa_slots(case.indices, case.block_table, case.token_to_req,
+                           case.num_cache_blocks, case.page_size)
+        ob = orc.qsa_offset_bits(case.page_size)
+        sub = sum(int(min(case.indices[r, -1], case.topk)) for r in rows)
+
+        def run():
+            orc.qsa_decode(case.q, case.k_cache, case.v_cache, so, case.indices, ob,
+                           case.softmax_scale, case.output_scale, case.gate, rows=rows,
+                           n_threads=threads)
+
+        v, reps, total = _timed_oracle(run, sub)
+        return dict(value=round(v, 1), unit="keys/s", cores=threads, kind="oracle",
+                    sample=f"sparse decode of {len(rows)} rows (all 32 heads, 2048 tokens each; "
+                           f"slots from the oracle's slot pass), {reps} run(s) in {total:.1f} s")
+
+    return dict(name=name, desc=desc, set_bytes=set_bytes, make_set=make_set,
+                calls={"qsa_slots": slots, "qsa_decode": decode}, work=work, pairs=selected,
+                steps=200, warmup=10, launches=40, cpu_baseline=cpu_baseline,
+                config={"rows": case.rows, "heads": case.Hq, "kv_heads": case.Hkv,
+                        "head_dim": D, "selected_per_row": case.topk,
+                        "cache_bytes": int(case.kv.nbytes)},
+                dtype="fp8 e4m3fn K/V (exact bf16 QK, fp16 PV, fp32 accumulate)")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -292,7 +369,7 @@ def main():
     assert torch.cuda.is_available(), "no GPU visible"
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    make = block_workload if args.workload == "block" else logits_workload
+    make = {"block": block_workload, "qsa": qsa_workload}.get(args.workload, logits_workload)
     W = make(args, torch, fp4, wl, dev)
     steps = args.steps if args.steps is not None else W["steps"]
     warmup = args.warmup if args.warmup is not None else W["warmup"]

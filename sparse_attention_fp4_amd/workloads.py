@@ -393,6 +393,20 @@ def make_qsa(name, *, ctx, rows_per_req=1, Hq, Hkv, D=128, page=64, topk=2048, s
                    {"seed": seed, "ctx": ctx})
 
 
+def qsa_selection(case: QsaCase, seed: int) -> np.ndarray:
+    """Another selection for the same requests and cache: per row, min(topk, ctx)
+    distinct tokens in increasing order, count in the last column."""
+    rng = np.random.default_rng(seed)
+    ctx = case.meta["ctx"]
+    ind = np.full_like(case.indices, -1)
+    for r in range(case.rows):
+        c = ctx[int(case.token_to_req[r])]
+        n = min(case.topk, c)
+        ind[r, :n] = np.sort(rng.choice(c, size=n, replace=False))
+        ind[r, case.topk] = n
+    return ind
+
+
 def qsa_decode_case(seed=1050, requests=128):
     """Large-batch sparse decode: 128 requests x 1 row, contexts U[8192, 32768], Hq=32,
     Hkv=4, D=128, 64-token pages, top-2048 selected tokens per row, softmax scale
