@@ -104,6 +104,40 @@ int fp4idx_logits_paged(int fmt,
                         float* logits, int64_t out_row_stride,
                         void* stream);
 
+/* Weighted-ReLU logits and their top-k in one call, without writing the logits [ISS
+ * "Fix (production target)": scores on the matrix cores, ReLU and head weights in the
+ * epilogue, the top-k selected without a serial heap].  The result is exactly that of
+ * fp4idx_topk over the logits fp4idx_logits_paged would write with the same arguments
+ * (out_cols columns): per row t, the k largest finite scores of the visible columns
+ * (ties to the smaller column), out_idx[t][0..m) = their columns in increasing order,
+ * m = min(k, #finite visible scores), out_idx[t][m..k) = -1; out_vals (nullable) the
+ * scores, -inf padded.  The logits arguments mean what they mean for
+ * fp4idx_logits_paged.
+ * How: the scores of every 16th page give each row a threshold that about 2k scores
+ * of the row reach; the scorer then keeps only scores at or above it, and the exact
+ * selection runs over those.  A row where fewer than k scores reach the threshold is
+ * scored again keeping every score, so the result never depends on the sample.
+ * workspace: fp4idx_logits_topk_workspace_bytes(...) bytes, 256-byte aligned,
+ * caller-owned device memory (contents need no initialisation; calls that run
+ * concurrently must not share one).  Only the kept scores (about 2k per row) are
+ * written there, plus the sampled scores (1/16 of the columns).
+ * Limits: 1 <= k <= 2048 and out_cols <= 2^24 (else EUNSUPPORTED); the logits limits
+ * otherwise; EWORKSPACE when the workspace is missing, short or misaligned. */
+size_t fp4idx_logits_topk_workspace_bytes(int fmt, int T, int B, int H, int Hkv, int page_size,
+                                          int table_width, int out_cols, int k);
+int fp4idx_logits_topk_paged(int fmt,
+                             const uint8_t* q_fp4, int64_t q_row_stride,
+                             const uint8_t* q_scale, int64_t qs_row_stride,
+                             const float* w, int64_t w_row_stride,
+                             const uint8_t* k_fp4, int64_t k_page_stride,
+                             const uint8_t* k_scale, int64_t ks_page_stride,
+                             const int32_t* block_table, int64_t bt_row_stride,
+                             const int32_t* cu_seqlens_q, const int32_t* row_lens,
+                             int T, int B, int H, int Hkv, int page_size, int num_pages,
+                             int table_width, int out_cols, int k,
+                             int32_t* out_idx, float* out_vals,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Per-head 128-token block-max scores [M3 数学语义]:
  *
  *     scores[hq][kb][q] = max over valid k_local in [128 kb, 128 kb + 128) of

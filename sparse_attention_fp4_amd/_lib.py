@@ -15,6 +15,8 @@ LIB_PATH = os.path.join(HERE, "libfp4idx.so")
 # the symbols include/fp4idx.h declares
 EXPORTS = (
     "fp4idx_logits_paged",
+    "fp4idx_logits_topk_workspace_bytes",
+    "fp4idx_logits_topk_paged",
     "fp4idx_block_scores",
     "fp4idx_block_topk",
     "fp4idx_topk_workspace_bytes",
@@ -49,6 +51,12 @@ def lib() -> ctypes.CDLL:
     L.fp4idx_logits_paged.restype = i32
     L.fp4idx_logits_paged.argtypes = [i32, P, i64, P, i64, P, i64, P, i64, P, i64, P, i64, P, P,
                                       i32, i32, i32, i32, i32, i32, i32, i32, P, i64, P]
+    L.fp4idx_logits_topk_workspace_bytes.restype = ctypes.c_size_t
+    L.fp4idx_logits_topk_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32]
+    L.fp4idx_logits_topk_paged.restype = i32
+    L.fp4idx_logits_topk_paged.argtypes = [i32, P, i64, P, i64, P, i64, P, i64, P, i64, P, i64, P,
+                                           P, i32, i32, i32, i32, i32, i32, i32, i32, i32, P, P,
+                                           P, ctypes.c_size_t, P]
     L.fp4idx_block_scores.restype = i32
     L.fp4idx_block_scores.argtypes = [i32, P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                       i32, i32, i32, P, P]

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libfp4idx.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["fp4idx_api.hip", "logits.hip", "block_scores.hip", "topk.hip", "topk_long.hip",
-           "topk_stream.hip", "block_topk.hip", "quantize.hip", "qsa.hip"]
+           "topk_stream.hip", "block_topk.hip", "quantize.hip", "qsa.hip", "fused_topk.hip"]
 ARCH = "gfx950"
 
 

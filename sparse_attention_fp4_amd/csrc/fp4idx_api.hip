@@ -31,42 +31,41 @@ const char* fp4idx_strerror(int code) {
     }
 }
 
-int fp4idx_logits_paged(int fmt,
-                        const uint8_t* q_fp4, int64_t q_row_stride,
-                        const uint8_t* q_scale, int64_t qs_row_stride,
-                        const float* w, int64_t w_row_stride,
-                        const uint8_t* k_fp4, int64_t k_page_stride,
-                        const uint8_t* k_scale, int64_t ks_page_stride,
-                        const int32_t* block_table, int64_t bt_row_stride,
-                        const int32_t* cu_seqlens_q, const int32_t* row_lens,
-                        int T, int B, int H, int Hkv, int page_size, int num_pages,
-                        int table_width, int out_cols,
-                        float* logits, int64_t out_row_stride,
-                        void* stream) {
+namespace {
+
+// Argument checks and parameter block shared by the logits and the fused top-k entry
+// points (out / out_row_stride are not checked when `need_out` is false).
+int logits_params(int fmt, const uint8_t* q_fp4, int64_t q_row_stride, const uint8_t* q_scale,
+                  int64_t qs_row_stride, const float* w, int64_t w_row_stride,
+                  const uint8_t* k_fp4, int64_t k_page_stride, const uint8_t* k_scale,
+                  int64_t ks_page_stride, const int32_t* block_table, int64_t bt_row_stride,
+                  const int32_t* cu_seqlens_q, const int32_t* row_lens, int T, int B, int H,
+                  int Hkv, int page_size, int num_pages, int table_width, int out_cols,
+                  float* logits, int64_t out_row_stride, bool need_out, fp4idx::LogitsParams& p) {
     if (fmt != FP4IDX_MXFP4 && fmt != FP4IDX_NVFP4) return FP4IDX_EINVAL;
     if (T < 0 || B < 1 || H < 1 || Hkv < 1 || num_pages < 0 || table_width < 0 || out_cols < 0)
         return FP4IDX_EINVAL;
     if (H % Hkv != 0) return FP4IDX_EINVAL;
     if (H > 128) return FP4IDX_EUNSUPPORTED;
     if (page_size != 64 && page_size != 128) return FP4IDX_EUNSUPPORTED;
-    if (T == 0 || out_cols == 0) return FP4IDX_OK;
-    if (!q_fp4 || !q_scale || !w || !cu_seqlens_q || !row_lens || !logits) return FP4IDX_EINVAL;
+    if (T == 0 || out_cols == 0) return -1;  // nothing to do
+    if (!q_fp4 || !q_scale || !w || !cu_seqlens_q || !row_lens || (need_out && !logits))
+        return FP4IDX_EINVAL;
     if (num_pages > 0 && table_width > 0 && (!k_fp4 || !k_scale || !block_table))
         return FP4IDX_EINVAL;
     const int G = fmt == FP4IDX_MXFP4 ? 4 : 8;
     if (q_row_stride < (int64_t)H * 64 || qs_row_stride < (int64_t)H * G || w_row_stride < H ||
-        out_row_stride < out_cols || bt_row_stride < table_width)
+        (need_out && out_row_stride < out_cols) || bt_row_stride < table_width)
         return FP4IDX_EINVAL;
     // output rows of one row block are addressed with 32-bit offsets
-    if (out_row_stride > ((int64_t)1 << 27)) return FP4IDX_EUNSUPPORTED;
+    if (need_out && out_row_stride > ((int64_t)1 << 27)) return FP4IDX_EUNSUPPORTED;
     if (k_page_stride < (int64_t)Hkv * page_size * 64 || ks_page_stride < (int64_t)Hkv * page_size * G)
         return FP4IDX_EINVAL;
     if (!aligned16(q_fp4) || (q_row_stride & 15) || !aligned16(k_fp4) || (k_page_stride & 15))
         return FP4IDX_EALIGN;
     if (num_pages > 0 && table_width > 0 && (!aligned16(k_scale) || (ks_page_stride & 15)))
         return FP4IDX_EALIGN;
-
-    fp4idx::LogitsParams p{};
+    p = fp4idx::LogitsParams{};
     p.q = q_fp4;
     p.q_rs = q_row_stride;
     p.qs = q_scale;
@@ -94,7 +93,82 @@ int fp4idx_logits_paged(int fmt,
     p.fmt = fmt;
     p.G = G;
     p.R = H / Hkv;
+    return FP4IDX_OK;
+}
+
+}  // namespace
+
+int fp4idx_logits_paged(int fmt,
+                        const uint8_t* q_fp4, int64_t q_row_stride,
+                        const uint8_t* q_scale, int64_t qs_row_stride,
+                        const float* w, int64_t w_row_stride,
+                        const uint8_t* k_fp4, int64_t k_page_stride,
+                        const uint8_t* k_scale, int64_t ks_page_stride,
+                        const int32_t* block_table, int64_t bt_row_stride,
+                        const int32_t* cu_seqlens_q, const int32_t* row_lens,
+                        int T, int B, int H, int Hkv, int page_size, int num_pages,
+                        int table_width, int out_cols,
+                        float* logits, int64_t out_row_stride,
+                        void* stream) {
+    fp4idx::LogitsParams p;
+    const int rc = logits_params(fmt, q_fp4, q_row_stride, q_scale, qs_row_stride, w, w_row_stride,
+                                 k_fp4, k_page_stride, k_scale, ks_page_stride, block_table,
+                                 bt_row_stride, cu_seqlens_q, row_lens, T, B, H, Hkv, page_size,
+                                 num_pages, table_width, out_cols, logits, out_row_stride, true, p);
+    if (rc != FP4IDX_OK) return rc < 0 ? FP4IDX_OK : rc;
     return hip_status(fp4idx::launch_logits(p, (hipStream_t)stream));
+}
+
+size_t fp4idx_logits_topk_workspace_bytes(int fmt, int T, int B, int H, int Hkv, int page_size,
+                                          int table_width, int out_cols, int k) {
+    if ((fmt != FP4IDX_MXFP4 && fmt != FP4IDX_NVFP4) || T <= 0 || B < 1 || H < 1 || Hkv < 1 ||
+        H % Hkv != 0 || H > 128 || (page_size != 64 && page_size != 128) || table_width < 0 ||
+        out_cols <= 0 || k < 1)
+        return 0;
+    fp4idx::LogitsParams p{};
+    p.T = T;
+    p.B = B;
+    p.H = H;
+    p.Hkv = Hkv;
+    p.page = page_size;
+    p.W = table_width;
+    p.out_cols = out_cols;
+    p.fmt = fmt;
+    p.G = fmt == FP4IDX_MXFP4 ? 4 : 8;
+    p.R = H / Hkv;
+    return fp4idx::logits_topk_workspace_bytes(p, k);
+}
+
+int fp4idx_logits_topk_paged(int fmt,
+                             const uint8_t* q_fp4, int64_t q_row_stride,
+                             const uint8_t* q_scale, int64_t qs_row_stride,
+                             const float* w, int64_t w_row_stride,
+                             const uint8_t* k_fp4, int64_t k_page_stride,
+                             const uint8_t* k_scale, int64_t ks_page_stride,
+                             const int32_t* block_table, int64_t bt_row_stride,
+                             const int32_t* cu_seqlens_q, const int32_t* row_lens,
+                             int T, int B, int H, int Hkv, int page_size, int num_pages,
+                             int table_width, int out_cols, int k,
+                             int32_t* out_idx, float* out_vals,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (k < 1) return FP4IDX_EINVAL;
+    if (k > 2048 || out_cols > (1 << 24)) return FP4IDX_EUNSUPPORTED;
+    fp4idx::LogitsParams p;
+    const int rc = logits_params(fmt, q_fp4, q_row_stride, q_scale, qs_row_stride, w, w_row_stride,
+                                 k_fp4, k_page_stride, k_scale, ks_page_stride, block_table,
+                                 bt_row_stride, cu_seqlens_q, row_lens, T, B, H, Hkv, page_size,
+                                 num_pages, table_width, out_cols, nullptr, 0, false, p);
+    if (rc > 0) return rc;
+    if (!out_idx && T > 0) return FP4IDX_EINVAL;
+    if (rc < 0) {  // no rows or no columns: nothing is selected
+        if (T == 0) return FP4IDX_OK;
+        return hip_status(fp4idx::launch_fill_empty_topk(T, k, out_idx, out_vals, (hipStream_t)stream));
+    }
+    const size_t need = fp4idx::logits_topk_workspace_bytes(p, k);
+    if (need == 0) return FP4IDX_EUNSUPPORTED;
+    if (!workspace || workspace_bytes < need || !aligned256(workspace)) return FP4IDX_EWORKSPACE;
+    return hip_status(fp4idx::launch_logits_topk(p, k, out_idx, out_vals, workspace,
+                                                 workspace_bytes, (hipStream_t)stream));
 }
 
 int fp4idx_block_scores(int fmt,

@@ -36,7 +36,24 @@ struct LogitsParams {
     int n_wgchunks;      // workgroups per row block (four chunks each)
     int n_rowblocks;
     int rows_per_block;  // RG: query rows sharing one A tile
+    // Fused scoring (top-k candidates instead of logits; `out` unused when cand is set):
+    // a score >= lo[t] (and > -inf) of row t is written as (value bits | column << 32)
+    // into cand[t][c0 + i], c0 = the first column of the wave's chunk and i the rank of
+    // that column among the chunk's kept columns; counts[t][chunk] receives the number
+    // kept.  flags (optional): only row blocks with a flagged row run, and a flagged row
+    // keeps every score.
+    const float* lo;
+    const int32_t* flags;
+    uint64_t* cand;
+    int64_t cand_rs;     // entries between candidate rows
+    int32_t* counts;
+    int counts_rs;       // ints between count rows
 };
+
+// Row blocks, tiles and column chunks of a logits launch (fills rows_per_block,
+// tiles_per_kv, n_tiles, n_rowblocks, ppw, n_wchunks, n_wgchunks).  false when the
+// head layout needs more A tiles than a block holds.
+bool plan_logits(LogitsParams& p);
 
 struct BlockParams {
     const uint8_t* q;
@@ -75,6 +92,12 @@ struct BlockTopkParams {
 };
 
 hipError_t launch_logits(const LogitsParams& p, hipStream_t stream);
+
+// Fused scorer + top-k: entry point pieces (fused_topk.hip).
+size_t logits_topk_workspace_bytes(const LogitsParams& p, int k);
+hipError_t launch_logits_topk(const LogitsParams& p, int k, int32_t* out_idx, float* out_vals,
+                              void* workspace, size_t ws_bytes, hipStream_t stream);
+hipError_t launch_fill_empty_topk(int T, int k, int32_t* out_idx, float* out_vals, hipStream_t stream);
 hipError_t launch_block_topk(const BlockTopkParams& p, hipStream_t stream);
 hipError_t launch_block_scores(const BlockParams& p, hipStream_t stream);
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);

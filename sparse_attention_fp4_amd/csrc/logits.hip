@@ -236,7 +236,9 @@ __device__ __forceinline__ v4f tile_dot_sel(const Operand<FMT>& a, uint32_t a_co
 
 // ---------------------------------------------------------------- the kernel
 // MKV: more than one key head (the tiles of key head hk only meet that head's slabs).
-template <int FMT, int RG, int NT, bool MKV>
+// FUSE: the scores are not stored; those at or above the row's threshold are kept as
+// top-k candidates (see LogitsParams).
+template <int FMT, int RG, int NT, bool MKV, bool FUSE>
 __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
     extern __shared__ __align__(16) uint8_t lds[];
     using L = ALayout<FMT, NT>;
@@ -258,6 +260,14 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
     const int t0 = rb * RG;
     const int nrows = min(RG, p.T - t0);
     const int t_last = t0 + nrows - 1;
+    if constexpr (FUSE) {
+        // second pass of the fused top-k: only row blocks holding a flagged row
+        if (p.flags) {
+            bool any = false;
+            for (int i = 0; i < nrows; i++) any = any || p.flags[t0 + i] != 0;
+            if (!any) return;
+        }
+    }
 
     const int n_pages_out = (p.out_cols + p.page - 1) / p.page;
     const int lp_begin = wc * p.ppw;
@@ -297,10 +307,51 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
         }
     };
     // -inf over the wave's pages [pi0, lp_end - lp_begin): no keys are read there
+    // (nothing to keep when fused)
     auto fill = [&](int pi0, bool st) {
+        if constexpr (FUSE) return;
         const float ninf[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
         for (int pi = pi0; pi < lp_end - lp_begin; pi++)
             for (int hf = 0; hf < halves; hf++) store_slab((lp_begin + pi) * p.page + hf * 64, ninf, st);
+    };
+    // ---- fused top-k candidates.  Lane (g, n) keeps those of its four scores that
+    // reach its row's threshold; ballots give every kept score its rank among the
+    // group's kept scores of the slab (column order), and the group's running count
+    // `run` places the slab after the earlier ones of the wave's chunk.  Stores go
+    // through a descriptor at row t0's candidates; a score not kept gets an offset past
+    // its range.
+    float lo_t = 0.f;
+    if constexpr (FUSE) {
+        const int tl = t0 + min(g % RG, max(nrows, 1) - 1);
+        lo_t = p.lo[tl];
+        if (p.flags && p.flags[tl] != 0) lo_t = -__builtin_inff();
+    }
+    const int64_t cand_c0 = (int64_t)lp_begin * p.page;  // the chunk's first column
+    const uint32_t cand_range = (uint32_t)(((int64_t)(RG - 1) * p.cand_rs + p.out_cols) * 8);
+    auto append = [&](int colb, const float (&o)[4], bool st, int& run) {
+        bool kp[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; tt++) kp[tt] = st && o[tt] >= lo_t && o[tt] > -__builtin_inff();
+        const uint64_t gmask = 0xffffull << (16 * g);
+        const uint64_t below = gmask & ((1ull << lane) - 1ull);
+        int pre = 0, tot = 0;
+#pragma unroll
+        for (int tt = 0; tt < 4; tt++) {
+            const uint64_t b = __ballot(kp[tt]);
+            pre += __popcll(b & below);
+            tot += __popcll(b & gmask);
+        }
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.cand + (int64_t)t0 * p.cand_rs, cand_range);
+        const int64_t base = (int64_t)(g % RG) * p.cand_rs + cand_c0 + run + pre;
+        int j = 0;
+#pragma unroll
+        for (int tt = 0; tt < 4; tt++) {
+            const uint64_t e = (uint64_t)__float_as_uint(o[tt]) | ((uint64_t)(uint32_t)(colb + 4 * n + tt) << 32);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, e), rc,
+                                                  kp[tt] ? (uint32_t)((base + j) * 8) : kOffNone, 0, 0);
+            j += kp[tt] ? 1 : 0;
+        }
+        run += tot;
     };
 
     // ---- prologue.  Loads go out in the order their results are needed: the first
@@ -365,6 +416,10 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
         const int wg_col0 = (blockIdx.x - bq * p.n_wgchunks) * kWavesPerBlock * p.ppw * p.page;
         if (wg_col0 >= wg_max) {
             if (has_work) fill(0, lane_stores && g < nrows);
+            if constexpr (FUSE) {
+                if (has_work && n == 0 && lane_stores && g < nrows)
+                    p.counts[(int64_t)(t0 + g) * p.counts_rs + wc] = 0;
+            }
             return;
         }
     }
@@ -520,6 +575,7 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
             issue(1, b1);
         }
         const bool st_lane = lane_stores && row_ok;
+        int run = 0;  // kept candidates of this lane's row in the chunk (fused)
         // ---- the wave's slabs: three buffers in a ring keep two slabs of keys in flight
         // while one is computed (slab s lives in buffer s % 3)
         // head sums: acc[set][key tile][i]; tiles 8*set .. 8*set+7 go to one set, so
@@ -636,7 +692,8 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
 #pragma unroll
                 for (int tt = 0; tt < 4; tt++) o[tt] = -__builtin_inff();
             }
-            store_slab(col0 - 4 * n, o, st_lane);
+            if constexpr (FUSE) append(col0 - 4 * n, o, st_lane, run);
+            else store_slab(col0 - 4 * n, o, st_lane);
         };
         // The loop body has no early exit: the last one or two slabs are computed
         // after it.  (An exit taken in the middle of the body would join the loop
@@ -664,21 +721,29 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
         if (s + 1 < n_vis) compute(s + 1, b1);
 #endif
         fill(vis_pages, st_lane);
+        if constexpr (FUSE) {
+            if (st_lane && n == 0) p.counts[(int64_t)t_out * p.counts_rs + wc] = run;
+        }
         t_seg = seg_end;
     }
 }
-template <int FMT, int RG, int NT>
-hipError_t launch3(const LogitsParams& p, hipStream_t stream) {
+template <int FMT, int RG, int NT, bool FUSE>
+hipError_t launch4(const LogitsParams& p, hipStream_t stream) {
     const int64_t blocks = (int64_t)p.n_rowblocks * p.n_wgchunks;
     if (blocks <= 0) return hipSuccess;
     const size_t lds = ALayout<FMT, NT>::kBytes;
     if (p.Hkv == 1)
-        hipLaunchKernelGGL((k_logits<FMT, RG, NT, false>), dim3((unsigned)blocks), dim3(kThreads), lds,
-                           stream, p);
+        hipLaunchKernelGGL((k_logits<FMT, RG, NT, false, FUSE>), dim3((unsigned)blocks), dim3(kThreads),
+                           lds, stream, p);
     else
-        hipLaunchKernelGGL((k_logits<FMT, RG, NT, true>), dim3((unsigned)blocks), dim3(kThreads), lds,
-                           stream, p);
+        hipLaunchKernelGGL((k_logits<FMT, RG, NT, true, FUSE>), dim3((unsigned)blocks), dim3(kThreads),
+                           lds, stream, p);
     return hipGetLastError();
+}
+
+template <int FMT, int RG, int NT>
+hipError_t launch3(const LogitsParams& p, hipStream_t stream) {
+    return p.cand ? launch4<FMT, RG, NT, true>(p, stream) : launch4<FMT, RG, NT, false>(p, stream);
 }
 
 template <int FMT, int RG>
@@ -702,8 +767,7 @@ hipError_t launch1(const LogitsParams& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_logits(const LogitsParams& p_in, hipStream_t stream) {
-    LogitsParams p = p_in;
+bool plan_logits(LogitsParams& p) {
     // Rows per A-tile group: as many as the average request holds (up to 4), reduced
     // while the block would need more than FP4IDX_LOGITS_MAX_NT A tiles (at most 16;
     // they live in LDS).  Any choice is correct; rows of different requests in one block
@@ -718,7 +782,7 @@ hipError_t launch_logits(const LogitsParams& p_in, hipStream_t stream) {
         if (p.n_tiles <= FP4IDX_LOGITS_MAX_NT || rg == 1) break;
         rg >>= 1;
     }
-    if (p.n_tiles > 8 * (rg == 1 ? 1 : 2)) return hipErrorInvalidValue;  // H <= 128 is checked by the caller
+    if (p.n_tiles > 8 * (rg == 1 ? 1 : 2)) return false;  // H <= 128 is checked by the caller
     p.rows_per_block = rg;
     p.n_rowblocks = (p.T + rg - 1) / rg;
     const int n_pages_out = (p.out_cols + p.page - 1) / p.page;
@@ -732,6 +796,12 @@ hipError_t launch_logits(const LogitsParams& p_in, hipStream_t stream) {
     p.ppw = (int)ppw;
     p.n_wchunks = (n_pages_out + p.ppw - 1) / p.ppw;
     p.n_wgchunks = (p.n_wchunks + kWavesPerBlock - 1) / kWavesPerBlock;
+    return true;
+}
+
+hipError_t launch_logits(const LogitsParams& p_in, hipStream_t stream) {
+    LogitsParams p = p_in;
+    if (!plan_logits(p)) return hipErrorInvalidValue;
     if (p.n_wchunks == 0 || p.n_rowblocks == 0) return hipSuccess;
     return p.fmt == 0 ? launch1<0>(p, stream) : launch1<1>(p, stream);
 }

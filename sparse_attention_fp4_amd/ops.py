@@ -60,15 +60,9 @@ def _u8(t):
     raise ValueError(f"expected a 1-byte dtype, got {t.dtype}")
 
 
-def logits_paged(q_fp4, q_scale, w, k_fp4, k_scale, block_table, cu_seqlens_q, row_lens, *,
-                 fmt="mxfp4", out_cols: int, out: Optional[torch.Tensor] = None,
-                 k_page_stride: Optional[int] = None, ks_page_stride: Optional[int] = None):
-    """Weighted-ReLU logits [T, out_cols] fp32 (-inf where invisible).
-
-    q_fp4 [T,H,64] u8 (row stride may exceed H*64), q_scale [T,H,G] u8, w [T,H] fp32,
-    k_fp4 [P,Hkv,page,64] u8, k_scale [P,Hkv,page,G] u8, block_table [B,W] int32,
-    cu_seqlens_q [B+1] int32, row_lens [T] int32.
-    """
+def _logits_args(q_fp4, q_scale, w, k_fp4, k_scale, block_table, cu_seqlens_q, row_lens, fmt,
+                 k_page_stride, ks_page_stride):
+    """Checked tensors and the scalar arguments shared by the logits entry points."""
     f = _fmt(fmt)
     G = _groups(f)
     q_fp4, q_scale, k_fp4, k_scale = _u8(q_fp4), _u8(q_scale), _u8(k_fp4), _u8(k_scale)
@@ -100,21 +94,71 @@ def logits_paged(q_fp4, q_scale, w, k_fp4, k_scale, block_table, cu_seqlens_q, r
             raise ValueError(f"{name} must be contiguous inside each page")
     if block_table.stride(1) != 1 or not cu_seqlens_q.is_contiguous() or not row_lens.is_contiguous():
         raise ValueError("metadata tensors must be contiguous")
+    kps = k_page_stride if k_page_stride is not None else (k_fp4.stride(0) if P > 0 else Hkv * page * 64)
+    ksps = ks_page_stride if ks_page_stride is not None else (k_scale.stride(0) if P > 0 else Hkv * page * G)
+    args = (f, _ptr(q_fp4), q_fp4.stride(0), _ptr(q_scale), q_scale.stride(0), _ptr(w), w.stride(0),
+            _ptr(k_fp4), kps, _ptr(k_scale), ksps, _ptr(block_table), block_table.stride(0),
+            _ptr(cu_seqlens_q), _ptr(row_lens), T, B, H, Hkv, page, P, W)
+    return args, dict(dev=dev, T=T, B=B, H=H, Hkv=Hkv, page=page, W=W, fmt=f)
+
+
+def logits_paged(q_fp4, q_scale, w, k_fp4, k_scale, block_table, cu_seqlens_q, row_lens, *,
+                 fmt="mxfp4", out_cols: int, out: Optional[torch.Tensor] = None,
+                 k_page_stride: Optional[int] = None, ks_page_stride: Optional[int] = None):
+    """Weighted-ReLU logits [T, out_cols] fp32 (-inf where invisible).
+
+    q_fp4 [T,H,64] u8 (row stride may exceed H*64), q_scale [T,H,G] u8, w [T,H] fp32,
+    k_fp4 [P,Hkv,page,64] u8, k_scale [P,Hkv,page,G] u8, block_table [B,W] int32,
+    cu_seqlens_q [B+1] int32, row_lens [T] int32.
+    """
+    args, d = _logits_args(q_fp4, q_scale, w, k_fp4, k_scale, block_table, cu_seqlens_q, row_lens,
+                           fmt, k_page_stride, ks_page_stride)
+    T, dev = d["T"], d["dev"]
     if out is None:
         out = torch.empty((T, out_cols), dtype=torch.float32, device=dev)
     else:
         _need(out, "out", torch.float32, 2, dev)
         if out.shape != (T, out_cols) or out.stride(1) != 1:
             raise ValueError("out must be [T, out_cols] with unit column stride")
-    kps = k_page_stride if k_page_stride is not None else (k_fp4.stride(0) if P > 0 else Hkv * page * 64)
-    ksps = ks_page_stride if ks_page_stride is not None else (k_scale.stride(0) if P > 0 else Hkv * page * G)
-    rc = lib().fp4idx_logits_paged(
-        f, _ptr(q_fp4), q_fp4.stride(0), _ptr(q_scale), q_scale.stride(0), _ptr(w), w.stride(0),
-        _ptr(k_fp4), kps, _ptr(k_scale), ksps, _ptr(block_table), block_table.stride(0),
-        _ptr(cu_seqlens_q), _ptr(row_lens), T, B, H, Hkv, page, P, W, out_cols,
-        _ptr(out), out.stride(0), _stream())
+    rc = lib().fp4idx_logits_paged(*args, out_cols, _ptr(out), out.stride(0), _stream())
     check("fp4idx_logits_paged", rc)
     return out
+
+
+def logits_topk_workspace_bytes(fmt, T, B, H, Hkv, page_size, table_width, out_cols, k) -> int:
+    return int(lib().fp4idx_logits_topk_workspace_bytes(_fmt(fmt), T, B, H, Hkv, page_size,
+                                                        table_width, out_cols, k))
+
+
+def logits_topk_paged(q_fp4, q_scale, w, k_fp4, k_scale, block_table, cu_seqlens_q, row_lens, *,
+                      fmt="mxfp4", out_cols: int, k: int, out_idx=None, out_vals=None,
+                      want_vals=True, workspace=None, k_page_stride: Optional[int] = None,
+                      ks_page_stride: Optional[int] = None):
+    """Top-k columns of the weighted-ReLU logits without writing the logits: exactly
+    topk(logits_paged(...), k, row_lens) -> (idx [T, k] int32 in increasing column order,
+    -1 padded; vals [T, k] fp32 or None).  workspace: optional uint8 device tensor of at
+    least logits_topk_workspace_bytes(...) bytes (allocated when omitted)."""
+    args, d = _logits_args(q_fp4, q_scale, w, k_fp4, k_scale, block_table, cu_seqlens_q, row_lens,
+                           fmt, k_page_stride, ks_page_stride)
+    T, dev = d["T"], d["dev"]
+    if out_idx is None:
+        out_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if out_vals is None and want_vals:
+        out_vals = torch.empty((T, k), dtype=torch.float32, device=dev)
+    for name, t, dt in (("out_idx", out_idx, torch.int32), ("out_vals", out_vals, torch.float32)):
+        if t is not None:
+            _need(t, name, dt, 2, dev)
+            if t.shape != (T, k) or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous [T, k] tensor")
+    need = logits_topk_workspace_bytes(d["fmt"], T, d["B"], d["H"], d["Hkv"], d["page"], d["W"],
+                                       out_cols, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = lib().fp4idx_logits_topk_paged(*args, out_cols, k, _ptr(out_idx), _ptr(out_vals),
+                                        _ptr(workspace), ws_bytes, _stream())
+    check("fp4idx_logits_topk_paged", rc)
+    return out_idx, out_vals
 
 
 def block_scores(q_fp4, k_fp4, q_scale, k_scale, cu_seqlens_q, cu_seqlens_k, cu_page_offsets, *,

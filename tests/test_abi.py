@@ -167,3 +167,44 @@ def _qsa_decode(**kw):
 ])
 def test_qsa_decode_argument_errors(kw, code):
     assert _qsa_decode(**kw) == code
+
+
+def _fused(ws_bytes=None, ws_off=0, **kw):
+    L = _lib.lib()
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = ctypes.cast(buf, ctypes.c_void_p).value
+    p16 = (p + 255) & ~255
+    a = dict(fmt=0, q=p16, qrs=32 * 64, qs=p16, qsrs=32 * 4, w=p16, wrs=32, k=p16,
+             kps=64 * 64, ks=p16, ksps=64 * 4, bt=p16, btrs=4, cu=p16, lens=p16, T=4, B=1, H=32,
+             Hkv=1, page=64, P=4, W=4, out_cols=256, kk=16, idx=p16, vals=None)
+    a.update(kw)
+    need = L.fp4idx_logits_topk_workspace_bytes(a["fmt"], a["T"], a["B"], a["H"], a["Hkv"],
+                                                a["page"], a["W"], a["out_cols"], a["kk"])
+    return L.fp4idx_logits_topk_paged(
+        a["fmt"], a["q"], a["qrs"], a["qs"], a["qsrs"], a["w"], a["wrs"], a["k"], a["kps"],
+        a["ks"], a["ksps"], a["bt"], a["btrs"], a["cu"], a["lens"], a["T"], a["B"], a["H"],
+        a["Hkv"], a["page"], a["P"], a["W"], a["out_cols"], a["kk"], a["idx"], a["vals"],
+        p16 + ws_off if ws_bytes != 0 else None, need if ws_bytes is None else ws_bytes, None)
+
+
+def test_logits_topk_workspace_size():
+    L = _lib.lib()
+    f = L.fp4idx_logits_topk_workspace_bytes
+    small = f(0, 4, 1, 32, 1, 64, 32, 2048, 256)
+    big = f(0, 4, 1, 32, 1, 64, 64, 4096, 256)
+    assert 0 < small < big
+    # the kept-score buffer (8 bytes per column and row) dominates: the logits would be 4
+    assert big >= 4 * 4096 * 8
+    assert f(0, 4, 1, 30, 4, 64, 32, 2048, 256) == 0       # H % Hkv != 0
+    assert f(0, 4, 1, 32, 1, 32, 32, 2048, 256) == 0       # page size
+    assert f(0, 0, 1, 32, 1, 64, 32, 2048, 256) == 0       # no rows
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kk=0), 1), (dict(kk=2049), 2), (dict(out_cols=(1 << 24) + 64), 2), (dict(fmt=3), 1),
+    (dict(H=6, Hkv=4), 1), (dict(page=32), 2), (dict(idx=None), 1), (dict(q=None), 1),
+    (dict(qrs=32 * 64 + 8), 3), (dict(ws_bytes=0), 5), (dict(ws_bytes=64), 5),
+    (dict(ws_off=16), 5), (dict(T=0), 0),
+])
+def test_logits_topk_argument_errors(kw, code):
+    assert _fused(**kw) == code
