@@ -50,6 +50,7 @@ KERNEL_SOURCES = {"logits": [CSRC + "logits.hip"] + COMMON_SOURCES,
                   "topk": [CSRC + "topk.hip", CSRC + "topk_long.hip", CSRC + "topk_stream.hip"] + COMMON_SOURCES,
                   "block_scores": [CSRC + "block_scores.hip"] + COMMON_SOURCES,
                   "block_topk": [CSRC + "block_topk.hip"] + COMMON_SOURCES,
+                  "logits_topk": [CSRC + "logits.hip", CSRC + "fused_topk.hip"] + COMMON_SOURCES,
                   "qsa_slots": [CSRC + "qsa.hip"] + COMMON_SOURCES,
                   "qsa_decode": [CSRC + "qsa.hip"] + COMMON_SOURCES}
 
@@ -63,6 +64,9 @@ def parse():
     ap.add_argument("--workload", choices=["verify", "batched", "prefill", "block", "qsa"],
                     default="verify")
     ap.add_argument("--topk", type=int, default=2048)
+    ap.add_argument("--fused", action="store_true",
+                    help="verify/batched/prefill: one fused scorer + top-k call per step "
+                         "(fp4idx_logits_topk_paged, no logits written) instead of logits + topk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-launches", type=int, default=None,
                     help="launches per timed graph replay, per entry point, for the roofline")
@@ -140,10 +144,16 @@ def logits_workload(args, torch, fp4, wl, dev):
                 ks=up(case.k_scale), bt=up(case.block_table), cu=up(case.cu_seqlens_q),
                 lens=up(case.row_lens))
     set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + T * out_cols * 4
+    fused_ws = (fp4.logits_topk_workspace_bytes("mxfp4", T, case.B, H, case.Hkv, case.page_size,
+                                                case.block_table.shape[1], out_cols, k)
+                if args.fused else 0)
 
     def make_set():
         s = {n: (t if n in ("cu", "lens", "bt") else t.clone()) for n, t in base.items()}
-        s["out"] = torch.empty((T, out_cols), dtype=torch.float32, device=dev)
+        if args.fused:
+            s["fws"] = torch.empty(fused_ws, dtype=torch.uint8, device=dev)
+        else:
+            s["out"] = torch.empty((T, out_cols), dtype=torch.float32, device=dev)
         s["idx"] = torch.empty((T, k), dtype=torch.int32, device=dev)
         return s
 
@@ -156,6 +166,11 @@ def logits_workload(args, torch, fp4, wl, dev):
 
     def topk(s):
         fp4.topk(s["out"], k, s["lens"], out_idx=s["idx"], want_vals=False, workspace=ws)
+
+    def logits_topk(s):
+        fp4.logits_topk_paged(s["q"], s["qs"], s["w"], s["k"], s["ks"], s["bt"], s["cu"],
+                              s["lens"], fmt="mxfp4", out_cols=out_cols, k=k, out_idx=s["idx"],
+                              want_vals=False, workspace=s["fws"])
 
     # algorithmic work: each input once, each output once; flops over visible pairs
     keys = case.unique_keys()
@@ -170,7 +185,15 @@ def logits_workload(args, torch, fp4, wl, dev):
         "logits": dict(bytes=logits_bytes, flops=2 * H * 128 * pairs,
                        bound="mfma" if args.workload == "prefill" else "hbm", dtype="fp4"),
         "topk": dict(bytes=topk_bytes, flops=0, bound="hbm", dtype=None),
+        # fused: the scorer's inputs in, the indices out (no logits in between)
+        "logits_topk": dict(bytes=logits_bytes - T * out_cols * 4 + T * k * 4,
+                            flops=2 * H * 128 * pairs,
+                            bound="mfma" if args.workload == "prefill" else "hbm", dtype="fp4"),
     }
+    calls = {"logits_topk": logits_topk} if args.fused else {"logits": logits, "topk": topk}
+    if args.fused:
+        name += "_fused"
+        desc += "; fused scorer + top-k (no logits written)"
 
     def cpu_baseline():
         from oracle import oracle as orc
@@ -199,7 +222,7 @@ def logits_workload(args, torch, fp4, wl, dev):
                     sample=f"{what}, {reps} run(s) in {total:.1f} s")
 
     return dict(name=name, desc=desc, set_bytes=set_bytes, make_set=make_set,
-                calls={"logits": logits, "topk": topk}, work=work, pairs=pairs,
+                calls=calls, work=work, pairs=pairs,
                 steps=steps, warmup=warmup, launches=launches, cpu_baseline=cpu_baseline,
                 config={"ctx": args.ctx if args.workload == "verify" else
                         ("4096..131072" if args.workload == "batched" else 32768),

@@ -33,7 +33,6 @@ namespace {
 constexpr int kSampleStride = 16;   // one logical page in 16 is scored first
 constexpr int kSelThreads = 256;
 constexpr int kMaxChunks = 8192;    // column chunks per row (the scorer's plan stays below)
-constexpr int kStageCap = 6144;     // kept entries of a row staged in LDS
 constexpr int kSortCap = 2048;      // largest k
 
 __device__ __forceinline__ uint32_t order_key(uint32_t u) {
@@ -72,7 +71,12 @@ __global__ __launch_bounds__(256) void k_sample_table(const SampleParams p) {
     }
 }
 
-// block-wide helpers for 256 threads
+// ---- wave-level reductions and scans (one wave handles one row; no workgroup barriers)
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+    return v;
+}
 __device__ __forceinline__ int wave_incl_scan(int v) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -82,37 +86,172 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
     }
     return v;
 }
+__device__ __forceinline__ void wave_minmax(uint32_t& lo, uint32_t& hi) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, d));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, d));
+    }
+}
 
-// One wave finds, in a 256-bin histogram, the digit where the count from the top
-// reaches `want` (bins read from LDS; lane l owns bins 255-4l .. 252-4l).
-__device__ __forceinline__ void pick_digit(const int* hist, int want, int& digit, int& above) {
+constexpr int kBins = 1024;  // histogram bins of one narrowing step
+
+
+// One narrowing step of a wave over the keys in [klo, khi] (visit(fn) calls fn(key) for
+// each key of the lane): bin (key - klo) >> sh into at most 1024 bins of the wave's LDS
+// histogram and find the bin holding the want-th largest key (want counted from the top
+// of the range, 1 <= want <= the keys in the range); `above` receives the number of keys
+// in higher bins.  Offsets from the range's bottom spread close values over many bins,
+// so few lanes add to one bin at a time.
+template <class Visit>
+__device__ __forceinline__ void wave_narrow(Visit visit, uint32_t klo, uint32_t khi, int want,
+                                            int* hist, int& bin, int& above, int& sh) {
     const int lane = threadIdx.x & 63;
+    const uint32_t span = khi - klo;
+    sh = span >= (uint32_t)kBins ? (32 - __builtin_clz(span)) - 10 : 0;
+#pragma unroll
+    for (int i = 0; i < kBins / 64; i++) hist[lane * (kBins / 64) + i] = 0;
+    __builtin_amdgcn_wave_barrier();
+    const int shv = sh;
+    visit([&](uint32_t key) {
+        if (key >= klo && key <= khi) atomicAdd(&hist[(key - klo) >> shv], 1);
+    });
+    __builtin_amdgcn_wave_barrier();
+    // lane l holds bins 1023-16l .. 1008-16l, in descending order
+    constexpr int kPerLane = kBins / 64;
+    int c[kPerLane], s = 0;
+#pragma unroll
+    for (int i = 0; i < kPerLane; i++) {
+        c[i] = hist[kBins - 1 - kPerLane * lane - i];
+        s += c[i];
+    }
+    const int incl = wave_incl_scan(s);
+    const int excl = incl - s;
+    const unsigned long long hit = __ballot(excl < want && want <= incl);
+    const int src = __ffsll((long long)hit) - 1;
+    int b = 0, ab = 0, run = excl;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < kPerLane; i++) {
+        if (!found && run + c[i] >= want) {
+            b = kBins - 1 - kPerLane * lane - i;
+            ab = run;
+            found = true;
+        }
+        run += c[i];
+    }
+    bin = __shfl(b, src);
+    above = __shfl(ab, src);
+    __builtin_amdgcn_wave_barrier();
+}
+
+// The want-th largest key (1 <= want <= the keys visited) of a wave: narrowing steps
+// from [kmin, kmax], each 1024 times narrower.  *above receives the number of keys
+// above the result.
+template <class Visit>
+__device__ __forceinline__ uint32_t wave_nth_largest(Visit visit, uint32_t kmin, uint32_t kmax,
+                                                     int want, int* hist, int* above_out) {
+    int above = 0;
+    while (kmin < kmax) {  // wave-uniform
+        int bin, ab, sh;
+        wave_narrow(visit, kmin, kmax, want - above, hist, bin, ab, sh);
+        above += ab;
+        const uint32_t nlo = kmin + ((uint32_t)bin << sh);
+        kmax = min(kmax, nlo + ((1u << sh) - 1u));
+        kmin = nlo;
+    }
+    *above_out = above;
+    return kmin;
+}
+
+__device__ __forceinline__ int block_sum(int v, int* red) {
+    v = wave_sum(v);
+    __syncthreads();  // the previous use of red is over
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return red[0] + red[1] + red[2] + red[3];
+}
+// exclusive prefix of v over the workgroup's lanes in order; *total receives the sum
+__device__ __forceinline__ int block_excl_scan(int v, int* red, int* total) {
+    const int incl = wave_incl_scan(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 63) red[threadIdx.x >> 6] = incl;
+    __syncthreads();
+    const int w = threadIdx.x >> 6;
+    int base = 0;
+    for (int i = 0; i < w; i++) base += red[i];
+    *total = red[0] + red[1] + red[2] + red[3];
+    return base + incl - v;
+}
+
+__device__ __forceinline__ void block_minmax(uint32_t& lo, uint32_t& hi, uint32_t* red8) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, d));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, d));
+    }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red8[threadIdx.x >> 6] = lo, red8[4 + (threadIdx.x >> 6)] = hi;
+    __syncthreads();
+    lo = min(min(red8[0], red8[1]), min(red8[2], red8[3]));
+    hi = max(max(red8[4], red8[5]), max(red8[6], red8[7]));
+}
+
+
+struct NarrowLds {
+    int hist[kBins];
+    int red[4];
+    uint32_t red8[8];
+    int misc[2];
+};
+
+// One narrowing step over the keys in [klo, khi] (visit(fn) calls fn(key) for each key
+// of the lane): bin (key - klo) >> sh into at most 1024 bins and find the bin holding
+// the want-th largest key (want counted from the top of the range, 1 <= want <= the
+// number of keys in the range); `above` receives the number of keys in higher bins.
+// Offsets from the range's bottom spread close values over many bins, so few lanes
+// add to one bin at a time.
+template <class Visit>
+__device__ __forceinline__ void narrow(Visit visit, uint32_t klo, uint32_t khi, int want,
+                                       NarrowLds& L, int& bin, int& above, int& sh) {
+    const uint32_t span = khi - klo;
+    sh = span >= (uint32_t)kBins ? (32 - __clz((int)span)) - 10 : 0;
+    if (span >= 0x80000000u) sh = 22;
+    for (int i = threadIdx.x; i < kBins; i += 256) L.hist[i] = 0;
+    __syncthreads();
+    const int shv = sh;
+    visit([&](uint32_t key) {
+        if (key >= klo && key <= khi) atomicAdd(&L.hist[(key - klo) >> shv], 1);
+    });
+    __syncthreads();
+    // lane t holds bins 1023-4t .. 1020-4t, in descending order
     int c[4], s = 0;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        c[i] = hist[255 - 4 * lane - i];
+        c[i] = L.hist[kBins - 1 - 4 * (int)threadIdx.x - i];
         s += c[i];
     }
-    const int incl = wave_incl_scan(s);  // keys in bins >= 252 - 4 lane
-    const int excl = incl - s;
-    const unsigned long long hit = __ballot(incl >= want && excl < want);
-    const int src = hit ? __ffsll((long long)hit) - 1 : 63;
-    int d = 0, a = 0;
-    if (lane == src) {
+    int tot;
+    const int excl = block_excl_scan(s, L.red, &tot);
+    if (excl < want && want <= excl + s) {
         int run = excl;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             if (run + c[i] >= want) {
-                d = 255 - 4 * lane - i;
-                a = run;
+                L.misc[0] = kBins - 1 - 4 * (int)threadIdx.x - i;
+                L.misc[1] = run;
                 break;
             }
             run += c[i];
         }
     }
-    digit = __shfl(d, src);
-    above = __shfl(a, src);
+    __syncthreads();
+    bin = L.misc[0];
+    above = L.misc[1];
+    __syncthreads();
 }
+
+constexpr int kThrPer = 48;  // sampled scores per lane held in registers (3072 per row)
 
 struct ThresholdParams {
     const float* slog;   // [T][cols_s]
@@ -121,50 +260,46 @@ struct ThresholdParams {
     float* lo;           // [T]
 };
 
-// lo of each row: one wave per row, four digit passes over its sampled scores.
+// lo of each row, one wave per row: the row's sampled scores (at most 3072; a longer
+// sample is thinned to every stride-th score, with m divided by the stride) in
+// registers; lo = their m-th largest, or -inf when fewer than m are finite.
 __global__ __launch_bounds__(256) void k_threshold(const ThresholdParams p) {
-    __shared__ int hist[4][256];
+    __shared__ int hist_all[4][kBins];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave;
-    if (t >= p.T) return;  // whole wave: no block barrier below
-    int* h = hist[wave];
+    if (t >= p.T) return;  // whole wave; nothing below waits for other waves
+    int* hist = hist_all[wave];
     const float* row = p.slog + (int64_t)t * p.cols_s;
     const int S = max(0, min(p.lens_s[t], p.cols_s));
-    uint32_t prefix = 0, mask = 0;
-    int want = p.m;
-    bool enough = true;
-    for (int pass = 0; pass < 4; pass++) {
-        const int shift = 24 - 8 * pass;
+    constexpr int per_wave = 64 * kThrPer;
+    const int stride = S > per_wave ? (S + per_wave - 1) / per_wave : 1;
+    const int n = (S + stride - 1) / stride;
+    const int m = (p.m + stride - 1) / stride;
+    uint32_t key[kThrPer];
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+    int finite = 0;
 #pragma unroll
-        for (int i = 0; i < 4; i++) h[lane * 4 + i] = 0;
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        for (int c = lane; c < S; c += 64) {
-            const float v = row[c];
-            if (!(v > -__builtin_inff())) continue;  // -inf and NaN are never chosen
-            const uint32_t key = order_key(__float_as_uint(v));
-            if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        if (pass == 0) {
-            int tot = 0;
-#pragma unroll
-            for (int i = 0; i < 4; i++) tot += h[lane * 4 + i];
-            tot = wave_incl_scan(tot);
-            if (__shfl(tot, 63) < want) {
-                enough = false;
-                break;
-            }
-        }
-        int digit, above;
-        pick_digit(h, want, digit, above);
-        want -= above;
-        prefix |= (uint32_t)digit << shift;
-        mask |= 255u << shift;
-        __builtin_amdgcn_wave_barrier();
+    for (int i = 0; i < kThrPer; i++) {
+        const int j = lane + 64 * i;
+        const float v = j < n ? row[(int64_t)j * stride] : -__builtin_inff();
+        const bool ok = v > -__builtin_inff();  // -inf and NaN are never chosen
+        key[i] = ok ? order_key(__float_as_uint(v)) : 0u;
+        finite += ok ? 1 : 0;
+        kmin = ok ? min(kmin, key[i]) : kmin;
+        kmax = ok ? max(kmax, key[i]) : kmax;
     }
-    if (lane == 0) p.lo[t] = enough ? __uint_as_float(key_value_bits(prefix)) : -__builtin_inff();
+    if (wave_sum(finite) < m) {
+        if (lane == 0) p.lo[t] = -__builtin_inff();
+        return;
+    }
+    wave_minmax(kmin, kmax);
+    int above;
+    const uint32_t kth = wave_nth_largest([&](auto&& fn) {
+#pragma unroll
+        for (int i = 0; i < kThrPer; i++)
+            if (key[i] != 0u) fn(key[i]);
+    }, kmin, kmax, m, hist, &above);
+    if (lane == 0) p.lo[t] = __uint_as_float(key_value_bits(kth));
 }
 
 struct SelectParams {
@@ -178,54 +313,42 @@ struct SelectParams {
     int T, k;
     int32_t* out_idx;       // [T][k]
     float* out_vals;        // [T][k] or null
-    int ent_off, sel_off;   // dynamic LDS: entry staging and sorting buffers (bytes)
-    int P;                  // sorting network width (power of two >= k, >= 64)
 };
 
-// Dynamic LDS of the selection: 256 histogram bins, 8 scalars, the prefix of the chunk
-// counts (nchunks + 1 ints), kStageCap staged entries, P sorting slots.
-constexpr int kSelPreOff = (256 + 8) * 4;
+constexpr int kSelPer = 24;  // kept entries per lane held in registers (6144 per row)
 
-// Exact top-k of one row's kept entries: one 256-lane workgroup per row.
+// Exact top-k of one row's kept entries: one 256-lane workgroup per row.  The entries
+// of the row, in chunk order and in column order inside a chunk, are in increasing
+// column order; lane l takes a contiguous range of them.  The k-th largest key comes
+// from a bit-by-bit count; the ties at it are taken in column order and every chosen
+// entry's output position is its rank in that order (two prefix scans, no sorting).
 __global__ __launch_bounds__(kSelThreads) void k_fused_select(const SelectParams p) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    struct {
-        int* hist;
-        int* misc;
-        int* pre;
-        uint64_t* ent;
-    } L = {reinterpret_cast<int*>(smem), reinterpret_cast<int*>(smem) + 256,
-           reinterpret_cast<int*>(smem + kSelPreOff), reinterpret_cast<uint64_t*>(smem + p.ent_off)};
-    uint64_t* const sel = reinterpret_cast<uint64_t*>(smem + p.sel_off);
+    extern __shared__ __align__(16) int pre[];  // [nchunks + 1] prefix of the chunk counts
+    __shared__ NarrowLds L;
+    int* const red = L.red;
     const int t = blockIdx.x;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x;
     if (p.second && p.flags[t] == 0) return;  // uniform
 
-    // ---- prefix of the chunk counts
+    // ---- prefix of the chunk counts (lane l takes consecutive chunks)
     const int nch = p.nchunks;
     const int32_t* cnt = p.counts + (int64_t)t * p.counts_rs;
-    constexpr int kPer = (kMaxChunks + kSelThreads - 1) / kSelThreads;
-    int loc[kPer], sum = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; i++) {
-        const int c = tid * kPer + i;
-        loc[i] = c < nch ? cnt[c] : 0;
-        sum += loc[i];
+    const int cper = (nch + kSelThreads - 1) / kSelThreads;
+    int sum = 0;
+    for (int i = 0; i < cper; i++) {
+        const int c = tid * cper + i;
+        sum += c < nch ? cnt[c] : 0;
     }
-    int incl = wave_incl_scan(sum);
-    if (lane == 63) L.misc[wave] = incl;
-    __syncthreads();
-    int wbase = 0;
-    for (int w = 0; w < wave; w++) wbase += L.misc[w];
-    const int N = L.misc[0] + L.misc[1] + L.misc[2] + L.misc[3];
-    int run = wbase + incl - sum;
-#pragma unroll
-    for (int i = 0; i < kPer; i++) {
-        const int c = tid * kPer + i;
-        if (c < nch) L.pre[c] = run;
-        run += loc[i];
+    int N;
+    int run = block_excl_scan(sum, red, &N);
+    for (int i = 0; i < cper; i++) {
+        const int c = tid * cper + i;
+        if (c < nch) {
+            pre[c] = run;
+            run += cnt[c];
+        }
     }
-    if (tid == 0) L.pre[nch] = N;
+    if (tid == 0) pre[nch] = N;
     const float lo_t = p.second ? -__builtin_inff() : p.lo[t];
     if (!p.second) {
         const bool flag = lo_t > -__builtin_inff() && N < p.k;
@@ -235,126 +358,145 @@ __global__ __launch_bounds__(kSelThreads) void k_fused_select(const SelectParams
     __syncthreads();
 
     const uint64_t* crow = p.cand + (int64_t)t * p.cand_rs;
-    auto fetch = [&](int i) -> uint64_t {  // entry i of the row (chunk by binary search)
-        int a = 0, b = nch;  // pre[a] <= i < pre[b]
+    auto fetch = [&](int i) -> uint64_t {  // entry i of the row (its chunk by binary search)
+        int a = 0, b = nch;                // pre[a] <= i < pre[b]
         while (b - a > 1) {
             const int mid = (a + b) >> 1;
-            if (L.pre[mid] <= i) a = mid;
+            if (pre[mid] <= i) a = mid;
             else b = mid;
         }
-        return crow[(int64_t)a * p.chunk_w + (i - L.pre[a])];
+        return crow[(int64_t)a * p.chunk_w + (i - pre[a])];
     };
-    const bool staged = N <= kStageCap;
-    if (staged) {
-        for (int i = tid; i < N; i += kSelThreads) L.ent[i] = fetch(i);
-        __syncthreads();
-    }
-    auto ent = [&](int i) -> uint64_t { return staged ? L.ent[i] : fetch(i); };
     auto key_of = [](uint64_t e) { return order_key((uint32_t)e); };
+    const int E = (N + kSelThreads - 1) / kSelThreads;  // entries per lane
+    const int i0 = tid * E, i1 = min(N, i0 + E);
+    const bool held = E <= kSelPer;                      // entries in registers
+    const int mine = max(0, i1 - i0);
+    uint64_t ent[kSelPer];
+    if (held) {
+        // the chunk of the lane's first entry by binary search, then forward: entries are
+        // consecutive, so each next one is in the same chunk or a later one
+        int a = 0;
+        if (mine > 0) {
+            int b = nch;
+            while (b - a > 1) {
+                const int mid = (a + b) >> 1;
+                if (pre[mid] <= i0) a = mid;
+                else b = mid;
+            }
+        }
+        int64_t off[kSelPer];
+#pragma unroll
+        for (int j = 0; j < kSelPer; j++) {
+            const int i = min(i0 + j, max(i1 - 1, i0));
+            while (a + 1 < nch && pre[a + 1] <= i) a++;
+            off[j] = (int64_t)a * p.chunk_w + (i - pre[a]);
+        }
+#pragma unroll
+        for (int j = 0; j < kSelPer; j++) ent[j] = j < mine ? crow[off[j]] : 0ull;
+    }
+    // visit this lane's entries in order (registers: a fully unrolled loop, so the array
+    // stays in registers)
+    auto visit = [&](auto&& fn) {
+        if (held) {
+#pragma unroll
+            for (int j = 0; j < kSelPer; j++)
+                if (j < mine) fn(ent[j]);
+        } else {
+            for (int j = 0; j < mine; j++) fn(fetch(i0 + j));
+        }
+    };
 
-    // ---- the k-th largest key (all entries are chosen when there are at most k)
+    // ---- the k-th largest key and how many of its ties are taken
+    const bool all = N <= p.k;
     uint32_t kth = 0;
-    int rest = N;        // entries equal to kth that are chosen
-    int32_t col_cut = 0x7fffffff;
-    if (N > p.k) {
-        uint32_t prefix = 0, mask = 0;
-        int want = p.k;
-        for (int pass = 0; pass < 4; pass++) {
-            const int shift = 24 - 8 * pass;
-            L.hist[tid] = 0;
-            __syncthreads();
-            for (int i = tid; i < N; i += kSelThreads) {
-                const uint32_t key = key_of(ent(i));
-                if ((key & mask) == prefix) atomicAdd(&L.hist[(key >> shift) & 255u], 1);
-            }
-            __syncthreads();
-            int digit = 0, above = 0;
-            if (wave == 0) {
-                pick_digit(L.hist, want, digit, above);
-                if (lane == 0) L.misc[4] = digit, L.misc[5] = above;
-            }
-            __syncthreads();
-            digit = L.misc[4];
-            above = L.misc[5];
-            want -= above;
-            prefix |= (uint32_t)digit << shift;
-            mask |= 255u << shift;
-            __syncthreads();
+    int need = 0;
+    if (!all) {
+        // narrow [smallest, largest key] down to the k-th key; `above` counts the keys
+        // above the current range
+        uint32_t klo = 0xffffffffu, khi = 0u;
+        visit([&](uint64_t e) {
+            klo = min(klo, key_of(e));
+            khi = max(khi, key_of(e));
+        });
+        block_minmax(klo, khi, L.red8);
+        int above = 0;
+        while (klo < khi) {  // uniform; each step shrinks the range 1024-fold
+            int bin, ab, sh;
+            narrow([&](auto&& fn) { visit([&](uint64_t e) { fn(key_of(e)); }); }, klo, khi,
+                   p.k - above, L, bin, ab, sh);
+            above += ab;
+            const uint32_t nlo = klo + ((uint32_t)bin << sh);
+            const uint32_t width = sh >= 32 ? 0xffffffffu : ((1u << sh) - 1u);
+            khi = min(khi, nlo + width);
+            klo = nlo;
         }
-        kth = prefix;
-        rest = want;
-        // ties at the k-th key: the `rest` smallest columns among them
-        if (tid == 0) L.misc[6] = 0;
-        __syncthreads();
-        int eq = 0;
-        for (int i = tid; i < N; i += kSelThreads) eq += key_of(ent(i)) == kth ? 1 : 0;
-        atomicAdd(&L.misc[6], eq);
-        __syncthreads();
-        const int n_eq = L.misc[6];
-        __syncthreads();
-        if (n_eq > rest) {
-            int a = 0, b = 0x7fffffff;  // the smallest c with #(tied columns <= c) >= rest
-            while (a < b) {
-                const int mid = a + ((b - a) >> 1);
-                if (tid == 0) L.misc[7] = 0;
-                __syncthreads();
-                int c = 0;
-                for (int i = tid; i < N; i += kSelThreads) {
-                    const uint64_t e = ent(i);
-                    c += (key_of(e) == kth && (int32_t)(e >> 32) <= mid) ? 1 : 0;
-                }
-                atomicAdd(&L.misc[7], c);
-                __syncthreads();
-                if (L.misc[7] >= rest) b = mid;
-                else a = mid + 1;
-                __syncthreads();
-            }
-            col_cut = a;
-        }
+        kth = klo;
+        need = p.k - above;  // keys above kth: every key above a range was counted
     }
-
-    // ---- the chosen entries, sorted by column (bitonic network over a power of two)
-    const int m = min(N, p.k);
-    const int P = p.P;
-    if (tid == 0) L.misc[4] = 0;
-    __syncthreads();
-    for (int i = tid; i < N; i += kSelThreads) {
-        const uint64_t e = ent(i);
-        const uint32_t key = key_of(e);
-        const bool take = N <= p.k || key > kth || (key == kth && (int32_t)(e >> 32) <= col_cut);
-        if (take) {
-            const int at = atomicAdd(&L.misc[4], 1);
-            // sort key: column in the high half
-            if (at < P) sel[at] = e;
-        }
-    }
-    __syncthreads();
-    for (int i = m + tid; i < P; i += kSelThreads) sel[i] = ~0ull;  // sorts last
-    __syncthreads();
-    for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < P; i += kSelThreads) {
-                const int j = i ^ stride;
-                if (j > i) {
-                    const uint64_t a = sel[i], b = sel[j];
-                    const bool up = (i & size) == 0;
-                    const bool sw = up ? ((a >> 32) > (b >> 32)) : ((a >> 32) < (b >> 32));
-                    if (sw) {
-                        sel[i] = b;
-                        sel[j] = a;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
+    // ---- ties in column order, then every chosen entry's output position
     int32_t* oi = p.out_idx + (int64_t)t * p.k;
     float* ov = p.out_vals ? p.out_vals + (int64_t)t * p.k : nullptr;
-    for (int i = tid; i < p.k; i += kSelThreads) {
-        const bool ok = i < m;
-        const uint64_t e = ok ? sel[i] : 0ull;
-        oi[i] = ok ? (int32_t)(e >> 32) : -1;
-        if (ov) ov[i] = ok ? __uint_as_float((uint32_t)e) : -__builtin_inff();
+    int m;
+    if (held) {
+        // branch-free: flags by arithmetic, stores through descriptors (an entry that is
+        // not chosen gets an offset past the row)
+        int ties = 0;
+#pragma unroll
+        for (int j = 0; j < kSelPer; j++) ties += (!all && j < mine && key_of(ent[j]) == kth) ? 1 : 0;
+        int tot;
+        const int tie0 = block_excl_scan(ties, red, &tot);
+        bool ch[kSelPer];
+        int take = 0, tr = tie0;
+#pragma unroll
+        for (int j = 0; j < kSelPer; j++) {
+            const uint32_t key = key_of(ent[j]);
+            const bool tie = !all && key == kth;
+            ch[j] = j < mine && (all || key > kth || (tie && tr < need));
+            tr += (j < mine && tie) ? 1 : 0;
+            take += ch[j] ? 1 : 0;
+        }
+        int pos = block_excl_scan(take, red, &m);
+        const uint32_t row_bytes = (uint32_t)p.k * 4u;
+        const __amdgpu_buffer_rsrc_t ri = make_rsrc(oi, row_bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(ov ? (const void*)ov : (const void*)oi, ov ? row_bytes : 0u);
+#pragma unroll
+        for (int j = 0; j < kSelPer; j++) {
+            const uint32_t o = ch[j] ? (uint32_t)pos * 4u : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(ent[j] >> 32), ri, o, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)ent[j], rv, o, 0, 0);
+            pos += ch[j] ? 1 : 0;
+        }
+    } else {
+        int ties = 0;
+        if (!all) visit([&](uint64_t e) { ties += key_of(e) == kth ? 1 : 0; });
+        int tot;
+        const int tie0 = block_excl_scan(ties, red, &tot);
+        auto chosen = [&](uint64_t e, int& tie_rank) {
+            if (all) return true;
+            const uint32_t key = key_of(e);
+            if (key > kth) return true;
+            if (key != kth) return false;
+            return tie_rank++ < need;
+        };
+        int take = 0;
+        {
+            int tr = tie0;
+            visit([&](uint64_t e) { take += chosen(e, tr) ? 1 : 0; });
+        }
+        int pos = block_excl_scan(take, red, &m);
+        int tr = tie0;
+        visit([&](uint64_t e) {
+            if (chosen(e, tr)) {
+                oi[pos] = (int32_t)(e >> 32);
+                if (ov) ov[pos] = __uint_as_float((uint32_t)e);
+                pos++;
+            }
+        });
+    }
+    for (int i = m + tid; i < p.k; i += kSelThreads) {
+        oi[i] = -1;
+        if (ov) ov[i] = -__builtin_inff();
     }
 }
 
@@ -490,20 +632,16 @@ hipError_t launch_logits_topk(const LogitsParams& p, int k, int32_t* out_idx, fl
     sel.k = k;
     sel.out_idx = out_idx;
     sel.out_vals = out_vals;
-    int P = 64;
-    while (P < k) P <<= 1;
-    sel.P = P;
-    sel.ent_off = (kSelPreOff + (pf.n_wchunks + 1) * 4 + 15) & ~15;
-    sel.sel_off = sel.ent_off + kStageCap * 8;
-    const size_t lds = (size_t)sel.sel_off + (size_t)P * 8;
-    hipLaunchKernelGGL(k_fused_select, dim3((unsigned)p.T), dim3(kSelThreads), lds, stream, sel);
+    const size_t lds = (size_t)(pf.n_wchunks + 1) * 4;
+    const dim3 sel_grid((unsigned)p.T);
+    hipLaunchKernelGGL(k_fused_select, sel_grid, dim3(kSelThreads), lds, stream, sel);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     // 6. flagged rows again, keeping every score
     pf.flags = flags;
     if ((e = launch_logits(pf, stream)) != hipSuccess) return e;
     sel.second = 1;
-    hipLaunchKernelGGL(k_fused_select, dim3((unsigned)p.T), dim3(kSelThreads), lds, stream, sel);
+    hipLaunchKernelGGL(k_fused_select, sel_grid, dim3(kSelThreads), lds, stream, sel);
     return hipGetLastError();
 }
 
