@@ -32,7 +32,7 @@ namespace {
 
 constexpr int kSampleStride = 16;   // one logical page in 16 is scored first
 constexpr int kSelThreads = 256;
-constexpr int kMaxChunks = 8192;    // column chunks per row (the scorer's plan stays below)
+constexpr int kMaxChunks = 32767;   // column chunks per row (their prefix lives in LDS)
 constexpr int kSortCap = 2048;      // largest k
 
 __device__ __forceinline__ uint32_t order_key(uint32_t u) {

@@ -51,7 +51,7 @@ namespace {
 constexpr int kWavesPerBlock = FP4IDX_LOGITS_WPB;
 constexpr int kThreads = 64 * kWavesPerBlock;
 #ifndef FP4IDX_LOGITS_WAVES
-#define FP4IDX_LOGITS_WAVES 8192   // target number of waves of one launch
+#define FP4IDX_LOGITS_WAVES 16384  // target number of waves of one launch
 #endif
 #ifndef FP4IDX_LOGITS_PIPE
 #define FP4IDX_LOGITS_PIPE 2       // products in flight in the epilogue pipeline
