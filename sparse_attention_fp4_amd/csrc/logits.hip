@@ -57,7 +57,7 @@ constexpr int kThreads = 64 * kWavesPerBlock;
 #define FP4IDX_LOGITS_PIPE 2       // products in flight in the epilogue pipeline
 #endif
 #ifndef FP4IDX_LOGITS_RING
-#define FP4IDX_LOGITS_RING 3       // key slabs in the ring (in flight + computing)
+#define FP4IDX_LOGITS_RING 2       // key slabs in the ring (in flight + computing)
 #endif
 #ifndef FP4IDX_LOGITS_WLDS
 #define FP4IDX_LOGITS_WLDS 0       // head weights read from LDS per tile (else registers)
@@ -576,8 +576,8 @@ __global__ __launch_bounds__(kThreads) void k_logits(const LogitsParams p) {
         }
         const bool st_lane = lane_stores && row_ok;
         int run = 0;  // kept candidates of this lane's row in the chunk (fused)
-        // ---- the wave's slabs: three buffers in a ring keep two slabs of keys in flight
-        // while one is computed (slab s lives in buffer s % 3)
+        // ---- the wave's slabs: a ring of FP4IDX_LOGITS_RING buffers (two by default:
+        // the next slab's keys are in flight while one is computed; with three, two are)
         // head sums: acc[set][key tile][i]; tiles 8*set .. 8*set+7 go to one set, so
         // no accumulation chain is longer than 8 multiply-adds
         constexpr int kSets = NT > 8 ? 2 : 1;
