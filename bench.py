@@ -509,6 +509,20 @@ def main():
                 "kernel": dom, "algorithmic_bytes_per_launch": d["bytes"],
                 "algorithmic_flops_per_launch": d["flops"], "avg_launch_us": round(d["us"], 3)}
 
+    # the same figures for every entry point of the step (the roofline above is the one
+    # that takes the most time)
+    roofline_all = {}
+    for name, kv in kern.items():
+        if kv["bound"] == "mfma":
+            a = kv["flops"] / (kv["us"] * 1e-6) / 1e12
+            pk, un = MFMA_PEAK_TFLOPS[kv["dtype"]], "TFLOP/s"
+        else:
+            a = kv["bytes"] / (kv["us"] * 1e-6) / 1e9
+            pk, un = HBM_PEAK_GBS, "GB/s"
+        roofline_all[name] = {"bound": kv["bound"], "achieved": round(a, 1), "peak": pk, "unit": un,
+                              "frac": round(a / pk, 4), "avg_launch_us": round(kv["us"], 3),
+                              "traffic": load_traffic(name, W["name"])}
+
     us = {n: round(kv["us"], 3) for n, kv in kern.items()}
     us["step_cold"] = round(ms_per_step * 1e3, 3)
     us["step_warm_same_buffers"] = round(warm_ms * 1e3, 3)
@@ -535,6 +549,7 @@ def main():
         "config": config,
         "us_per_call": us,
         "roofline": roofline,
+        "roofline_all": roofline_all,
         "context": {"pages_sm120_logits_us_at_100k": 59.9,
                     "note": "the pages' SGLang scorer on RTX PRO 6000 (SM120), logits only"},
     }
