@@ -63,6 +63,183 @@ __device__ __forceinline__ float max3_raw(float a, float b, float c) {
     return r;
 }
 
+// NVFP4, the four query tiles of a workgroup in one batch item: the waves walk the same
+// key tiles in step and share their decoding.  Wave w loads dword w of every lane's key
+// bytes (its quarter of the tile) and the scale it needs, decodes it to fp16 into LDS
+// (two tiles per barrier, two such pairs double-buffered), and every wave then reads the
+// whole decoded tile as its MFMA operand: a quarter of the decoding and of the key reads
+// per wave.  A wave whose own keys end earlier keeps decoding for the others.
+template <int NB>
+__device__ __forceinline__ void block_scores_shared(const BlockParams& p, int hk, int kc, int h0,
+                                                    int nh, int qt, int b, v8h (*sk)[2][4][64],
+                                                    int* s_kt) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4, n = lane & 15;
+    const int kb_lo = kc * p.kb_chunk;
+    const int kb_hi = min(kb_lo + p.kb_chunk, p.ktiles);
+    const int cq0 = p.cu_q[b], cq1 = p.cu_q[b + 1];
+    const int q_len = cq1 - cq0;
+    const int k_len = min(p.cu_k[b + 1] - p.cu_k[b], p.ktiles * 128);
+    const int offset = p.qo_offset ? p.qo_offset[b] : (p.cu_k[b + 1] - p.cu_k[b]) - q_len;
+    const int page0 = p.cu_p[b];
+    const int qg = qt * 16 + n;
+    const bool col_ok = qg < p.Tq && qg >= cq0 && qg < cq1;
+    int kv_lim = k_len;
+    if (p.causal) kv_lim = min(kv_lim, max(qg - cq0 + offset + 1, 0));
+    if (!col_ok) kv_lim = 0;
+    int kv_max = kv_lim;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) kv_max = max(kv_max, __shfl_xor(kv_max, d));
+    kv_max = uniform(kv_max);
+    int kv_min = col_ok ? kv_lim : 0x7fffffff;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) kv_min = min(kv_min, __shfl_xor(kv_min, d));
+    kv_min = uniform(kv_min);
+
+    QOperand<1> qop[NB];
+#pragma unroll
+    for (int hb = 0; hb < NB; hb++) {
+        const bool ok = col_ok && hb < nh;
+        const int64_t row = (int64_t)qg * p.Hq + h0 + hb;
+        v4i raw = v4i{0, 0, 0, 0};
+        uint32_t sc = 0;
+        if (ok) {
+            raw = load16(p.q + row * 64 + 16 * g);
+            sc = (uint32_t)p.qs[row * 8 + 2 * g] | ((uint32_t)p.qs[row * 8 + 2 * g + 1] << 8);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            float pw, bb;
+            e4m3_split((sc >> (8 * (c >> 1))) & 0xffu, pw, bb);
+            qop[hb].v[c] = decode8_f16((uint32_t)raw[c], pw, bb);
+        }
+    }
+
+    const int n_kt = (kv_max + 15) / 16;  // this wave's key tiles with a visible key
+    const int kt_lo = min(kb_lo * 8, n_kt), kt_hi = min(kb_hi * 8, n_kt);
+    // the workgroup walks the union of its waves' tiles
+    if (lane == 0) s_kt[wave] = n_kt;
+    __syncthreads();
+    const int n_kt_wg = max(max(s_kt[0], s_kt[1]), max(s_kt[2], s_kt[3]));
+    const int wkt_lo = min(kb_lo * 8, n_kt_wg), wkt_hi = min(kb_hi * 8, n_kt_wg);
+    const int kb_done_wg = (n_kt_wg + 7) / 8;
+    float run[NB];
+#pragma unroll
+    for (int hb = 0; hb < NB; hb++) run[hb] = -__builtin_inff();
+
+    int win = -64 - 64, my_phys = -1;
+    auto window = [&](int kb) {
+        if (kb - win >= 64 || kb < win) {
+            win = kb & ~63;
+            const int i = win + lane;
+            int v = -1;
+            if (p.kv_indices && i < kb_done_wg) v = p.kv_indices[page0 + i];
+            my_phys = (v >= 0 && v < p.num_pages) ? v : -1;
+        }
+        return __builtin_amdgcn_readlane(my_phys, kb - win);
+    };
+    // this wave's quarter of key tile kt: dword `wave` of lane (g, n)'s 16 key bytes and
+    // the scale code of its group
+    struct KPart {
+        uint32_t k, s;
+        int phys;
+    };
+    auto fetch = [&](int kt, KPart& t) {
+        t.phys = kt < wkt_hi ? window(kt >> 3) : -1;
+        const bool ok = t.phys >= 0;
+        const int64_t tok0 = ((int64_t)(ok ? t.phys : 0) * p.Hkv + hk) * 128 + (kt & 7) * 16;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(ok ? p.k + tok0 * 64 : p.k, ok ? 16u * 64u : 0u);
+        t.k = __builtin_amdgcn_raw_buffer_load_b32(rk, n * 64 + 16 * g + 4 * wave, 0, 0);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(ok ? p.ks + tok0 * 8 : p.ks, ok ? 16u * 8u : 0u);
+        t.s = __builtin_amdgcn_raw_buffer_load_b8(rs, n * 8 + 2 * g + (wave >> 1), 0, 0);
+    };
+    auto stage = [&](const KPart& t, v8h (*slot)[64]) {
+        float pw, bb;
+        e4m3_split(t.s & 0xffu, pw, bb);
+        slot[wave][lane] = decode8_f16(t.k, pw, bb);  // zeros for an invalid page
+    };
+    auto compute = [&](int kt, int phys, const v8h* buf) {
+        const int kb = kt >> 3;
+        if (kt >= kt_lo && kt < kt_hi && phys >= 0) {  // wave-uniform
+            const int kbase = kt * 16 + 4 * g;
+            const bool full = __ballot(kbase + 3 >= kv_min) == 0;
+            v8h kd[4];
+#pragma unroll
+            for (int c = 0; c < 4; c++) kd[c] = buf[c * 64 + lane];
+            v4f d[NB];
+#pragma unroll
+            for (int hb = 0; hb < NB; hb++) d[hb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < 4; c++)
+#pragma unroll
+                for (int hb = 0; hb < NB; hb++) d[hb] = mfma_f16_16x16x32(kd[c], qop[hb].v[c], d[hb]);
+            if (__builtin_expect(full, 1)) {
+#pragma unroll
+                for (int hb = 0; hb < NB; hb++)
+                    run[hb] = max3_raw(max3_raw(run[hb], d[hb][0], d[hb][1]), d[hb][2], d[hb][3]);
+            } else {
+#pragma unroll
+                for (int hb = 0; hb < NB; hb++) {
+                    v4f e = d[hb];
+#pragma unroll
+                    for (int i = 0; i < 4; i++) e[i] = kbase + i < kv_lim ? e[i] : -__builtin_inff();
+                    run[hb] = max3_raw(max3_raw(run[hb], e[0], e[1]), e[2], e[3]);
+                }
+            }
+        }
+        if (kt >= kt_lo && kt < kt_hi && ((kt & 7) == 7 || kt == n_kt - 1)) {  // wave-uniform
+#pragma unroll
+            for (int hb = 0; hb < NB; hb++) {
+                float v = run[hb];
+                v = max_lane_xor16(v);
+                v = max_lane_xor32(v);
+                if (g == 0 && col_ok && hb < nh)
+                    p.scores[((int64_t)(h0 + hb) * p.ktiles + kb) * p.Tq + qg] = v;
+                run[hb] = -__builtin_inff();
+            }
+        }
+    };
+    // two key tiles (kt even, kt + 1) per barrier; LDS buffers alternate between pairs
+    auto pair = [&](int kt, const KPart& a, const KPart& b) {
+        v8h (*buf)[4][64] = sk[(kt >> 1) & 1];
+        stage(a, buf[0]);
+        stage(b, buf[1]);
+        __syncthreads();
+        compute(kt, a.phys, buf[0][0]);
+        compute(kt + 1, b.phys, buf[1][0]);
+    };
+    // tiles are fetched two pairs ahead; the loop bound is the workgroup's (every wave
+    // takes every barrier) and starts at an even tile whenever the range is not empty
+    KPart a0, b0, a1, b1, a2, b2;
+    fetch(wkt_lo, a0);
+    fetch(wkt_lo + 1, b0);
+    fetch(wkt_lo + 2, a1);
+    fetch(wkt_lo + 3, b1);
+    for (int kt = wkt_lo; kt < wkt_hi; kt += 6) {
+        fetch(kt + 4, a2);
+        fetch(kt + 5, b2);
+        pair(kt, a0, b0);
+        if (kt + 2 >= wkt_hi) break;
+        fetch(kt + 6, a0);
+        fetch(kt + 7, b0);
+        pair(kt + 2, a1, b1);
+        if (kt + 4 >= wkt_hi) break;
+        fetch(kt + 8, a1);
+        fetch(kt + 9, b1);
+        pair(kt + 4, a2, b2);
+    }
+    // blocks of the chunk this wave never reached: -inf
+    const int kb_done = (n_kt + 7) / 8;
+    for (int kb = max(kb_done, kb_lo); kb < kb_hi; kb++) {
+        if (g == 0 && col_ok) {
+#pragma unroll
+            for (int hb = 0; hb < NB; hb++)
+                if (hb < nh) p.scores[((int64_t)(h0 + hb) * p.ktiles + kb) * p.Tq + qg] = -__builtin_inff();
+        }
+    }
+}
+
 template <int FMT, int NB>
 __global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
     const int lane = threadIdx.x & 63;
@@ -80,6 +257,20 @@ __global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
     rem -= kc * n_hgrp * qt_blocks;
     const int hgrp = rem / qt_blocks;
     const int qt = (rem - hgrp * qt_blocks) * kWavesPerBlock + (threadIdx.x >> 6);
+    if constexpr (FMT == 1) {
+        // the workgroup's 64 tokens in one batch item: shared key decoding
+        __shared__ __align__(16) v8h sk[2][2][4][64];
+        __shared__ int s_kt[kWavesPerBlock];
+        const int qt0 = (rem - hgrp * qt_blocks) * kWavesPerBlock;
+        const int t_first = qt0 * 16, t_last = min(qt0 * 16 + 64, p.Tq) - 1;
+        const RowRequest ra = find_request(p.cu_q, p.B, t_first);
+        const RowRequest rb = find_request(p.cu_q, p.B, t_last);
+        if (hk < p.Hkv && ra.ok && rb.ok && ra.b == rb.b) {  // uniform per workgroup
+            block_scores_shared<NB>(p, hk, kc, hk * p.R + hgrp * NB, min(NB, p.R - hgrp * NB), qt,
+                                    ra.b, sk, s_kt);
+            return;
+        }
+    }
     if (hk >= p.Hkv || qt >= n_qtiles) return;  // uniform per wave
     const int kb_lo = kc * p.kb_chunk;                       // this wave's blocks
     const int kb_hi = min(kb_lo + p.kb_chunk, p.ktiles);
