@@ -53,26 +53,22 @@ struct QOperand<1> {
     v8h v[4];
 };
 
-// max of three floats in one instruction.  The hardware max skips a NaN operand (the
-// block max's reading of fmax); written out because the compiler would first quiet
-// every matrix-core result (a no-op here: those are never signalling NaNs), which costs
-// as much as the max itself.
+// max of three floats; fmax skips a NaN operand (the block max's reading of fmax)
 __device__ __forceinline__ float max3_raw(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
+    return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 
 // NVFP4, the four query tiles of a workgroup in one batch item: the waves walk the same
-// key tiles in step and share their decoding.  Wave w loads dword w of every lane's key
-// bytes (its quarter of the tile) and the scale it needs, decodes it to fp16 into LDS
-// (two tiles per barrier, two such pairs double-buffered), and every wave then reads the
-// whole decoded tile as its MFMA operand: a quarter of the decoding and of the key reads
-// per wave.  A wave whose own keys end earlier keeps decoding for the others.
+// 128-key blocks in step and share their decoding.  Per block, wave w loads and decodes
+// key tiles w and w + 4 (16 keys each) to fp16 in LDS; after one barrier every wave
+// reads all eight tiles as MFMA operands for its own query tile.  A quarter of the
+// decoding and of the key reads per wave, one buffer descriptor and one block-table
+// lookup per block; the next block's bytes are loaded while the current one is computed.
+// A wave whose own keys end earlier keeps decoding for the others.
 template <int NB>
 __device__ __forceinline__ void block_scores_shared(const BlockParams& p, int hk, int kc, int h0,
-                                                    int nh, int qt, int b, v8h (*sk)[2][4][64],
-                                                    int* s_kt) {
+                                                    int nh, int qt, int b, int t_last,
+                                                    v8h (*sk)[8][4][64]) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 4, n = lane & 15;
@@ -84,10 +80,11 @@ __device__ __forceinline__ void block_scores_shared(const BlockParams& p, int hk
     const int offset = p.qo_offset ? p.qo_offset[b] : (p.cu_k[b + 1] - p.cu_k[b]) - q_len;
     const int page0 = p.cu_p[b];
     const int qg = qt * 16 + n;
-    const bool col_ok = qg < p.Tq && qg >= cq0 && qg < cq1;
-    int kv_lim = k_len;
-    if (p.causal) kv_lim = min(kv_lim, max(qg - cq0 + offset + 1, 0));
-    if (!col_ok) kv_lim = 0;
+    const bool col_ok = qg <= t_last;  // the workgroup's tokens up to t_last are all in batch item b
+    auto visible = [&](int t) {        // keys visible to token t of batch item b (exclusive bound)
+        return p.causal ? min(k_len, max(t - cq0 + offset + 1, 0)) : k_len;
+    };
+    const int kv_lim = col_ok ? visible(qg) : 0;
     int kv_max = kv_lim;
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) kv_max = max(kv_max, __shfl_xor(kv_max, d));
@@ -116,17 +113,12 @@ __device__ __forceinline__ void block_scores_shared(const BlockParams& p, int hk
         }
     }
 
-    const int n_kt = (kv_max + 15) / 16;  // this wave's key tiles with a visible key
-    const int kt_lo = min(kb_lo * 8, n_kt), kt_hi = min(kb_hi * 8, n_kt);
-    // the workgroup walks the union of its waves' tiles
-    if (lane == 0) s_kt[wave] = n_kt;
-    __syncthreads();
-    const int n_kt_wg = max(max(s_kt[0], s_kt[1]), max(s_kt[2], s_kt[3]));
-    const int wkt_lo = min(kb_lo * 8, n_kt_wg), wkt_hi = min(kb_hi * 8, n_kt_wg);
-    const int kb_done_wg = (n_kt_wg + 7) / 8;
+    const int n_kt = (kv_max + 15) / 16;        // this wave's key tiles with a visible key
+    const int kb_done = (n_kt + 7) / 8;         // and its blocks
+    // the workgroup walks the blocks of its last token (visibility grows with the token)
+    const int kb_done_wg = (visible(t_last) + 127) / 128;
+    const int wkb_hi = min(kb_hi, kb_done_wg);
     float run[NB];
-#pragma unroll
-    for (int hb = 0; hb < NB; hb++) run[hb] = -__builtin_inff();
 
     int win = -64 - 64, my_phys = -1;
     auto window = [&](int kb) {
@@ -139,98 +131,94 @@ __device__ __forceinline__ void block_scores_shared(const BlockParams& p, int hk
         }
         return __builtin_amdgcn_readlane(my_phys, kb - win);
     };
-    // this wave's quarter of key tile kt: dword `wave` of lane (g, n)'s 16 key bytes and
-    // the scale code of its group
-    struct KPart {
-        uint32_t k, s;
+    // this wave's two tiles of block kb (w and w + 4): lane (g, n) holds the 16 bytes of
+    // key n, dims 32g..32g+31, and their two scale codes
+    struct KBlk {
+        v4i k0, k1;
+        uint32_t s0, s1;
         int phys;
     };
-    auto fetch = [&](int kt, KPart& t) {
-        t.phys = kt < wkt_hi ? window(kt >> 3) : -1;
+    auto fetch = [&](int kb, KBlk& t) {
+        t.phys = kb < wkb_hi ? window(kb) : -1;
         const bool ok = t.phys >= 0;
-        const int64_t tok0 = ((int64_t)(ok ? t.phys : 0) * p.Hkv + hk) * 128 + (kt & 7) * 16;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(ok ? p.k + tok0 * 64 : p.k, ok ? 16u * 64u : 0u);
-        t.k = __builtin_amdgcn_raw_buffer_load_b32(rk, n * 64 + 16 * g + 4 * wave, 0, 0);
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(ok ? p.ks + tok0 * 8 : p.ks, ok ? 16u * 8u : 0u);
-        t.s = __builtin_amdgcn_raw_buffer_load_b8(rs, n * 8 + 2 * g + (wave >> 1), 0, 0);
+        const int64_t tok0 = ((int64_t)(ok ? t.phys : 0) * p.Hkv + hk) * 128;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(ok ? p.k + tok0 * 64 : p.k, ok ? 128u * 64u : 0u);
+        const int koff = (wave * 16 + n) * 64 + 16 * g;
+        t.k0 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 0, 0));
+        t.k1 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 4 * 16 * 64, 0));
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(ok ? p.ks + tok0 * 8 : p.ks, ok ? 128u * 8u : 0u);
+        const int soff = (wave * 16 + n) * 8 + 2 * g;
+        t.s0 = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, 0, 0);
+        t.s1 = __builtin_amdgcn_raw_buffer_load_b16(rs, soff + 4 * 16 * 8, 0, 0);
     };
-    auto stage = [&](const KPart& t, v8h (*slot)[64]) {
-        float pw, bb;
-        e4m3_split(t.s & 0xffu, pw, bb);
-        slot[wave][lane] = decode8_f16(t.k, pw, bb);  // zeros for an invalid page
+    auto stage = [&](const v4i& k, uint32_t sc, v8h (*tile)[64]) {
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            float pw, bb;
+            e4m3_split((sc >> (8 * (c >> 1))) & 0xffu, pw, bb);
+            tile[c][lane] = decode8_f16((uint32_t)k[c], pw, bb);  // zeros for an invalid page
+        }
     };
-    auto compute = [&](int kt, int phys, const v8h* buf) {
-        const int kb = kt >> 3;
-        if (kt >= kt_lo && kt < kt_hi && phys >= 0) {  // wave-uniform
-            const int kbase = kt * 16 + 4 * g;
-            const bool full = __ballot(kbase + 3 >= kv_min) == 0;
-            v8h kd[4];
+    auto block = [&](int kb, const KBlk& t) {
+        v8h (*buf)[4][64] = sk[kb & 1];
+        stage(t.k0, t.s0, buf[wave]);
+        stage(t.k1, t.s1, buf[wave + 4]);
+        __syncthreads();
+        if (kb < kb_lo || kb >= kb_done) return;  // wave-uniform: no key of this block is visible
 #pragma unroll
-            for (int c = 0; c < 4; c++) kd[c] = buf[c * 64 + lane];
-            v4f d[NB];
+        for (int hb = 0; hb < NB; hb++) run[hb] = -__builtin_inff();
+        if (t.phys >= 0) {
+            const int nt = min(8, n_kt - kb * 8);            // tiles with a visible key
+            const bool full = kb * 128 + 128 <= kv_min;      // every key of the block visible
 #pragma unroll
-            for (int hb = 0; hb < NB; hb++) d[hb] = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < 8; j++) {
+                if (j >= nt) break;
+                v8h kd[4];
 #pragma unroll
-            for (int c = 0; c < 4; c++)
+                for (int c = 0; c < 4; c++) kd[c] = buf[j][c][lane];
+                v4f d[NB];
 #pragma unroll
-                for (int hb = 0; hb < NB; hb++) d[hb] = mfma_f16_16x16x32(kd[c], qop[hb].v[c], d[hb]);
-            if (__builtin_expect(full, 1)) {
+                for (int hb = 0; hb < NB; hb++) d[hb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int hb = 0; hb < NB; hb++)
-                    run[hb] = max3_raw(max3_raw(run[hb], d[hb][0], d[hb][1]), d[hb][2], d[hb][3]);
-            } else {
+                for (int c = 0; c < 4; c++)
 #pragma unroll
-                for (int hb = 0; hb < NB; hb++) {
-                    v4f e = d[hb];
+                    for (int hb = 0; hb < NB; hb++) d[hb] = mfma_f16_16x16x32(kd[c], qop[hb].v[c], d[hb]);
+                if (__builtin_expect(full, 1)) {
 #pragma unroll
-                    for (int i = 0; i < 4; i++) e[i] = kbase + i < kv_lim ? e[i] : -__builtin_inff();
-                    run[hb] = max3_raw(max3_raw(run[hb], e[0], e[1]), e[2], e[3]);
+                    for (int hb = 0; hb < NB; hb++)
+                        run[hb] = max3_raw(max3_raw(run[hb], d[hb][0], d[hb][1]), d[hb][2], d[hb][3]);
+                } else {
+                    const int kbase = kb * 128 + j * 16 + 4 * g;
+#pragma unroll
+                    for (int hb = 0; hb < NB; hb++) {
+                        v4f e = d[hb];
+#pragma unroll
+                        for (int i = 0; i < 4; i++) e[i] = kbase + i < kv_lim ? e[i] : -__builtin_inff();
+                        run[hb] = max3_raw(max3_raw(run[hb], e[0], e[1]), e[2], e[3]);
+                    }
                 }
             }
         }
-        if (kt >= kt_lo && kt < kt_hi && ((kt & 7) == 7 || kt == n_kt - 1)) {  // wave-uniform
 #pragma unroll
-            for (int hb = 0; hb < NB; hb++) {
-                float v = run[hb];
-                v = max_lane_xor16(v);
-                v = max_lane_xor32(v);
-                if (g == 0 && col_ok && hb < nh)
-                    p.scores[((int64_t)(h0 + hb) * p.ktiles + kb) * p.Tq + qg] = v;
-                run[hb] = -__builtin_inff();
-            }
+        for (int hb = 0; hb < NB; hb++) {
+            float v = run[hb];
+            v = max_lane_xor16(v);
+            v = max_lane_xor32(v);
+            if (g == 0 && col_ok && hb < nh) p.scores[((int64_t)(h0 + hb) * p.ktiles + kb) * p.Tq + qg] = v;
         }
     };
-    // two key tiles (kt even, kt + 1) per barrier; LDS buffers alternate between pairs
-    auto pair = [&](int kt, const KPart& a, const KPart& b) {
-        v8h (*buf)[4][64] = sk[(kt >> 1) & 1];
-        stage(a, buf[0]);
-        stage(b, buf[1]);
-        __syncthreads();
-        compute(kt, a.phys, buf[0][0]);
-        compute(kt + 1, b.phys, buf[1][0]);
-    };
-    // tiles are fetched two pairs ahead; the loop bound is the workgroup's (every wave
-    // takes every barrier) and starts at an even tile whenever the range is not empty
-    KPart a0, b0, a1, b1, a2, b2;
-    fetch(wkt_lo, a0);
-    fetch(wkt_lo + 1, b0);
-    fetch(wkt_lo + 2, a1);
-    fetch(wkt_lo + 3, b1);
-    for (int kt = wkt_lo; kt < wkt_hi; kt += 6) {
-        fetch(kt + 4, a2);
-        fetch(kt + 5, b2);
-        pair(kt, a0, b0);
-        if (kt + 2 >= wkt_hi) break;
-        fetch(kt + 6, a0);
-        fetch(kt + 7, b0);
-        pair(kt + 2, a1, b1);
-        if (kt + 4 >= wkt_hi) break;
-        fetch(kt + 8, a1);
-        fetch(kt + 9, b1);
-        pair(kt + 4, a2, b2);
+    // the loop bound is the workgroup's: every wave takes every barrier.  LDS buffers
+    // alternate between blocks, so one barrier per block orders both reuse and reads.
+    KBlk A, B;
+    fetch(kb_lo, A);
+    for (int kb = kb_lo; kb < wkb_hi; kb += 2) {
+        fetch(kb + 1, B);
+        block(kb, A);
+        if (kb + 1 >= wkb_hi) break;
+        fetch(kb + 2, A);
+        block(kb + 1, B);
     }
     // blocks of the chunk this wave never reached: -inf
-    const int kb_done = (n_kt + 7) / 8;
     for (int kb = max(kb_done, kb_lo); kb < kb_hi; kb++) {
         if (g == 0 && col_ok) {
 #pragma unroll
@@ -259,15 +247,14 @@ __global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
     const int qt = (rem - hgrp * qt_blocks) * kWavesPerBlock + (threadIdx.x >> 6);
     if constexpr (FMT == 1) {
         // the workgroup's 64 tokens in one batch item: shared key decoding
-        __shared__ __align__(16) v8h sk[2][2][4][64];
-        __shared__ int s_kt[kWavesPerBlock];
+        __shared__ __align__(16) v8h sk[2][8][4][64];
         const int qt0 = (rem - hgrp * qt_blocks) * kWavesPerBlock;
         const int t_first = qt0 * 16, t_last = min(qt0 * 16 + 64, p.Tq) - 1;
         const RowRequest ra = find_request(p.cu_q, p.B, t_first);
         const RowRequest rb = find_request(p.cu_q, p.B, t_last);
         if (hk < p.Hkv && ra.ok && rb.ok && ra.b == rb.b) {  // uniform per workgroup
             block_scores_shared<NB>(p, hk, kc, hk * p.R + hgrp * NB, min(NB, p.R - hgrp * NB), qt,
-                                    ra.b, sk, s_kt);
+                                    ra.b, t_last, sk);
             return;
         }
     }
