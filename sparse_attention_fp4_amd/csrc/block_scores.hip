@@ -35,6 +35,12 @@ namespace fp4idx {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
+#ifndef FP4IDX_BLOCK_LDS_BUFS
+#define FP4IDX_BLOCK_LDS_BUFS 1  // decoded NVFP4 key blocks in LDS: 1 (32 KB) or 2 (64 KB)
+#endif
+#ifndef FP4IDX_BLOCK_CHUNK_NV
+#define FP4IDX_BLOCK_CHUNK_NV 8  // 128-key blocks per NVFP4 workgroup
+#endif
 #ifndef FP4IDX_BLOCK_CHUNK
 #define FP4IDX_BLOCK_CHUNK 16  // 128-key blocks per wave
 #endif
@@ -60,10 +66,12 @@ __device__ __forceinline__ float max3_raw(float a, float b, float c) {
 
 // NVFP4, the four query tiles of a workgroup in one batch item: the waves walk the same
 // 128-key blocks in step and share their decoding.  Per block, wave w loads and decodes
-// key tiles w and w + 4 (16 keys each) to fp16 in LDS; after one barrier every wave
-// reads all eight tiles as MFMA operands for its own query tile.  A quarter of the
-// decoding and of the key reads per wave, one buffer descriptor and one block-table
-// lookup per block; the next block's bytes are loaded while the current one is computed.
+// key tiles w and w + 4 (16 keys each) to fp16 in LDS; after a barrier every wave reads
+// all eight tiles as MFMA operands for its own query tile.  A quarter of the decoding and
+// of the key reads per wave, one buffer descriptor and one block-table lookup per block;
+// the next block's bytes are loaded while the current one is computed.  With one LDS
+// buffer (32 KB: three workgroups per CU) a second barrier per block guards its reuse;
+// two buffers need one barrier but leave room for two workgroups, which measured slower.
 // A wave whose own keys end earlier keeps decoding for the others.
 template <int NB>
 __device__ __forceinline__ void block_scores_shared(const BlockParams& p, int hk, int kc, int h0,
@@ -160,7 +168,8 @@ __device__ __forceinline__ void block_scores_shared(const BlockParams& p, int hk
         }
     };
     auto block = [&](int kb, const KBlk& t) {
-        v8h (*buf)[4][64] = sk[kb & 1];
+        v8h (*buf)[4][64] = sk[FP4IDX_BLOCK_LDS_BUFS == 2 ? (kb & 1) : 0];
+        if (FP4IDX_BLOCK_LDS_BUFS == 1) __syncthreads();
         stage(t.k0, t.s0, buf[wave]);
         stage(t.k1, t.s1, buf[wave + 4]);
         __syncthreads();
@@ -207,8 +216,7 @@ __device__ __forceinline__ void block_scores_shared(const BlockParams& p, int hk
             if (g == 0 && col_ok && hb < nh) p.scores[((int64_t)(h0 + hb) * p.ktiles + kb) * p.Tq + qg] = v;
         }
     };
-    // the loop bound is the workgroup's: every wave takes every barrier.  LDS buffers
-    // alternate between blocks, so one barrier per block orders both reuse and reads.
+    // the loop bound is the workgroup's: every wave takes every barrier
     KBlk A, B;
     fetch(kb_lo, A);
     for (int kb = kb_lo; kb < wkb_hi; kb += 2) {
@@ -247,7 +255,7 @@ __global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
     const int qt = (rem - hgrp * qt_blocks) * kWavesPerBlock + (threadIdx.x >> 6);
     if constexpr (FMT == 1) {
         // the workgroup's 64 tokens in one batch item: shared key decoding
-        __shared__ __align__(16) v8h sk[2][8][4][64];
+        __shared__ __align__(16) v8h sk[FP4IDX_BLOCK_LDS_BUFS][8][4][64];
         const int qt0 = (rem - hgrp * qt_blocks) * kWavesPerBlock;
         const int t_first = qt0 * 16, t_last = min(qt0 * 16 + 64, p.Tq) - 1;
         const RowRequest ra = find_request(p.cu_q, p.B, t_first);
@@ -461,7 +469,7 @@ hipError_t launch_fmt_nb(const BlockParams& p, hipStream_t stream) {
 
 hipError_t launch_block_scores(const BlockParams& p_in, hipStream_t stream) {
     BlockParams p = p_in;
-    p.kb_chunk = FP4IDX_BLOCK_CHUNK;
+    p.kb_chunk = p.fmt == 0 ? FP4IDX_BLOCK_CHUNK : FP4IDX_BLOCK_CHUNK_NV;
     p.n_kchunks = (p.ktiles + p.kb_chunk - 1) / p.kb_chunk;
     if (p.n_kchunks == 0) p.n_kchunks = 1;  // no blocks: the grid still runs its (empty) chunk
     if (p.fmt == 0) {
