@@ -94,6 +94,44 @@ def test_on_config1_logits_within_tie_tolerance():
         say(f"    row {t}: symmetric difference {len(a ^ b)}")
 
 
+def test_long_rows_largest_keys_crowded_into_one_chunk():
+    """Long rows whose largest scores crowd into one 4096-column stretch instead of
+    spreading along the row: 4000 raised scores in one stretch, 3000 equal largest
+    scores (ties at the k-th), exactly k raised scores in one stretch, and a plain row."""
+    rng = np.random.default_rng(31)
+    rows, cols, k = 4, 100_000, 2048
+    s = rng.standard_normal((rows, cols)).astype(np.float32)
+    s[0, 8192:8192 + 4000] += 10.0
+    s[1, :3000] = 50.0
+    s[2, 50_000:50_000 + k] = (9.0 + rng.random(k)).astype(np.float32)
+    say(f"[gpu] topk crowded chunks rows={rows} cols={cols} k={k}")
+    _same(s, k)
+
+
+def test_long_rows_all_equal_and_mixed_lengths():
+    """A row of equal scores (all ties: the first k columns win) next to rows of lengths
+    0, 1, k - 1, k, k + 1 and 3000, in a batch wider than 32768 columns."""
+    rng = np.random.default_rng(32)
+    rows, cols, k = 8, 200_000, 2048
+    s = rng.standard_normal((rows, cols)).astype(np.float32)
+    s[0] = 1.5
+    lens = np.array([cols, cols, 0, 1, k - 1, k, k + 1, 3000], np.int32)
+    say(f"[gpu] topk equal scores and lengths rows={rows} cols={cols} k={k}")
+    _same(s, k, lens)
+
+
+@pytest.mark.parametrize("k", [1, 7, 300, 2048])
+def test_long_rows_k_sizes(k):
+    rng = np.random.default_rng(40 + k)
+    rows, cols = 3, 150_000
+    s = rng.standard_normal((rows, cols)).astype(np.float32)
+    s[0, rng.integers(0, cols, 500)] = -np.inf
+    s[1, rng.integers(0, cols, 500)] = np.nan
+    lens = np.array([cols, cols - 17, 33_000], np.int32)
+    say(f"[gpu] topk long rows k={k}")
+    _same(s, k, lens)
+
+
 def test_workspace_reused_across_calls_without_clearing():
     """The long-row path leaves its workspace ready for the next call."""
     import torch
