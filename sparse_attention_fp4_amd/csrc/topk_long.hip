@@ -36,8 +36,12 @@ namespace fp4idx {
 namespace {
 
 constexpr int kChunk = 4096;          // columns per chunk workgroup
-constexpr int kCT = 256;              // threads of a workgroup
+#ifndef FP4IDX_TOPK_LONG_CT
+#define FP4IDX_TOPK_LONG_CT 512  // 8 keys per thread (a chunk's waves run one per SIMD)
+#endif
+constexpr int kCT = FP4IDX_TOPK_LONG_CT;  // threads of a chunk workgroup
 constexpr int kPer = kChunk / kCT;    // elements per thread
+static_assert(kPer * (kCT / 64) == 64, "the collect scan covers 64 (step, wave) blocks");
 constexpr int kBins = 4096;
 constexpr int kWords = kChunk / 32;   // bitmap words per chunk
 constexpr int kMaxChunks = 128;    // rows of up to 524288 columns
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(kCT) void k_collect(const TopkParams p, LongWs ws) 
         if (cand[j]) atomicAdd(&sh.h2[(kj >> 8) & 0xfffu], 1u);
     }
     lds_barrier();
-    if (wave == 0) {  // exclusive scan over the kPer * 4 = 64 (step, wave) blocks
+    if (wave == 0) {  // exclusive scan over the kPer * kCT / 64 = 64 (step, wave) blocks
         const int x = sh.cnt[lane];
         const int s = wave_incl_scan(x);
         sh.off[lane] = s - x;
