@@ -197,8 +197,9 @@ size_t fp4idx_topk_workspace_bytes(int rows, int cols, int k);
  * matching scores, -inf in the padding.
  * scores: [rows][row_stride] float (row_stride >= cols); out_idx, out_vals: [rows][k].
  * workspace: device memory of at least fp4idx_topk_workspace_bytes(rows, cols, k),
- * 256-byte aligned, owned by the caller (NULL allowed when that size is 0; rows of at
- * most 32768 columns need none).  It carries per-row histograms between the kernels
+ * 256-byte aligned, owned by the caller (NULL allowed when that size is 0: rows of at
+ * most 8192 columns, or of at most 32768 columns when there are more than 64 rows, need
+ * none).  It carries per-row histograms between the kernels
  * of one call: it must be zero-filled before its first use, and every call that
  * returns FP4IDX_OK leaves it ready for the next one.  Calls that run concurrently
  * must not share a workspace.

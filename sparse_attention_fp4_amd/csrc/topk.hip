@@ -7,7 +7,8 @@
 // selected; -0 equals +0.  Output: the selected columns in increasing order, padded
 // with -1.
 //
-// Method (rows of at most 32768 columns; longer rows go to topk_long.hip): radix-style
+// Method (rows of at most 32768 columns; longer rows, and a few rows of more than 8192,
+// go to topk_long.hip): radix-style
 // select on order-preserving 32-bit keys held in registers.  One workgroup (16 waves,
 // 1024 lanes) takes one row: lane x holds elements x, x + 1024, x + 2048, ... loaded in
 // one burst.  It narrows the key range [lo, hi] that holds the k-th largest key with
@@ -336,12 +337,12 @@ __global__ __launch_bounds__(kThreads) void k_topk(const TopkParams p) {
 
 }  // namespace
 
-bool topk_long_rows(int cols);
+bool topk_long_rows(int rows, int cols);
 size_t topk_long_workspace_bytes(int rows, int cols, int k);
 hipError_t launch_topk_long(const TopkParams& p, void* workspace, hipStream_t stream);
 
 size_t topk_workspace_bytes(int rows, int cols, int k) {
-    return topk_long_rows(cols) ? topk_long_workspace_bytes(rows, cols, k) : 0;
+    return topk_long_rows(rows, cols) ? topk_long_workspace_bytes(rows, cols, k) : 0;
 }
 
 #ifndef FP4IDX_TOPK_STREAM
@@ -359,7 +360,7 @@ bool topk_use_stream(const TopkParams& p) {
 hipError_t launch_topk(const TopkParams& p_in, hipStream_t stream) {
     TopkParams p = p_in;
     if (topk_use_stream(p)) return launch_topk_stream(p, stream);
-    if (topk_long_rows(p.cols)) return launch_topk_long(p, p.workspace, stream);
+    if (topk_long_rows(p.rows, p.cols)) return launch_topk_long(p, p.workspace, stream);
     hipLaunchKernelGGL(k_topk, dim3(p.rows), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }

@@ -305,6 +305,9 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws) {
     // ---- one round of loads: state, candidate counts, second histogram, bitmap, and the
     // first `spec` candidate slots of every chunk (read before the counts are known;
     // slots past a count are ignored)
+    // the digit-1 histogram was last read by the collect pass: clear it for the next
+    // call now, so the stores drain while this workgroup works
+    for (int i = threadIdx.x; i < kBins; i += kFT) gh[i] = 0u;
     const int d1 = ws.st[row].d1;
     int kk = ws.st[row].kk;
     const int my_cnum = threadIdx.x < nch ? ws.cnum[(int64_t)row * nch + threadIdx.x] : 0;
@@ -357,6 +360,9 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws) {
     if (d1 >= 0) {
         // ---- digit 2 from the row's second histogram (pick_bin ends with a barrier)
         pick_bin<kFT, per>(c2, bin2, kk, sh.wtot, sh.pick);
+        // each thread has its bins' counts in registers: clear them for the next call
+#pragma unroll
+        for (int b = 0; b < per; b++) gh2[bin2[b]] = 0u;
         const uint32_t preA = ((uint32_t)d1 << 12) | (uint32_t)sh.pick[0];
         kk -= sh.pick[1];                      // keys wanted with prefix preA, >= 1
         const int n_pre = sh.pick[3];          // candidates with prefix preA
@@ -457,11 +463,6 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws) {
         oidx[i] = -1;
         if (oval) oval[i] = -__builtin_inff();
     }
-    // ---- leave the row's histograms zero for the next call
-    for (int i = threadIdx.x; i < kBins; i += kFT) {
-        gh[i] = 0u;
-        gh2[i] = 0u;
-    }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -490,7 +491,11 @@ LongWs carve(void* base, int rows, int cols, size_t* bytes) {
 
 }  // namespace
 
-bool topk_long_rows(int cols) { return cols > 32768; }
+// Rows longer than one workgroup holds go here; so do rows of more than 8192 columns
+// when there are few of them: spread over chunk workgroups they finish sooner than with
+// one workgroup per row (4 rows of 16384 columns: 14.5 against 16.5 us), while many
+// rows keep the chip busy one workgroup each.
+bool topk_long_rows(int rows, int cols) { return cols > 32768 || (cols > 8192 && rows <= 64); }
 
 size_t topk_long_workspace_bytes(int rows, int cols, int k) {
     (void)k;

@@ -88,7 +88,10 @@ def test_topk_argument_errors_and_workspace():
     assert L.fp4idx_topk(256, 10, 2, 10, None, 9000, 256, None, None, 0, None) == 2   # k too big
     assert L.fp4idx_topk(256, 1 << 20, 1, 1 << 20, None, 8, 256, None, None, 0, None) == 2  # cols
     assert L.fp4idx_topk(256, 5, 2, 10, None, 4, 256, None, None, 0, None) == 1       # stride
-    assert L.fp4idx_topk_workspace_bytes(4, 32768, 2048) == 0                        # fits in LDS
+    assert L.fp4idx_topk_workspace_bytes(4, 8192, 2048) == 0                         # one workgroup a row
+    assert L.fp4idx_topk_workspace_bytes(65, 32768, 2048) == 0
+    assert L.fp4idx_topk_workspace_bytes(64, 8193, 2048) > 0                         # chunked
+    assert L.fp4idx_topk_workspace_bytes(600, 32769, 2048) > 0
     need = L.fp4idx_topk_workspace_bytes(4, 100_000, 2048)
     assert need > 0
     assert L.fp4idx_topk(256, 100_000, 4, 100_000, None, 2048, 256, None, None, 0, None) == 5
