@@ -84,6 +84,31 @@ def test_nvfp4_nan_scale_codes_are_skipped_by_the_max():
     _check(case, nan_codes=True)
 
 
+def test_nvfp4_shared_decoding_noncausal_bad_pages_and_head_groups():
+    """NVFP4 workgroups whose 64 tokens lie in one batch item share their key decoding;
+    the one that straddles items 1 and 2 decodes per wave.  Non-causal items of 64 or
+    more tokens, a missing page and one outside the cache, more output blocks than any
+    item fills, six query heads per key head (the second head group of each key head is
+    partial) and a NaN key scale inside a shared block."""
+    case = wl.make_block("nv_shared", fmt=wl.NVFP4, q_lens=[64, 100, 70], k_lens=[700, 1500, 260],
+                         Hq=12, Hkv=2, seed=5, causal=False)
+    case.max_seqlen_k = 1800
+    o1 = int(case.cu_page_offsets[1])
+    case.kv_indices[o1 + 3] = -1
+    case.kv_indices[o1 + 5] = case.k_fp4.shape[0] + 2
+    p0 = int(case.kv_indices[1])
+    case.k_scale[p0, 1, 7, 3] = 0x7F
+    _check(case, nan_codes=True)
+
+
+def test_nvfp4_shared_decoding_long_keys_with_offset():
+    """One causal item whose 130 tokens see 8801..8930 keys (past 64 blocks, so the
+    block-table window moves, and across several key chunks), through qo_offset."""
+    case = wl.make_block("nv_long", fmt=wl.NVFP4, q_lens=[130], k_lens=[9000], Hq=8, Hkv=1,
+                         seed=6, causal=True, qo_offset=[8800])
+    _check(case, rows=[0, 1, 17, 63, 64, 65, 100, 127, 128, 129])
+
+
 def test_config3_nvfp4_prefill_sampled_queries():
     case = wl.config3()
     rng = np.random.default_rng(1030)
