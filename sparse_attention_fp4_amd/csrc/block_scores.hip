@@ -22,7 +22,9 @@
 // Key tiles are fetched two ahead of the one being computed, through buffer
 // descriptors built per tile (an invalid page gets a zero-byte descriptor, so the
 // loads stay unconditional); the block-table entries of 64 blocks come in with one
-// load.
+// load.  NVFP4 workgroups whose 64 tokens lie in one batch item instead walk whole
+// 128-key blocks in step and decode each block once into LDS for their four waves
+// (block_scores_shared below).
 //
 // MXFP4 uses the scaled FP4 MFMA (one instruction per 16x16 tile covers all 128
 // products).  NVFP4 decodes both operands exactly to fp16 (E2M1 * 2^a * b, b the E4M3
@@ -39,10 +41,10 @@ constexpr int kWavesPerBlock = 4;
 #define FP4IDX_BLOCK_LDS_BUFS 1  // decoded NVFP4 key blocks in LDS: 1 (32 KB) or 2 (64 KB)
 #endif
 #ifndef FP4IDX_BLOCK_CHUNK_NV
-#define FP4IDX_BLOCK_CHUNK_NV 8  // 128-key blocks per NVFP4 workgroup
+#define FP4IDX_BLOCK_CHUNK_NV 8  // 128-key blocks per NVFP4 wave
 #endif
 #ifndef FP4IDX_BLOCK_CHUNK
-#define FP4IDX_BLOCK_CHUNK 16  // 128-key blocks per wave
+#define FP4IDX_BLOCK_CHUNK 16  // 128-key blocks per MXFP4 wave
 #endif
 
 template <int FMT>
