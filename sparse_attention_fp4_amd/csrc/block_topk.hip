@@ -41,25 +41,44 @@ __global__ __launch_bounds__(256) void k_block_topk(const BlockTopkParams p) {
     int lb[KMAX];
 #pragma unroll
     for (int i = 0; i < KMAX; i++) lk[i] = 0u, lb[i] = -1;
-    float nxt = p.Kt > 0 ? col[0] : 0.f;
-    for (int kb = 0; kb < p.Kt; kb++) {
-        const float v = nxt;
-        if (kb + 1 < p.Kt) nxt = col[(kb + 1) * step];
-        const uint32_t key = active ? bkey(v) : 0u;
-        if (__ballot(key > lk[KMAX - 1]) == 0ull) continue;
-        // insert at the first slot holding a smaller key and shift the rest down one
-        // (the list is sorted, so c[i] is false up to that slot and true after it;
-        // equal keys stay in block order)
-        bool c[KMAX];
+    // block rows are read kB at a time, the next kB in flight while these are inserted
+    constexpr int kB = 8;
+    auto load = [&](int kb0, float (&v)[kB]) {
 #pragma unroll
-        for (int i = 0; i < KMAX; i++) c[i] = key > lk[i];
-#pragma unroll
-        for (int i = KMAX - 1; i > 0; i--) {
-            lk[i] = c[i] ? (c[i - 1] ? lk[i - 1] : key) : lk[i];
-            lb[i] = c[i] ? (c[i - 1] ? lb[i - 1] : kb) : lb[i];
+        for (int u = 0; u < kB; u++) {
+            const int kb = kb0 + u;
+            v[u] = kb < p.Kt ? col[(int64_t)kb * step] : -__builtin_inff();
         }
-        lk[0] = c[0] ? key : lk[0];
-        lb[0] = c[0] ? kb : lb[0];
+    };
+    auto insert = [&](int kb0, const float (&v)[kB]) {
+#pragma unroll
+        for (int u = 0; u < kB; u++) {
+            const int kb = kb0 + u;
+            const uint32_t key = active ? bkey(v[u]) : 0u;  // past Kt: -inf, key 0
+            if (__ballot(key > lk[KMAX - 1]) == 0ull) continue;
+            // insert at the first slot holding a smaller key and shift the rest down
+            // one (the list is sorted, so c[i] is false up to that slot and true after
+            // it; equal keys stay in block order)
+            bool c[KMAX];
+#pragma unroll
+            for (int i = 0; i < KMAX; i++) c[i] = key > lk[i];
+#pragma unroll
+            for (int i = KMAX - 1; i > 0; i--) {
+                lk[i] = c[i] ? (c[i - 1] ? lk[i - 1] : key) : lk[i];
+                lb[i] = c[i] ? (c[i - 1] ? lb[i - 1] : kb) : lb[i];
+            }
+            lk[0] = c[0] ? key : lk[0];
+            lb[0] = c[0] ? kb : lb[0];
+        }
+    };
+    float va[kB], vb[kB];
+    load(0, va);
+    for (int kb0 = 0; kb0 < p.Kt; kb0 += 2 * kB) {
+        load(kb0 + kB, vb);
+        insert(kb0, va);
+        if (kb0 + kB >= p.Kt) break;
+        load(kb0 + 2 * kB, va);
+        insert(kb0 + kB, vb);
     }
     if (!active) return;
     // The list's first k entries are the chosen blocks: put them in block order (a
