@@ -132,6 +132,19 @@ def test_long_rows_k_sizes(k):
     _same(s, k, lens)
 
 
+@pytest.mark.parametrize("rows,cols", [(64, 8193), (65, 8193), (64, 8192), (1, 32768), (511, 32768)])
+def test_routing_boundaries(rows, cols):
+    """Both sides of the routing between one workgroup per row and the chunked path
+    (more than 8192 columns and at most 64 rows go to the chunked path)."""
+    rng = np.random.default_rng(rows * 3 + cols)
+    s = rng.standard_normal((rows, cols)).astype(np.float32)
+    s[0, rng.integers(0, cols, 40)] = -np.inf
+    lens = rng.integers(0, cols + 1, rows).astype(np.int32)
+    lens[0] = cols
+    say(f"[gpu] topk routing rows={rows} cols={cols}")
+    _same(s, 2048, lens)
+
+
 def test_workspace_reused_across_calls_without_clearing():
     """The long-row path leaves its workspace ready for the next call."""
     import torch
