@@ -116,11 +116,13 @@ int fp4idx_logits_paged(int fmt,
  * How: the scores of every 16th page give each row a threshold that about 2k scores
  * of the row reach; the scorer then keeps only scores at or above it, and the exact
  * selection runs over those.  A row where fewer than k scores reach the threshold is
- * scored again keeping every score, so the result never depends on the sample.
+ * scored again keeping every score, so the result never depends on the sample.  With
+ * fewer than 512 rows the logits are written into the workspace instead and the plain
+ * top-k (fp4idx_topk) selects from them: the same result, faster for few rows.
  * workspace: fp4idx_logits_topk_workspace_bytes(...) bytes, 256-byte aligned,
  * caller-owned device memory (contents need no initialisation; calls that run
- * concurrently must not share one).  Only the kept scores (about 2k per row) are
- * written there, plus the sampled scores (1/16 of the columns).
+ * concurrently must not share one).  With 512 rows or more only the kept scores
+ * (about 2k per row) are written there, plus the sampled scores (1/16 of the columns).
  * Limits: 1 <= k <= 2048 and out_cols <= 2^24 (else EUNSUPPORTED); the logits limits
  * otherwise; EWORKSPACE when the workspace is missing, short or misaligned. */
 size_t fp4idx_logits_topk_workspace_bytes(int fmt, int T, int B, int H, int Hkv, int page_size,

@@ -33,7 +33,7 @@ struct LogitsParams {
     int n_tiles;         // Hkv * tiles_per_kv
     int ppw;             // pages per wave
     int n_wchunks;       // column chunks (of ppw pages) per row block
-    int n_wgchunks;      // workgroups per row block (four chunks each)
+    int n_wgchunks;      // workgroups per row block (one chunk per wave)
     int n_rowblocks;
     int rows_per_block;  // RG: query rows sharing one A tile
     // Fused scoring (top-k candidates instead of logits; `out` unused when cand is set):
@@ -155,5 +155,7 @@ struct QsaDecodeParams {
 hipError_t launch_qsa_slots(const QsaSlotParams& p, hipStream_t stream);
 hipError_t launch_qsa_decode(const QsaDecodeParams& p, hipStream_t stream);
 size_t topk_workspace_bytes(int rows, int cols, int k);
+// leading bytes of that workspace that must be zero when a call starts
+size_t topk_workspace_zero_bytes(int rows, int cols, int k);
 
 }  // namespace fp4idx

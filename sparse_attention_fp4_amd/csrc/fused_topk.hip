@@ -509,6 +509,21 @@ __global__ __launch_bounds__(256) void k_fill_empty(int64_t n, int32_t* idx, flo
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+__global__ __launch_bounds__(256) void k_zero_words(int64_t n, uint32_t* w) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) w[i] = 0u;
+}
+
+// Fewer rows than this: the scorer writes the logits into the workspace and the plain
+// top-k selects from them.  The sampled-threshold path pays off when many rows share
+// the chip (prefill); with few rows its one-workgroup-per-row selection over each
+// row's kept scores is the slow part (4 rows of 100k: 190 against 22 us).
+constexpr int kFusedMinRows = 512;
+
+bool logits_topk_via_logits(const LogitsParams& p) { return p.T < kFusedMinRows; }
+
+size_t via_logits_bytes(const LogitsParams& p) { return align256((size_t)p.T * p.out_cols * 4); }
+
 struct FusedLayout {
     size_t bt_s, lens_s, slog, lo, flags, counts, cand, total;
     int Ws, cols_s;
@@ -542,9 +557,9 @@ hipError_t launch_fill_empty_topk(int T, int k, int32_t* out_idx, float* out_val
 }
 
 size_t logits_topk_workspace_bytes(const LogitsParams& p, int k) {
-    (void)k;
     LogitsParams pf = p;
     if (!plan_logits(pf)) return 0;
+    if (logits_topk_via_logits(p)) return via_logits_bytes(p) + align256(topk_workspace_bytes(p.T, p.out_cols, k));
     return fused_layout(pf).total;
 }
 
@@ -552,6 +567,38 @@ hipError_t launch_logits_topk(const LogitsParams& p, int k, int32_t* out_idx, fl
                               void* workspace, size_t ws_bytes, hipStream_t stream) {
     LogitsParams pf = p;
     if (!plan_logits(pf)) return hipErrorInvalidValue;
+    if (logits_topk_via_logits(p)) {
+        const size_t lb = via_logits_bytes(p);
+        const size_t tb = align256(topk_workspace_bytes(p.T, p.out_cols, k));
+        if (ws_bytes < lb + tb || k < 1) return hipErrorInvalidValue;
+        uint8_t* ws = static_cast<uint8_t*>(workspace);
+        LogitsParams pl = p;
+        pl.out = reinterpret_cast<float*>(ws);
+        pl.out_rs = p.out_cols;
+        pl.lo = nullptr;
+        pl.flags = nullptr;
+        pl.cand = nullptr;
+        pl.counts = nullptr;
+        hipError_t e = launch_logits(pl, stream);
+        if (e != hipSuccess) return e;
+        TopkParams tp{};
+        tp.scores = pl.out;
+        tp.row_stride = p.out_cols;
+        tp.rows = p.T;
+        tp.cols = p.out_cols;
+        tp.k = k;
+        tp.row_lens = p.lens;
+        tp.out_idx = out_idx;
+        tp.out_vals = out_vals;
+        tp.workspace = tb ? ws + lb : nullptr;
+        const size_t zb = topk_workspace_zero_bytes(p.T, p.out_cols, k);
+        if (zb) {  // the top-k's histograms start zero (a kernel, not a memset)
+            const int64_t n = (int64_t)((zb + 3) / 4);
+            hipLaunchKernelGGL(k_zero_words, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, n,
+                               reinterpret_cast<uint32_t*>(ws + lb));
+        }
+        return launch_topk(tp, stream);
+    }
     if (pf.n_wchunks > kMaxChunks || k < 1 || k > kSortCap) return hipErrorInvalidValue;
     const FusedLayout l = fused_layout(pf);
     if (ws_bytes < l.total) return hipErrorInvalidValue;

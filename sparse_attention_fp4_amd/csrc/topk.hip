@@ -345,6 +345,12 @@ size_t topk_workspace_bytes(int rows, int cols, int k) {
     return topk_long_rows(rows, cols) ? topk_long_workspace_bytes(rows, cols, k) : 0;
 }
 
+size_t topk_long_zero_bytes(int rows, int cols);
+size_t topk_workspace_zero_bytes(int rows, int cols, int k) {
+    (void)k;
+    return topk_long_rows(rows, cols) ? topk_long_zero_bytes(rows, cols) : 0;
+}
+
 #ifndef FP4IDX_TOPK_STREAM
 #define FP4IDX_TOPK_STREAM 0
 #endif

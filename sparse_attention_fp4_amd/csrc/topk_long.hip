@@ -61,6 +61,7 @@ struct LongWs {
     uint2* cand;         // [rows][n_chunks][kChunk]  candidates (bin d1): (key, column), column order
     int32_t* cnum;       // [rows][n_chunks]          candidates per chunk
     int n_chunks;
+    size_t zero_end;     // bytes from the base through hist2: zero when a call starts
 };
 
 __device__ __forceinline__ uint32_t to_key(float v) {
@@ -479,6 +480,7 @@ LongWs carve(void* base, int rows, int cols, size_t* bytes) {
     o = align256(o + (size_t)rows * kBins * 4);
     w.hist2 = reinterpret_cast<uint32_t*>(b + o);
     o = align256(o + (size_t)rows * kBins * 4);
+    w.zero_end = o;
     w.bitmap = reinterpret_cast<uint32_t*>(b + o);
     o = align256(o + rc * kWords * 4);
     w.cand = reinterpret_cast<uint2*>(b + o);
@@ -496,6 +498,11 @@ LongWs carve(void* base, int rows, int cols, size_t* bytes) {
 // one workgroup per row (4 rows of 16384 columns: 14.5 against 16.5 us), while many
 // rows keep the chip busy one workgroup each.
 bool topk_long_rows(int rows, int cols) { return cols > 32768 || (cols > 8192 && rows <= 64); }
+
+// Leading workspace bytes that must be zero when a call starts: the row states and the
+// two histograms come first in the layout (a caller that cannot keep the workspace
+// between calls clears just these).
+size_t topk_long_zero_bytes(int rows, int cols) { return carve(nullptr, rows, cols, nullptr).zero_end; }
 
 size_t topk_long_workspace_bytes(int rows, int cols, int k) {
     (void)k;

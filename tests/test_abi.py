@@ -196,8 +196,10 @@ def test_logits_topk_workspace_size():
     small = f(0, 4, 1, 32, 1, 64, 32, 2048, 256)
     big = f(0, 4, 1, 32, 1, 64, 64, 4096, 256)
     assert 0 < small < big
-    # the kept-score buffer (8 bytes per column and row) dominates: the logits would be 4
-    assert big >= 4 * 4096 * 8
+    # fewer than 512 rows: the logits themselves (4 bytes per column and row) and the
+    # top-k's histograms; 512 rows or more: the kept-score buffer (8 bytes each)
+    assert big >= 4 * 4096 * 4
+    assert f(0, 600, 2, 32, 1, 64, 64, 4096, 256) >= 600 * 4096 * 8
     assert f(0, 4, 1, 30, 4, 64, 32, 2048, 256) == 0       # H % Hkv != 0
     assert f(0, 4, 1, 32, 1, 32, 32, 2048, 256) == 0       # page size
     assert f(0, 0, 1, 32, 1, 64, 32, 2048, 256) == 0       # no rows

@@ -1,5 +1,8 @@
 """GPU parity of fp4idx_logits_topk_paged (scores and top-k without writing the logits).
 
+Fewer than 512 rows go through the logits (in the workspace) and the plain top-k; 512
+or more take the sampled-threshold path, whose cases below use 560-600 rows.
+
 Against the oracle: the chosen column sets equal the oracle's top-k of its own logits,
 except for columns whose oracle scores tie with the oracle's k-th within the logits
 tolerance (1e-6 of the summed |w ReLU(dot)| of both columns), as for the unfused path.
@@ -157,3 +160,38 @@ def test_config4_prefill_sampled_rows():
     ui, uv = _unfused(case, 2048)
     np.testing.assert_array_equal(gi, ui)
     np.testing.assert_array_equal(gv.view(np.uint32), uv.view(np.uint32))
+
+
+# ---- the sampled-threshold path (512 rows or more)
+
+def test_sampled_path_many_rows():
+    case = wl.make_logits("fused_many", q_per_req=[300, 260], ctx=[9000, 5000], H=32, seed=91)
+    gi, gv = _fused(case, 512)
+    _check_oracle(case, gi, 512, rows=[0, 1, 150, 299, 300, 301, 559])
+    _check_unfused(case, gi, gv, 512)
+
+
+def test_sampled_path_defeated_rows_take_the_second_pass():
+    """As test_sample_defeated_rows_take_the_second_pass, with enough rows for the
+    sampled-threshold path: request 0's largest scores all lie on sampled pages."""
+    case = wl.make_logits("defeat_many", q_per_req=[300, 300], ctx=[60000, 50000], H=32, seed=78)
+    case.k_scale[...] = 123
+    W = case.block_table.shape[1]
+    for lp in range(0, W, 16):
+        ph = case.block_table[0, lp]
+        if ph >= 0:
+            case.k_scale[ph] = 131
+    gi, gv = _fused(case, 2048)
+    _check_oracle(case, gi, 2048, rows=[0, 5, 299, 300, 599])
+    _check_unfused(case, gi, gv, 2048)
+
+
+def test_sampled_path_invalid_pages_and_rows_outside_requests():
+    case = wl.make_logits("holes_many", q_per_req=[300, 300], ctx=[8000, 6000], H=32, seed=13)
+    case.block_table[0, 5] = -1
+    case.block_table[1, 2] = case.k_fp4.shape[0] + 3
+    case.cu_seqlens_q[-1] -= 1                       # the last row belongs to no request
+    gi, gv = _fused(case, 1024)
+    _check_oracle(case, gi, 1024, rows=[0, 1, 299, 300, 598])
+    assert np.all(gi[-1] == -1) and np.all(gv[-1] == -np.inf)
+    _check_unfused(case, gi, gv, 1024)
