@@ -23,6 +23,8 @@
 //   6. the scorer runs again for the row blocks holding a flagged row, keeping every
 //      score of those rows, and the selection is redone for them (both launches find
 //      nothing to do when no row is flagged).
+// That pipeline pays off with many rows (prefill).  With fewer than 512 rows the
+// logits do go to the workspace, and the plain top-k selects from them.
 #include "device_common.hpp"
 #include "fp4idx_internal.hpp"
 
