@@ -195,3 +195,14 @@ def test_sampled_path_invalid_pages_and_rows_outside_requests():
     _check_oracle(case, gi, 1024, rows=[0, 1, 299, 300, 598])
     assert np.all(gi[-1] == -1) and np.all(gv[-1] == -np.inf)
     _check_unfused(case, gi, gv, 1024)
+
+
+def test_sampled_path_one_row_per_request():
+    """520 requests of one row each: the sampled-threshold path with one-row blocks
+    (two waves per scorer workgroup), contexts from 300 to 5000 keys."""
+    rng = np.random.default_rng(93)
+    ctx = rng.integers(300, 5000, 520).tolist()
+    case = wl.make_logits("fused_one_row", q_per_req=[1] * 520, ctx=ctx, H=64, seed=94)
+    gi, gv = _fused(case, 1024)
+    _check_oracle(case, gi, 1024, rows=[0, 1, 2, 259, 518, 519])
+    _check_unfused(case, gi, gv, 1024)
