@@ -40,6 +40,9 @@ constexpr int kWavesPerBlock = 4;
 #ifndef FP4IDX_BLOCK_LDS_BUFS
 #define FP4IDX_BLOCK_LDS_BUFS 1  // decoded NVFP4 key blocks in LDS: 1 (32 KB) or 2 (64 KB)
 #endif
+#ifndef FP4IDX_BLOCK_XCD_RUN
+#define FP4IDX_BLOCK_XCD_RUN 32  // consecutive workgroups kept on one XCD (0: dispatch order)
+#endif
 #ifndef FP4IDX_BLOCK_CHUNK_NV
 #define FP4IDX_BLOCK_CHUNK_NV 8  // 128-key blocks per NVFP4 wave
 #endif
@@ -245,10 +248,13 @@ __global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
     const int n_qtiles = (p.Tq + 15) / 16;
     const int n_hgrp = (p.R + NB - 1) / NB;
     // block index -> (kv head, key chunk, head group, 4 consecutive query tiles); the
-    // query tiles of one key chunk are neighbours, so their key reads meet in L2
+    // query tiles of one key chunk are neighbours, so their key reads meet in L2 -- and
+    // runs of 32 neighbours go to one XCD, whose L2 is its own (half the HBM fetches of
+    // dispatch order, same time)
     const int qt_blocks = (n_qtiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int bx = blockIdx.x;
     const int per_hk = p.n_kchunks * n_hgrp * qt_blocks;
+    const int bx = FP4IDX_BLOCK_XCD_RUN ? xcd_order(blockIdx.x, FP4IDX_BLOCK_XCD_RUN) : (int)blockIdx.x;
+    if (bx >= p.Hkv * per_hk) return;  // grid padding
     const int hk = bx / per_hk;
     int rem = bx - hk * per_hk;
     const int kc = rem / (n_hgrp * qt_blocks);
@@ -463,7 +469,8 @@ hipError_t launch_fmt_nb(const BlockParams& p, hipStream_t stream) {
     const int qt_blocks = (n_qtiles + kWavesPerBlock - 1) / kWavesPerBlock;
     const int64_t blocks = (int64_t)p.Hkv * p.n_kchunks * n_hgrp * qt_blocks;
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((k_block_scores<FMT, NB>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    const int64_t grid = FP4IDX_BLOCK_XCD_RUN ? xcd_grid(blocks, FP4IDX_BLOCK_XCD_RUN) : blocks;
+    hipLaunchKernelGGL((k_block_scores<FMT, NB>), dim3((unsigned)grid), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

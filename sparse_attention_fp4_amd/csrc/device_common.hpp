@@ -92,6 +92,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// The dispatcher deals consecutive workgroups to the chip's 8 dies (XCDs, each with its
+// own L2) in turn.  xcd_order maps a dispatched block index to a logical one so that runs
+// of `run` consecutive logical blocks land on one die: neighbours that read the same data
+// share an L2.  The grid must be a multiple of 8 * run (xcd_grid); logical indices past
+// the real block count must exit.
+__device__ __forceinline__ int xcd_order(int b, int run) {
+    const int k = b >> 3;
+    return (k / run) * (8 * run) + (b & 7) * run + k % run;
+}
+inline int64_t xcd_grid(int64_t blocks, int run) {
+    const int64_t g = 8 * (int64_t)run;
+    return (blocks + g - 1) / g * g;
+}
+
 // Workgroup barrier that orders LDS only.  Every barrier in this library guards data in
 // LDS; __syncthreads() would also wait for each wave's outstanding global loads and
 // stores, which keeps prefetched data from staying in flight across the barrier.
