@@ -170,19 +170,27 @@ long orc_logits_paged(int fmt,
     int G = orc_groups(fmt);
     int R = H / Hkv;
     int nr = rows ? n_rows : T;
+    /* the work is shared out by (row, run of ORC_COLS columns) so that a few long rows
+     * still keep every thread busy; each output element is computed the same way */
+    enum { ORC_COLS = 2048 };
+    int n_runs = (out_cols + ORC_COLS - 1) / ORC_COLS;
     long inexact = 0;
+    (void)T;
 #ifdef _OPENMP
     if (n_threads > 0) omp_set_num_threads(n_threads);
 #else
     (void)n_threads;
 #endif
 #pragma omp parallel for schedule(dynamic, 1) reduction(+ : inexact)
-    for (int ri = 0; ri < nr; ri++) {
+    for (int64_t it = 0; it < (int64_t)nr * n_runs; it++) {
+        int ri = (int)(it / n_runs);
+        int s_begin = (int)(it % n_runs) * ORC_COLS;
+        int s_end = s_begin + ORC_COLS < out_cols ? s_begin + ORC_COLS : out_cols;
         int t = rows ? rows[ri] : ri;
         int b = 0;
         while (b + 1 <= B && cu_seqlens_q[b + 1] <= t) b++;
         if (b >= B) { /* a row outside every request sees nothing */
-            for (int s = 0; s < out_cols; s++) {
+            for (int s = s_begin; s < s_end; s++) {
                 logits[(int64_t)t * out_rs + s] = -INFINITY;
                 if (tolbase) tolbase[(int64_t)t * out_rs + s] = 0.0f;
             }
@@ -193,7 +201,7 @@ long orc_logits_paged(int fmt,
         for (int h = 0; h < H; h++)
             orc_dequant_vec(fmt, q_fp4 + (int64_t)t * q_rs + (int64_t)h * 64,
                             q_scale + (int64_t)t * qs_rs + (int64_t)h * G, qv + (size_t)h * 128);
-        for (int s = 0; s < out_cols; s++) {
+        for (int s = s_begin; s < s_end; s++) {
             float* o = logits + (int64_t)t * out_rs + s;
             if (tolbase) tolbase[(int64_t)t * out_rs + s] = 0.0f;
             int visible = s < row_lens[t];
@@ -207,9 +215,11 @@ long orc_logits_paged(int fmt,
             double acc = 0.0, tb = 0.0;
             for (int h = 0; h < H; h++) {
                 int hk = h / R;
-                const uint8_t* kp = k_fp4 + (int64_t)phys * kp_s + ((int64_t)hk * page + off) * 64;
-                const uint8_t* ks = k_scale + (int64_t)phys * ksp_s + ((int64_t)hk * page + off) * G;
-                orc_dequant_vec(fmt, kp, ks, kv);
+                if (h % R == 0) { /* the first query head of key head hk: decode that key */
+                    const uint8_t* kp = k_fp4 + (int64_t)phys * kp_s + ((int64_t)hk * page + off) * 64;
+                    const uint8_t* ks = k_scale + (int64_t)phys * ksp_s + ((int64_t)hk * page + off) * G;
+                    orc_dequant_vec(fmt, kp, ks, kv);
+                }
                 double dot, asum;
                 if (!orc_dot(qv + (size_t)h * 128, kv, &dot, &asum)) inexact++;
                 /* the exact dot rounded once to fp32 is the per-head logit; the weighted

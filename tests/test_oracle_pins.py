@@ -299,6 +299,27 @@ def test_invalid_page_ids_are_invisible():
 
 
 # ---------------------------------------------------------------- block-score pins
+def test_rows_outside_every_request_see_nothing():
+    """A row t >= cu_seqlens_q[B] belongs to no request, so it sees no key and is -inf
+    everywhere (with tolerance base 0), however long its row_lens entry.  Pinned against
+    the same rows counted into the last request, where they see that request's keys
+    (finite values): an oracle that gave an orphan row to request B-1 fails here.  The
+    rows inside requests must not change."""
+    case = _small_logits(seed=17, ctx=(150, 90), q_per_req=(2, 3))
+    full, _, _ = _run(case)
+    T = case.T
+    last = range(int(case.cu_seqlens_q[1]), T)
+    for t in last:
+        assert np.all(np.isfinite(full[t, :90])) and np.all(full[t, 90:] == -np.inf)
+    case.cu_seqlens_q[-1] = T - 2            # the last two rows now belong to no request
+    cut, tb, _ = orc.logits_paged(case.fmt, case.q_fp4, case.q_scale, case.w, case.k_fp4,
+                                  case.k_scale, case.block_table, case.cu_seqlens_q,
+                                  case.row_lens, case.page_size, case.out_cols,
+                                  want_tolbase=True)
+    assert np.all(cut[T - 2:] == -np.inf) and np.all(tb[T - 2:] == 0)
+    np.testing.assert_array_equal(cut[:T - 2], full[:T - 2])
+
+
 def test_causal_visibility_fixture():
     for q_len, k_len, qo, ql, vis in _rows("causal_visibility.txt"):
         q_len, k_len, ql = int(q_len), int(k_len), int(ql)
