@@ -36,7 +36,12 @@
  *     value 2^(code-127); NVFP4 = one E4M3 (fn) code per 16 values (G=8), with no
  *     tensor-level global scale.  real[d] = E2M1[d] * scale[floor(d / S)].  E8M0 codes
  *     0 and 255 are outside the stored range 1..254 [SGL Modifications]; what they give
- *     is not specified.
+ *     is not specified (a code-255 scale makes the matrix core return NaN, and an MXFP4
+ *     logit that holds such a head dot is NaN).  Every stored code 1..254 and every
+ *     E4M3 code is decoded exactly.
+ *   - NaN: a NaN head dot (only a NaN E4M3 scale code, or the E8M0 code 255 above, can
+ *     make one) counts as 0 in the NVFP4 ReLU and is skipped by the block maxima; top-k
+ *     never selects NaN.
  */
 #ifndef FP4IDX_H
 #define FP4IDX_H
@@ -83,7 +88,8 @@ enum {
  *           page (values then scales, [SGL] bench) is k_scale = k_fp4 + Hkv*page_size*64
  *           with both page strides = Hkv*page_size*(64+G).
  *   block_table [B][table_width] int32 (rows bt_row_stride apart), -1 = no page
- *   cu_seqlens_q [B+1] int32, nondecreasing, cu_seqlens_q[0] = 0, cu_seqlens_q[B] = T
+ *   cu_seqlens_q [B+1] int32, nondecreasing, cu_seqlens_q[0] = 0, cu_seqlens_q[B] <= T;
+ *           a row t >= cu_seqlens_q[B] belongs to no request and is -inf everywhere
  *   row_lens [T] int32
  *   logits [T][out_cols] float, rows out_row_stride floats apart
  * Alignment: q_fp4, k_fp4, k_scale and their row/page strides must be multiples of 16
@@ -203,8 +209,9 @@ size_t fp4idx_topk_workspace_bytes(int rows, int cols, int k);
  * most 8192 columns, or of at most 32768 columns when there are more than 64 rows, need
  * none).  It carries per-row histograms between the kernels
  * of one call: it must be zero-filled before its first use, and every call that
- * returns FP4IDX_OK leaves it ready for the next one.  Calls that run concurrently
- * must not share a workspace.
+ * returns FP4IDX_OK leaves it ready for the next one (also under graph replay).  After
+ * a call that returns FP4IDX_EHIP (a launch failed part way) it must be zero-filled
+ * again.  Calls that run concurrently must not share a workspace.
  * Limits: 1 <= k <= 8192 and cols <= 524288 (else EUNSUPPORTED). */
 int fp4idx_topk(const float* scores, int64_t row_stride, int rows, int cols,
                 const int32_t* row_lens, int k,

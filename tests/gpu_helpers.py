@@ -11,6 +11,18 @@ import sparse_attention_fp4_amd as fp4
 from oracle import oracle as orc
 
 
+# Per-head dot bound, |gpu - exact| <= DOT_BOUND[fmt] * sum_d |q_d k_d|:
+#  MXFP4: the scaled FP4 matrix core forms each 32-element block sum exactly, scales it
+#         and adds the four block values to the fp32 accumulator in order (measured: every
+#         dot bit-exact at scale codes 123..131), so at most three roundings: 2^-22.
+#  NVFP4: four fp16 MFMAs of 32 exact products each, chained through the accumulator.
+#         How one such instruction adds its products is not documented and no exact-sum
+#         model reproduces it (measured: up to 4.6 * 2^-24 * (sum |products| + |C|) for a
+#         single instruction); the bound assumes only one rounding per addition, in any
+#         order, over the 128 products: 128 * 2^-24 = 2^-17.
+DOT_BOUND = {0: 2.0 ** -22, 1: 2.0 ** -17}
+
+
 def say(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()
@@ -90,3 +102,28 @@ def gpu_topk(scores_np, k, row_lens=None):
     idx, vals = fp4.topk(s, k, rl)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), vals.cpu().numpy()
+
+
+def check_topk_against_oracle(ref, tb, gidx, k, lens, label="rows"):
+    """Tie-tolerant comparison of GPU top-k indices with the oracle's top-k of its own
+    scores `ref` (rows of the same length as gidx): the chosen sets have the oracle's
+    size, are listed in increasing column order and -1 padded, and may differ only in
+    columns whose oracle score ties with the oracle's k-th within the logits tolerance
+    (1e-6 of the summed |w ReLU(dot)| of both columns).  Returns the number of such
+    columns."""
+    oi, _ = orc.topk(ref, k, lens)
+    ndiff = 0
+    for i in range(ref.shape[0]):
+        g = gidx[i]
+        a, b = set(g[g >= 0].tolist()), set(oi[i][oi[i] >= 0].tolist())
+        assert len(a) == len(b), (label, i, len(a), len(b))
+        assert np.all(g[len(a):] == -1) and np.all(np.diff(g[:len(a)]) > 0)
+        if not b:
+            continue
+        sel = np.array(sorted(b))
+        kcol = sel[np.argmin(ref[i][sel])]
+        for c in a ^ b:
+            gap = abs(float(ref[i, c]) - float(ref[i, kcol]))
+            assert gap <= 1e-6 * (float(tb[i, c]) + float(tb[i, kcol])) + 1e-30, (label, i, c)
+        ndiff += len(a ^ b)
+    return ndiff

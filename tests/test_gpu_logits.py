@@ -14,7 +14,7 @@ import sparse_attention_fp4_amd as fp4
 from oracle import oracle as orc
 from sparse_attention_fp4_amd import workloads as wl
 
-from .gpu_helpers import check_logits, dev, gpu_logits, oracle_logits, say
+from .gpu_helpers import DOT_BOUND, check_logits, dev, gpu_logits, oracle_logits, say
 
 pytestmark = pytest.mark.gpu
 
@@ -37,15 +37,12 @@ def test_config1_decode_contexts(ctx):
     _parity(wl.config1(ctx))
 
 
-def test_config1_400k_sampled_rows_match():
-    case = wl.config1(400_000)
-    _parity(case, rows=[0, 3])
+def test_config1_400k_all_rows():
+    _parity(wl.config1(400_000))
 
 
-def test_config2_batched_decode_sampled_rows():
-    case = wl.config2()
-    rows = [0, 1, 17, 40, 63]
-    _parity(case, rows=rows)
+def test_config2_batched_decode_all_rows():
+    _parity(wl.config2())
 
 
 SMALL = [
@@ -85,10 +82,15 @@ def test_visibility_boundaries():
 
 
 def test_invalid_pages_and_rows_outside_requests():
+    """A -1 page and a page past the cache are invisible; the last row lies past
+    cu_seqlens_q[B], belongs to no request and must be -inf everywhere."""
     case = wl.make_logits("invalid", q_per_req=[3, 2], ctx=[300, 200], H=32, seed=8)
     case.block_table[0, 1] = -1
     case.block_table[1, 2] = case.num_pages + 5
-    _parity(case)
+    case.cu_seqlens_q[-1] = case.T - 1
+    got, _ = _parity(case)
+    assert np.all(got[case.T - 1] == -np.inf)
+    assert np.all(np.isfinite(got[case.T - 2, :128]))
 
 
 def test_page_permutation_gives_identical_logits():
@@ -156,22 +158,23 @@ def _flip_sign(packed):
     return packed ^ np.uint8(0x88)
 
 
-@pytest.mark.parametrize("e8", [(123, 131), (120, 134)])
-def test_per_head_dots_through_one_hot_weights(e8):
-    """w = e_h gives ReLU(dot_h) with no further rounding; flipping every query sign
-    bit gives ReLU(-dot_h).  The MFMA adds its four exact 32-element block sums in fp32,
-    so a dot differs from the correctly rounded one only when such an addition rounds:
-    at scale codes 123..131 at least 99.9% must be bit-exact; every dot is held to
-    three fp32 roundings, 2^-22 * sum_d |q_d k_d|."""
-    case = wl.make_logits("onehot", q_per_req=[4], ctx=[640], H=32, seed=31, e8_lo=e8[0],
-                          e8_hi=e8[1])
-    K = orc.dequant(0, case.k_fp4[:, 0], case.k_scale[:, 0])      # [P, page, 128] physical
-    Kl = K[case.block_table[0, :10]].reshape(-1, 128)[:640]         # logical order
+def _one_hot_head_dots(fmt, heads, **kw):
+    """Per-head dots through one-hot head weights: w = e_h gives ReLU(dot_h) with no
+    further rounding; flipping every query sign bit gives ReLU(-dot_h).  Returns (bit-exact
+    count, total) over the visible values; every dot is held to DOT_BOUND[fmt] *
+    sum_d |q_d k_d| and to the oracle's -inf pattern."""
+    base = wl.make_logits("onehot", fmt=fmt, **kw)
+    Hkv = base.Hkv
+    R = base.H // Hkv
     mism = total = 0
-    for h in (0, 5, 17, 31):
+    for h in heads:
+        hk = h // R
+        K = orc.dequant(fmt, base.k_fp4[:, hk], base.k_scale[:, hk])   # [P, page, 128]
+        n_keys = int(base.row_lens.max())
+        npg = -(-n_keys // base.page_size)
+        Kl = K[base.block_table[0, :npg]].reshape(-1, 128)[:n_keys]     # logical order
         for sign in (1, -1):
-            c = wl.make_logits("onehot", q_per_req=[4], ctx=[640], H=32, seed=31, e8_lo=e8[0],
-                               e8_hi=e8[1])
+            c = wl.make_logits("onehot", fmt=fmt, **kw)
             c.w[:] = 0
             c.w[:, h] = 1.0
             if sign < 0:
@@ -179,17 +182,44 @@ def test_per_head_dots_through_one_hot_weights(e8):
             got = gpu_logits(c)
             ref, _, inexact = oracle_logits(c)
             assert inexact == 0
-            Q = orc.dequant(0, c.q_fp4[:, h], c.q_scale[:, h])       # [4, 128]
-            absbase = np.abs(Q) @ np.abs(Kl).T                       # [4, 640]
+            Q = orc.dequant(fmt, c.q_fp4[:, h], c.q_scale[:, h])
+            absbase = np.abs(Q) @ np.abs(Kl).T
             vis = ref != -np.inf
-            diff = got[vis] != ref[vis]
-            mism += int(diff.sum())
+            assert np.array_equal(got == -np.inf, ~vis)
+            mism += int((got[vis] != ref[vis]).sum())
             total += int(vis.sum())
             err = np.abs(got[vis].astype(np.float64) - ref[vis])
-            assert np.all(err <= 2.0 ** -22 * absbase[vis])
-    say(f"    per-head bit-exact: {total - mism}/{total}")
-    if e8 == (123, 131):
-        assert mism <= 1e-3 * total
+            assert np.all(err <= DOT_BOUND[fmt] * absbase[:, :ref.shape[1]][vis])
+    return total - mism, total
+
+
+def test_per_head_dots_bit_exact_at_scale_codes_123_131():
+    """MXFP4: the scaled MFMA forms each 32-element block sum exactly, scales it and adds
+    the four block values in fp32; at scale codes 123..131 (configs 0, 1 and 4) every one
+    of these per-head dots is the correctly rounded value."""
+    ok, total = _one_hot_head_dots(wl.MXFP4, (0, 5, 17, 31), q_per_req=[4], ctx=[640], H=32,
+                                   seed=31, e8_lo=123, e8_hi=131)
+    say(f"    per-head bit-exact: {ok}/{total}")
+    assert ok == total
+
+
+def test_per_head_dots_at_scale_codes_120_134():
+    """Config 2's wider code range: a block addition can round; the exact fraction is
+    reported and held to the 2^-22 bound everywhere (measured 98.8%)."""
+    ok, total = _one_hot_head_dots(wl.MXFP4, (0, 5, 17, 31), q_per_req=[4], ctx=[640], H=32,
+                                   seed=31, e8_lo=120, e8_hi=134)
+    say(f"    per-head bit-exact: {ok}/{total} = {ok / total:.4f}")
+    assert ok >= 0.98 * total
+
+
+def test_per_head_dots_nvfp4():
+    """NVFP4 (config 3's E4M3 codes): four fp16 MFMAs of 32 exact products, accumulated in
+    fp32; the bit-exact fraction is reported and asserted (measured 95.0%), every dot is
+    within the NVFP4 bound."""
+    ok, total = _one_hot_head_dots(wl.NVFP4, (0, 3, 6), q_per_req=[4], ctx=[700], H=8, Hkv=2,
+                                   seed=37)
+    say(f"    per-head bit-exact: {ok}/{total} = {ok / total:.4f}")
+    assert ok >= 0.94 * total
 
 
 # ---- long causal prefill at full size: 32768 x 32768 logits stay on the device; the
