@@ -37,18 +37,9 @@ namespace fp4idx {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
-#ifndef FP4IDX_BLOCK_LDS_BUFS
-#define FP4IDX_BLOCK_LDS_BUFS 1  // decoded NVFP4 key blocks in LDS: 1 (32 KB) or 2 (64 KB)
-#endif
-#ifndef FP4IDX_BLOCK_XCD_RUN
-#define FP4IDX_BLOCK_XCD_RUN 32  // consecutive workgroups kept on one XCD (0: dispatch order)
-#endif
-#ifndef FP4IDX_BLOCK_CHUNK_NV
-#define FP4IDX_BLOCK_CHUNK_NV 8  // 128-key blocks per NVFP4 wave
-#endif
-#ifndef FP4IDX_BLOCK_CHUNK
-#define FP4IDX_BLOCK_CHUNK 16  // 128-key blocks per MXFP4 wave
-#endif
+constexpr int kXcdRun = 32;     // consecutive workgroups kept on one XCD
+constexpr int kChunkNv = 8;     // 128-key blocks per NVFP4 wave
+constexpr int kChunkMx = 16;    // 128-key blocks per MXFP4 wave
 
 template <int FMT>
 struct QOperand;
@@ -81,7 +72,7 @@ __device__ __forceinline__ float max3_raw(float a, float b, float c) {
 template <int NB>
 __device__ __forceinline__ void block_scores_shared(const BlockParams& p, int hk, int kc, int h0,
                                                     int nh, int qt, int b, int t_last,
-                                                    v8h (*sk)[8][4][64]) {
+                                                    v8h (*sk)[4][64]) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 4, n = lane & 15;
@@ -173,8 +164,10 @@ __device__ __forceinline__ void block_scores_shared(const BlockParams& p, int hk
         }
     };
     auto block = [&](int kb, const KBlk& t) {
-        v8h (*buf)[4][64] = sk[FP4IDX_BLOCK_LDS_BUFS == 2 ? (kb & 1) : 0];
-        if (FP4IDX_BLOCK_LDS_BUFS == 1) __syncthreads();
+        // one 32 KB tile (three workgroups per CU; two buffers measured slower): wait
+        // until every wave is done with the previous block
+        v8h (*buf)[4][64] = sk;
+        __syncthreads();
         stage(t.k0, t.s0, buf[wave]);
         stage(t.k1, t.s1, buf[wave + 4]);
         __syncthreads();
@@ -253,7 +246,7 @@ __global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
     // dispatch order, same time)
     const int qt_blocks = (n_qtiles + kWavesPerBlock - 1) / kWavesPerBlock;
     const int per_hk = p.n_kchunks * n_hgrp * qt_blocks;
-    const int bx = FP4IDX_BLOCK_XCD_RUN ? xcd_order(blockIdx.x, FP4IDX_BLOCK_XCD_RUN) : (int)blockIdx.x;
+    const int bx = xcd_order(blockIdx.x, kXcdRun);
     if (bx >= p.Hkv * per_hk) return;  // grid padding
     const int hk = bx / per_hk;
     int rem = bx - hk * per_hk;
@@ -263,7 +256,7 @@ __global__ __launch_bounds__(256) void k_block_scores(const BlockParams p) {
     const int qt = (rem - hgrp * qt_blocks) * kWavesPerBlock + (threadIdx.x >> 6);
     if constexpr (FMT == 1) {
         // the workgroup's 64 tokens in one batch item: shared key decoding
-        __shared__ __align__(16) v8h sk[FP4IDX_BLOCK_LDS_BUFS][8][4][64];
+        __shared__ __align__(16) v8h sk[8][4][64];
         const int qt0 = (rem - hgrp * qt_blocks) * kWavesPerBlock;
         const int t_first = qt0 * 16, t_last = min(qt0 * 16 + 64, p.Tq) - 1;
         const RowRequest ra = find_request(p.cu_q, p.B, t_first);
@@ -469,7 +462,7 @@ hipError_t launch_fmt_nb(const BlockParams& p, hipStream_t stream) {
     const int qt_blocks = (n_qtiles + kWavesPerBlock - 1) / kWavesPerBlock;
     const int64_t blocks = (int64_t)p.Hkv * p.n_kchunks * n_hgrp * qt_blocks;
     if (blocks <= 0) return hipSuccess;
-    const int64_t grid = FP4IDX_BLOCK_XCD_RUN ? xcd_grid(blocks, FP4IDX_BLOCK_XCD_RUN) : blocks;
+    const int64_t grid = xcd_grid(blocks, kXcdRun);
     hipLaunchKernelGGL((k_block_scores<FMT, NB>), dim3((unsigned)grid), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
@@ -478,7 +471,7 @@ hipError_t launch_fmt_nb(const BlockParams& p, hipStream_t stream) {
 
 hipError_t launch_block_scores(const BlockParams& p_in, hipStream_t stream) {
     BlockParams p = p_in;
-    p.kb_chunk = p.fmt == 0 ? FP4IDX_BLOCK_CHUNK : FP4IDX_BLOCK_CHUNK_NV;
+    p.kb_chunk = p.fmt == 0 ? kChunkMx : kChunkNv;
     p.n_kchunks = (p.ktiles + p.kb_chunk - 1) / p.kb_chunk;
     if (p.n_kchunks == 0) p.n_kchunks = 1;  // no blocks: the grid still runs its (empty) chunk
     if (p.fmt == 0) {

@@ -45,36 +45,15 @@ namespace fp4idx {
 
 namespace {
 
-#ifndef FP4IDX_LOGITS_WPB
-#define FP4IDX_LOGITS_WPB 4     // waves per workgroup sharing a row block of 2 or 4 rows
-#endif
-#ifndef FP4IDX_LOGITS_WPB_R1
-#define FP4IDX_LOGITS_WPB_R1 2  // with one row per block (batched decode: 77.5 -> 75.6 us)
-#endif
+constexpr int kWavesMultiRow = 4;  // waves per workgroup sharing a row block of 2 or 4 rows
+constexpr int kWavesOneRow = 2;    // with one row per block (batched decode: 77.5 -> 75.6 us)
 constexpr int waves_per_block(int rows_per_block) {
-    return rows_per_block == 1 ? FP4IDX_LOGITS_WPB_R1 : FP4IDX_LOGITS_WPB;
+    return rows_per_block == 1 ? kWavesOneRow : kWavesMultiRow;
 }
-#ifndef FP4IDX_LOGITS_WAVES
-#define FP4IDX_LOGITS_WAVES 16384  // target number of waves of one launch
-#endif
-#ifndef FP4IDX_LOGITS_PIPE
-#define FP4IDX_LOGITS_PIPE 2       // products in flight in the epilogue pipeline
-#endif
-#ifndef FP4IDX_LOGITS_RING
-#define FP4IDX_LOGITS_RING 2       // key slabs in the ring (in flight + computing)
-#endif
-#ifndef FP4IDX_LOGITS_WLDS
-#define FP4IDX_LOGITS_WLDS 0       // head weights read from LDS per tile (else registers)
-#endif
-#ifndef FP4IDX_LOGITS_MAX_NT
-#define FP4IDX_LOGITS_MAX_NT 16    // A tiles per block at most (8 or 16)
-#endif
-#ifndef FP4IDX_LOGITS_REVERSE
-#define FP4IDX_LOGITS_REVERSE 0
-#endif
-#ifndef FP4IDX_LOGITS_MAX_PPW
-#define FP4IDX_LOGITS_MAX_PPW 128  // at most this many pages per wave (a multiple of 64)
-#endif
+constexpr int kTargetWaves = 16384;    // waves of one launch (8192 .. 65536 measured)
+constexpr int kPipe = 2;               // products in flight in the epilogue pipeline
+constexpr int kMaxTiles = 16;          // A tiles per block at most (8 or 16)
+constexpr int kMaxPagesPerWave = 128;  // pages per wave at most (a multiple of 64)
 
 // ---------------------------------------------------------------- operand types
 template <int FMT>
@@ -258,12 +237,7 @@ __global__ __launch_bounds__(64 * waves_per_block(RG)) void k_logits(const Logit
     const int g = lane >> 4, n = lane & 15;
     const int bq = blockIdx.x / p.n_wgchunks;
     const int wc = (blockIdx.x - bq * p.n_wgchunks) * kWavesPerBlock + wave;
-#if FP4IDX_LOGITS_REVERSE
-    const int rb = p.n_rowblocks - 1 - bq;
-#else
-    const int rb = bq;
-#endif
-    const int t0 = rb * RG;
+    const int t0 = bq * RG;
     const int nrows = min(RG, p.T - t0);
     const int t_last = t0 + nrows - 1;
     if constexpr (FUSE) {
@@ -373,7 +347,7 @@ __global__ __launch_bounds__(64 * waves_per_block(RG)) void k_logits(const Logit
     RowRequest rq = find_request(p.cu, p.B, t0);
     const int nr1 = max(nrows, 1);  // a row block always holds at least one row
     const int lens_raw = p.lens[t0 + min(g % RG, nr1 - 1)];
-    constexpr int kWin = (FP4IDX_LOGITS_MAX_PPW + 63) / 64;  // 64-page windows per wave
+    constexpr int kWin = (kMaxPagesPerWave + 63) / 64;  // 64-page windows per wave
     int bt_raw[kWin];  // the block-table entry of page lp_begin + 64w + lane (clamped)
 #pragma unroll
     for (int w = 0; w < kWin; w++) {
@@ -494,9 +468,6 @@ __global__ __launch_bounds__(64 * waves_per_block(RG)) void k_logits(const Logit
             dst.s[c] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, soff + 16 * c, 0, 0));
     };
     Slab<FMT> b0, b1;
-#if FP4IDX_LOGITS_RING != 2
-    Slab<FMT> b2;
-#endif
     setup_segment(t0, true);
     issue(0, b0);
     issue(1, b1);
@@ -535,7 +506,7 @@ __global__ __launch_bounds__(64 * waves_per_block(RG)) void k_logits(const Logit
     // products of its own query row
     auto w_tile = [&](int j) { return *reinterpret_cast<const v4f*>(sw + (j * 4 + g) * 4); };
     // more than 8 tiles: the weights are read from LDS a tile at a time
-    constexpr bool kWLds = FP4IDX_LOGITS_WLDS || NT > 8;
+    constexpr bool kWLds = NT > 8;
     v4f wv[kWLds ? 1 : NT];
     if constexpr (!kWLds) {
 #pragma unroll
@@ -582,8 +553,8 @@ __global__ __launch_bounds__(64 * waves_per_block(RG)) void k_logits(const Logit
         }
         const bool st_lane = lane_stores && row_ok;
         int run = 0;  // kept candidates of this lane's row in the chunk (fused)
-        // ---- the wave's slabs: a ring of FP4IDX_LOGITS_RING buffers (two by default:
-        // the next slab's keys are in flight while one is computed; with three, two are)
+        // ---- the wave's slabs: two buffers in turn (the next slab's keys are in flight
+        // while one is computed; a third measured slower)
         // head sums: acc[set][key tile][i]; tiles 8*set .. 8*set+7 go to one set, so
         // no accumulation chain is longer than 8 multiply-adds
         constexpr int kSets = NT > 8 ? 2 : 1;
@@ -621,7 +592,7 @@ __global__ __launch_bounds__(64 * waves_per_block(RG)) void k_logits(const Logit
                 // compiler puts each product's epilogue right behind it and the wave
                 // waits for every product in turn).
                 constexpr int NP = 4 * NT;
-                constexpr int DEPTH = FP4IDX_LOGITS_PIPE;  // products in flight
+                constexpr int DEPTH = kPipe;  // products in flight
                 v4f dq[DEPTH];
                 Operand<FMT> anext = acur;
 #pragma unroll
@@ -706,7 +677,6 @@ __global__ __launch_bounds__(64 * waves_per_block(RG)) void k_logits(const Logit
         // head and make the wait counters there assume that the latest slab must be
         // in, which drains the ring once per pass.)
         int s = 0;
-#if FP4IDX_LOGITS_RING == 2
         for (; s + 2 <= n_vis; s += 2) {
             compute(s, b0);
             issue(s + 2, b0);
@@ -714,18 +684,6 @@ __global__ __launch_bounds__(64 * waves_per_block(RG)) void k_logits(const Logit
             issue(s + 3, b1);
         }
         if (s < n_vis) compute(s, b0);
-#else
-        for (; s + 3 <= n_vis; s += 3) {
-            issue(s + 2, b2);
-            compute(s, b0);
-            issue(s + 3, b0);
-            compute(s + 1, b1);
-            issue(s + 4, b1);
-            compute(s + 2, b2);
-        }
-        if (s < n_vis) compute(s, b0);
-        if (s + 1 < n_vis) compute(s + 1, b1);
-#endif
         fill(vis_pages, st_lane);
         if constexpr (FUSE) {
             if (st_lane && n == 0) p.counts[(int64_t)t_out * p.counts_rs + wc] = run;
@@ -774,7 +732,7 @@ hipError_t launch1(const LogitsParams& p, hipStream_t stream) {
 
 bool plan_logits(LogitsParams& p) {
     // Rows per A-tile group: as many as the average request holds (up to 4), reduced
-    // while the block would need more than FP4IDX_LOGITS_MAX_NT A tiles (at most 16;
+    // while the block would need more than kMaxTiles A tiles (at most 16;
     // they live in LDS).  Any choice is correct; rows of different requests in one block
     // are handled in separate passes.
     int rg = 1;
@@ -784,20 +742,20 @@ bool plan_logits(LogitsParams& p) {
         const int hpt = 16 / rg;  // heads per A tile per row
         p.tiles_per_kv = (p.R + hpt - 1) / hpt;
         p.n_tiles = p.Hkv * p.tiles_per_kv;
-        if (p.n_tiles <= FP4IDX_LOGITS_MAX_NT || rg == 1) break;
+        if (p.n_tiles <= kMaxTiles || rg == 1) break;
         rg >>= 1;
     }
     if (p.n_tiles > 8 * (rg == 1 ? 1 : 2)) return false;  // H <= 128 is checked by the caller
     p.rows_per_block = rg;
     p.n_rowblocks = (p.T + rg - 1) / rg;
     const int n_pages_out = (p.out_cols + p.page - 1) / p.page;
-    // pages per wave: about FP4IDX_LOGITS_WAVES waves, at most FP4IDX_LOGITS_MAX_PPW
+    // pages per wave: about kTargetWaves waves, at most kMaxPagesPerWave
     // pages each.  Long waves spread the per-workgroup set-up (operand staging, the
     // first key loads) over more work; enough of them keep every SIMD busy.  Pages past
     // every row's end only get -inf, from a loop that reads no keys.
     const int64_t total = (int64_t)p.n_rowblocks * n_pages_out;
-    int64_t ppw = (total + FP4IDX_LOGITS_WAVES - 1) / FP4IDX_LOGITS_WAVES;
-    ppw = ppw < 1 ? 1 : (ppw > FP4IDX_LOGITS_MAX_PPW ? FP4IDX_LOGITS_MAX_PPW : ppw);
+    int64_t ppw = (total + kTargetWaves - 1) / kTargetWaves;
+    ppw = ppw < 1 ? 1 : (ppw > kMaxPagesPerWave ? kMaxPagesPerWave : ppw);
     p.ppw = (int)ppw;
     p.n_wchunks = (n_pages_out + p.ppw - 1) / p.ppw;
     const int wpb = waves_per_block(rg);

@@ -351,15 +351,10 @@ size_t topk_workspace_zero_bytes(int rows, int cols, int k) {
     return topk_long_rows(rows, cols) ? topk_long_zero_bytes(rows, cols) : 0;
 }
 
-#ifndef FP4IDX_TOPK_STREAM
-#define FP4IDX_TOPK_STREAM 0
-#endif
-
 // Many rows of at most 32768 columns (prefill): one streaming workgroup per row (see
 // topk_stream.hip) keeps the whole chip busy and reads each row once.  Few rows: the
 // per-row work is spread over many workgroups (topk_long.hip) or held in LDS here.
 bool topk_use_stream(const TopkParams& p) {
-    if (FP4IDX_TOPK_STREAM == 2) return true;
     return p.rows >= 512 && p.cols <= kMaxElems && topk_stream_cap(p.cols, p.k) >= 0;
 }
 

@@ -36,10 +36,8 @@ namespace fp4idx {
 namespace {
 
 constexpr int kChunk = 4096;          // columns per chunk workgroup
-#ifndef FP4IDX_TOPK_LONG_CT
-#define FP4IDX_TOPK_LONG_CT 512  // 8 keys per thread (a chunk's waves run one per SIMD)
-#endif
-constexpr int kCT = FP4IDX_TOPK_LONG_CT;  // threads of a chunk workgroup
+constexpr int kCT = 512;            // threads of a chunk workgroup: 8 keys per thread
+                                    // (its waves run one per SIMD)
 constexpr int kPer = kChunk / kCT;    // elements per thread
 static_assert(kPer * (kCT / 64) == 64, "the collect scan covers 64 (step, wave) blocks");
 constexpr int kBins = 4096;

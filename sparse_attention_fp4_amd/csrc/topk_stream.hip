@@ -32,11 +32,8 @@ namespace fp4idx {
 
 namespace {
 
-#ifndef FP4IDX_TOPK_U
-#define FP4IDX_TOPK_U 4
-#endif
 constexpr int kSBins = 4096;
-constexpr int kU = FP4IDX_TOPK_U;  // 16-byte loads per thread in one chunk of the row
+constexpr int kU = 4;  // 16-byte loads per thread in one chunk of the row
 
 __device__ __forceinline__ uint32_t skey(float v) {
     if (!(v > -__builtin_inff())) return 0u;
