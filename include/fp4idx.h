@@ -146,6 +146,30 @@ int fp4idx_logits_topk_paged(int fmt,
                              int32_t* out_idx, float* out_vals,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Allocation-free fp4idx_logits_topk_paged, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): same arguments and result, without the workspace.  Its scratch is one
+ * static array of FP4IDX_NOALLOC_SCRATCH_BYTES in the library's code object on each
+ * GPU (reserved when the library is first used on that GPU, held until the process
+ * ends); the call allocates nothing.  The stream must belong to the current device.
+ * A request whose fp4idx_logits_topk_workspace_bytes(...) exceeds that size returns
+ * FP4IDX_EWORKSPACE before anything is enqueued (4 rows of 400k columns, or 64 rows of
+ * 131072, fit; long prefills do not).  Every call on one GPU uses the same array, so
+ * calls that overlap on one GPU (other streams, other threads) race: the caller
+ * serialises them.  What must start zeroed is cleared by each call's own kernels. */
+#define FP4IDX_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int fp4idx_logits_topk_paged_noalloc(int fmt,
+                                     const uint8_t* q_fp4, int64_t q_row_stride,
+                                     const uint8_t* q_scale, int64_t qs_row_stride,
+                                     const float* w, int64_t w_row_stride,
+                                     const uint8_t* k_fp4, int64_t k_page_stride,
+                                     const uint8_t* k_scale, int64_t ks_page_stride,
+                                     const int32_t* block_table, int64_t bt_row_stride,
+                                     const int32_t* cu_seqlens_q, const int32_t* row_lens,
+                                     int T, int B, int H, int Hkv, int page_size, int num_pages,
+                                     int table_width, int out_cols, int k,
+                                     int32_t* out_idx, float* out_vals, void* stream);
+
 /* Per-head 128-token block-max scores [M3 数学语义]:
  *
  *     scores[hq][kb][q] = max over valid k_local in [128 kb, 128 kb + 128) of

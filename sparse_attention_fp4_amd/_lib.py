@@ -17,6 +17,7 @@ EXPORTS = (
     "fp4idx_logits_paged",
     "fp4idx_logits_topk_workspace_bytes",
     "fp4idx_logits_topk_paged",
+    "fp4idx_logits_topk_paged_noalloc",
     "fp4idx_block_scores",
     "fp4idx_block_topk",
     "fp4idx_topk_workspace_bytes",
@@ -57,6 +58,10 @@ def lib() -> ctypes.CDLL:
     L.fp4idx_logits_topk_paged.argtypes = [i32, P, i64, P, i64, P, i64, P, i64, P, i64, P, i64, P,
                                            P, i32, i32, i32, i32, i32, i32, i32, i32, i32, P, P,
                                            P, ctypes.c_size_t, P]
+    L.fp4idx_logits_topk_paged_noalloc.restype = i32
+    L.fp4idx_logits_topk_paged_noalloc.argtypes = [i32, P, i64, P, i64, P, i64, P, i64, P, i64, P,
+                                                   i64, P, P, i32, i32, i32, i32, i32, i32, i32,
+                                                   i32, i32, P, P, P]
     L.fp4idx_block_scores.restype = i32
     L.fp4idx_block_scores.argtypes = [i32, P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                       i32, i32, i32, P, P]

@@ -6,6 +6,8 @@
 #include "fp4idx.h"
 #include "fp4idx_internal.hpp"
 
+#include <mutex>
+
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -139,6 +141,61 @@ size_t fp4idx_logits_topk_workspace_bytes(int fmt, int T, int B, int H, int Hkv,
     return fp4idx::logits_topk_workspace_bytes(p, k);
 }
 
+namespace {
+
+// Checks shared by the fused entry point and its allocation-free variant.  Returns
+// FP4IDX_OK with `p` filled when there is work, -1 when the call is complete (no rows,
+// or nothing to select: the output padding is then enqueued), else an error code.
+int logits_topk_prepare(int fmt, const uint8_t* q_fp4, int64_t q_row_stride,
+                        const uint8_t* q_scale, int64_t qs_row_stride, const float* w,
+                        int64_t w_row_stride, const uint8_t* k_fp4, int64_t k_page_stride,
+                        const uint8_t* k_scale, int64_t ks_page_stride,
+                        const int32_t* block_table, int64_t bt_row_stride,
+                        const int32_t* cu_seqlens_q, const int32_t* row_lens, int T, int B,
+                        int H, int Hkv, int page_size, int num_pages, int table_width,
+                        int out_cols, int k, int32_t* out_idx, float* out_vals, void* stream,
+                        fp4idx::LogitsParams& p, size_t& need) {
+    if (k < 1) return FP4IDX_EINVAL;
+    if (k > 2048 || out_cols > (1 << 24)) return FP4IDX_EUNSUPPORTED;
+    const int rc = logits_params(fmt, q_fp4, q_row_stride, q_scale, qs_row_stride, w, w_row_stride,
+                                 k_fp4, k_page_stride, k_scale, ks_page_stride, block_table,
+                                 bt_row_stride, cu_seqlens_q, row_lens, T, B, H, Hkv, page_size,
+                                 num_pages, table_width, out_cols, nullptr, 0, false, p);
+    if (rc > 0) return rc;
+    if (!out_idx && T > 0) return FP4IDX_EINVAL;
+    if (rc < 0) {  // no rows or no columns: nothing is selected
+        if (T == 0) return -1;
+        const int e = hip_status(fp4idx::launch_fill_empty_topk(T, k, out_idx, out_vals, (hipStream_t)stream));
+        return e == FP4IDX_OK ? -1 : e;
+    }
+    need = fp4idx::logits_topk_workspace_bytes(p, k);
+    if (need == 0) return FP4IDX_EUNSUPPORTED;
+    return FP4IDX_OK;
+}
+
+// ---- scratch of the allocation-free entry point: one array per GPU, in the code
+// object, found once per device; host code uses only the looked-up device address.
+constexpr size_t kNoAllocScratchBytes = FP4IDX_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP4IDX_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FP4IDX_EHIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return FP4IDX_OK;
+}
+
+}  // namespace
+
 int fp4idx_logits_topk_paged(int fmt,
                              const uint8_t* q_fp4, int64_t q_row_stride,
                              const uint8_t* q_scale, int64_t qs_row_stride,
@@ -151,24 +208,44 @@ int fp4idx_logits_topk_paged(int fmt,
                              int table_width, int out_cols, int k,
                              int32_t* out_idx, float* out_vals,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    if (k < 1) return FP4IDX_EINVAL;
-    if (k > 2048 || out_cols > (1 << 24)) return FP4IDX_EUNSUPPORTED;
     fp4idx::LogitsParams p;
-    const int rc = logits_params(fmt, q_fp4, q_row_stride, q_scale, qs_row_stride, w, w_row_stride,
-                                 k_fp4, k_page_stride, k_scale, ks_page_stride, block_table,
-                                 bt_row_stride, cu_seqlens_q, row_lens, T, B, H, Hkv, page_size,
-                                 num_pages, table_width, out_cols, nullptr, 0, false, p);
-    if (rc > 0) return rc;
-    if (!out_idx && T > 0) return FP4IDX_EINVAL;
-    if (rc < 0) {  // no rows or no columns: nothing is selected
-        if (T == 0) return FP4IDX_OK;
-        return hip_status(fp4idx::launch_fill_empty_topk(T, k, out_idx, out_vals, (hipStream_t)stream));
-    }
-    const size_t need = fp4idx::logits_topk_workspace_bytes(p, k);
-    if (need == 0) return FP4IDX_EUNSUPPORTED;
+    size_t need = 0;
+    const int rc = logits_topk_prepare(fmt, q_fp4, q_row_stride, q_scale, qs_row_stride, w,
+                                       w_row_stride, k_fp4, k_page_stride, k_scale, ks_page_stride,
+                                       block_table, bt_row_stride, cu_seqlens_q, row_lens, T, B, H,
+                                       Hkv, page_size, num_pages, table_width, out_cols, k, out_idx,
+                                       out_vals, stream, p, need);
+    if (rc != FP4IDX_OK) return rc < 0 ? FP4IDX_OK : rc;
     if (!workspace || workspace_bytes < need || !aligned256(workspace)) return FP4IDX_EWORKSPACE;
     return hip_status(fp4idx::launch_logits_topk(p, k, out_idx, out_vals, workspace,
                                                  workspace_bytes, (hipStream_t)stream));
+}
+
+int fp4idx_logits_topk_paged_noalloc(int fmt,
+                                     const uint8_t* q_fp4, int64_t q_row_stride,
+                                     const uint8_t* q_scale, int64_t qs_row_stride,
+                                     const float* w, int64_t w_row_stride,
+                                     const uint8_t* k_fp4, int64_t k_page_stride,
+                                     const uint8_t* k_scale, int64_t ks_page_stride,
+                                     const int32_t* block_table, int64_t bt_row_stride,
+                                     const int32_t* cu_seqlens_q, const int32_t* row_lens,
+                                     int T, int B, int H, int Hkv, int page_size, int num_pages,
+                                     int table_width, int out_cols, int k,
+                                     int32_t* out_idx, float* out_vals, void* stream) {
+    fp4idx::LogitsParams p;
+    size_t need = 0;
+    const int rc = logits_topk_prepare(fmt, q_fp4, q_row_stride, q_scale, qs_row_stride, w,
+                                       w_row_stride, k_fp4, k_page_stride, k_scale, ks_page_stride,
+                                       block_table, bt_row_stride, cu_seqlens_q, row_lens, T, B, H,
+                                       Hkv, page_size, num_pages, table_width, out_cols, k, out_idx,
+                                       out_vals, stream, p, need);
+    if (rc != FP4IDX_OK) return rc < 0 ? FP4IDX_OK : rc;
+    if (need > kNoAllocScratchBytes) return FP4IDX_EWORKSPACE;
+    void* ws = nullptr;
+    const int src = scratch_of_current_device(&ws);
+    if (src != FP4IDX_OK) return src;
+    return hip_status(fp4idx::launch_logits_topk(p, k, out_idx, out_vals, ws, kNoAllocScratchBytes,
+                                                 (hipStream_t)stream));
 }
 
 int fp4idx_block_scores(int fmt,

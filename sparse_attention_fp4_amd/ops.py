@@ -161,6 +161,26 @@ def logits_topk_paged(q_fp4, q_scale, w, k_fp4, k_scale, block_table, cu_seqlens
     return out_idx, out_vals
 
 
+def logits_topk_paged_noalloc(q_fp4, q_scale, w, k_fp4, k_scale, block_table, cu_seqlens_q,
+                              row_lens, *, fmt="mxfp4", out_cols: int, k: int, out_idx,
+                              out_vals=None, k_page_stride: Optional[int] = None,
+                              ks_page_stride: Optional[int] = None):
+    """logits_topk_paged without a workspace: the library's per-GPU static scratch is used
+    and nothing is allocated (out_idx, and out_vals if wanted, are the caller's)."""
+    args, d = _logits_args(q_fp4, q_scale, w, k_fp4, k_scale, block_table, cu_seqlens_q, row_lens,
+                           fmt, k_page_stride, ks_page_stride)
+    T, dev = d["T"], d["dev"]
+    for name, t, dt in (("out_idx", out_idx, torch.int32), ("out_vals", out_vals, torch.float32)):
+        if t is not None:
+            _need(t, name, dt, 2, dev)
+            if t.shape != (T, k) or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous [T, k] tensor")
+    rc = lib().fp4idx_logits_topk_paged_noalloc(*args, out_cols, k, _ptr(out_idx), _ptr(out_vals),
+                                                _stream())
+    check("fp4idx_logits_topk_paged_noalloc", rc)
+    return out_idx, out_vals
+
+
 def block_scores(q_fp4, k_fp4, q_scale, k_scale, cu_seqlens_q, cu_seqlens_k, cu_page_offsets, *,
                  max_seqlen_q: int, max_seqlen_k: int, kv_indices, fmt="nvfp4", causal=True,
                  qo_offset=None, out: Optional[torch.Tensor] = None):

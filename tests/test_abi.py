@@ -213,3 +213,33 @@ def test_logits_topk_workspace_size():
 ])
 def test_logits_topk_argument_errors(kw, code):
     assert _fused(**kw) == code
+
+
+def _noalloc(**kw):
+    L = _lib.lib()
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = ctypes.cast(buf, ctypes.c_void_p).value
+    p16 = (p + 255) & ~255
+    a = dict(fmt=0, q=p16, qrs=32 * 64, qs=p16, qsrs=32 * 4, w=p16, wrs=32, k=p16,
+             kps=64 * 64, ks=p16, ksps=64 * 4, bt=p16, btrs=4, cu=p16, lens=p16, T=4, B=1, H=32,
+             Hkv=1, page=64, P=4, W=4, out_cols=256, kk=16, idx=p16, vals=None)
+    a.update(kw)
+    return L.fp4idx_logits_topk_paged_noalloc(
+        a["fmt"], a["q"], a["qrs"], a["qs"], a["qsrs"], a["w"], a["wrs"], a["k"], a["kps"],
+        a["ks"], a["ksps"], a["bt"], a["btrs"], a["cu"], a["lens"], a["T"], a["B"], a["H"],
+        a["Hkv"], a["page"], a["P"], a["W"], a["out_cols"], a["kk"], a["idx"], a["vals"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kk=0), 1), (dict(kk=2049), 2), (dict(fmt=3), 1), (dict(idx=None), 1),
+    (dict(qrs=32 * 64 + 8), 3), (dict(T=0), 0),
+    # the kept-score buffer of 600 rows x 32768 columns (8 bytes each) exceeds the
+    # static scratch: refused before anything is enqueued
+    (dict(T=600, out_cols=32768), 5),
+])
+def test_logits_topk_noalloc_argument_errors(kw, code):
+    assert _noalloc(**kw) == code
+    if code == 5:
+        L = _lib.lib()
+        need = L.fp4idx_logits_topk_workspace_bytes(0, kw["T"], 1, 32, 1, 64, 4, kw["out_cols"], 16)
+        assert need > (128 << 20)
