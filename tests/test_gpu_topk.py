@@ -165,6 +165,36 @@ def test_workspace_reused_across_calls_without_clearing():
         assert np.array_equal(vals.cpu().numpy().view(np.uint32), ov.view(np.uint32))
 
 
+def _sampled_columns(length):
+    """128 runs of 32 columns at run starts floor(r * length / 128) rounded down to a
+    multiple of 32 (the whole row when it has at most 4096 columns): a fixed 4% sample
+    that a sampled threshold could be placed from."""
+    if length <= 4096:
+        return np.arange(length)
+    starts = ((np.arange(128, dtype=np.int64) * length) // 128) & ~31
+    return (starts[:, None] + np.arange(32)[None, :]).ravel()
+
+
+@pytest.mark.parametrize("rows,cols,k", [(3, 100_000, 2048), (2, 40_000, 300), (70, 40_000, 2048)])
+def test_long_rows_where_the_sample_misjudges(rows, cols, k):
+    """Rows whose largest scores sit on a regular 4% sample of the columns (a threshold
+    placed from that sample would let through far fewer than k keys), and a row whose
+    largest scores lie only off it: the selection is exact regardless."""
+    rng = np.random.default_rng(rows + cols + k)
+    s = rng.standard_normal((rows, cols)).astype(np.float32)
+    lens = np.full(rows, cols, np.int32)
+    lens[-1] = cols - 777
+    for r in range(rows):
+        samp = _sampled_columns(int(lens[r]))
+        if r == 1:
+            off = np.setdiff1d(np.arange(lens[r]), samp)
+            s[r, off[rng.choice(off.size, 3 * k, replace=False)]] += 20.0
+        else:
+            s[r, samp] += 20.0
+    say(f"[gpu] topk sample-defeating rows rows={rows} cols={cols} k={k}")
+    _same(s, k, lens)
+
+
 @pytest.mark.parametrize("rows,cols,k,kind", [(600, 4096, 2048, "normal"), (520, 32768, 2048, "ties"),
                                               (512, 20000, 100, "clustered"), (700, 3000, 2048, "normal")])
 def test_many_short_rows(rows, cols, k, kind):
