@@ -112,21 +112,26 @@ __device__ __forceinline__ void wave_narrow(Visit visit, uint32_t klo, uint32_t 
     const uint32_t span = khi - klo;
     sh = span >= (uint32_t)kBins ? (32 - __builtin_clz(span)) - 10 : 0;
 #pragma unroll
-    for (int i = 0; i < kBins / 64; i++) hist[lane * (kBins / 64) + i] = 0;
+    for (int i = 0; i < kBins / 64; i++) hist[64 * i + lane] = 0;  // consecutive lanes, consecutive banks
     __builtin_amdgcn_wave_barrier();
     const int shv = sh;
     visit([&](uint32_t key) {
         if (key >= klo && key <= khi) atomicAdd(&hist[(key - klo) >> shv], 1);
     });
     __builtin_amdgcn_wave_barrier();
-    // lane l holds bins 1023-16l .. 1008-16l, in descending order
+    // lane l holds bins 1023-16l .. 1008-16l, in descending order, read 16 bytes at a
+    // time (one word per read would put the lanes' bins, 16 words apart, in few banks)
     constexpr int kPerLane = kBins / 64;
     int c[kPerLane], s = 0;
+    const v4i* hv = reinterpret_cast<const v4i*>(hist + kBins - kPerLane * (lane + 1));
 #pragma unroll
-    for (int i = 0; i < kPerLane; i++) {
-        c[i] = hist[kBins - 1 - kPerLane * lane - i];
-        s += c[i];
+    for (int q = 0; q < kPerLane / 4; q++) {
+        const v4i v = hv[q];
+#pragma unroll
+        for (int e = 0; e < 4; e++) c[kPerLane - 1 - (4 * q + e)] = v[e];
     }
+#pragma unroll
+    for (int i = 0; i < kPerLane; i++) s += c[i];
     const int incl = wave_incl_scan(s);
     const int excl = incl - s;
     const unsigned long long hit = __ballot(excl < want && want <= incl);
@@ -201,7 +206,7 @@ __device__ __forceinline__ void block_minmax(uint32_t& lo, uint32_t& hi, uint32_
 
 
 struct NarrowLds {
-    int hist[kBins];
+    alignas(16) int hist[kBins];  // read 16 bytes at a time
     int red[4];
     uint32_t red8[8];
     int misc[2];
@@ -226,12 +231,15 @@ __device__ __forceinline__ void narrow(Visit visit, uint32_t klo, uint32_t khi, 
         if (key >= klo && key <= khi) atomicAdd(&L.hist[(key - klo) >> shv], 1);
     });
     __syncthreads();
-    // lane t holds bins 1023-4t .. 1020-4t, in descending order
+    // lane t holds bins 1023-4t .. 1020-4t, in descending order (one 16-byte read)
     int c[4], s = 0;
+    {
+        const v4i v = *reinterpret_cast<const v4i*>(L.hist + kBins - 4 * ((int)threadIdx.x + 1));
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        c[i] = L.hist[kBins - 1 - 4 * (int)threadIdx.x - i];
-        s += c[i];
+        for (int i = 0; i < 4; i++) {
+            c[i] = v[3 - i];
+            s += c[i];
+        }
     }
     int tot;
     const int excl = block_excl_scan(s, L.red, &tot);
@@ -266,7 +274,7 @@ struct ThresholdParams {
 // sample is thinned to every stride-th score, with m divided by the stride) in
 // registers; lo = their m-th largest, or -inf when fewer than m are finite.
 __global__ __launch_bounds__(256) void k_threshold(const ThresholdParams p) {
-    __shared__ int hist_all[4][kBins];
+    __shared__ __align__(16) int hist_all[4][kBins];  // read 16 bytes at a time
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave;
     if (t >= p.T) return;  // whole wave; nothing below waits for other waves

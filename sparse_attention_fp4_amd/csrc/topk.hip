@@ -51,7 +51,7 @@ __device__ __forceinline__ float from_key(uint32_t k) {
 constexpr int kRankMax = 1024;  // threshold-bin candidates ranked by direct comparison
 
 struct Shared {
-    uint32_t hist[kBins];
+    alignas(16) uint32_t hist[kBins];  // read 16 bytes at a time by the bin picks
     uint32_t mkey[kRankMax];     // candidates in the threshold bin of the value pass
     int midx[kRankMax];
     int nm;
@@ -69,6 +69,27 @@ struct Shared {
     int pick[4];
     int total;
 };
+
+// Thread t's bins for a pick from the top: the kPickPer words ending at bin
+// kBins - 1 - kPickPer * t, read 16 bytes at a time (one word per read would put the
+// threads' bins, kPickPer words apart, in few LDS banks); c[b] / bin[b] in descending
+// bin order.
+constexpr int kPickPer = kBins / kThreads;
+static_assert(kPickPer % 4 == 0, "whole 16-byte reads");
+__device__ __forceinline__ void read_bins_desc(const uint32_t* hist, int tid, int (&c)[kPickPer],
+                                               int (&bin)[kPickPer]) {
+    const int lo_bin = kBins - kPickPer * (tid + 1);
+    const v4u* hv = reinterpret_cast<const v4u*>(hist + lo_bin);
+#pragma unroll
+    for (int q = 0; q < kPickPer / 4; q++) {
+        const v4u v = hv[q];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            bin[kPickPer - 1 - (4 * q + e)] = lo_bin + 4 * q + e;
+            c[kPickPer - 1 - (4 * q + e)] = (int)v[e];
+        }
+    }
+}
 
 __device__ __forceinline__ void clear_hist(Shared& sh) {
     for (int i = threadIdx.x; i < kBins; i += kThreads) sh.hist[i] = 0u;
@@ -165,14 +186,9 @@ __global__ __launch_bounds__(kThreads) void k_topk(const TopkParams p) {
             }
             lds_barrier();
             {
-                constexpr int per = kBins / kThreads;
-                int c[per], bin[per];
-#pragma unroll
-                for (int b = 0; b < per; b++) {
-                    bin[b] = kBins - 1 - (tid * per + b);
-                    c[b] = (int)sh.hist[bin[b]];
-                }
-                pick_bin<kThreads, per>(c, bin, kk, sh.wtot, sh.pick);
+                int c[kPickPer], bin[kPickPer];
+                read_bins_desc(sh.hist, tid, c, bin);
+                pick_bin<kThreads, kPickPer>(c, bin, kk, sh.wtot, sh.pick);
             }
             const int d = sh.pick[0];
             const int nd = sh.pick[3];
@@ -235,14 +251,9 @@ __global__ __launch_bounds__(kThreads) void k_topk(const TopkParams p) {
             }
             lds_barrier();
             {
-                constexpr int per = kBins / kThreads;  // bins per thread, walked from the top
-                int c[per], bin[per];
-#pragma unroll
-                for (int b = 0; b < per; b++) {
-                    bin[b] = kBins - 1 - (tid * per + b);
-                    c[b] = (int)sh.hist[bin[b]];
-                }
-                pick_bin<kThreads, per>(c, bin, kk, sh.wtot, sh.pick);
+                int c[kPickPer], bin[kPickPer];
+                read_bins_desc(sh.hist, tid, c, bin);
+                pick_bin<kThreads, kPickPer>(c, bin, kk, sh.wtot, sh.pick);
             }
             const uint32_t dsel = (uint32_t)sh.pick[0];
             kk -= sh.pick[1];

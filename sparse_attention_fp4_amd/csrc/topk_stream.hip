@@ -105,12 +105,21 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
     // The bin holding the kk-th largest of the histogrammed keys: thread t owns bins
     // kSBins-1-PB*t .. kSBins-PB*t-PB (descending).  pick[0] = bin, [1] = keys in
     // higher bins, [2] = total, [3] = keys in the bin.  Ends with a barrier.
+    // The bins are read 16 bytes at a time: with one word per read the threads' bins, PB
+    // words apart, would fall into few LDS banks.
     auto pick_desc = [&](int kk) {
         int c[PB], bin[PB];
+        const int lo_bin = kSBins - PB * (tid + 1);  // thread t's lowest bin (16-byte aligned)
+        const v4u* hv = reinterpret_cast<const v4u*>(L.hist + lo_bin);
 #pragma unroll
-        for (int b = 0; b < PB; b++) {
-            bin[b] = kSBins - 1 - (PB * tid + b);
-            c[b] = (int)L.hist[bin[b]];
+        for (int q = 0; q < PB / 4; q++) {
+            const v4u v = hv[q];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int b = PB - 1 - (4 * q + e);  // descending: b = 0 is the highest bin
+                bin[b] = lo_bin + 4 * q + e;
+                c[b] = (int)v[e];
+            }
         }
         pick_bin<NT, PB>(c, bin, kk, L.wtot, L.pick);
     };
