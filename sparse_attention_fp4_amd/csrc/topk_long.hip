@@ -217,7 +217,7 @@ constexpr int kCR = 8;       // candidates per thread per round
 constexpr int kRankMax = 1024;  // candidates at the threshold prefix ranked by comparison
 
 struct FinishShared {
-    uint32_t h[kBins];
+    alignas(16) uint32_t h[kBins];
     uint32_t bits[kMaxWords];  // the row's bitmap
     uint32_t mkey[kRankMax];   // candidates with the threshold prefix (d1, d2)
     int mcol[kRankMax];
@@ -229,7 +229,8 @@ struct FinishShared {
 };
 
 // Candidate registers: kCR per thread.  In the common case they hold every candidate
-// of the row (slot i = threadIdx.x + kFT * j is slot i % spec of chunk i / spec);
+// of the row (registers 2j and 2j+1 hold slots 2q % spec and 2q % spec + 1 of chunk
+// 2q / spec, q = threadIdx.x + kFT * j);
 // otherwise ("flat" mode) they hold candidates [round * kFT * kCR, +kFT * kCR) of the
 // row in chunk order, reloaded round by round.
 struct CandRegs {
@@ -299,41 +300,52 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws) {
     uint32_t* gh = ws.hist + (int64_t)row * kBins;
     uint32_t* gh2 = ws.hist2 + (int64_t)row * kBins;
     constexpr int lspec = 6;            // candidate slots read per chunk up front: 64
-    constexpr int spec = 1 << lspec;    // (kMaxChunks * spec = kFT * kCR)
+    constexpr int spec = 1 << lspec;
+    static_assert(kMaxChunks * spec == kFT * kCR && kCR % 2 == 0 && kMaxWords % (4 * kFT) == 0,
+                  "up-front loads fill the candidate registers in slot pairs");
 
     // ---- one round of loads: state, candidate counts, second histogram, bitmap, and the
     // first `spec` candidate slots of every chunk (read before the counts are known;
-    // slots past a count are ignored)
+    // slots past a count are ignored).  This workgroup is alone on its CU, where the
+    // number of load instructions, not their latency, sets the pace: every array is read
+    // 16 bytes per lane.
     // the digit-1 histogram was last read by the collect pass: clear it for the next
     // call now, so the stores drain while this workgroup works
-    for (int i = threadIdx.x; i < kBins; i += kFT) gh[i] = 0u;
+    static_assert(kBins == 4 * kFT, "one 16-byte store per thread clears a histogram");
+    reinterpret_cast<uint4*>(gh)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
     const int d1 = ws.st[row].d1;
     int kk = ws.st[row].kk;
     const int my_cnum = threadIdx.x < nch ? ws.cnum[(int64_t)row * nch + threadIdx.x] : 0;
+    // second histogram: thread t owns bins 4095-4t .. 4092-4t (one 16-byte load)
     constexpr int per = kBins / kFT;
-    int c2[per], bin2[per];
+    uint4* h2v = reinterpret_cast<uint4*>(gh2) + (kFT - 1 - threadIdx.x);
+    const uint4 h2 = *h2v;
+    int c2[per] = {(int)h2.w, (int)h2.z, (int)h2.y, (int)h2.x}, bin2[per];
 #pragma unroll
-    for (int b = 0; b < per; b++) {
-        bin2[b] = kBins - 1 - (threadIdx.x * per + b);
-        c2[b] = (int)gh2[bin2[b]];
+    for (int b = 0; b < per; b++) bin2[b] = kBins - 1 - (threadIdx.x * per + b);
+    // bitmap: words 4q .. 4q+3 for q = threadIdx.x + kFT * j
+    constexpr int kXQ = kMaxWords / (4 * kFT);
+    const uint4* rbits4 = reinterpret_cast<const uint4*>(rbits);
+    uint4 x[kXQ];
+#pragma unroll
+    for (int j = 0; j < kXQ; j++) {
+        const int q = threadIdx.x + kFT * j;
+        x[j] = 4 * q < nwords ? rbits4[q] : make_uint4(0u, 0u, 0u, 0u);
     }
-    uint32_t x[16];
+    // candidate slot pairs: pair q = threadIdx.x + kFT * j holds slots 2q % spec and
+    // 2q % spec + 1 of chunk 2q / spec
+    uint4 sv[kCR / 2];
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-        const int w = threadIdx.x + kFT * j;
-        x[j] = w < nwords ? rbits[w] : 0u;
-    }
-    uint2 sv[kCR];
-#pragma unroll
-    for (int j = 0; j < kCR; j++) {
-        const int i = threadIdx.x + kFT * j;
-        const int c = i >> lspec, slot = i & (spec - 1);
-        sv[j] = c < nch ? ws.cand[((int64_t)row * nch + c) * kChunk + slot] : make_uint2(0u, 0xffffffffu);
+    for (int j = 0; j < kCR / 2; j++) {
+        const int q = threadIdx.x + kFT * j;
+        const int c = (2 * q) >> lspec, slot = (2 * q) & (spec - 1);
+        sv[j] = c < nch ? *reinterpret_cast<const uint4*>(ws.cand + ((int64_t)row * nch + c) * kChunk + slot)
+                        : make_uint4(0u, 0xffffffffu, 0u, 0xffffffffu);
     }
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-        const int w = threadIdx.x + kFT * j;
-        if (w < nwords) sh.bits[w] = x[j];
+    for (int j = 0; j < kXQ; j++) {
+        const int q = threadIdx.x + kFT * j;
+        if (4 * q < nwords) reinterpret_cast<uint4*>(sh.bits)[q] = x[j];
     }
     if (threadIdx.x < nch) sh.cnum[threadIdx.x] = my_cnum;
     if (threadIdx.x == 0) sh.nm = 0;
@@ -348,20 +360,21 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws) {
     const int rounds = flat ? (m + kFT * kCR - 1) / (kFT * kCR) : 1;
     CandRegs r;
 #pragma unroll
-    for (int j = 0; j < kCR; j++) {
-        const int i = threadIdx.x + kFT * j;
-        const int c = i >> lspec, slot = i & (spec - 1);
-        const bool ok = c < nch && slot < sh.cnum[c < nch ? c : 0];
-        r.key[j] = sv[j].x;
-        r.col[j] = ok ? (int)sv[j].y : -1;
+    for (int j = 0; j < kCR / 2; j++) {
+        const int q = threadIdx.x + kFT * j;
+        const int c = (2 * q) >> lspec, slot = (2 * q) & (spec - 1);
+        const int cn = c < nch ? sh.cnum[c] : 0;
+        r.key[2 * j] = sv[j].x;
+        r.col[2 * j] = slot < cn ? (int)sv[j].y : -1;
+        r.key[2 * j + 1] = sv[j].z;
+        r.col[2 * j + 1] = slot + 1 < cn ? (int)sv[j].w : -1;
     }
 
     if (d1 >= 0) {
         // ---- digit 2 from the row's second histogram (pick_bin ends with a barrier)
         pick_bin<kFT, per>(c2, bin2, kk, sh.wtot, sh.pick);
         // each thread has its bins' counts in registers: clear them for the next call
-#pragma unroll
-        for (int b = 0; b < per; b++) gh2[bin2[b]] = 0u;
+        *h2v = make_uint4(0u, 0u, 0u, 0u);
         const uint32_t preA = ((uint32_t)d1 << 12) | (uint32_t)sh.pick[0];
         kk -= sh.pick[1];                      // keys wanted with prefix preA, >= 1
         const int n_pre = sh.pick[3];          // candidates with prefix preA
