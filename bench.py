@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--workload", choices=["verify", "batched", "prefill", "block", "qsa"],
                     default="verify")
     ap.add_argument("--topk", type=int, default=2048)
+    ap.add_argument("--k-layout", choices=["combined", "split"], default="combined",
+                    help="verify/batched/prefill key cache: one buffer per page holding the "
+                         "nibbles then the scales (the SGLang table, 68 B a token) or two arrays")
     ap.add_argument("--fused", action="store_true",
                     help="verify/batched/prefill: one fused scorer + top-k call per step "
                          "(fp4idx_logits_topk_paged, no logits written) instead of logits + topk")
@@ -179,9 +182,16 @@ def logits_workload(args, torch, fp4, wl, dev):
     def up(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    base = dict(q=up(case.q_fp4), qs=up(case.q_scale), w=up(case.w), k=up(case.k_fp4),
-                ks=up(case.k_scale), bt=up(case.block_table), cu=up(case.cu_seqlens_q),
-                lens=up(case.row_lens))
+    P, page, G = case.num_pages, case.page_size, case.k_scale.shape[-1]
+    if args.k_layout == "combined":
+        # [SGL]'s key table: page p is one row of page * 68 bytes, the nibbles of its
+        # tokens, then their scales
+        table = np.concatenate([case.k_fp4.reshape(P, -1), case.k_scale.reshape(P, -1)], axis=1)
+        kv = dict(kt=up(table))
+    else:
+        kv = dict(k=up(case.k_fp4), ks=up(case.k_scale))
+    base = dict(q=up(case.q_fp4), qs=up(case.q_scale), w=up(case.w), **kv,
+                bt=up(case.block_table), cu=up(case.cu_seqlens_q), lens=up(case.row_lens))
     set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + T * out_cols * 4
     fused_ws = (fp4.logits_topk_workspace_bytes("mxfp4", T, case.B, H, case.Hkv, case.page_size,
                                                 case.block_table.shape[1], out_cols, k)
@@ -189,6 +199,9 @@ def logits_workload(args, torch, fp4, wl, dev):
 
     def make_set():
         s = {n: (t if n in ("cu", "lens", "bt") else t.clone()) for n, t in base.items()}
+        if "kt" in s:  # the nibble and scale views of the set's own table
+            s["k"] = s["kt"][:, :page * 64 * case.Hkv].view(P, case.Hkv, page, 64)
+            s["ks"] = s["kt"][:, page * 64 * case.Hkv:].view(P, case.Hkv, page, G)
         if args.fused:
             s["fws"] = torch.empty(fused_ws, dtype=torch.uint8, device=dev)
         else:
@@ -230,6 +243,11 @@ def logits_workload(args, torch, fp4, wl, dev):
                             bound="mfma" if args.workload == "prefill" else "hbm", dtype="fp4"),
     }
     calls = {"logits_topk": logits_topk} if args.fused else {"logits": logits, "topk": topk}
+    if args.k_layout == "combined":
+        desc += "; keys in one table, a page = its tokens' nibbles then their scales (68 B a token)"
+    else:
+        name += "_split"
+        desc += "; nibbles and scales in two arrays"
     if args.fused:
         name += "_fused"
         desc += "; fused scorer + top-k (no logits written)"
