@@ -48,6 +48,12 @@ struct LogitsParams {
     int64_t cand_rs;     // entries between candidate rows
     int32_t* counts;
     int counts_rs;       // ints between count rows
+    // Optional: zero_words (< 2^31) words from `zero` are cleared by the launch (a
+    // region the next kernels on the stream need zeroed, cleared without a kernel of its
+    // own); zero_per_block is set by the launcher.
+    uint32_t* zero;
+    int zero_words;
+    int zero_per_block;
 };
 
 // Row blocks, tiles and column chunks of a logits launch (fills rows_per_block,

@@ -582,6 +582,10 @@ hipError_t launch_logits_topk(const LogitsParams& p, int k, int32_t* out_idx, fl
         const size_t tb = align256(topk_workspace_bytes(p.T, p.out_cols, k));
         if (ws_bytes < lb + tb || k < 1) return hipErrorInvalidValue;
         uint8_t* ws = static_cast<uint8_t*>(workspace);
+        // the top-k's histograms start zero: the scorer clears them (no memset, and no
+        // kernel of their own unless the scorer has no blocks)
+        const size_t zb = topk_workspace_zero_bytes(p.T, p.out_cols, k);
+        const bool scorer_runs = pf.n_wchunks > 0 && pf.n_rowblocks > 0;
         LogitsParams pl = p;
         pl.out = reinterpret_cast<float*>(ws);
         pl.out_rs = p.out_cols;
@@ -589,8 +593,15 @@ hipError_t launch_logits_topk(const LogitsParams& p, int k, int32_t* out_idx, fl
         pl.flags = nullptr;
         pl.cand = nullptr;
         pl.counts = nullptr;
+        pl.zero = zb && scorer_runs ? reinterpret_cast<uint32_t*>(ws + lb) : nullptr;
+        pl.zero_words = (int)((zb + 3) / 4);  // at most 512 rows of two 16 KB histograms
         hipError_t e = launch_logits(pl, stream);
         if (e != hipSuccess) return e;
+        if (zb && !scorer_runs) {
+            const int64_t n = (int64_t)((zb + 3) / 4);
+            hipLaunchKernelGGL(k_zero_words, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, n,
+                               reinterpret_cast<uint32_t*>(ws + lb));
+        }
         TopkParams tp{};
         tp.scores = pl.out;
         tp.row_stride = p.out_cols;
@@ -601,12 +612,6 @@ hipError_t launch_logits_topk(const LogitsParams& p, int k, int32_t* out_idx, fl
         tp.out_idx = out_idx;
         tp.out_vals = out_vals;
         tp.workspace = tb ? ws + lb : nullptr;
-        const size_t zb = topk_workspace_zero_bytes(p.T, p.out_cols, k);
-        if (zb) {  // the top-k's histograms start zero (a kernel, not a memset)
-            const int64_t n = (int64_t)((zb + 3) / 4);
-            hipLaunchKernelGGL(k_zero_words, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, n,
-                               reinterpret_cast<uint32_t*>(ws + lb));
-        }
         return launch_topk(tp, stream);
     }
     if (pf.n_wchunks > kMaxChunks || k < 1 || k > kSortCap) return hipErrorInvalidValue;

@@ -388,6 +388,10 @@ __global__ __launch_bounds__(64 * waves_per_block(RG)) void k_logits(const Logit
         st_w[k] = p.w[(int64_t)(t0 + (ok ? to : 0)) * p.w_rs + (ok ? hk * p.R + hlo : 0)];
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (p.zero) {  // this workgroup's share of a region to clear, after its own loads
+        const int w0 = blockIdx.x * p.zero_per_block, w1 = min(w0 + p.zero_per_block, p.zero_words);
+        for (int w = w0 + threadIdx.x; w < w1; w += kThreads) p.zero[w] = 0u;
+    }
     // A workgroup whose columns all lie past every row's end only writes -inf (all its
     // waves see the same rows, so they all leave here or none does).
     {
@@ -692,9 +696,11 @@ __global__ __launch_bounds__(64 * waves_per_block(RG)) void k_logits(const Logit
     }
 }
 template <int FMT, int RG, int NT, bool FUSE>
-hipError_t launch4(const LogitsParams& p, hipStream_t stream) {
+hipError_t launch4(const LogitsParams& p_in, hipStream_t stream) {
+    LogitsParams p = p_in;
     const int64_t blocks = (int64_t)p.n_rowblocks * p.n_wgchunks;
     if (blocks <= 0) return hipSuccess;
+    if (p.zero) p.zero_per_block = (int)((p.zero_words + blocks - 1) / blocks);
     const size_t lds = ALayout<FMT, NT>::kBytes;
     const dim3 threads(64 * waves_per_block(RG));
     if (p.Hkv == 1)
