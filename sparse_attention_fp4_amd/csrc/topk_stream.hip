@@ -47,46 +47,43 @@ __device__ __forceinline__ float from_skey(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// LDS layout (uint32 words): histogram, candidate keys, candidate columns, bitmap,
-// then a small area for scan totals and shared scalars.
+// LDS layout: the histogram (uint32 words; once the last digit is settled the same
+// words hold the row's column bitmap, at most 1024 words for 32768 columns), candidate
+// keys (uint32), candidate columns (uint16: rows have at most 32768 columns), then a
+// small area for scan totals and shared scalars.  Under 40 KB with 4080 candidates,
+// so four row workgroups share a CU.
+constexpr int kStreamMaxCols = 32768;
+
 struct StreamLds {
     uint32_t* hist;
+    uint32_t* bmap;   // aliases hist
     uint32_t* ckey;
-    uint32_t* ccol;
-    uint32_t* bmap;
+    uint16_t* ccol;
     int* wtot;   // [16] wave totals of block scans
     int* pick;   // [4] pick_bin results
     int* ctr;    // [4] candidate count
 };
 
-__device__ __forceinline__ StreamLds carve(uint32_t* lds, int cap, int words) {
+__device__ __forceinline__ StreamLds carve(uint32_t* lds, int cap) {
     StreamLds s;
     s.hist = lds;
+    s.bmap = lds;
     s.ckey = s.hist + kSBins;
-    s.ccol = s.ckey + cap;
-    s.bmap = s.ccol + cap;
-    s.wtot = reinterpret_cast<int*>(s.bmap + words);
+    s.ccol = reinterpret_cast<uint16_t*>(s.ckey + cap);
+    s.wtot = reinterpret_cast<int*>(s.ckey + cap + cap / 2);  // cap is even
     s.pick = s.wtot + 16;
     s.ctr = s.pick + 4;
     return s;
 }
 
-}  // namespace
-
-size_t topk_stream_lds_bytes(int cols, int cap) {
-    const int words = (cols + 31) / 32;
-    return 4 * ((size_t)kSBins + 2 * (size_t)cap + words + 24);
-}
-
-namespace {
+size_t topk_stream_lds_bytes(int cap) { return 4 * ((size_t)kSBins + (size_t)cap + (size_t)cap / 2 + 24); }
 
 template <int NT>
 __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap) {
     extern __shared__ __align__(16) uint32_t lds_words[];
     constexpr int NW = NT / 64;
     constexpr int PB = kSBins / NT;  // histogram bins per thread
-    const int words = (p.cols + 31) / 32;
-    const StreamLds L = carve(lds_words, cap, words);
+    const StreamLds L = carve(lds_words, cap);
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -124,9 +121,8 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
         pick_bin<NT, PB>(c, bin, kk, L.wtot, L.pick);
     };
 
-    // ---- clear the histogram, the counter and the row's bitmap words
+    // ---- clear the histogram and the counter
     clear_hist();
-    for (int w = tid; w < rwords; w += NT) L.bmap[w] = 0u;
     if (tid == 0) L.ctr[0] = 0;
     lds_barrier();
 
@@ -135,7 +131,7 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
     // rho = 64 + 32 + 1 (four standard deviations of the sample count), so about
     // 1.5 k keys of the row are >= lo and fewer than k only with probability ~1e-4.
     // Short rows (len <= 2k) keep every valid key.
-    constexpr int kSPer = NT >= 1024 ? 16 : 4;  // samples per thread at most
+    constexpr int kSPer = 4;  // samples per thread at most
     uint32_t lo = 1u;
     if (len > 2 * k) {
         const int S = (int)min((int64_t)NT * kSPer, max((int64_t)1, ((int64_t)len * 64 + k - 1) / k));
@@ -246,7 +242,7 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
                             atomicAdd(&L.hist[(kv >> hshift) & hmask], 1u);
                         if (pos < cap) {
                             L.ckey[pos] = kv;
-                            L.ccol[pos] = (uint32_t)c;
+                            L.ccol[pos] = (uint16_t)c;
                         }
                         pos++;
                     }
@@ -324,6 +320,10 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
         level++;
     }
 
+    // the histogram is done with: its words hold the row's column bitmap from here on
+    for (int w = tid; w < rwords; w += NT) L.bmap[w] = 0u;
+    lds_barrier();
+
     // ---- mark the selected columns
     // keys equal to K* are in LDS unless the last pass kept only keys above it
     const bool ties_kept = level < 3;
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
         const uint32_t key = L.ckey[i];
         const bool take = all_valid || key > kstar || (key == kstar && ties == need && ties_kept);
         if (take) {
-            const uint32_t col = L.ccol[i];
+            const uint32_t col = L.ccol[i];  // uint16 in LDS
             atomicOr(&L.bmap[col >> 5], 1u << (col & 31));
         }
     }
@@ -399,26 +399,25 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
 
 }  // namespace
 
-// Candidates kept in LDS: k plus slack, within the LDS left after the histogram and
-// the bitmap (at least k, which the exact fallbacks need).
+// Candidates kept in LDS: k plus slack (at least k, which the exact fallbacks need).
+// With k plus about 2000 the LDS stays under 40 KB, so four row workgroups share a
+// CU (the waves' registers allow four as well): 4080 candidates for k = 2048; larger k
+// take up to 150 KB.
 int topk_stream_cap(int cols, int k) {
-    const size_t budget = 150u * 1024u;
-    const size_t fixed = topk_stream_lds_bytes(cols, 0);
-    size_t room = budget > fixed ? (budget - fixed) / 8 : 0;
-    const size_t want = (size_t)k + 2048;
-    const int cap = (int)(room < want ? room : want);
+    if (cols > kStreamMaxCols || k < 1) return -1;
+    const size_t fixed = topk_stream_lds_bytes(0);
+    auto room = [&](size_t budget) { return budget > fixed ? (int)(((budget - fixed) / 6) & ~(size_t)1) : 0; };
+    const int want = k + 2048;
+    const int cap40 = room(40u * 1024u);
+    int cap = want <= cap40 + 16 ? (want < cap40 ? want : cap40) : (want < room(150u * 1024u) ? want : room(150u * 1024u));
+    cap &= ~1;
     return cap < k ? -1 : cap;
 }
 
 hipError_t launch_topk_stream(const TopkParams& p, hipStream_t stream) {
     const int cap = topk_stream_cap(p.cols, p.k);
     if (cap < 0) return hipErrorInvalidValue;
-    const size_t lds = topk_stream_lds_bytes(p.cols, cap);
-    // many short rows: 256 threads a row (several rows share a CU); otherwise 1024
-    if (p.rows >= 512 && p.cols <= 32768)
-        hipLaunchKernelGGL(k_topk_stream<256>, dim3(p.rows), dim3(256), lds, stream, p, cap);
-    else
-        hipLaunchKernelGGL(k_topk_stream<1024>, dim3(p.rows), dim3(1024), lds, stream, p, cap);
+    hipLaunchKernelGGL(k_topk_stream<256>, dim3(p.rows), dim3(256), topk_stream_lds_bytes(cap), stream, p, cap);
     return hipGetLastError();
 }
 
