@@ -15,6 +15,9 @@ the FP4 indexer scorer...", Speed Tests: 4 verify rows, 32 heads, contexts 16,38
   qsa      the consumer of the top-k selection (vLLM qsa_fp8 API page): slot pass and
            sparse grouped-query attention over the top-2048 tokens of 128 decode rows,
            fp8 e4m3fn K/V cache (contexts U[8192, 32768], 64-token pages), Hq=32, Hkv=4.
+  quantize the key store ("[DSv4.1] Speed up the FP4 indexer scorer..." bench): MXFP4
+           quantize-and-store of a 32768-token prefill's bf16 keys into page-shuffled
+           64-token cache pages.
 
 Timing: inputs are resident in HBM before the timed region.  Enough independent
 input/output sets are allocated that at least 512 MiB of other sets (twice the 256 MiB
@@ -56,7 +59,8 @@ KERNEL_SOURCES = {"logits": [CSRC + "logits.hip"] + COMMON_SOURCES,
                   "block_topk": [CSRC + "block_topk.hip"] + COMMON_SOURCES,
                   "logits_topk": [CSRC + "logits.hip", CSRC + "fused_topk.hip"] + COMMON_SOURCES,
                   "qsa_slots": [CSRC + "qsa.hip"] + COMMON_SOURCES,
-                  "qsa_decode": [CSRC + "qsa.hip"] + COMMON_SOURCES}
+                  "qsa_decode": [CSRC + "qsa.hip"] + COMMON_SOURCES,
+                  "quantize": [CSRC + "quantize.hip"] + COMMON_SOURCES}
 
 
 def parse():
@@ -65,7 +69,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default per workload)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default per workload)")
     ap.add_argument("--ctx", type=int, default=100_000, help="context of the verify workload")
-    ap.add_argument("--workload", choices=["verify", "batched", "prefill", "block", "qsa"],
+    ap.add_argument("--workload", choices=["verify", "batched", "prefill", "block", "qsa", "quantize"],
                     default="verify")
     ap.add_argument("--topk", type=int, default=2048)
     ap.add_argument("--k-layout", choices=["combined", "split"], default="combined",
@@ -142,10 +146,12 @@ def _timed_oracle(run, sub_pairs, budget_s=10.0, max_reps=8):
     return sub_pairs * reps / total, reps, total
 
 
-def _baseline(run_all, all_pairs, what_all, run_one, one_pairs, what_one):
-    """The oracle timed on every host thread it may use, then on one thread (a smaller
-    part of the same sample), as the cpu_baseline object."""
-    threads = host_threads()
+def _baseline(run_all, all_pairs, what_all, run_one, one_pairs, what_one, max_threads=None,
+              parallel_over="(row, 2048-key run) for logits; rows for top-k and block scores"):
+    """The oracle timed on every host thread it may use (at most max_threads, the
+    threads that oracle routine uses), then on one thread (a smaller part of the same
+    sample), as the cpu_baseline object."""
+    threads = host_threads() if max_threads is None else min(host_threads(), max_threads)
     v, reps, total = _timed_oracle(lambda: run_all(threads), all_pairs)
     v1, reps1, total1 = _timed_oracle(lambda: run_one(1), one_pairs, budget_s=6.0, max_reps=3)
     return dict(value=round(v, 1), unit="keys/s", cores=threads, kind="oracle",
@@ -153,7 +159,7 @@ def _baseline(run_all, all_pairs, what_all, run_one, one_pairs, what_one):
                 cpu_model=cpu_model(), host_cpus_visible=len(os.sched_getaffinity(0)),
                 single_thread=dict(value=round(v1, 1), unit="keys/s",
                                    sample=f"{what_one}, {reps1} run(s) in {total1:.1f} s"),
-                parallel_over="(row, 2048-key run) for logits; rows for top-k and block scores")
+                parallel_over=parallel_over)
 
 
 def logits_workload(args, torch, fp4, wl, dev):
@@ -442,6 +448,53 @@ def qsa_workload(args, torch, fp4, wl, dev):
                 dtype="fp8 e4m3fn K/V (exact bf16 QK, fp16 PV, fp32 accumulate)")
 
 
+def quantize_workload(args, torch, fp4, wl, dev):
+    """Row f1: MXFP4 quantize-and-store of a prefill's new keys into the paged cache."""
+    N, page = 32768, 64
+    P = N // page
+    name = f"quantize_store_{N}"
+    desc = (f"{name}: MXFP4 quantize-and-store of {N} bf16 keys (D=128, the new keys of a "
+            f"{N}-token prefill) into a cache of {P} shuffled {page}-token pages; key values "
+            f"k/8 with k uniform in -8..8, slots page-shuffled (the SGLang bench's)")
+    rng = np.random.default_rng(1060)
+    keys = (rng.integers(-8, 9, (N, 128)) / 8.0).astype(np.float32)
+    slots = (rng.permutation(P)[:, None] * page + np.arange(page)).reshape(-1).astype(np.int64)
+    kt = torch.from_numpy(keys).to(torch.bfloat16).to(dev)
+    st = torch.from_numpy(slots).to(dev)
+    per_key = 128 * 2 + 8 + 64 + 4          # bf16 key and slot in, nibbles and scales out
+    set_bytes = N * per_key
+
+    def make_set():
+        return dict(keys=kt.clone(), slots=st.clone(),
+                    kf=torch.empty((P, 1, page, 64), dtype=torch.uint8, device=dev),
+                    ks=torch.empty((P, 1, page, 4), dtype=torch.uint8, device=dev))
+
+    def quant(s):
+        fp4.quantize_store_k(s["keys"], s["slots"], s["kf"], s["ks"])
+
+    work = {"quantize": dict(bytes=N * per_key, flops=0, bound="hbm", dtype=None)}
+
+    def cpu_baseline():
+        from oracle import oracle as orc
+        kd = keys.astype(np.float64)           # bf16 -> exact in float64 (k/8)
+        kf0 = np.zeros((P, 1, page, 64), np.uint8)
+        ks0 = np.zeros((P, 1, page, 4), np.uint8)
+        part = N // 8
+
+        def run(n):
+            orc.quantize_store(kd[:n], slots[:n], kf0, ks0)
+
+        return _baseline(lambda th: run(N), N, f"all {N} keys (the oracle quantizes on one thread)",
+                         lambda th: run(part), part, f"{part} of the keys",
+                         max_threads=1, parallel_over="none (one thread)")
+
+    return dict(name=name, desc=desc, set_bytes=set_bytes, make_set=make_set,
+                calls={"quantize": quant}, work=work, pairs=N, k_tokens=N,
+                steps=256, warmup=16, launches=64, cpu_baseline=cpu_baseline,
+                config={"keys": N, "head_dim": 128, "page": page, "pages": P},
+                dtype="bf16 keys in, mxfp4 (e2m1 x e8m0) cache out")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -458,7 +511,8 @@ def main():
     assert torch.cuda.is_available(), "no GPU visible"
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    make = {"block": block_workload, "qsa": qsa_workload}.get(args.workload, logits_workload)
+    make = {"block": block_workload, "qsa": qsa_workload,
+            "quantize": quantize_workload}.get(args.workload, logits_workload)
     W = make(args, torch, fp4, wl, dev)
     steps = args.steps if args.steps is not None else W["steps"]
     warmup = args.warmup if args.warmup is not None else W["warmup"]

@@ -119,6 +119,8 @@ struct QuantParams {
     uint8_t* ks;           // scale pages, ksp_s bytes apart: [page][4]
     int64_t ksp_s;
     int N, page, num_pages;
+    int k_aligned4;        // set by the launcher: k and kp_s allow 4-byte stores
+    int keys_aligned16;    // set by the launcher: keys and key_rs allow 16-byte loads
 };
 
 hipError_t launch_quantize_store(const QuantParams& p, hipStream_t stream);

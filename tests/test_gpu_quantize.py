@@ -83,3 +83,45 @@ def test_quantized_cache_feeds_the_scorer():
                                         want_tolbase=True)
     assert inexact == 0
     check_logits(got.cpu().numpy(), ref, tb)
+
+
+@pytest.mark.parametrize("key_rs,kp_extra,ksp_extra,key_off", [
+    (128, 0, 0, 0),      # contiguous: 16-byte key loads, 4-byte nibble stores
+    (132, 6, 3, 2),      # key rows 4-byte aligned only, odd page strides: the narrow paths
+    (130, 2, 1, 0),      # key row stride 260 bytes, page strides not multiples of 4
+])
+def test_quantize_store_strided_through_the_c_abi(key_rs, kp_extra, ksp_extra, key_off):
+    """fp4idx_quantize_store_k with key rows and cache pages padded: every written byte
+    equals the oracle's, the padding between rows and pages is left as it was."""
+    from sparse_attention_fp4_amd._lib import lib
+    rng = np.random.default_rng(key_rs + kp_extra)
+    N, page, P = 200, 64, 5
+    k = _keys(rng, N)
+    kt, kd = _bf16(k)
+    slots = rng.permutation(P * page)[:N].astype(np.int64)
+    slots[7::13] = -1
+    # keys: [key_off + N * key_rs] bf16, row n at key_off + n * key_rs
+    kb = torch.zeros(key_off + N * key_rs + 8, dtype=torch.bfloat16)
+    kb[key_off:key_off + N * key_rs].view(N, key_rs)[:, :128] = kt
+    kp, ksp = page * 64 + kp_extra, page * 4 + ksp_extra
+    kf0 = rng.integers(0, 256, (P, 1, page, 64), dtype=np.uint8)
+    ks0 = rng.integers(0, 256, (P, 1, page, 4), dtype=np.uint8)
+    fbuf = rng.integers(0, 256, P * kp, dtype=np.uint8)       # pages padded with noise
+    sbuf = rng.integers(0, 256, P * ksp, dtype=np.uint8)
+    for p_ in range(P):
+        fbuf[p_ * kp:p_ * kp + page * 64] = kf0[p_].reshape(-1)
+        sbuf[p_ * ksp:p_ * ksp + page * 4] = ks0[p_].reshape(-1)
+    want_f, want_s = orc.quantize_store(kd, slots, kf0, ks0)
+    gk, gsl, gf, gs = kb.to("cuda"), dev(slots), dev(fbuf), dev(sbuf)
+    say(f"[gpu] quantize_store strided key_rs={key_rs} kp={kp} ksp={ksp} key_off={key_off}")
+    rc = lib().fp4idx_quantize_store_k(gk.data_ptr() + 2 * key_off, key_rs, gsl.data_ptr(), N,
+                                       gf.data_ptr(), kp, gs.data_ptr(), ksp, page, P,
+                                       torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    gotf, gots = gf.cpu().numpy(), gs.cpu().numpy()
+    for p_ in range(P):
+        assert np.array_equal(gotf[p_ * kp:p_ * kp + page * 64], want_f[p_].reshape(-1)), p_
+        assert np.array_equal(gotf[p_ * kp + page * 64:(p_ + 1) * kp], fbuf[p_ * kp + page * 64:(p_ + 1) * kp])
+        assert np.array_equal(gots[p_ * ksp:p_ * ksp + page * 4], want_s[p_].reshape(-1)), p_
+        assert np.array_equal(gots[p_ * ksp + page * 4:(p_ + 1) * ksp], sbuf[p_ * ksp + page * 4:(p_ + 1) * ksp])
