@@ -60,7 +60,7 @@ enum { FP4IDX_MXFP4 = 0, FP4IDX_NVFP4 = 1 };
 enum {
     FP4IDX_OK = 0,
     FP4IDX_EINVAL = 1,       /* null required pointer, bad dimension, bad format, ... */
-    FP4IDX_EUNSUPPORTED = 2, /* a valid request this build does not implement */
+    FP4IDX_EUNSUPPORTED = 2, /* a valid request the library does not implement */
     FP4IDX_EALIGN = 3,       /* a pointer or stride that must be 16-byte aligned is not */
     FP4IDX_EHIP = 4,         /* the HIP runtime reported an error at launch */
     FP4IDX_EWORKSPACE = 5    /* workspace missing or smaller than required */
