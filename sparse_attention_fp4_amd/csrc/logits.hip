@@ -222,7 +222,11 @@ __device__ __forceinline__ v4f tile_dot_sel(const Operand<FMT>& a, uint32_t a_co
 // FUSE: the scores are not stored; those at or above the row's threshold are kept as
 // top-k candidates (see LogitsParams).
 template <int FMT, int RG, int NT, bool MKV, bool FUSE>
-__global__ __launch_bounds__(64 * waves_per_block(RG)) void k_logits(const LogitsParams p) {
+// MXFP4 16-tile blocks that store their scores (prefill) are held to four waves per SIMD
+// (128 registers, a few spilled outside the slab loop).  The fused variant and smaller
+// blocks keep their registers: there the spills cost more than the extra wave gains.
+__global__ __launch_bounds__(64 * waves_per_block(RG))
+__attribute__((amdgpu_waves_per_eu(FMT == 0 && NT == 16 && !FUSE ? 4 : 1, 8))) void k_logits(const LogitsParams p) {
     constexpr int kWavesPerBlock = waves_per_block(RG);
     constexpr int kThreads = 64 * kWavesPerBlock;
     extern __shared__ __align__(16) uint8_t lds[];
