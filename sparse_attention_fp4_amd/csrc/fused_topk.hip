@@ -594,7 +594,7 @@ hipError_t launch_logits_topk(const LogitsParams& p, int k, int32_t* out_idx, fl
         pl.cand = nullptr;
         pl.counts = nullptr;
         pl.zero = zb && scorer_runs ? reinterpret_cast<uint32_t*>(ws + lb) : nullptr;
-        pl.zero_words = (int)((zb + 3) / 4);  // at most 512 rows of two 16 KB histograms
+        pl.zero_words = (int)((zb + 3) / 4);  // at most 512 rows of one 16 KB histogram
         hipError_t e = launch_logits(pl, stream);
         if (e != hipSuccess) return e;
         if (zb && !scorer_runs) {

@@ -13,19 +13,20 @@
 //   1. hist:    each chunk builds the histogram of digit 1 of its keys in LDS and adds
 //               its nonzero bins to the row's histogram (global atomics).
 //   2. collect: each chunk reads the row's histogram, finds the bin d1 holding the
-//               row's k-th largest key, stores a bitmap of its columns above d1 (all
-//               selected) and its keys in d1 (the candidates, with their columns and
-//               count), and adds the digit-2 histogram of those candidates to the
-//               row's second histogram.
-//   3. finish:  one workgroup per row reads the second histogram, the candidate counts,
-//               the bitmap and the first slots of every chunk's candidates in one
-//               round of loads (a chunk with more candidates sends the workgroup
-//               through a slower path that reloads them), finds the digit-2 bin d2 holding
-//               the k-th key, selects every candidate above prefix (d1, d2), ranks the
-//               few candidates inside it by direct comparison (a digit-pass fallback
-//               handles more than 1024 of them), writes the columns in order from
-//               popcount scans of the bitmap, and clears its histograms and counter
-//               for the next call.
+//               row's k-th largest key, and stores a bitmap of its columns above d1
+//               (all selected) with their count, and its keys in d1 (the candidates,
+//               with their columns and count).
+//   3. finish:  one workgroup per group of up to 8 consecutive chunks (one chunk each
+//               when there are few rows).  Each reads the row's candidates (every
+//               chunk's first slots in one round of loads; a chunk with more sends the
+//               workgroups through a slower path that reloads them), the counts and its
+//               chunks' bitmaps, finds the digit-2 bin d2 holding the k-th key from an
+//               LDS histogram of the candidates, ranks the candidates with prefix (d1,
+//               d2) by direct comparison when not all of them are kept (digit passes
+//               handle more than 1024 of them), and counts the selected columns of the earlier chunks: that count
+//               is where its own chunks' columns go in the output, written in order from
+//               popcount scans of their bitmaps.  The first group's workgroup clears the
+//               row's histogram for the next call.
 // The workspace must be zero-filled before its first use; every call leaves the
 // histograms zero-filled again.
 #include "device_common.hpp"
@@ -43,7 +44,6 @@ static_assert(kPer * (kCT / 64) == 64, "the collect scan covers 64 (step, wave) 
 constexpr int kBins = 4096;
 constexpr int kWords = kChunk / 32;   // bitmap words per chunk
 constexpr int kMaxChunks = 128;    // rows of up to 524288 columns
-constexpr int kMaxWords = kMaxChunks * kWords;
 constexpr int kMaxK = 8192;
 
 struct RowState {
@@ -54,12 +54,12 @@ struct RowState {
 struct LongWs {
     RowState* st;        // [rows]
     uint32_t* hist;      // [rows][kBins]            digit 1 of the keys; zero between calls
-    uint32_t* hist2;     // [rows][kBins]            digit 2 of the candidates; zero between calls
-    uint32_t* bitmap;    // [rows][n_chunks * kWords] columns above bin d1 (+ selected candidates)
+    uint32_t* bitmap;    // [rows][n_chunks * kWords] columns above bin d1
     uint2* cand;         // [rows][n_chunks][kChunk]  candidates (bin d1): (key, column), column order
     int32_t* cnum;       // [rows][n_chunks]          candidates per chunk
+    int32_t* cabove;     // [rows][n_chunks]          columns above bin d1 per chunk
     int n_chunks;
-    size_t zero_end;     // bytes from the base through hist2: zero when a call starts
+    size_t zero_end;     // bytes from the base through hist: zero when a call starts
 };
 
 __device__ __forceinline__ uint32_t to_key(float v) {
@@ -115,10 +115,10 @@ __global__ __launch_bounds__(kCT) void k_hist(const TopkParams p, LongWs ws) {
 
 // ---------------------------------------------------------------- 2. collect
 struct CollectShared {
-    uint32_t h2[kBins];
     int wtot[kCT / 64];
     int pick[4];
     int total;
+    int above;
     uint32_t bits[kWords];
     int cnt[kPer * (kCT / 64)];
     int off[kPer * (kCT / 64)];
@@ -129,13 +129,15 @@ struct CollectShared {
 __device__ __forceinline__ void row_threshold_bin(CollectShared& sh, const TopkParams& p, const LongWs& ws,
                                                   int row, int& d1, int& kk) {
     constexpr int per = kBins / kCT;
+    static_assert(per == 8, "two 16-byte loads per thread cover its bins");
     int c[per], bin[per];
-    const uint32_t* gh = ws.hist + (int64_t)row * kBins;
+    // thread t owns bins 4095-8t .. 4088-8t, walked from the top ("before" = larger keys)
+    const uint4* gh4 = reinterpret_cast<const uint4*>(ws.hist + (int64_t)row * kBins);
+    const uint4 a = gh4[kBins / 4 - 1 - 2 * threadIdx.x], b = gh4[kBins / 4 - 2 - 2 * threadIdx.x];
+    c[0] = (int)a.w; c[1] = (int)a.z; c[2] = (int)a.y; c[3] = (int)a.x;
+    c[4] = (int)b.w; c[5] = (int)b.z; c[6] = (int)b.y; c[7] = (int)b.x;
 #pragma unroll
-    for (int b = 0; b < per; b++) {  // walked from the top: "before" = larger keys
-        bin[b] = kBins - 1 - (threadIdx.x * per + b);
-        c[b] = (int)gh[bin[b]];
-    }
+    for (int i = 0; i < per; i++) bin[i] = kBins - 1 - (threadIdx.x * per + i);
     pick_bin<kCT, per>(c, bin, p.k, sh.wtot, sh.pick);
     if (sh.pick[2] <= p.k) {
         d1 = -1;
@@ -154,28 +156,30 @@ __global__ __launch_bounds__(kCT) void k_collect(const TopkParams p, LongWs ws) 
     const int nch = ws.n_chunks;
     uint32_t key[kPer];
     load_chunk(p, row, chunk, key);  // in flight with the histogram loads
-    for (int i = threadIdx.x; i < kBins; i += kCT) sh.h2[i] = 0u;
+    if (threadIdx.x == 0) sh.above = 0;
     int d1, kk;
     row_threshold_bin(sh, p, ws, row, d1, kk);  // ends with a barrier
     const int c0 = chunk * kChunk;
 
-    // ---- bitmap of the columns above bin d1; candidates of bin d1 and their digit 2
+    // ---- bitmap of the columns above bin d1 and its count; candidates of bin d1
     bool cand[kPer];
+    int above = 0;  // this wave's columns above d1 (uniform)
 #pragma unroll
     for (int j = 0; j < kPer; j++) {
         const uint32_t kj = key[j];
         const int dig = (int)(kj >> 20);
-        const bool above = kj != 0u && (d1 < 0 || dig > d1);
+        const bool up = kj != 0u && (d1 < 0 || dig > d1);
         // a wave covers 64 consecutive columns = two bitmap words
-        const unsigned long long ma = __ballot(above);
+        const unsigned long long ma = __ballot(up);
+        above += __popcll(ma);
         const int w0 = (threadIdx.x + kCT * j) >> 5;
         if (lane == 0) sh.bits[w0] = (uint32_t)ma;
         if (lane == 32) sh.bits[w0] = (uint32_t)(ma >> 32);
         cand[j] = d1 >= 0 && kj != 0u && dig == d1;
         const unsigned long long mc = __ballot(cand[j]);
         if (lane == 0) sh.cnt[j * (kCT / 64) + wave] = __popcll(mc);
-        if (cand[j]) atomicAdd(&sh.h2[(kj >> 8) & 0xfffu], 1u);
     }
+    if (lane == 0 && above) atomicAdd(&sh.above, above);
     lds_barrier();
     if (wave == 0) {  // exclusive scan over the kPer * kCT / 64 = 64 (step, wave) blocks
         const int x = sh.cnt[lane];
@@ -198,34 +202,35 @@ __global__ __launch_bounds__(kCT) void k_collect(const TopkParams p, LongWs ws) 
     for (int i = threadIdx.x; i < kWords; i += kCT) gbits[i] = sh.bits[i];
     if (threadIdx.x == 0) {
         ws.cnum[(int64_t)row * nch + chunk] = sh.total;
+        ws.cabove[(int64_t)row * nch + chunk] = sh.above;
         if (chunk == 0) {
             ws.st[row].d1 = d1;
             ws.st[row].kk = kk;
         }
     }
-    // the chunk's digit-2 counts join the row's second histogram
-    uint32_t* gh2 = ws.hist2 + (int64_t)row * kBins;
-    for (int i = threadIdx.x; i < kBins; i += kCT) {
-        const uint32_t v = sh.h2[i];
-        if (v) atomicAdd(&gh2[i], v);
-    }
 }
 
 // ---------------------------------------------------------------- 3. finish
-constexpr int kFT = 1024;    // threads of the finishing workgroup
-constexpr int kCR = 8;       // candidates per thread per round
+constexpr int kFT = 512;        // threads of a finishing workgroup
+constexpr int kGMax = kFT / 64;  // chunks per finishing workgroup: one wave writes each
+constexpr int kCR = 8;          // candidates per thread per round
 constexpr int kRankMax = 1024;  // candidates at the threshold prefix ranked by comparison
+static_assert(kMaxChunks * 32 == kFT * kCR && kCR % 2 == 0,
+              "up-front loads fill the candidate registers in slot pairs, 32 slots a chunk or more");
 
 struct FinishShared {
-    alignas(16) uint32_t h[kBins];
-    uint32_t bits[kMaxWords];  // the row's bitmap
-    uint32_t mkey[kRankMax];   // candidates with the threshold prefix (d1, d2)
+    alignas(16) uint32_t h[kBins];     // digit-2 histogram, then the narrowing passes'
+    alignas(16) uint32_t bits[kGMax * kWords];  // this workgroup's chunks' bitmaps
+    uint32_t mkey[kRankMax];           // candidates with the threshold prefix (d1, d2)
     int mcol[kRankMax];
     int cnum[kMaxChunks];
-    int coff[kMaxChunks + 1];  // candidate prefix over chunks
+    int coff[kMaxChunks + 1];          // candidate prefix over chunks (flat mode)
     int wtot[kFT / 64];
+    int part[2][3];                    // waves 0, 1: columns above d1 before this chunk, in the row; candidates
     int pick[4];
+    int ctot[kGMax];                   // selected columns of each of this workgroup's chunks
     int nm;
+    int before;                        // selected candidates of earlier chunks
 };
 
 // Candidate registers: kCR per thread.  In the common case they hold every candidate
@@ -266,14 +271,13 @@ __device__ __forceinline__ void load_flat(CandRegs& r, const FinishShared& sh, c
 
 // One digit pass over the candidates that pass `keep`: histogram of digit(key, col)
 // and the bin holding the kk-th element in the given order.
-template <typename Keep, typename Digit>
+template <bool FLAT, typename Keep, typename Digit>
 __device__ __forceinline__ void cand_pass(FinishShared& sh, CandRegs& r, const LongWs& ws, int row, int nch,
-                                          int m, int rounds, bool flat, int kk, bool descending, Keep keep,
-                                          Digit digit) {
+                                          int m, int rounds, int kk, bool descending, Keep keep, Digit digit) {
     for (int i = threadIdx.x; i < kBins; i += kFT) sh.h[i] = 0u;
     lds_barrier();
     for (int round = 0; round < rounds; round++) {
-        if (flat) load_flat(r, sh, ws, row, nch, m, round);
+        if (FLAT) load_flat(r, sh, ws, row, nch, m, round);
 #pragma unroll
         for (int j = 0; j < kCR; j++)
             if (r.col[j] >= 0 && keep(r.key[j], r.col[j])) atomicAdd(&sh.h[digit(r.key[j], r.col[j])], 1u);
@@ -289,191 +293,270 @@ __device__ __forceinline__ void cand_pass(FinishShared& sh, CandRegs& r, const L
     pick_bin<kFT, per>(c, bin, kk, sh.wtot, sh.pick);
 }
 
-__global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws) {
-    __shared__ FinishShared sh;
-    const int row = blockIdx.x;
-    if (row >= p.rows) return;
-    const int nch = ws.n_chunks;
-    const int k = p.k;
-    const int nwords = nch * kWords;
-    const uint32_t* rbits = ws.bitmap + (int64_t)row * nch * kWords;
-    uint32_t* gh = ws.hist + (int64_t)row * kBins;
-    uint32_t* gh2 = ws.hist2 + (int64_t)row * kBins;
-    constexpr int lspec = 6;            // candidate slots read per chunk up front: 64
-    constexpr int spec = 1 << lspec;
-    static_assert(kMaxChunks * spec == kFT * kCR && kCR % 2 == 0 && kMaxWords % (4 * kFT) == 0,
-                  "up-front loads fill the candidate registers in slot pairs");
-
-    // ---- one round of loads: state, candidate counts, second histogram, bitmap, and the
-    // first `spec` candidate slots of every chunk (read before the counts are known;
-    // slots past a count are ignored).  This workgroup is alone on its CU, where the
-    // number of load instructions, not their latency, sets the pace: every array is read
-    // 16 bytes per lane.
-    // the digit-1 histogram was last read by the collect pass: clear it for the next
-    // call now, so the stores drain while this workgroup works
-    static_assert(kBins == 4 * kFT, "one 16-byte store per thread clears a histogram");
-    reinterpret_cast<uint4*>(gh)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
-    const int d1 = ws.st[row].d1;
-    int kk = ws.st[row].kk;
-    const int my_cnum = threadIdx.x < nch ? ws.cnum[(int64_t)row * nch + threadIdx.x] : 0;
-    // second histogram: thread t owns bins 4095-4t .. 4092-4t (one 16-byte load)
-    constexpr int per = kBins / kFT;
-    uint4* h2v = reinterpret_cast<uint4*>(gh2) + (kFT - 1 - threadIdx.x);
-    const uint4 h2 = *h2v;
-    int c2[per] = {(int)h2.w, (int)h2.z, (int)h2.y, (int)h2.x}, bin2[per];
+// Marks this workgroup's selected candidates in its bitmaps and adds those of earlier
+// chunks to sh.before.  FLAT: the candidates are reloaded round by round (some chunk has
+// more than its up-front slots); otherwise registers [0, 2 * jr) hold them all.
+template <bool FLAT>
+__device__ __forceinline__ void select_candidates(FinishShared& sh, CandRegs& r, const LongWs& ws, int row, int nch,
+                                                  int m, int rounds, int jr, int d1, int kk, int chunk, int nown) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int before = 0;  // this thread's selected candidates of earlier chunks
+    // ---- digit 2 of the candidates: LDS histogram, picked by wave 0
+    for (int round = 0; round < rounds; round++) {
+        if (FLAT) load_flat(r, sh, ws, row, nch, m, round);
 #pragma unroll
-    for (int b = 0; b < per; b++) bin2[b] = kBins - 1 - (threadIdx.x * per + b);
-    // bitmap: words 4q .. 4q+3 for q = threadIdx.x + kFT * j
-    constexpr int kXQ = kMaxWords / (4 * kFT);
-    const uint4* rbits4 = reinterpret_cast<const uint4*>(rbits);
-    uint4 x[kXQ];
+        for (int j = 0; j < kCR; j++)
+            if (j < 2 * jr && r.col[j] >= 0) atomicAdd(&sh.h[(r.key[j] >> 8) & (kBins - 1)], 1u);
+    }
+    lds_barrier();
+    if (wave == 0) {
+        // lane l owns bins 4095-64l .. 4032-64l, walked from the top; the lane whose
+        // range holds the kk-th key then has its 64 bins scanned by the whole wave
+        static_assert(kBins == 64 * 64, "64 bins per lane");
+        const uint4* h4 = reinterpret_cast<const uint4*>(sh.h) + (kBins - 64 - 64 * lane) / 4;
+        int s = 0;
 #pragma unroll
-    for (int j = 0; j < kXQ; j++) {
-        const int q = threadIdx.x + kFT * j;
-        x[j] = 4 * q < nwords ? rbits4[q] : make_uint4(0u, 0u, 0u, 0u);
+        for (int i = 0; i < 16; i++) {
+            const uint4 v = h4[i];
+            s += (int)(v.x + v.y + v.z + v.w);
+        }
+        const int incl = wave_incl_scan(s);
+        const unsigned long long own = __ballot(incl - s < kk && kk <= incl);
+        int pk0 = 0, pk1 = 0, pk3 = 0;
+        if (own) {
+            const int L = __ffsll((long long)own) - 1;
+            const int ex = __builtin_amdgcn_readlane(incl - s, L);
+            const int c = (int)sh.h[kBins - 1 - 64 * L - lane];
+            const int incl2 = wave_incl_scan(c);
+            const unsigned long long at = __ballot(ex + incl2 >= kk);
+            const int J = at ? __ffsll((long long)at) - 1 : 63;
+            pk0 = kBins - 1 - 64 * L - J;
+            pk1 = ex + __builtin_amdgcn_readlane(incl2 - c, J);
+            pk3 = __builtin_amdgcn_readlane(c, J);
+        }
+        if (lane == 0) {
+            sh.pick[0] = pk0;
+            sh.pick[1] = pk1;
+            sh.pick[3] = pk3;
+        }
     }
-    // candidate slot pairs: pair q = threadIdx.x + kFT * j holds slots 2q % spec and
-    // 2q % spec + 1 of chunk 2q / spec
-    uint4 sv[kCR / 2];
-#pragma unroll
-    for (int j = 0; j < kCR / 2; j++) {
-        const int q = threadIdx.x + kFT * j;
-        const int c = (2 * q) >> lspec, slot = (2 * q) & (spec - 1);
-        sv[j] = c < nch ? *reinterpret_cast<const uint4*>(ws.cand + ((int64_t)row * nch + c) * kChunk + slot)
-                        : make_uint4(0u, 0xffffffffu, 0u, 0xffffffffu);
-    }
-#pragma unroll
-    for (int j = 0; j < kXQ; j++) {
-        const int q = threadIdx.x + kFT * j;
-        if (4 * q < nwords) reinterpret_cast<uint4*>(sh.bits)[q] = x[j];
-    }
-    if (threadIdx.x < nch) sh.cnum[threadIdx.x] = my_cnum;
-    if (threadIdx.x == 0) sh.nm = 0;
-    {
-        int before, total;
-        block_excl_scan<kFT>(my_cnum, sh.wtot, before, total);  // barriers inside
-        if (threadIdx.x < nch) sh.coff[threadIdx.x] = before;
-        if (threadIdx.x == 0) sh.coff[nch] = total;
-    }
-    const bool flat = __syncthreads_or(my_cnum > spec) != 0;  // also publishes coff
-    const int m = sh.coff[nch];
-    const int rounds = flat ? (m + kFT * kCR - 1) / (kFT * kCR) : 1;
-    CandRegs r;
-#pragma unroll
-    for (int j = 0; j < kCR / 2; j++) {
-        const int q = threadIdx.x + kFT * j;
-        const int c = (2 * q) >> lspec, slot = (2 * q) & (spec - 1);
-        const int cn = c < nch ? sh.cnum[c] : 0;
-        r.key[2 * j] = sv[j].x;
-        r.col[2 * j] = slot < cn ? (int)sv[j].y : -1;
-        r.key[2 * j + 1] = sv[j].z;
-        r.col[2 * j + 1] = slot + 1 < cn ? (int)sv[j].w : -1;
-    }
-
-    if (d1 >= 0) {
-        // ---- digit 2 from the row's second histogram (pick_bin ends with a barrier)
-        pick_bin<kFT, per>(c2, bin2, kk, sh.wtot, sh.pick);
-        // each thread has its bins' counts in registers: clear them for the next call
-        *h2v = make_uint4(0u, 0u, 0u, 0u);
-        const uint32_t preA = ((uint32_t)d1 << 12) | (uint32_t)sh.pick[0];
-        kk -= sh.pick[1];                      // keys wanted with prefix preA, >= 1
-        const int n_pre = sh.pick[3];          // candidates with prefix preA
-        // ---- candidates above the prefix are selected; those at it are collected
+    lds_barrier();
+    const uint32_t preA = ((uint32_t)d1 << 12) | (uint32_t)sh.pick[0];
+    kk -= sh.pick[1];                      // keys wanted with prefix preA, >= 1
+    const int n_pre = sh.pick[3];          // candidates with prefix preA
+    // selected: prefix above preA, or at it and within the first kk of the row's
+    // order (larger key, then smaller column): key > T, or key == T and col <= c_cut
+    uint32_t T = preA << 8;
+    int c_cut = 0x7fffffff;                // every candidate at the prefix when kk == n_pre
+    if (__builtin_expect(kk < n_pre && n_pre <= kRankMax, 0)) {
+        // ---- the candidates at the prefix go to LDS and are ranked by comparison
         for (int round = 0; round < rounds; round++) {
-            if (flat) load_flat(r, sh, ws, row, nch, m, round);
+            if (FLAT) load_flat(r, sh, ws, row, nch, m, round);
 #pragma unroll
             for (int j = 0; j < kCR; j++) {
-                const uint32_t pre = r.key[j] >> 8;
-                const int col = r.col[j];
-                if (col < 0) continue;
-                if (pre > preA) {
-                    atomicOr(&sh.bits[col >> 5], 1u << (col & 31));
-                } else if (pre == preA && n_pre <= kRankMax) {
+                if (j < 2 * jr && r.col[j] >= 0 && (r.key[j] >> 8) == preA) {
                     const int at = atomicAdd(&sh.nm, 1);
                     if (at < kRankMax) {   // n_pre bounds it; the test keeps LDS safe
                         sh.mkey[at] = r.key[j];
-                        sh.mcol[at] = col;
+                        sh.mcol[at] = r.col[j];
                     }
                 }
             }
         }
         lds_barrier();
-        if (n_pre <= kRankMax) {
-            // ---- rank each collected candidate by direct comparison
-            const int nm = min(sh.nm, kRankMax);
-            for (int t = threadIdx.x; t < nm; t += kFT) {
-                const uint32_t kt = sh.mkey[t];
-                const int ct = sh.mcol[t];
-                int rank = 0;
-                for (int u = 0; u < nm; u++) {
-                    const uint32_t ku = sh.mkey[u];
-                    rank += (ku > kt || (ku == kt && sh.mcol[u] < ct)) ? 1 : 0;
-                }
-                if (rank < kk) atomicOr(&sh.bits[ct >> 5], 1u << (ct & 31));
+        const int nm = min(sh.nm, kRankMax);
+        // the kk-th of the prefix candidates in the row's order sets (T, c_cut)
+        for (int t = threadIdx.x; t < nm; t += kFT) {
+            const uint32_t kt = sh.mkey[t];
+            const int ct = sh.mcol[t];
+            int rank = 0;
+            for (int u = 0; u < nm; u++) {
+                const uint32_t ku = sh.mkey[u];
+                rank += (ku > kt || (ku == kt && sh.mcol[u] < ct)) ? 1 : 0;
             }
-        } else {
-            // ---- many candidates share the prefix: digit passes over them
-            cand_pass(sh, r, ws, row, nch, m, rounds, flat, kk, true,
-                      [&](uint32_t kx, int) { return (kx >> 8) == preA; },
-                      [&](uint32_t kx, int) { return (int)(kx & 0xffu); });
-            const uint32_t T = (preA << 8) | (uint32_t)sh.pick[0];
-            kk -= sh.pick[1];  // ties at T to keep, >= 1
-            const int ties = sh.pick[3];
-            int c_cut = 0x7fffffff;
-            if (kk < ties) {
-                // the kk-th smallest column among the ties at T: bits [30:20], [19:8], [7:0]
-                cand_pass(sh, r, ws, row, nch, m, rounds, flat, kk, false, [&](uint32_t kx, int) { return kx == T; },
-                          [&](uint32_t, int col) { return (int)(((uint32_t)col >> 20) & 0x7ffu); });
-                const uint32_t c1 = (uint32_t)sh.pick[0];
-                kk -= sh.pick[1];
-                cand_pass(sh, r, ws, row, nch, m, rounds, flat, kk, false,
-                          [&](uint32_t kx, int col) { return kx == T && ((uint32_t)col >> 20) == c1; },
-                          [&](uint32_t, int col) { return (int)(((uint32_t)col >> 8) & 0xfffu); });
-                const uint32_t c2 = (c1 << 12) | (uint32_t)sh.pick[0];
-                kk -= sh.pick[1];
-                cand_pass(sh, r, ws, row, nch, m, rounds, flat, kk, false,
-                          [&](uint32_t kx, int col) { return kx == T && ((uint32_t)col >> 8) == c2; },
-                          [&](uint32_t, int col) { return (int)((uint32_t)col & 0xffu); });
-                c_cut = (int)((c2 << 8) | (uint32_t)sh.pick[0]);
+            if (rank == kk - 1) {
+                sh.pick[0] = (int)kt;
+                sh.pick[1] = ct;
             }
-            for (int round = 0; round < rounds; round++) {
-                if (flat) load_flat(r, sh, ws, row, nch, m, round);
+        }
+        lds_barrier();
+        T = (uint32_t)sh.pick[0];
+        c_cut = sh.pick[1];
+    } else if (__builtin_expect(kk < n_pre, 0)) {
+        // ---- many candidates share the prefix: digit passes over them
+        cand_pass<FLAT>(sh, r, ws, row, nch, m, rounds, kk, true,
+                  [&](uint32_t kx, int) { return (kx >> 8) == preA; },
+                  [&](uint32_t kx, int) { return (int)(kx & 0xffu); });
+        T = (preA << 8) | (uint32_t)sh.pick[0];
+        kk -= sh.pick[1];  // ties at T to keep, >= 1
+        const int ties = sh.pick[3];
+        if (kk < ties) {
+            // the kk-th smallest column among the ties at T: bits [30:20], [19:8], [7:0]
+            cand_pass<FLAT>(sh, r, ws, row, nch, m, rounds, kk, false, [&](uint32_t kx, int) { return kx == T; },
+                      [&](uint32_t, int col) { return (int)(((uint32_t)col >> 20) & 0x7ffu); });
+            const uint32_t c1 = (uint32_t)sh.pick[0];
+            kk -= sh.pick[1];
+            cand_pass<FLAT>(sh, r, ws, row, nch, m, rounds, kk, false,
+                      [&](uint32_t kx, int col) { return kx == T && ((uint32_t)col >> 20) == c1; },
+                      [&](uint32_t, int col) { return (int)(((uint32_t)col >> 8) & 0xfffu); });
+            const uint32_t c2 = (c1 << 12) | (uint32_t)sh.pick[0];
+            kk -= sh.pick[1];
+            cand_pass<FLAT>(sh, r, ws, row, nch, m, rounds, kk, false,
+                      [&](uint32_t kx, int col) { return kx == T && ((uint32_t)col >> 8) == c2; },
+                      [&](uint32_t, int col) { return (int)((uint32_t)col & 0xffu); });
+            c_cut = (int)((c2 << 8) | (uint32_t)sh.pick[0]);
+        }
+    }
+    // ---- selected candidates: earlier chunks' are counted, this workgroup's marked
+    for (int round = 0; round < rounds; round++) {
+        if (FLAT) load_flat(r, sh, ws, row, nch, m, round);
 #pragma unroll
-                for (int j = 0; j < kCR; j++) {
-                    const uint32_t kx = r.key[j];
-                    const int col = r.col[j];
-                    if (col >= 0 && (kx >> 8) == preA && (kx > T || (kx == T && col <= c_cut)))
-                        atomicOr(&sh.bits[col >> 5], 1u << (col & 31));
-                }
+        for (int j = 0; j < kCR; j++) {
+            const uint32_t kx = r.key[j];
+            const int col = r.col[j];
+            if (j >= 2 * jr || col < 0) continue;
+            const uint32_t pre = kx >> 8;
+            const bool sel = pre > preA || (pre == preA && (kx > T || (kx == T && col <= c_cut)));
+            if (!sel) continue;
+            const int c = col / kChunk;
+            if (c < chunk) before++;
+            else if (c < chunk + nown) atomicOr(&sh.bits[(c - chunk) * kWords + ((col & (kChunk - 1)) >> 5)], 1u << (col & 31));
+        }
+    }
+    const int wb = wave_sum_i32(before);
+    if (lane == 0 && wb) atomicAdd(&sh.before, wb);
+    lds_barrier();
+}
+
+// gsz: chunks per workgroup (1..kGMax); chunks [grp * gsz, +gsz) of the row.
+__global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws, int gsz) {
+    __shared__ FinishShared sh;
+    const int nch = ws.n_chunks;
+    const int ngrp = (nch + gsz - 1) / gsz;
+    const int row = blockIdx.x / ngrp, grp = blockIdx.x - row * ngrp;
+    if (row >= p.rows) return;
+    const int chunk = grp * gsz, nown = min(gsz, nch - chunk);  // first chunk, chunks owned
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int k = p.k;
+    const int64_t rc = (int64_t)row * nch;
+    const int lspec = nch <= 64 ? 6 : 5;  // candidate slots read per chunk up front: 64 or 32
+    const int spec = 1 << lspec;
+    // slot-pair registers that can hold a candidate up front (the rest stay empty)
+    const int jn = min(kCR / 2, (nch * spec / 2 + kFT - 1) / kFT);
+
+    // ---- one round of loads: state, counts, these chunks' bitmaps and the first `spec`
+    // candidate slots of every chunk (read before the counts are known; slots past a
+    // count are ignored), 16 bytes per lane where the arrays allow
+    if (grp == 0) {  // the digit-1 histogram was last read by the collect pass: clear it
+        uint4* gh = reinterpret_cast<uint4*>(ws.hist + (int64_t)row * kBins);
+        for (int i = threadIdx.x; i < kBins / 4; i += kFT) gh[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    const int d1 = ws.st[row].d1;
+    int kk = ws.st[row].kk;
+    const int my_cnum = threadIdx.x < nch ? ws.cnum[rc + threadIdx.x] : 0;
+    const int my_above = threadIdx.x < nch ? ws.cabove[rc + threadIdx.x] : 0;
+    static_assert(kGMax * kWords / 4 <= kFT, "one 16-byte bitmap load per thread at most");
+    uint4 bw = make_uint4(0u, 0u, 0u, 0u);
+    if (threadIdx.x < nown * (kWords / 4))
+        bw = reinterpret_cast<const uint4*>(ws.bitmap + (rc + chunk) * kWords)[threadIdx.x];
+    uint4 sv[kCR / 2];
+#pragma unroll
+    for (int j = 0; j < kCR / 2; j++) {
+        const int q = threadIdx.x + kFT * j;
+        const int c = (2 * q) >> lspec, slot = (2 * q) & (spec - 1);
+        sv[j] = j < jn && c < nch ? *reinterpret_cast<const uint4*>(ws.cand + (rc + c) * kChunk + slot)
+                                  : make_uint4(0u, 0xffffffffu, 0u, 0xffffffffu);
+    }
+    // LDS set-up while the loads are in flight
+    static_assert(kBins == 8 * kFT, "two 16-byte clearing stores per thread");
+    reinterpret_cast<uint4*>(sh.h)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+    reinterpret_cast<uint4*>(sh.h)[threadIdx.x + kFT] = make_uint4(0u, 0u, 0u, 0u);
+    if (threadIdx.x == 0) {
+        sh.nm = 0;
+        sh.before = 0;
+    }
+    static_assert(kMaxChunks <= 128, "per-chunk counts fit waves 0 and 1");
+    if (wave < 2) {  // sums over chunks: threads 0..127 hold one chunk each
+        const int ab = wave_sum_i32(threadIdx.x < chunk ? my_above : 0);
+        const int at = wave_sum_i32(my_above);
+        const int cs = wave_incl_scan(my_cnum);
+        if (threadIdx.x < nch) sh.coff[threadIdx.x + 1] = cs;  // this wave's part; wave 1 adds wave 0's below
+        if (lane == 0) {
+            sh.part[wave][0] = ab;
+            sh.part[wave][1] = at;
+        }
+        if (lane == 63) sh.part[wave][2] = cs;
+    }
+    if (threadIdx.x < nch) sh.cnum[threadIdx.x] = my_cnum;
+    if (threadIdx.x < kGMax * kWords / 4) reinterpret_cast<uint4*>(sh.bits)[threadIdx.x] = bw;
+    const bool flat = __syncthreads_or(my_cnum > spec) != 0;
+    const int above_before = sh.part[0][0] + sh.part[1][0];
+    const int above_total = sh.part[0][1] + sh.part[1][1];
+    const int m = sh.part[0][2] + sh.part[1][2];  // candidates of the row
+    int rounds = 1;                               // reload rounds
+    CandRegs r;
+    if (flat) {
+        // chunk-order prefix of the candidate counts for the flat reloads
+        if (threadIdx.x == 0) sh.coff[0] = 0;
+        if (threadIdx.x >= 64 && threadIdx.x < nch) sh.coff[threadIdx.x + 1] += sh.part[0][2];
+        lds_barrier();
+        rounds = (m + kFT * kCR - 1) / (kFT * kCR);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kCR / 2; j++) {
+            const int q = threadIdx.x + kFT * j;
+            const int c = (2 * q) >> lspec, slot = (2 * q) & (spec - 1);
+            const int cn = c < nch ? sh.cnum[c] : 0;
+            r.key[2 * j] = sv[j].x;
+            r.col[2 * j] = slot < cn ? (int)sv[j].y : -1;
+            r.key[2 * j + 1] = sv[j].z;
+            r.col[2 * j + 1] = slot + 1 < cn ? (int)sv[j].w : -1;
+        }
+    }
+
+    if (d1 >= 0) {
+        if (__builtin_expect(flat, 0)) select_candidates<true>(sh, r, ws, row, nch, m, rounds, kCR / 2, d1, kk, chunk, nown);
+        else select_candidates<false>(sh, r, ws, row, nch, m, 1, jn, d1, kk, chunk, nown);
+    }
+
+    // ---- the chunks' columns in order: wave w writes chunk chunk + w, lane l its
+    // bitmap words 2l and 2l+1
+    static_assert(kWords == 128, "two bitmap words per lane of one wave");
+    const uint32_t w0 = sh.bits[wave * kWords + 2 * lane], w1 = sh.bits[wave * kWords + 2 * lane + 1];
+    const int cnt = __popc(w0) + __popc(w1);
+    const int incl = wave_incl_scan(cnt);
+    if (gsz > 1) {
+        if (lane == 63) sh.ctot[wave] = incl;
+        lds_barrier();
+    }
+    if (wave < nown) {
+        int base = above_before + sh.before;
+        for (int w = 0; w < wave; w++) base += sh.ctot[w];
+        int pos = base + incl - cnt;
+        const float* srow = p.scores + (int64_t)row * p.row_stride;
+        int32_t* oidx = p.out_idx + (int64_t)row * k;
+        float* oval = p.out_vals ? p.out_vals + (int64_t)row * k : nullptr;
+        const int cbase = (chunk + wave) * kChunk + 64 * lane;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            uint32_t bits = h ? w1 : w0;
+            while (bits && pos < k) {
+                const int col = cbase + 32 * h + __ffs((int)bits) - 1;
+                oidx[pos] = col;
+                if (oval) oval[pos] = srow[col];
+                pos++;
+                bits &= bits - 1u;
             }
         }
     }
-    lds_barrier();
-
-    // ---- columns in order: thread t owns words [t*wpt, (t+1)*wpt) of the bitmap; a
-    // block scan of their popcounts gives each thread its output offset
-    const float* srow = p.scores + (int64_t)row * p.row_stride;
-    int32_t* oidx = p.out_idx + (int64_t)row * k;
-    float* oval = p.out_vals ? p.out_vals + (int64_t)row * k : nullptr;
-    const int wpt = (nwords + kFT - 1) / kFT;
-    const int wa = threadIdx.x * wpt, wb = min(wa + wpt, nwords);
-    int cnt = 0;
-    for (int w = wa; w < wb; w++) cnt += __popc(sh.bits[w]);
-    int pos, done;
-    block_excl_scan<kFT>(cnt, sh.wtot, pos, done);
-    for (int w = wa; w < wb && pos < k; w++) {
-        uint32_t bits = sh.bits[w];
-        while (bits && pos < k) {
-            const int col = w * 32 + __ffs((int)bits) - 1;
-            oidx[pos] = col;
-            if (oval) oval[pos] = srow[col];
-            pos++;
-            bits &= bits - 1u;
+    // every valid key kept (fewer than k): the last group pads the row
+    if (d1 < 0 && grp == ngrp - 1) {
+        int32_t* oidx = p.out_idx + (int64_t)row * k;
+        float* oval = p.out_vals ? p.out_vals + (int64_t)row * k : nullptr;
+        for (int i = min(above_total, k) + threadIdx.x; i < k; i += kFT) {
+            oidx[i] = -1;
+            if (oval) oval[i] = -__builtin_inff();
         }
-    }
-    for (int i = min(done, k) + threadIdx.x; i < k; i += kFT) {
-        oidx[i] = -1;
-        if (oval) oval[i] = -__builtin_inff();
     }
 }
 
@@ -489,14 +572,14 @@ LongWs carve(void* base, int rows, int cols, size_t* bytes) {
     o = align256(o + (size_t)rows * sizeof(RowState));
     w.hist = reinterpret_cast<uint32_t*>(b + o);
     o = align256(o + (size_t)rows * kBins * 4);
-    w.hist2 = reinterpret_cast<uint32_t*>(b + o);
-    o = align256(o + (size_t)rows * kBins * 4);
     w.zero_end = o;
     w.bitmap = reinterpret_cast<uint32_t*>(b + o);
     o = align256(o + rc * kWords * 4);
     w.cand = reinterpret_cast<uint2*>(b + o);
     o = align256(o + rc * kChunk * sizeof(uint2));
     w.cnum = reinterpret_cast<int32_t*>(b + o);
+    o = align256(o + rc * 4);
+    w.cabove = reinterpret_cast<int32_t*>(b + o);
     o = align256(o + rc * 4);
     if (bytes) *bytes = o;
     return w;
@@ -511,7 +594,7 @@ LongWs carve(void* base, int rows, int cols, size_t* bytes) {
 bool topk_long_rows(int rows, int cols) { return cols > 32768 || (cols > 8192 && rows <= 64); }
 
 // Leading workspace bytes that must be zero when a call starts: the row states and the
-// two histograms come first in the layout (a caller that cannot keep the workspace
+// histogram come first in the layout (a caller that cannot keep the workspace
 // between calls clears just these).
 size_t topk_long_zero_bytes(int rows, int cols) { return carve(nullptr, rows, cols, nullptr).zero_end; }
 
@@ -528,7 +611,13 @@ hipError_t launch_topk_long(const TopkParams& p, void* workspace, hipStream_t st
     const unsigned grid = (unsigned)(p.rows * w.n_chunks);
     hipLaunchKernelGGL(k_hist, dim3(grid), dim3(kCT), 0, stream, p, w);
     hipLaunchKernelGGL(k_collect, dim3(grid), dim3(kCT), 0, stream, p, w);
-    hipLaunchKernelGGL(k_finish, dim3(p.rows), dim3(kFT), 0, stream, p, w);
+    // Few rows: one finishing workgroup per chunk spreads the output; many rows: up to
+    // kGMax chunks per workgroup, so that the redundant reading and ranking of each row's
+    // candidates stays near one pass over the chip.
+    int gsz = 1;
+    while (gsz < kGMax && (int64_t)p.rows * ((w.n_chunks + gsz - 1) / gsz) > 512) gsz *= 2;
+    const unsigned fgrid = (unsigned)(p.rows * ((w.n_chunks + gsz - 1) / gsz));
+    hipLaunchKernelGGL(k_finish, dim3(fgrid), dim3(kFT), 0, stream, p, w, gsz);
     return hipGetLastError();
 }
 
