@@ -45,6 +45,7 @@ constexpr int kBins = 4096;
 constexpr int kWords = kChunk / 32;   // bitmap words per chunk
 constexpr int kMaxChunks = 128;    // rows of up to 524288 columns
 constexpr int kMaxK = 8192;
+constexpr int kWaveOfGroups = 512;  // workgroups that keep the chip busy (two a CU)
 
 struct RowState {
     int d1;         // digit-1 bin of the k-th largest key, or -1 when every valid key is kept
@@ -79,34 +80,43 @@ __device__ __forceinline__ int row_len(const TopkParams& p, int row) {
     return len;
 }
 
-// Thread t holds elements t + kCT * j of the chunk (index order = j, wave, lane).
-__device__ __forceinline__ void load_chunk(const TopkParams& p, int row, int chunk, uint32_t (&key)[kPer]) {
-    const int len = row_len(p, row);
+// Thread t holds elements t + kCT * j of the chunk (index order = j, wave, lane);
+// columns at or past len read as -inf.
+__device__ __forceinline__ void load_chunk_raw(const TopkParams& p, int row, int len, int chunk, float (&v)[kPer]) {
     const int c0 = chunk * kChunk;
     const int n = max(0, min(len - c0, kChunk));
     const float* src = p.scores + (int64_t)row * p.row_stride + c0;
-    float v[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; j++) {
         const int i = threadIdx.x + kCT * j;
         v[j] = i < n ? src[i] : -__builtin_inff();
     }
-#pragma unroll
-    for (int j = 0; j < kPer; j++) key[j] = to_key(v[j]);
 }
 
 // ---------------------------------------------------------------- 1. hist
-__global__ __launch_bounds__(kCT) void k_hist(const TopkParams p, LongWs ws) {
+// hs: chunks per workgroup (chunks [hg * hs, +hs) of the row, one LDS histogram and one
+// flush for all of them); chunks past the row's end are skipped.
+__global__ __launch_bounds__(kCT) void k_hist(const TopkParams p, LongWs ws, int hs) {
     __shared__ uint32_t h[kBins];
-    const int row = blockIdx.x / ws.n_chunks, chunk = blockIdx.x - row * ws.n_chunks;
+    const int nhg = (ws.n_chunks + hs - 1) / hs;
+    const int row = blockIdx.x / nhg, hg = blockIdx.x - row * nhg;
     if (row >= p.rows) return;
+    const int len = row_len(p, row);
+    const int c_begin = hg * hs, c_end = min(min(c_begin + hs, ws.n_chunks), (len + kChunk - 1) / kChunk);
+    if (c_begin >= c_end) return;  // past the row's end
     for (int i = threadIdx.x; i < kBins; i += kCT) h[i] = 0u;
-    uint32_t key[kPer];
-    load_chunk(p, row, chunk, key);
+    float v[kPer];
+    load_chunk_raw(p, row, len, c_begin, v);
     lds_barrier();
+    for (int c = c_begin; c < c_end; c++) {
+        uint32_t key[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; j++)
-        if (key[j]) atomicAdd(&h[key[j] >> 20], 1u);
+        for (int j = 0; j < kPer; j++) key[j] = to_key(v[j]);
+        if (c + 1 < c_end) load_chunk_raw(p, row, len, c + 1, v);  // in flight with the atomics
+#pragma unroll
+        for (int j = 0; j < kPer; j++)
+            if (key[j]) atomicAdd(&h[key[j] >> 20], 1u);
+    }
     lds_barrier();
     uint32_t* gh = ws.hist + (int64_t)row * kBins;
     for (int i = threadIdx.x; i < kBins; i += kCT)
@@ -118,22 +128,21 @@ struct CollectShared {
     int wtot[kCT / 64];
     int pick[4];
     int total;
-    int above;
-    uint32_t bits[kWords];
+    int wab[kCT / 64];                 // columns above d1 of each wave
+    alignas(8) uint32_t bits[kWords];
     int cnt[kPer * (kCT / 64)];
     int off[kPer * (kCT / 64)];
 };
 
-// The bin of the row's k-th largest key from the row's histogram.  Returns d1 (-1 when
-// every valid key is kept) and kk, the keys wanted in d1.
-__device__ __forceinline__ void row_threshold_bin(CollectShared& sh, const TopkParams& p, const LongWs& ws,
-                                                  int row, int& d1, int& kk) {
+// The bin of the row's k-th largest key from the row's histogram (a, b: this thread's
+// two 16-byte loads of it, bins 4095-8t .. 4088-8t).  Returns d1 (-1 when every valid key
+// is kept) and kk, the keys wanted in d1.
+__device__ __forceinline__ void row_threshold_bin(CollectShared& sh, const TopkParams& p, const uint4 a,
+                                                  const uint4 b, int& d1, int& kk) {
     constexpr int per = kBins / kCT;
     static_assert(per == 8, "two 16-byte loads per thread cover its bins");
     int c[per], bin[per];
-    // thread t owns bins 4095-8t .. 4088-8t, walked from the top ("before" = larger keys)
-    const uint4* gh4 = reinterpret_cast<const uint4*>(ws.hist + (int64_t)row * kBins);
-    const uint4 a = gh4[kBins / 4 - 1 - 2 * threadIdx.x], b = gh4[kBins / 4 - 2 - 2 * threadIdx.x];
+    // walked from the top ("before" = larger keys)
     c[0] = (int)a.w; c[1] = (int)a.z; c[2] = (int)a.y; c[3] = (int)a.x;
     c[4] = (int)b.w; c[5] = (int)b.z; c[6] = (int)b.y; c[7] = (int)b.x;
 #pragma unroll
@@ -150,16 +159,25 @@ __device__ __forceinline__ void row_threshold_bin(CollectShared& sh, const TopkP
 
 __global__ __launch_bounds__(kCT) void k_collect(const TopkParams p, LongWs ws) {
     __shared__ CollectShared sh;
-    const int row = blockIdx.x / ws.n_chunks, chunk = blockIdx.x - row * ws.n_chunks;
+    const int nch = ws.n_chunks;
+    const int row = blockIdx.x / nch, chunk = blockIdx.x - row * nch;
     if (row >= p.rows) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nch = ws.n_chunks;
-    uint32_t key[kPer];
-    load_chunk(p, row, chunk, key);  // in flight with the histogram loads
-    if (threadIdx.x == 0) sh.above = 0;
-    int d1, kk;
-    row_threshold_bin(sh, p, ws, row, d1, kk);  // ends with a barrier
+    // the row's histogram first (it does not wait for the row's length), then the chunk
+    const uint4* gh4 = reinterpret_cast<const uint4*>(ws.hist + (int64_t)row * kBins);
+    const uint4 ha = gh4[kBins / 4 - 1 - 2 * threadIdx.x], hb = gh4[kBins / 4 - 2 - 2 * threadIdx.x];
+    const int len = row_len(p, row);
     const int c0 = chunk * kChunk;
+    float v[kPer];
+    load_chunk_raw(p, row, len, chunk, v);
+    // a chunk past the row's end stores nothing (the finish never reads it); the first
+    // chunk always runs, since it stores the row's state
+    if (chunk > 0 && c0 >= len) return;
+    uint32_t key[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; j++) key[j] = to_key(v[j]);
+    int d1, kk;
+    row_threshold_bin(sh, p, ha, hb, d1, kk);  // ends with a barrier
 
     // ---- bitmap of the columns above bin d1 and its count; candidates of bin d1
     bool cand[kPer];
@@ -169,17 +187,15 @@ __global__ __launch_bounds__(kCT) void k_collect(const TopkParams p, LongWs ws) 
         const uint32_t kj = key[j];
         const int dig = (int)(kj >> 20);
         const bool up = kj != 0u && (d1 < 0 || dig > d1);
-        // a wave covers 64 consecutive columns = two bitmap words
+        // a wave covers 64 consecutive columns = two bitmap words, from an even word
         const unsigned long long ma = __ballot(up);
         above += __popcll(ma);
-        const int w0 = (threadIdx.x + kCT * j) >> 5;
-        if (lane == 0) sh.bits[w0] = (uint32_t)ma;
-        if (lane == 32) sh.bits[w0] = (uint32_t)(ma >> 32);
+        if (lane == 0) *reinterpret_cast<unsigned long long*>(&sh.bits[(threadIdx.x + kCT * j) >> 5]) = ma;
         cand[j] = d1 >= 0 && kj != 0u && dig == d1;
         const unsigned long long mc = __ballot(cand[j]);
         if (lane == 0) sh.cnt[j * (kCT / 64) + wave] = __popcll(mc);
     }
-    if (lane == 0 && above) atomicAdd(&sh.above, above);
+    if (lane == 0) sh.wab[wave] = above;
     lds_barrier();
     if (wave == 0) {  // exclusive scan over the kPer * kCT / 64 = 64 (step, wave) blocks
         const int x = sh.cnt[lane];
@@ -201,8 +217,11 @@ __global__ __launch_bounds__(kCT) void k_collect(const TopkParams p, LongWs ws) 
     uint32_t* gbits = ws.bitmap + (int64_t)row * nch * kWords + chunk * kWords;
     for (int i = threadIdx.x; i < kWords; i += kCT) gbits[i] = sh.bits[i];
     if (threadIdx.x == 0) {
+        int ab = 0;
+#pragma unroll
+        for (int w = 0; w < kCT / 64; w++) ab += sh.wab[w];
         ws.cnum[(int64_t)row * nch + chunk] = sh.total;
-        ws.cabove[(int64_t)row * nch + chunk] = sh.above;
+        ws.cabove[(int64_t)row * nch + chunk] = ab;
         if (chunk == 0) {
             ws.st[row].d1 = d1;
             ws.st[row].kk = kk;
@@ -277,7 +296,7 @@ __device__ __forceinline__ void cand_pass(FinishShared& sh, CandRegs& r, const L
     for (int i = threadIdx.x; i < kBins; i += kFT) sh.h[i] = 0u;
     lds_barrier();
     for (int round = 0; round < rounds; round++) {
-        if (FLAT) load_flat(r, sh, ws, row, nch, m, round);
+        if (FLAT && rounds > 1) load_flat(r, sh, ws, row, nch, m, round);
 #pragma unroll
         for (int j = 0; j < kCR; j++)
             if (r.col[j] >= 0 && keep(r.key[j], r.col[j])) atomicAdd(&sh.h[digit(r.key[j], r.col[j])], 1u);
@@ -294,16 +313,18 @@ __device__ __forceinline__ void cand_pass(FinishShared& sh, CandRegs& r, const L
 }
 
 // Marks this workgroup's selected candidates in its bitmaps and adds those of earlier
-// chunks to sh.before.  FLAT: the candidates are reloaded round by round (some chunk has
-// more than its up-front slots); otherwise registers [0, 2 * jr) hold them all.
+// chunks to sh.before.  FLAT (some chunk has more candidates than its up-front slots):
+// the candidates are read in row order, once when they fit the registers, else again
+// in every pass, round by round.  Otherwise registers [0, 2 * jr) hold them all.
 template <bool FLAT>
 __device__ __forceinline__ void select_candidates(FinishShared& sh, CandRegs& r, const LongWs& ws, int row, int nch,
                                                   int m, int rounds, int jr, int d1, int kk, int chunk, int nown) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int before = 0;  // this thread's selected candidates of earlier chunks
+    if (FLAT && rounds == 1) load_flat(r, sh, ws, row, nch, m, 0);
     // ---- digit 2 of the candidates: LDS histogram, picked by wave 0
     for (int round = 0; round < rounds; round++) {
-        if (FLAT) load_flat(r, sh, ws, row, nch, m, round);
+        if (FLAT && rounds > 1) load_flat(r, sh, ws, row, nch, m, round);
 #pragma unroll
         for (int j = 0; j < kCR; j++)
             if (j < 2 * jr && r.col[j] >= 0) atomicAdd(&sh.h[(r.key[j] >> 8) & (kBins - 1)], 1u);
@@ -351,7 +372,7 @@ __device__ __forceinline__ void select_candidates(FinishShared& sh, CandRegs& r,
     if (__builtin_expect(kk < n_pre && n_pre <= kRankMax, 0)) {
         // ---- the candidates at the prefix go to LDS and are ranked by comparison
         for (int round = 0; round < rounds; round++) {
-            if (FLAT) load_flat(r, sh, ws, row, nch, m, round);
+            if (FLAT && rounds > 1) load_flat(r, sh, ws, row, nch, m, round);
 #pragma unroll
             for (int j = 0; j < kCR; j++) {
                 if (j < 2 * jr && r.col[j] >= 0 && (r.key[j] >> 8) == preA) {
@@ -409,7 +430,7 @@ __device__ __forceinline__ void select_candidates(FinishShared& sh, CandRegs& r,
     }
     // ---- selected candidates: earlier chunks' are counted, this workgroup's marked
     for (int round = 0; round < rounds; round++) {
-        if (FLAT) load_flat(r, sh, ws, row, nch, m, round);
+        if (FLAT && rounds > 1) load_flat(r, sh, ws, row, nch, m, round);
 #pragma unroll
         for (int j = 0; j < kCR; j++) {
             const uint32_t kx = r.key[j];
@@ -435,7 +456,7 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws, i
     const int ngrp = (nch + gsz - 1) / gsz;
     const int row = blockIdx.x / ngrp, grp = blockIdx.x - row * ngrp;
     if (row >= p.rows) return;
-    const int chunk = grp * gsz, nown = min(gsz, nch - chunk);  // first chunk, chunks owned
+    const int chunk = grp * gsz;  // first chunk
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int k = p.k;
     const int64_t rc = (int64_t)row * nch;
@@ -453,11 +474,14 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws, i
     }
     const int d1 = ws.st[row].d1;
     int kk = ws.st[row].kk;
-    const int my_cnum = threadIdx.x < nch ? ws.cnum[rc + threadIdx.x] : 0;
-    const int my_above = threadIdx.x < nch ? ws.cabove[rc + threadIdx.x] : 0;
+    // everything is loaded for all nch chunks and masked once the row's length is in:
+    // the collect pass wrote nothing for chunks past the row's end (ncr: chunks in use)
+    const int len = row_len(p, row);
+    int my_cnum = threadIdx.x < nch ? ws.cnum[rc + threadIdx.x] : 0;
+    int my_above = threadIdx.x < nch ? ws.cabove[rc + threadIdx.x] : 0;
     static_assert(kGMax * kWords / 4 <= kFT, "one 16-byte bitmap load per thread at most");
     uint4 bw = make_uint4(0u, 0u, 0u, 0u);
-    if (threadIdx.x < nown * (kWords / 4))
+    if (threadIdx.x < min(gsz, nch - chunk) * (kWords / 4))
         bw = reinterpret_cast<const uint4*>(ws.bitmap + (rc + chunk) * kWords)[threadIdx.x];
     uint4 sv[kCR / 2];
 #pragma unroll
@@ -468,6 +492,11 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws, i
                                   : make_uint4(0u, 0xffffffffu, 0u, 0xffffffffu);
     }
     // LDS set-up while the loads are in flight
+    const int ncr = max(1, (len + kChunk - 1) / kChunk);
+    if (chunk >= ncr) return;  // only chunks past the row's end
+    const int nown = min(gsz, ncr - chunk);  // chunks this workgroup writes
+    if (threadIdx.x >= ncr) my_cnum = my_above = 0;
+    if (threadIdx.x >= nown * (kWords / 4)) bw = make_uint4(0u, 0u, 0u, 0u);
     static_assert(kBins == 8 * kFT, "two 16-byte clearing stores per thread");
     reinterpret_cast<uint4*>(sh.h)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
     reinterpret_cast<uint4*>(sh.h)[threadIdx.x + kFT] = make_uint4(0u, 0u, 0u, 0u);
@@ -549,8 +578,8 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws, i
             }
         }
     }
-    // every valid key kept (fewer than k): the last group pads the row
-    if (d1 < 0 && grp == ngrp - 1) {
+    // every valid key kept (fewer than k): the workgroup of the row's last chunk pads it
+    if (d1 < 0 && chunk + nown == ncr) {
         int32_t* oidx = p.out_idx + (int64_t)row * k;
         float* oval = p.out_vals ? p.out_vals + (int64_t)row * k : nullptr;
         for (int i = min(above_total, k) + threadIdx.x; i < k; i += kFT) {
@@ -608,14 +637,20 @@ size_t topk_long_workspace_bytes(int rows, int cols, int k) {
 hipError_t launch_topk_long(const TopkParams& p, void* workspace, hipStream_t stream) {
     LongWs w = carve(workspace, p.rows, p.cols, nullptr);
     if (w.n_chunks > kMaxChunks) return hipErrorInvalidValue;
-    const unsigned grid = (unsigned)(p.rows * w.n_chunks);
-    hipLaunchKernelGGL(k_hist, dim3(grid), dim3(kCT), 0, stream, p, w);
-    hipLaunchKernelGGL(k_collect, dim3(grid), dim3(kCT), 0, stream, p, w);
-    // Few rows: one finishing workgroup per chunk spreads the output; many rows: up to
-    // kGMax chunks per workgroup, so that the redundant reading and ranking of each row's
-    // candidates stays near one pass over the chip.
-    int gsz = 1;
-    while (gsz < kGMax && (int64_t)p.rows * ((w.n_chunks + gsz - 1) / gsz) > 512) gsz *= 2;
+    // Few rows: one workgroup per chunk keeps each one short.  Many rows: the histogram
+    // pass takes up to kHMax chunks per workgroup (fewer global atomics on each row's
+    // histogram) and the finish up to kGMax, so that the redundant reading and ranking
+    // of each row's candidates stays near one pass over the chip.
+    constexpr int kHMax = 4;
+    auto per_group = [&](int most, int limit) {
+        int g = 1;
+        while (g < most && (int64_t)p.rows * ((w.n_chunks + g - 1) / g) > limit) g *= 2;
+        return g;
+    };
+    const int hs = per_group(kHMax, kWaveOfGroups), gsz = per_group(kGMax, kWaveOfGroups / 2);
+    hipLaunchKernelGGL(k_hist, dim3((unsigned)(p.rows * ((w.n_chunks + hs - 1) / hs))), dim3(kCT), 0, stream, p, w,
+                       hs);
+    hipLaunchKernelGGL(k_collect, dim3((unsigned)(p.rows * w.n_chunks)), dim3(kCT), 0, stream, p, w);
     const unsigned fgrid = (unsigned)(p.rows * ((w.n_chunks + gsz - 1) / gsz));
     hipLaunchKernelGGL(k_finish, dim3(fgrid), dim3(kFT), 0, stream, p, w, gsz);
     return hipGetLastError();

@@ -132,6 +132,21 @@ def test_long_rows_k_sizes(k):
     _same(s, k, lens)
 
 
+def test_many_long_rows_of_mixed_lengths():
+    """64 rows of up to 131072 columns with lengths spread like batched decode (several
+    chunks per histogram and finishing workgroup, chunks past a row's end skipped),
+    plus rows of length 0, 1, k and k + 1 and a row of ties."""
+    rng = np.random.default_rng(77)
+    rows, cols, k = 64, 131_072, 2048
+    s = rng.standard_normal((rows, cols)).astype(np.float32)
+    s[5] = (rng.integers(-8, 8, cols) / 2).astype(np.float32)
+    lens = rng.integers(4096, cols + 1, rows).astype(np.int32)
+    lens[:4] = [0, 1, k, k + 1]
+    lens[4] = cols
+    say(f"[gpu] topk many long rows rows={rows} cols={cols} k={k}")
+    _same(s, k, lens)
+
+
 @pytest.mark.parametrize("rows,cols", [(64, 8193), (65, 8193), (64, 8192), (1, 32768), (511, 32768)])
 def test_routing_boundaries(rows, cols):
     """Both sides of the routing between one workgroup per row and the chunked path
