@@ -245,7 +245,8 @@ struct FinishShared {
     int cnum[kMaxChunks];
     int coff[kMaxChunks + 1];          // candidate prefix over chunks (flat mode)
     int wtot[kFT / 64];
-    int part[2][3];                    // waves 0, 1: columns above d1 before this chunk, in the row; candidates
+    int part[2][4];                    // waves 0, 1: columns above d1 before this chunk, in the row;
+                                       // candidates, most candidates of one chunk
     int pick[4];
     int ctot[kGMax];                   // selected columns of each of this workgroup's chunks
     int nm;
@@ -460,7 +461,10 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws, i
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int k = p.k;
     const int64_t rc = (int64_t)row * nch;
-    const int lspec = nch <= 64 ? 6 : 5;  // candidate slots read per chunk up front: 64 or 32
+    // candidate slots read per chunk up front: 2048 / nch rounded down to a power of two,
+    // from 32 (128 chunks fill the registers) to 256 (few chunks cost few loads)
+    int lspec = 5;
+    while (lspec < 8 && (nch << (lspec + 1)) <= 2048) lspec++;
     const int spec = 1 << lspec;
     // slot-pair registers that can hold a candidate up front (the rest stay empty)
     const int jn = min(kCR / 2, (nch * spec / 2 + kFT - 1) / kFT);
@@ -515,14 +519,36 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws, i
             sh.part[wave][1] = at;
         }
         if (lane == 63) sh.part[wave][2] = cs;
+        const int mx = (int)wave_max_u32((uint32_t)my_cnum);
+        if (lane == 0) sh.part[wave][3] = mx;
     }
     if (threadIdx.x < nch) sh.cnum[threadIdx.x] = my_cnum;
     if (threadIdx.x < kGMax * kWords / 4) reinterpret_cast<uint4*>(sh.bits)[threadIdx.x] = bw;
-    const bool flat = __syncthreads_or(my_cnum > spec) != 0;
+    bool flat = __syncthreads_or(my_cnum > spec) != 0;
     const int above_before = sh.part[0][0] + sh.part[1][0];
     const int above_total = sh.part[0][1] + sh.part[1][1];
     const int m = sh.part[0][2] + sh.part[1][2];  // candidates of the row
     int rounds = 1;                               // reload rounds
+    int ls = lspec, jr = jn;                      // slots a chunk (log2), pair registers in use
+    if (flat) {
+        // some chunk has more candidates than its up-front slots: when wider slots still
+        // fit every chunk in the registers, one more round of loads reads them that way
+        const int cmax = max(sh.part[0][3], sh.part[1][3]);
+        int lw = lspec + 1;
+        while ((1 << lw) < cmax) lw++;
+        if ((nch << lw) <= kFT * kCR) {
+            ls = lw;
+            jr = min(kCR / 2, ((nch << lw) / 2 + kFT - 1) / kFT);
+#pragma unroll
+            for (int j = 0; j < kCR / 2; j++) {
+                const int q = threadIdx.x + kFT * j;
+                const int c = (2 * q) >> ls, slot = (2 * q) & ((1 << ls) - 1);
+                sv[j] = j < jr && c < nch ? *reinterpret_cast<const uint4*>(ws.cand + (rc + c) * kChunk + slot)
+                                          : make_uint4(0u, 0xffffffffu, 0u, 0xffffffffu);
+            }
+            flat = false;
+        }
+    }
     CandRegs r;
     if (flat) {
         // chunk-order prefix of the candidate counts for the flat reloads
@@ -534,7 +560,7 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws, i
 #pragma unroll
         for (int j = 0; j < kCR / 2; j++) {
             const int q = threadIdx.x + kFT * j;
-            const int c = (2 * q) >> lspec, slot = (2 * q) & (spec - 1);
+            const int c = (2 * q) >> ls, slot = (2 * q) & ((1 << ls) - 1);
             const int cn = c < nch ? sh.cnum[c] : 0;
             r.key[2 * j] = sv[j].x;
             r.col[2 * j] = slot < cn ? (int)sv[j].y : -1;
@@ -545,7 +571,7 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws, i
 
     if (d1 >= 0) {
         if (__builtin_expect(flat, 0)) select_candidates<true>(sh, r, ws, row, nch, m, rounds, kCR / 2, d1, kk, chunk, nown);
-        else select_candidates<false>(sh, r, ws, row, nch, m, 1, jn, d1, kk, chunk, nown);
+        else select_candidates<false>(sh, r, ws, row, nch, m, 1, jr, d1, kk, chunk, nown);
     }
 
     // ---- the chunks' columns in order: wave w writes chunk chunk + w, lane l its

@@ -132,6 +132,21 @@ def test_long_rows_k_sizes(k):
     _same(s, k, lens)
 
 
+@pytest.mark.parametrize("extra", [80, 1500])
+def test_long_rows_one_chunk_overflowing_its_slots(extra):
+    """One 4096-column chunk holds `extra` more keys of the threshold's digit bin than the
+    rest: 80 overflow its up-front candidate slots but fit wider ones, 1500 need the
+    round-by-round reads."""
+    rng = np.random.default_rng(90 + extra)
+    rows, cols, k = 3, 100_000, 2048
+    s = rng.standard_normal((rows, cols)).astype(np.float32)
+    for r in range(rows):
+        t = np.sort(s[r])[-k]
+        s[r, 5 * 4096:5 * 4096 + extra] = (t * (1 + 1e-4 * rng.standard_normal(extra))).astype(np.float32)
+    say(f"[gpu] topk overflowing chunk extra={extra}")
+    _same(s, k)
+
+
 def test_many_long_rows_of_mixed_lengths():
     """64 rows of up to 131072 columns with lengths spread like batched decode (several
     chunks per histogram and finishing workgroup, chunks past a row's end skipped),
