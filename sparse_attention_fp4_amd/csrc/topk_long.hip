@@ -7,28 +7,29 @@
 // Same order and output as topk.hip (larger first, ties to the smaller column, -inf
 // and NaN never selected, result in increasing column order, -1 padded).  Scores map
 // to order-preserving 32-bit keys; digit 1 is key bits [31:20], digit 2 bits [19:8].
-// A row is cut into chunks of 4096 columns.  Workgroups exchange data only across
-// kernel boundaries (a device-wide fence inside a kernel costs microseconds on this
-// multi-die part):
-//   1. hist:    each chunk builds the histogram of digit 1 of its keys in LDS and adds
-//               its nonzero bins to the row's histogram (global atomics).
+// A row is cut into chunks of 4096 columns; chunks past a row's end are skipped.
+// Workgroups exchange data only across kernel boundaries (a device-wide fence inside a
+// kernel costs microseconds on this multi-die part):
+//   1. hist:    each chunk (a few consecutive chunks when many rows fill the chip)
+//               builds the histogram of digit 1 of its keys in LDS and adds its
+//               nonzero bins to the row's histogram (global atomics).
 //   2. collect: each chunk reads the row's histogram, finds the bin d1 holding the
 //               row's k-th largest key, and stores a bitmap of its columns above d1
 //               (all selected) with their count, and its keys in d1 (the candidates,
 //               with their columns and count).
 //   3. finish:  one workgroup per group of up to 8 consecutive chunks (one chunk each
 //               when there are few rows).  Each reads the row's candidates (every
-//               chunk's first slots in one round of loads; a chunk with more sends the
-//               workgroups through a slower path that reloads them), the counts and its
-//               chunks' bitmaps, finds the digit-2 bin d2 holding the k-th key from an
-//               LDS histogram of the candidates, ranks the candidates with prefix (d1,
-//               d2) by direct comparison when not all of them are kept (digit passes
-//               handle more than 1024 of them), and counts the selected columns of the earlier chunks: that count
-//               is where its own chunks' columns go in the output, written in order from
-//               popcount scans of their bitmaps.  The first group's workgroup clears the
-//               row's histogram for the next call.
+//               chunk's first slots in one round of loads; a chunk with more is read
+//               again with wider slots, or round by round), the counts and its chunks'
+//               bitmaps, finds the digit-2 bin d2 holding the k-th key from an LDS
+//               histogram of the candidates, ranks the candidates with prefix (d1, d2)
+//               by direct comparison when not all of them are kept (digit passes
+//               handle more than 1024 of them), and counts the selected columns of the
+//               earlier chunks: that count is where its own chunks' columns go in the
+//               output, written in order from popcount scans of their bitmaps.  The
+//               first group's workgroup clears the row's histogram for the next call.
 // The workspace must be zero-filled before its first use; every call leaves the
-// histograms zero-filled again.
+// histogram zero-filled again.
 #include "device_common.hpp"
 #include "fp4idx_internal.hpp"
 
@@ -323,7 +324,7 @@ __device__ __forceinline__ void select_candidates(FinishShared& sh, CandRegs& r,
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int before = 0;  // this thread's selected candidates of earlier chunks
     if (FLAT && rounds == 1) load_flat(r, sh, ws, row, nch, m, 0);
-    // ---- digit 2 of the candidates: LDS histogram, picked by wave 0
+    // ---- digit 2 of the candidates: LDS histogram and its pick
     for (int round = 0; round < rounds; round++) {
         if (FLAT && rounds > 1) load_flat(r, sh, ws, row, nch, m, round);
 #pragma unroll
@@ -331,35 +332,32 @@ __device__ __forceinline__ void select_candidates(FinishShared& sh, CandRegs& r,
             if (j < 2 * jr && r.col[j] >= 0) atomicAdd(&sh.h[(r.key[j] >> 8) & (kBins - 1)], 1u);
     }
     lds_barrier();
-    if (wave == 0) {
-        // lane l owns bins 4095-64l .. 4032-64l, walked from the top; the lane whose
-        // range holds the kk-th key then has its 64 bins scanned by the whole wave
-        static_assert(kBins == 64 * 64, "64 bins per lane");
-        const uint4* h4 = reinterpret_cast<const uint4*>(sh.h) + (kBins - 64 - 64 * lane) / 4;
+    {
+        // thread t owns bins 4095-8t .. 4088-8t (two 16-byte reads), walked from the top:
+        // wave totals first, then the thread whose bins hold the kk-th key finds its bin
+        static_assert(kBins == 8 * kFT, "8 bins per thread");
+        const uint4* h4 = reinterpret_cast<const uint4*>(sh.h + (kBins - 8 - 8 * threadIdx.x));
+        const uint4 lo = h4[0], hi = h4[1];
+        const int c[8] = {(int)hi.w, (int)hi.z, (int)hi.y, (int)hi.x, (int)lo.w, (int)lo.z, (int)lo.y, (int)lo.x};
         int s = 0;
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const uint4 v = h4[i];
-            s += (int)(v.x + v.y + v.z + v.w);
-        }
+        for (int b = 0; b < 8; b++) s += c[b];
         const int incl = wave_incl_scan(s);
-        const unsigned long long own = __ballot(incl - s < kk && kk <= incl);
-        int pk0 = 0, pk1 = 0, pk3 = 0;
-        if (own) {
-            const int L = __ffsll((long long)own) - 1;
-            const int ex = __builtin_amdgcn_readlane(incl - s, L);
-            const int c = (int)sh.h[kBins - 1 - 64 * L - lane];
-            const int incl2 = wave_incl_scan(c);
-            const unsigned long long at = __ballot(ex + incl2 >= kk);
-            const int J = at ? __ffsll((long long)at) - 1 : 63;
-            pk0 = kBins - 1 - 64 * L - J;
-            pk1 = ex + __builtin_amdgcn_readlane(incl2 - c, J);
-            pk3 = __builtin_amdgcn_readlane(c, J);
-        }
-        if (lane == 0) {
-            sh.pick[0] = pk0;
-            sh.pick[1] = pk1;
-            sh.pick[3] = pk3;
+        if (lane == 63) sh.wtot[wave] = incl;
+        lds_barrier();
+        int ex = incl - s;  // keys in the bins above this thread's
+        for (int w = 0; w < wave; w++) ex += sh.wtot[w];
+        if (ex < kk && kk <= ex + s) {
+#pragma unroll
+            for (int b = 0; b < 8; b++) {
+                if (ex + c[b] >= kk) {
+                    sh.pick[0] = kBins - 1 - 8 * threadIdx.x - b;
+                    sh.pick[1] = ex;
+                    sh.pick[3] = c[b];
+                    break;
+                }
+                ex += c[b];
+            }
         }
     }
     lds_barrier();
