@@ -51,6 +51,7 @@ constexpr int waves_per_block(int rows_per_block) {
     return rows_per_block == 1 ? kWavesOneRow : kWavesMultiRow;
 }
 constexpr int kTargetWaves = 16384;    // waves of one launch (8192 .. 65536 measured)
+constexpr int kTargetWavesOneRequest = 1600;  // with a single request (see plan_logits)
 constexpr int kPipe = 2;               // products in flight in the epilogue pipeline
 constexpr int kMaxTiles = 16;          // A tiles per block at most (8 or 16)
 constexpr int kMaxPagesPerWave = 128;  // pages per wave at most (a multiple of 64)
@@ -761,10 +762,14 @@ bool plan_logits(LogitsParams& p) {
     const int n_pages_out = (p.out_cols + p.page - 1) / p.page;
     // pages per wave: about kTargetWaves waves, at most kMaxPagesPerWave
     // pages each.  Long waves spread the per-workgroup set-up (operand staging, the
-    // first key loads) over more work; enough of them keep every SIMD busy.  Pages past
-    // every row's end only get -inf, from a loop that reads no keys.
+    // first key loads) over more work; enough of them keep every SIMD busy.  A single
+    // request's rows (decode verify rows) have few pages and are latency-bound: about
+    // one round of waves does best there (4 rows x 400k keys: 12.4 us with 4 pages a
+    // wave, 15.0 with 1, 13.7 with 8; 100k keys: 1 page a wave).  Pages past every
+    // row's end only get -inf, from a loop that reads no keys.
     const int64_t total = (int64_t)p.n_rowblocks * n_pages_out;
-    int64_t ppw = (total + kTargetWaves - 1) / kTargetWaves;
+    const int64_t target = p.B == 1 ? kTargetWavesOneRequest : kTargetWaves;
+    int64_t ppw = (total + target - 1) / target;
     ppw = ppw < 1 ? 1 : (ppw > kMaxPagesPerWave ? kMaxPagesPerWave : ppw);
     p.ppw = (int)ppw;
     p.n_wchunks = (n_pages_out + p.ppw - 1) / p.ppw;
