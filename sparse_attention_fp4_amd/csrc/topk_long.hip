@@ -38,14 +38,14 @@ namespace fp4idx {
 namespace {
 
 constexpr int kChunk = 4096;          // columns per chunk workgroup
-constexpr int kCT = 512;            // threads of a chunk workgroup: 8 keys per thread
-                                    // (its waves run one per SIMD)
-constexpr int kPer = kChunk / kCT;    // elements per thread
-static_assert(kPer * (kCT / 64) == 64, "the collect scan covers 64 (step, wave) blocks");
+// Threads of a histogram or collect workgroup (CT below): 1024 (4 keys a thread) when
+// few rows leave most of the chip idle, so each chunk's per-key loops are short
+// (4 rows x 100k: top-k 14.6 -> 14.0 us); 512 (8 keys a thread) when many rows fill
+// it (64 rows: 27.8 against 32.7 us with 1024).
+constexpr int kCTFew = 1024, kCTMany = 512;
 constexpr int kBins = 4096;
 constexpr int kWords = kChunk / 32;   // bitmap words per chunk
 constexpr int kMaxChunks = 128;    // rows of up to 524288 columns
-constexpr int kMaxK = 8192;
 constexpr int kWaveOfGroups = 512;  // workgroups that keep the chip busy (two a CU)
 
 struct RowState {
@@ -81,15 +81,17 @@ __device__ __forceinline__ int row_len(const TopkParams& p, int row) {
     return len;
 }
 
-// Thread t holds elements t + kCT * j of the chunk (index order = j, wave, lane);
+// Thread t of CT holds elements t + CT * j of the chunk (index order = j, wave, lane);
 // columns at or past len read as -inf.
-__device__ __forceinline__ void load_chunk_raw(const TopkParams& p, int row, int len, int chunk, float (&v)[kPer]) {
+template <int CT>
+__device__ __forceinline__ void load_chunk_raw(const TopkParams& p, int row, int len, int chunk,
+                                               float (&v)[kChunk / CT]) {
     const int c0 = chunk * kChunk;
     const int n = max(0, min(len - c0, kChunk));
     const float* src = p.scores + (int64_t)row * p.row_stride + c0;
 #pragma unroll
-    for (int j = 0; j < kPer; j++) {
-        const int i = threadIdx.x + kCT * j;
+    for (int j = 0; j < kChunk / CT; j++) {
+        const int i = threadIdx.x + CT * j;
         v[j] = i < n ? src[i] : -__builtin_inff();
     }
 }
@@ -97,7 +99,9 @@ __device__ __forceinline__ void load_chunk_raw(const TopkParams& p, int row, int
 // ---------------------------------------------------------------- 1. hist
 // hs: chunks per workgroup (chunks [hg * hs, +hs) of the row, one LDS histogram and one
 // flush for all of them); chunks past the row's end are skipped.
-__global__ __launch_bounds__(kCT) void k_hist(const TopkParams p, LongWs ws, int hs) {
+template <int CT>
+__global__ __launch_bounds__(CT) void k_hist(const TopkParams p, LongWs ws, int hs) {
+    constexpr int kP = kChunk / CT;
     __shared__ uint32_t h[kBins];
     const int nhg = (ws.n_chunks + hs - 1) / hs;
     const int row = blockIdx.x / nhg, hg = blockIdx.x - row * nhg;
@@ -105,50 +109,64 @@ __global__ __launch_bounds__(kCT) void k_hist(const TopkParams p, LongWs ws, int
     const int len = row_len(p, row);
     const int c_begin = hg * hs, c_end = min(min(c_begin + hs, ws.n_chunks), (len + kChunk - 1) / kChunk);
     if (c_begin >= c_end) return;  // past the row's end
-    for (int i = threadIdx.x; i < kBins; i += kCT) h[i] = 0u;
-    float v[kPer];
-    load_chunk_raw(p, row, len, c_begin, v);
+    for (int i = threadIdx.x; i < kBins; i += CT) h[i] = 0u;
+    float v[kP];
+    load_chunk_raw<CT>(p, row, len, c_begin, v);
     lds_barrier();
     for (int c = c_begin; c < c_end; c++) {
-        uint32_t key[kPer];
+        uint32_t key[kP];
 #pragma unroll
-        for (int j = 0; j < kPer; j++) key[j] = to_key(v[j]);
-        if (c + 1 < c_end) load_chunk_raw(p, row, len, c + 1, v);  // in flight with the atomics
+        for (int j = 0; j < kP; j++) key[j] = to_key(v[j]);
+        if (c + 1 < c_end) load_chunk_raw<CT>(p, row, len, c + 1, v);  // in flight with the atomics
 #pragma unroll
-        for (int j = 0; j < kPer; j++)
+        for (int j = 0; j < kP; j++)
             if (key[j]) atomicAdd(&h[key[j] >> 20], 1u);
     }
     lds_barrier();
     uint32_t* gh = ws.hist + (int64_t)row * kBins;
-    for (int i = threadIdx.x; i < kBins; i += kCT)
+    for (int i = threadIdx.x; i < kBins; i += CT)
         if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
 // ---------------------------------------------------------------- 2. collect
+template <int CT>
 struct CollectShared {
-    int wtot[kCT / 64];
+    static_assert((kChunk / CT) * (CT / 64) == 64, "the collect scan covers 64 (step, wave) blocks");
+    int wtot[CT / 64];
     int pick[4];
     int total;
-    int wab[kCT / 64];                 // columns above d1 of each wave
+    int wab[CT / 64];                  // columns above d1 of each wave
     alignas(8) uint32_t bits[kWords];
-    int cnt[kPer * (kCT / 64)];
-    int off[kPer * (kCT / 64)];
+    int cnt[64];
+    int off[64];
 };
 
-// The bin of the row's k-th largest key from the row's histogram (a, b: this thread's
-// two 16-byte loads of it, bins 4095-8t .. 4088-8t).  Returns d1 (-1 when every valid key
-// is kept) and kk, the keys wanted in d1.
-__device__ __forceinline__ void row_threshold_bin(CollectShared& sh, const TopkParams& p, const uint4 a,
-                                                  const uint4 b, int& d1, int& kk) {
-    constexpr int per = kBins / kCT;
-    static_assert(per == 8, "two 16-byte loads per thread cover its bins");
+// This thread's bins of the row's histogram, 4095 - (kBins / CT) t down, as 16-byte loads.
+template <int CT>
+__device__ __forceinline__ void load_hist_bins(const LongWs& ws, int row, uint4 (&hv)[kBins / CT / 4]) {
+    const uint4* gh4 = reinterpret_cast<const uint4*>(ws.hist + (int64_t)row * kBins);
+#pragma unroll
+    for (int i = 0; i < kBins / CT / 4; i++) hv[i] = gh4[kBins / 4 - 1 - (kBins / CT / 4) * threadIdx.x - i];
+}
+
+// The bin of the row's k-th largest key from the row's histogram (hv: this thread's
+// bins).  Returns d1 (-1 when every valid key is kept) and kk, the keys wanted in d1.
+template <int CT>
+__device__ __forceinline__ void row_threshold_bin(CollectShared<CT>& sh, const TopkParams& p,
+                                                  const uint4 (&hv)[kBins / CT / 4], int& d1, int& kk) {
+    constexpr int per = kBins / CT;
     int c[per], bin[per];
     // walked from the top ("before" = larger keys)
-    c[0] = (int)a.w; c[1] = (int)a.z; c[2] = (int)a.y; c[3] = (int)a.x;
-    c[4] = (int)b.w; c[5] = (int)b.z; c[6] = (int)b.y; c[7] = (int)b.x;
+#pragma unroll
+    for (int i = 0; i < per / 4; i++) {
+        c[4 * i] = (int)hv[i].w;
+        c[4 * i + 1] = (int)hv[i].z;
+        c[4 * i + 2] = (int)hv[i].y;
+        c[4 * i + 3] = (int)hv[i].x;
+    }
 #pragma unroll
     for (int i = 0; i < per; i++) bin[i] = kBins - 1 - (threadIdx.x * per + i);
-    pick_bin<kCT, per>(c, bin, p.k, sh.wtot, sh.pick);
+    pick_bin<CT, per>(c, bin, p.k, sh.wtot, sh.pick);
     if (sh.pick[2] <= p.k) {
         d1 = -1;
         kk = 0;
@@ -158,47 +176,49 @@ __device__ __forceinline__ void row_threshold_bin(CollectShared& sh, const TopkP
     }
 }
 
-__global__ __launch_bounds__(kCT) void k_collect(const TopkParams p, LongWs ws) {
-    __shared__ CollectShared sh;
+template <int CT>
+__global__ __launch_bounds__(CT) void k_collect(const TopkParams p, LongWs ws) {
+    constexpr int kP = kChunk / CT;
+    __shared__ CollectShared<CT> sh;
     const int nch = ws.n_chunks;
     const int row = blockIdx.x / nch, chunk = blockIdx.x - row * nch;
     if (row >= p.rows) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     // the row's histogram first (it does not wait for the row's length), then the chunk
-    const uint4* gh4 = reinterpret_cast<const uint4*>(ws.hist + (int64_t)row * kBins);
-    const uint4 ha = gh4[kBins / 4 - 1 - 2 * threadIdx.x], hb = gh4[kBins / 4 - 2 - 2 * threadIdx.x];
+    uint4 hv[kBins / CT / 4];
+    load_hist_bins<CT>(ws, row, hv);
     const int len = row_len(p, row);
     const int c0 = chunk * kChunk;
-    float v[kPer];
-    load_chunk_raw(p, row, len, chunk, v);
+    float v[kP];
+    load_chunk_raw<CT>(p, row, len, chunk, v);
     // a chunk past the row's end stores nothing (the finish never reads it); the first
     // chunk always runs, since it stores the row's state
     if (chunk > 0 && c0 >= len) return;
-    uint32_t key[kPer];
+    uint32_t key[kP];
 #pragma unroll
-    for (int j = 0; j < kPer; j++) key[j] = to_key(v[j]);
+    for (int j = 0; j < kP; j++) key[j] = to_key(v[j]);
     int d1, kk;
-    row_threshold_bin(sh, p, ha, hb, d1, kk);  // ends with a barrier
+    row_threshold_bin<CT>(sh, p, hv, d1, kk);  // ends with a barrier
 
     // ---- bitmap of the columns above bin d1 and its count; candidates of bin d1
-    bool cand[kPer];
+    bool cand[kP];
     int above = 0;  // this wave's columns above d1 (uniform)
 #pragma unroll
-    for (int j = 0; j < kPer; j++) {
+    for (int j = 0; j < kP; j++) {
         const uint32_t kj = key[j];
         const int dig = (int)(kj >> 20);
         const bool up = kj != 0u && (d1 < 0 || dig > d1);
         // a wave covers 64 consecutive columns = two bitmap words, from an even word
         const unsigned long long ma = __ballot(up);
         above += __popcll(ma);
-        if (lane == 0) *reinterpret_cast<unsigned long long*>(&sh.bits[(threadIdx.x + kCT * j) >> 5]) = ma;
+        if (lane == 0) *reinterpret_cast<unsigned long long*>(&sh.bits[(threadIdx.x + CT * j) >> 5]) = ma;
         cand[j] = d1 >= 0 && kj != 0u && dig == d1;
         const unsigned long long mc = __ballot(cand[j]);
-        if (lane == 0) sh.cnt[j * (kCT / 64) + wave] = __popcll(mc);
+        if (lane == 0) sh.cnt[j * (CT / 64) + wave] = __popcll(mc);
     }
     if (lane == 0) sh.wab[wave] = above;
     lds_barrier();
-    if (wave == 0) {  // exclusive scan over the kPer * kCT / 64 = 64 (step, wave) blocks
+    if (wave == 0) {  // exclusive scan over the 64 (step, wave) blocks
         const int x = sh.cnt[lane];
         const int s = wave_incl_scan(x);
         sh.off[lane] = s - x;
@@ -208,19 +228,19 @@ __global__ __launch_bounds__(kCT) void k_collect(const TopkParams p, LongWs ws) 
     // Global writes come last: a barrier after them would wait for their completion.
     uint2* dst = ws.cand + ((int64_t)row * nch + chunk) * kChunk;
 #pragma unroll
-    for (int j = 0; j < kPer; j++) {
+    for (int j = 0; j < kP; j++) {
         const unsigned long long mc = __ballot(cand[j]);
         if (cand[j]) {
-            const int pos = sh.off[j * (kCT / 64) + wave] + lanes_below(mc);
-            dst[pos] = make_uint2(key[j], (uint32_t)(c0 + threadIdx.x + kCT * j));
+            const int pos = sh.off[j * (CT / 64) + wave] + lanes_below(mc);
+            dst[pos] = make_uint2(key[j], (uint32_t)(c0 + threadIdx.x + CT * j));
         }
     }
     uint32_t* gbits = ws.bitmap + (int64_t)row * nch * kWords + chunk * kWords;
-    for (int i = threadIdx.x; i < kWords; i += kCT) gbits[i] = sh.bits[i];
+    for (int i = threadIdx.x; i < kWords; i += CT) gbits[i] = sh.bits[i];
     if (threadIdx.x == 0) {
         int ab = 0;
 #pragma unroll
-        for (int w = 0; w < kCT / 64; w++) ab += sh.wab[w];
+        for (int w = 0; w < CT / 64; w++) ab += sh.wab[w];
         ws.cnum[(int64_t)row * nch + chunk] = sh.total;
         ws.cabove[(int64_t)row * nch + chunk] = ab;
         if (chunk == 0) {
@@ -674,9 +694,14 @@ hipError_t launch_topk_long(const TopkParams& p, void* workspace, hipStream_t st
         return g;
     };
     const int hs = per_group(kHMax, 2 * kWaveOfGroups), gsz = per_group(kGMax, kWaveOfGroups / 2);
-    hipLaunchKernelGGL(k_hist, dim3((unsigned)(p.rows * ((w.n_chunks + hs - 1) / hs))), dim3(kCT), 0, stream, p, w,
-                       hs);
-    hipLaunchKernelGGL(k_collect, dim3((unsigned)(p.rows * w.n_chunks)), dim3(kCT), 0, stream, p, w);
+    const unsigned hgrid = (unsigned)(p.rows * ((w.n_chunks + hs - 1) / hs)), cgrid = (unsigned)(p.rows * w.n_chunks);
+    if ((int64_t)p.rows * w.n_chunks <= kWaveOfGroups) {
+        hipLaunchKernelGGL(k_hist<kCTFew>, dim3(hgrid), dim3(kCTFew), 0, stream, p, w, hs);
+        hipLaunchKernelGGL(k_collect<kCTFew>, dim3(cgrid), dim3(kCTFew), 0, stream, p, w);
+    } else {
+        hipLaunchKernelGGL(k_hist<kCTMany>, dim3(hgrid), dim3(kCTMany), 0, stream, p, w, hs);
+        hipLaunchKernelGGL(k_collect<kCTMany>, dim3(cgrid), dim3(kCTMany), 0, stream, p, w);
+    }
     const unsigned fgrid = (unsigned)(p.rows * ((w.n_chunks + gsz - 1) / gsz));
     hipLaunchKernelGGL(k_finish, dim3(fgrid), dim3(kFT), 0, stream, p, w, gsz);
     return hipGetLastError();
