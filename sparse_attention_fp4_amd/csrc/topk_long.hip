@@ -251,21 +251,23 @@ __global__ __launch_bounds__(CT) void k_collect(const TopkParams p, LongWs ws) {
 }
 
 // ---------------------------------------------------------------- 3. finish
-constexpr int kFT = 512;        // threads of a finishing workgroup
-constexpr int kGMax = kFT / 64;  // chunks per finishing workgroup: one wave writes each
-constexpr int kCR = 8;          // candidates per thread per round
+// FT: threads of a finishing workgroup (kCTFew or kCTMany, as for the other passes).
+// Its candidate registers hold kSlots candidates, FT / 64 chunks' columns at most
+// (one wave writes each).
+constexpr int kSlots = 4096;
 constexpr int kRankMax = 1024;  // candidates at the threshold prefix ranked by comparison
-static_assert(kMaxChunks * 32 == kFT * kCR && kCR % 2 == 0,
-              "up-front loads fill the candidate registers in slot pairs, 32 slots a chunk or more");
+static_assert(kMaxChunks * 32 == kSlots, "32 up-front candidate slots a chunk or more");
 
+template <int FT>
 struct FinishShared {
+    static constexpr int kGMax = FT / 64;
     alignas(16) uint32_t h[kBins];     // digit-2 histogram, then the narrowing passes'
     alignas(16) uint32_t bits[kGMax * kWords];  // this workgroup's chunks' bitmaps
     uint32_t mkey[kRankMax];           // candidates with the threshold prefix (d1, d2)
     int mcol[kRankMax];
     int cnum[kMaxChunks];
     int coff[kMaxChunks + 1];          // candidate prefix over chunks (flat mode)
-    int wtot[kFT / 64];
+    int wtot[FT / 64];
     int part[2][4];                    // waves 0, 1: columns above d1 before this chunk, in the row;
                                        // candidates, most candidates of one chunk
     int pick[4];
@@ -274,18 +276,22 @@ struct FinishShared {
     int before;                        // selected candidates of earlier chunks
 };
 
-// Candidate registers: kCR per thread.  In the common case they hold every candidate
-// of the row (registers 2j and 2j+1 hold slots 2q % spec and 2q % spec + 1 of chunk
-// 2q / spec, q = threadIdx.x + kFT * j);
-// otherwise ("flat" mode) they hold candidates [round * kFT * kCR, +kFT * kCR) of the
-// row in chunk order, reloaded round by round.
+// Candidate registers: kSlots / FT per thread.  In the common case they hold every
+// candidate of the row (registers 2j and 2j+1 hold slots 2q % spec and 2q % spec + 1 of
+// chunk 2q / spec, q = threadIdx.x + FT * j); otherwise ("flat" mode) they hold
+// candidates [round * kSlots, +kSlots) of the row in chunk order, reloaded round by
+// round.
+template <int FT>
 struct CandRegs {
+    static constexpr int kCR = kSlots / FT;
+    static_assert(kCR % 2 == 0, "up-front loads fill the registers in slot pairs");
     uint32_t key[kCR];
     int col[kCR];  // -1: no candidate
 };
 
 // Candidate i of the row (flat order) lives in chunk c with coff[c] <= i < coff[c+1].
-__device__ __forceinline__ int64_t cand_slot(const FinishShared& sh, int row, int nch, int i) {
+template <int FT>
+__device__ __forceinline__ int64_t cand_slot(const FinishShared<FT>& sh, int row, int nch, int i) {
     int lo = 0, hi = nch;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -295,12 +301,14 @@ __device__ __forceinline__ int64_t cand_slot(const FinishShared& sh, int row, in
     return ((int64_t)row * nch + lo) * kChunk + (i - sh.coff[lo]);
 }
 
-__device__ __forceinline__ void load_flat(CandRegs& r, const FinishShared& sh, const LongWs& ws, int row,
+template <int FT>
+__device__ __forceinline__ void load_flat(CandRegs<FT>& r, const FinishShared<FT>& sh, const LongWs& ws, int row,
                                           int nch, int m, int round) {
+    constexpr int kCR = CandRegs<FT>::kCR;
     uint2 v[kCR];
 #pragma unroll
     for (int j = 0; j < kCR; j++) {
-        const int i = round * kFT * kCR + threadIdx.x + kFT * j;
+        const int i = round * kSlots + threadIdx.x + FT * j;
         v[j] = i < m ? ws.cand[cand_slot(sh, row, nch, i)] : make_uint2(0u, 0xffffffffu);
     }
 #pragma unroll
@@ -312,10 +320,11 @@ __device__ __forceinline__ void load_flat(CandRegs& r, const FinishShared& sh, c
 
 // One digit pass over the candidates that pass `keep`: histogram of digit(key, col)
 // and the bin holding the kk-th element in the given order.
-template <bool FLAT, typename Keep, typename Digit>
-__device__ __forceinline__ void cand_pass(FinishShared& sh, CandRegs& r, const LongWs& ws, int row, int nch,
+template <int FT, bool FLAT, typename Keep, typename Digit>
+__device__ __forceinline__ void cand_pass(FinishShared<FT>& sh, CandRegs<FT>& r, const LongWs& ws, int row, int nch,
                                           int m, int rounds, int kk, bool descending, Keep keep, Digit digit) {
-    for (int i = threadIdx.x; i < kBins; i += kFT) sh.h[i] = 0u;
+    constexpr int kCR = CandRegs<FT>::kCR;
+    for (int i = threadIdx.x; i < kBins; i += FT) sh.h[i] = 0u;
     lds_barrier();
     for (int round = 0; round < rounds; round++) {
         if (FLAT && rounds > 1) load_flat(r, sh, ws, row, nch, m, round);
@@ -324,23 +333,25 @@ __device__ __forceinline__ void cand_pass(FinishShared& sh, CandRegs& r, const L
             if (r.col[j] >= 0 && keep(r.key[j], r.col[j])) atomicAdd(&sh.h[digit(r.key[j], r.col[j])], 1u);
     }
     lds_barrier();
-    constexpr int per = kBins / kFT;
+    constexpr int per = kBins / FT;
     int c[per], bin[per];
 #pragma unroll
     for (int b = 0; b < per; b++) {
         bin[b] = descending ? kBins - 1 - (threadIdx.x * per + b) : threadIdx.x * per + b;
         c[b] = (int)sh.h[bin[b]];
     }
-    pick_bin<kFT, per>(c, bin, kk, sh.wtot, sh.pick);
+    pick_bin<FT, per>(c, bin, kk, sh.wtot, sh.pick);
 }
 
 // Marks this workgroup's selected candidates in its bitmaps and adds those of earlier
 // chunks to sh.before.  FLAT (some chunk has more candidates than its up-front slots):
 // the candidates are read in row order, once when they fit the registers, else again
 // in every pass, round by round.  Otherwise registers [0, 2 * jr) hold them all.
-template <bool FLAT>
-__device__ __forceinline__ void select_candidates(FinishShared& sh, CandRegs& r, const LongWs& ws, int row, int nch,
-                                                  int m, int rounds, int jr, int d1, int kk, int chunk, int nown) {
+template <int FT, bool FLAT>
+__device__ __forceinline__ void select_candidates(FinishShared<FT>& sh, CandRegs<FT>& r, const LongWs& ws, int row,
+                                                  int nch, int m, int rounds, int jr, int d1, int kk, int chunk,
+                                                  int nown) {
+    constexpr int kCR = CandRegs<FT>::kCR;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int before = 0;  // this thread's selected candidates of earlier chunks
     if (FLAT && rounds == 1) load_flat(r, sh, ws, row, nch, m, 0);
@@ -353,15 +364,24 @@ __device__ __forceinline__ void select_candidates(FinishShared& sh, CandRegs& r,
     }
     lds_barrier();
     {
-        // thread t owns bins 4095-8t .. 4088-8t (two 16-byte reads), walked from the top:
-        // wave totals first, then the thread whose bins hold the kk-th key finds its bin
-        static_assert(kBins == 8 * kFT, "8 bins per thread");
-        const uint4* h4 = reinterpret_cast<const uint4*>(sh.h + (kBins - 8 - 8 * threadIdx.x));
-        const uint4 lo = h4[0], hi = h4[1];
-        const int c[8] = {(int)hi.w, (int)hi.z, (int)hi.y, (int)hi.x, (int)lo.w, (int)lo.z, (int)lo.y, (int)lo.x};
+        // thread t owns PB = kBins / FT bins, 4095 - PB t down (16-byte reads), walked from
+        // the top: wave totals first, then the thread whose bins hold the kk-th key finds
+        // its bin
+        constexpr int PB = kBins / FT;
+        static_assert(PB % 4 == 0, "whole 16-byte reads");
+        const uint4* h4 = reinterpret_cast<const uint4*>(sh.h + (kBins - PB - PB * threadIdx.x));
+        int c[PB];
+#pragma unroll
+        for (int i = 0; i < PB / 4; i++) {
+            const uint4 v = h4[PB / 4 - 1 - i];
+            c[4 * i] = (int)v.w;
+            c[4 * i + 1] = (int)v.z;
+            c[4 * i + 2] = (int)v.y;
+            c[4 * i + 3] = (int)v.x;
+        }
         int s = 0;
 #pragma unroll
-        for (int b = 0; b < 8; b++) s += c[b];
+        for (int b = 0; b < PB; b++) s += c[b];
         const int incl = wave_incl_scan(s);
         if (lane == 63) sh.wtot[wave] = incl;
         lds_barrier();
@@ -369,9 +389,9 @@ __device__ __forceinline__ void select_candidates(FinishShared& sh, CandRegs& r,
         for (int w = 0; w < wave; w++) ex += sh.wtot[w];
         if (ex < kk && kk <= ex + s) {
 #pragma unroll
-            for (int b = 0; b < 8; b++) {
+            for (int b = 0; b < PB; b++) {
                 if (ex + c[b] >= kk) {
-                    sh.pick[0] = kBins - 1 - 8 * threadIdx.x - b;
+                    sh.pick[0] = kBins - 1 - PB * threadIdx.x - b;
                     sh.pick[1] = ex;
                     sh.pick[3] = c[b];
                     break;
@@ -406,7 +426,7 @@ __device__ __forceinline__ void select_candidates(FinishShared& sh, CandRegs& r,
         lds_barrier();
         const int nm = min(sh.nm, kRankMax);
         // the kk-th of the prefix candidates in the row's order sets (T, c_cut)
-        for (int t = threadIdx.x; t < nm; t += kFT) {
+        for (int t = threadIdx.x; t < nm; t += FT) {
             const uint32_t kt = sh.mkey[t];
             const int ct = sh.mcol[t];
             int rank = 0;
@@ -424,7 +444,7 @@ __device__ __forceinline__ void select_candidates(FinishShared& sh, CandRegs& r,
         c_cut = sh.pick[1];
     } else if (__builtin_expect(kk < n_pre, 0)) {
         // ---- many candidates share the prefix: digit passes over them
-        cand_pass<FLAT>(sh, r, ws, row, nch, m, rounds, kk, true,
+        cand_pass<FT, FLAT>(sh, r, ws, row, nch, m, rounds, kk, true,
                   [&](uint32_t kx, int) { return (kx >> 8) == preA; },
                   [&](uint32_t kx, int) { return (int)(kx & 0xffu); });
         T = (preA << 8) | (uint32_t)sh.pick[0];
@@ -432,16 +452,16 @@ __device__ __forceinline__ void select_candidates(FinishShared& sh, CandRegs& r,
         const int ties = sh.pick[3];
         if (kk < ties) {
             // the kk-th smallest column among the ties at T: bits [30:20], [19:8], [7:0]
-            cand_pass<FLAT>(sh, r, ws, row, nch, m, rounds, kk, false, [&](uint32_t kx, int) { return kx == T; },
+            cand_pass<FT, FLAT>(sh, r, ws, row, nch, m, rounds, kk, false, [&](uint32_t kx, int) { return kx == T; },
                       [&](uint32_t, int col) { return (int)(((uint32_t)col >> 20) & 0x7ffu); });
             const uint32_t c1 = (uint32_t)sh.pick[0];
             kk -= sh.pick[1];
-            cand_pass<FLAT>(sh, r, ws, row, nch, m, rounds, kk, false,
+            cand_pass<FT, FLAT>(sh, r, ws, row, nch, m, rounds, kk, false,
                       [&](uint32_t kx, int col) { return kx == T && ((uint32_t)col >> 20) == c1; },
                       [&](uint32_t, int col) { return (int)(((uint32_t)col >> 8) & 0xfffu); });
             const uint32_t c2 = (c1 << 12) | (uint32_t)sh.pick[0];
             kk -= sh.pick[1];
-            cand_pass<FLAT>(sh, r, ws, row, nch, m, rounds, kk, false,
+            cand_pass<FT, FLAT>(sh, r, ws, row, nch, m, rounds, kk, false,
                       [&](uint32_t kx, int col) { return kx == T && ((uint32_t)col >> 8) == c2; },
                       [&](uint32_t, int col) { return (int)((uint32_t)col & 0xffu); });
             c_cut = (int)((c2 << 8) | (uint32_t)sh.pick[0]);
@@ -468,9 +488,11 @@ __device__ __forceinline__ void select_candidates(FinishShared& sh, CandRegs& r,
     lds_barrier();
 }
 
-// gsz: chunks per workgroup (1..kGMax); chunks [grp * gsz, +gsz) of the row.
-__global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws, int gsz) {
-    __shared__ FinishShared sh;
+// gsz: chunks per workgroup (1..FT / 64); chunks [grp * gsz, +gsz) of the row.
+template <int FT>
+__global__ __launch_bounds__(FT) void k_finish(const TopkParams p, LongWs ws, int gsz) {
+    constexpr int kCR = CandRegs<FT>::kCR, kGMax = FT / 64;
+    __shared__ FinishShared<FT> sh;
     const int nch = ws.n_chunks;
     const int ngrp = (nch + gsz - 1) / gsz;
     const int row = blockIdx.x / ngrp, grp = blockIdx.x - row * ngrp;
@@ -485,14 +507,14 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws, i
     while (lspec < 8 && (nch << (lspec + 1)) <= 2048) lspec++;
     const int spec = 1 << lspec;
     // slot-pair registers that can hold a candidate up front (the rest stay empty)
-    const int jn = min(kCR / 2, (nch * spec / 2 + kFT - 1) / kFT);
+    const int jn = min(kCR / 2, (nch * spec / 2 + FT - 1) / FT);
 
     // ---- one round of loads: state, counts, these chunks' bitmaps and the first `spec`
     // candidate slots of every chunk (read before the counts are known; slots past a
     // count are ignored), 16 bytes per lane where the arrays allow
     if (grp == 0) {  // the digit-1 histogram was last read by the collect pass: clear it
         uint4* gh = reinterpret_cast<uint4*>(ws.hist + (int64_t)row * kBins);
-        for (int i = threadIdx.x; i < kBins / 4; i += kFT) gh[i] = make_uint4(0u, 0u, 0u, 0u);
+        for (int i = threadIdx.x; i < kBins / 4; i += FT) gh[i] = make_uint4(0u, 0u, 0u, 0u);
     }
     const int d1 = ws.st[row].d1;
     int kk = ws.st[row].kk;
@@ -501,14 +523,14 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws, i
     const int len = row_len(p, row);
     int my_cnum = threadIdx.x < nch ? ws.cnum[rc + threadIdx.x] : 0;
     int my_above = threadIdx.x < nch ? ws.cabove[rc + threadIdx.x] : 0;
-    static_assert(kGMax * kWords / 4 <= kFT, "one 16-byte bitmap load per thread at most");
+    static_assert(kGMax * kWords / 4 <= FT, "one 16-byte bitmap load per thread at most");
     uint4 bw = make_uint4(0u, 0u, 0u, 0u);
     if (threadIdx.x < min(gsz, nch - chunk) * (kWords / 4))
         bw = reinterpret_cast<const uint4*>(ws.bitmap + (rc + chunk) * kWords)[threadIdx.x];
     uint4 sv[kCR / 2];
 #pragma unroll
     for (int j = 0; j < kCR / 2; j++) {
-        const int q = threadIdx.x + kFT * j;
+        const int q = threadIdx.x + FT * j;
         const int c = (2 * q) >> lspec, slot = (2 * q) & (spec - 1);
         sv[j] = j < jn && c < nch ? *reinterpret_cast<const uint4*>(ws.cand + (rc + c) * kChunk + slot)
                                   : make_uint4(0u, 0xffffffffu, 0u, 0xffffffffu);
@@ -519,9 +541,8 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws, i
     const int nown = min(gsz, ncr - chunk);  // chunks this workgroup writes
     if (threadIdx.x >= ncr) my_cnum = my_above = 0;
     if (threadIdx.x >= nown * (kWords / 4)) bw = make_uint4(0u, 0u, 0u, 0u);
-    static_assert(kBins == 8 * kFT, "two 16-byte clearing stores per thread");
-    reinterpret_cast<uint4*>(sh.h)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
-    reinterpret_cast<uint4*>(sh.h)[threadIdx.x + kFT] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < kBins / 4 / FT; i++) reinterpret_cast<uint4*>(sh.h)[threadIdx.x + FT * i] = make_uint4(0u, 0u, 0u, 0u);
     if (threadIdx.x == 0) {
         sh.nm = 0;
         sh.before = 0;
@@ -554,12 +575,12 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws, i
         const int cmax = max(sh.part[0][3], sh.part[1][3]);
         int lw = lspec + 1;
         while ((1 << lw) < cmax) lw++;
-        if ((nch << lw) <= kFT * kCR) {
+        if ((nch << lw) <= kSlots) {
             ls = lw;
-            jr = min(kCR / 2, ((nch << lw) / 2 + kFT - 1) / kFT);
+            jr = min(kCR / 2, ((nch << lw) / 2 + FT - 1) / FT);
 #pragma unroll
             for (int j = 0; j < kCR / 2; j++) {
-                const int q = threadIdx.x + kFT * j;
+                const int q = threadIdx.x + FT * j;
                 const int c = (2 * q) >> ls, slot = (2 * q) & ((1 << ls) - 1);
                 sv[j] = j < jr && c < nch ? *reinterpret_cast<const uint4*>(ws.cand + (rc + c) * kChunk + slot)
                                           : make_uint4(0u, 0xffffffffu, 0u, 0xffffffffu);
@@ -567,17 +588,17 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws, i
             flat = false;
         }
     }
-    CandRegs r;
+    CandRegs<FT> r;
     if (flat) {
         // chunk-order prefix of the candidate counts for the flat reloads
         if (threadIdx.x == 0) sh.coff[0] = 0;
         if (threadIdx.x >= 64 && threadIdx.x < nch) sh.coff[threadIdx.x + 1] += sh.part[0][2];
         lds_barrier();
-        rounds = (m + kFT * kCR - 1) / (kFT * kCR);
+        rounds = (m + kSlots - 1) / kSlots;
     } else {
 #pragma unroll
         for (int j = 0; j < kCR / 2; j++) {
-            const int q = threadIdx.x + kFT * j;
+            const int q = threadIdx.x + FT * j;
             const int c = (2 * q) >> ls, slot = (2 * q) & ((1 << ls) - 1);
             const int cn = c < nch ? sh.cnum[c] : 0;
             r.key[2 * j] = sv[j].x;
@@ -588,8 +609,10 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws, i
     }
 
     if (d1 >= 0) {
-        if (__builtin_expect(flat, 0)) select_candidates<true>(sh, r, ws, row, nch, m, rounds, kCR / 2, d1, kk, chunk, nown);
-        else select_candidates<false>(sh, r, ws, row, nch, m, 1, jr, d1, kk, chunk, nown);
+        if (__builtin_expect(flat, 0))
+            select_candidates<FT, true>(sh, r, ws, row, nch, m, rounds, kCR / 2, d1, kk, chunk, nown);
+        else
+            select_candidates<FT, false>(sh, r, ws, row, nch, m, 1, jr, d1, kk, chunk, nown);
     }
 
     // ---- the chunks' columns in order: wave w writes chunk chunk + w, lane l its
@@ -626,7 +649,7 @@ __global__ __launch_bounds__(kFT) void k_finish(const TopkParams p, LongWs ws, i
     if (d1 < 0 && chunk + nown == ncr) {
         int32_t* oidx = p.out_idx + (int64_t)row * k;
         float* oval = p.out_vals ? p.out_vals + (int64_t)row * k : nullptr;
-        for (int i = min(above_total, k) + threadIdx.x; i < k; i += kFT) {
+        for (int i = min(above_total, k) + threadIdx.x; i < k; i += FT) {
             oidx[i] = -1;
             if (oval) oval[i] = -__builtin_inff();
         }
@@ -681,29 +704,33 @@ size_t topk_long_workspace_bytes(int rows, int cols, int k) {
 hipError_t launch_topk_long(const TopkParams& p, void* workspace, hipStream_t stream) {
     LongWs w = carve(workspace, p.rows, p.cols, nullptr);
     if (w.n_chunks > kMaxChunks) return hipErrorInvalidValue;
-    // Few rows: one workgroup per chunk keeps each one short.  Many rows: the histogram
-    // pass takes up to kHMax chunks per workgroup (fewer global atomics on each row's
-    // histogram; 64 rows of 32 chunks: 7.8 us with two chunks, 8.1 with four, 8.4 with
-    // one) and the finish up to kGMax, so that the redundant reading and ranking of each
-    // row's candidates stays near one pass over the chip (8.8 us with eight chunks, 9.9
-    // with four).  A 256-lane collect pass for many rows measured slower (12.5 vs 11.6 us).
+    // Few rows: one workgroup per chunk keeps each one short, with 1024 lanes.  Many
+    // rows: 512 lanes; the histogram pass takes up to kHMax chunks per workgroup (fewer
+    // global atomics on each row's histogram; 64 rows of 32 chunks: 7.8 us with two
+    // chunks, 8.1 with four, 8.4 with one) and the finish up to 8, so that the redundant
+    // reading and ranking of each row's candidates stays near one pass over the chip
+    // (8.8 us with eight chunks, 9.9 with four).  A 256-lane collect pass for many rows
+    // measured slower (12.5 vs 11.6 us).
     constexpr int kHMax = 4;
     auto per_group = [&](int most, int limit) {
         int g = 1;
         while (g < most && (int64_t)p.rows * ((w.n_chunks + g - 1) / g) > limit) g *= 2;
         return g;
     };
-    const int hs = per_group(kHMax, 2 * kWaveOfGroups), gsz = per_group(kGMax, kWaveOfGroups / 2);
+    const bool few = (int64_t)p.rows * w.n_chunks <= kWaveOfGroups;
+    const int hs = per_group(kHMax, 2 * kWaveOfGroups);
+    const int gsz = per_group((few ? kCTFew : kCTMany) / 64, kWaveOfGroups / 2);
     const unsigned hgrid = (unsigned)(p.rows * ((w.n_chunks + hs - 1) / hs)), cgrid = (unsigned)(p.rows * w.n_chunks);
-    if ((int64_t)p.rows * w.n_chunks <= kWaveOfGroups) {
+    const unsigned fgrid = (unsigned)(p.rows * ((w.n_chunks + gsz - 1) / gsz));
+    if (few) {
         hipLaunchKernelGGL(k_hist<kCTFew>, dim3(hgrid), dim3(kCTFew), 0, stream, p, w, hs);
         hipLaunchKernelGGL(k_collect<kCTFew>, dim3(cgrid), dim3(kCTFew), 0, stream, p, w);
+        hipLaunchKernelGGL(k_finish<kCTFew>, dim3(fgrid), dim3(kCTFew), 0, stream, p, w, gsz);
     } else {
         hipLaunchKernelGGL(k_hist<kCTMany>, dim3(hgrid), dim3(kCTMany), 0, stream, p, w, hs);
         hipLaunchKernelGGL(k_collect<kCTMany>, dim3(cgrid), dim3(kCTMany), 0, stream, p, w);
+        hipLaunchKernelGGL(k_finish<kCTMany>, dim3(fgrid), dim3(kCTMany), 0, stream, p, w, gsz);
     }
-    const unsigned fgrid = (unsigned)(p.rows * ((w.n_chunks + gsz - 1) / gsz));
-    hipLaunchKernelGGL(k_finish, dim3(fgrid), dim3(kFT), 0, stream, p, w, gsz);
     return hipGetLastError();
 }
 
