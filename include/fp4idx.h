@@ -231,16 +231,28 @@ size_t fp4idx_topk_workspace_bytes(int rows, int cols, int k);
  * workspace: device memory of at least fp4idx_topk_workspace_bytes(rows, cols, k),
  * 256-byte aligned, owned by the caller (NULL allowed when that size is 0: rows of at
  * most 8192 columns, or of at most 32768 columns when there are more than 64 rows, need
- * none).  It carries per-row histograms between the kernels
- * of one call: it must be zero-filled before its first use, and every call that
- * returns FP4IDX_OK leaves it ready for the next one (also under graph replay).  After
- * a call that returns FP4IDX_EHIP (a launch failed part way) it must be zero-filled
- * again.  Calls that run concurrently must not share a workspace.
+ * none).  It carries per-row histograms and arrival counters between the kernels, or
+ * the workgroups, of one call: it must be zero-filled before its first use, and every
+ * call that returns FP4IDX_OK leaves it ready for the next one with the same rows and
+ * cols (also under graph replay).  Its layout depends on both, so memory that served
+ * another shape must be zero-filled again first, and so must a workspace after a call
+ * that returns FP4IDX_EHIP (a launch failed part way).  Calls that run concurrently
+ * must not share a workspace.
  * Limits: 1 <= k <= 8192 and cols <= 524288 (else EUNSUPPORTED). */
 int fp4idx_topk(const float* scores, int64_t row_stride, int rows, int cols,
                 const int32_t* row_lens, int k,
                 int32_t* out_idx, float* out_vals,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* With at most 8 long rows, fp4idx_topk (and the few-rows route of
+ * fp4idx_logits_topk_paged) runs one kernel whose workgroups wait for each other in
+ * memory.  Each such wait polls at most `polls` times (default 65536, about 30 ms or
+ * more); a wait that runs out -- the row's workgroups could not all run at once, e.g.
+ * beside other work on the GPU -- has one workgroup recompute the row from its scores:
+ * the same result, later.  0 forces that path (for tests).  Sets the bound for later
+ * launches from this process and returns the previous one; negative values leave it
+ * unchanged. */
+int fp4idx_set_topk_wait_limit(int polls);
 
 /* MXFP4 quantize-and-store of index keys into the paged cache ([SGL] Modifications and
  * bench: bf16 keys become E2M1 nibbles plus one E8M0 code per 32 values, rounded to

@@ -22,6 +22,7 @@ EXPORTS = (
     "fp4idx_block_topk",
     "fp4idx_topk_workspace_bytes",
     "fp4idx_topk",
+    "fp4idx_set_topk_wait_limit",
     "fp4idx_quantize_store_k",
     "fp4idx_qsa_slots",
     "fp4idx_qsa_decode",
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.fp4idx_topk_workspace_bytes.argtypes = [i32, i32, i32]
     L.fp4idx_topk.restype = i32
     L.fp4idx_topk.argtypes = [P, i64, i32, i32, P, i32, P, P, P, ctypes.c_size_t, P]
+    L.fp4idx_set_topk_wait_limit.restype = i32
+    L.fp4idx_set_topk_wait_limit.argtypes = [i32]
     L.fp4idx_quantize_store_k.restype = i32
     L.fp4idx_quantize_store_k.argtypes = [P, i64, P, i32, P, i64, P, i64, i32, i32, P]
     L.fp4idx_qsa_slots.restype = i32

@@ -452,6 +452,10 @@ int fp4idx_qsa_decode(const uint16_t* q, int64_t q_row_stride, int64_t q_head_st
     return hip_status(fp4idx::launch_qsa_decode(p, (hipStream_t)stream));
 }
 
+int fp4idx_set_topk_wait_limit(int polls) {
+    return fp4idx::set_topk_wait_limit(polls);
+}
+
 size_t fp4idx_topk_workspace_bytes(int rows, int cols, int k) {
     if (rows <= 0 || cols <= 0 || k <= 0) return 0;
     return fp4idx::topk_workspace_bytes(rows, cols, k);

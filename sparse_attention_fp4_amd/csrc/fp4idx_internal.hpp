@@ -108,6 +108,9 @@ hipError_t launch_block_topk(const BlockTopkParams& p, hipStream_t stream);
 hipError_t launch_block_scores(const BlockParams& p, hipStream_t stream);
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
 hipError_t launch_topk_stream(const TopkParams& p, hipStream_t stream);
+// Bound on each in-kernel wait of the long-row top-k (polls of its arrival counter);
+// when one runs out the row is recomputed by one workgroup.  0 forces that path.
+int set_topk_wait_limit(int polls);  // returns the previous bound; < 0 reads it
 int topk_stream_cap(int cols, int k);
 
 struct QuantParams {

@@ -8,8 +8,10 @@
 // and NaN never selected, result in increasing column order, -1 padded).  Scores map
 // to order-preserving 32-bit keys; digit 1 is key bits [31:20], digit 2 bits [19:8].
 // A row is cut into chunks of 4096 columns; chunks past a row's end are skipped.
-// Workgroups exchange data only across kernel boundaries (a device-wide fence inside a
-// kernel costs microseconds on this multi-die part):
+// At most 8 rows of at most 8 chunks run as one kernel whose workgroups wait for each
+// other in memory (k_coop, below).  Otherwise workgroups exchange data only across
+// kernel boundaries (a device-wide fence inside a kernel costs microseconds on this
+// multi-die part), in three kernels:
 //   1. hist:    each chunk (a few consecutive chunks when many rows fill the chip)
 //               builds the histogram of digit 1 of its keys in LDS and adds its
 //               nonzero bins to the row's histogram (global atomics).
@@ -30,6 +32,8 @@
 //               first group's workgroup clears the row's histogram for the next call.
 // The workspace must be zero-filled before its first use; every call leaves the
 // histogram zero-filled again.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "fp4idx_internal.hpp"
 
@@ -54,6 +58,8 @@ struct RowState {
 };
 
 struct LongWs {
+    uint32_t* ctr;       // [rows][64]  one-kernel path: arrivals, wait failed, done (a line of its
+                         //             own per row); zero between calls
     RowState* st;        // [rows]
     uint32_t* hist;      // [rows][kBins]            digit 1 of the keys; zero between calls
     uint32_t* bitmap;    // [rows][n_chunks * kWords] columns above bin d1
@@ -61,6 +67,7 @@ struct LongWs {
     int32_t* cnum;       // [rows][n_chunks]          candidates per chunk
     int32_t* cabove;     // [rows][n_chunks]          columns above bin d1 per chunk
     int n_chunks;
+    int cstride;         // candidate slots a chunk (its columns)
     size_t zero_end;     // bytes from the base through hist: zero when a call starts
 };
 
@@ -79,6 +86,14 @@ __device__ __forceinline__ int row_len(const TopkParams& p, int row) {
     int len = p.cols;
     if (p.row_lens) len = min(max(p.row_lens[row], 0), p.cols);
     return len;
+}
+
+// A candidate (key, column) read at device scope: in the one-kernel path other
+// workgroups of the same kernel wrote it (device-scope stores, counted before the wait
+// that ends).
+__device__ __forceinline__ uint2 ld_cand(const uint2* q) {
+    const uint64_t x = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<uint2*>(q)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_uint2((uint32_t)x, (uint32_t)(x >> 32));
 }
 
 // Thread t of CT holds elements t + CT * j of the chunk (index order = j, wave, lane);
@@ -291,14 +306,14 @@ struct CandRegs {
 
 // Candidate i of the row (flat order) lives in chunk c with coff[c] <= i < coff[c+1].
 template <int FT>
-__device__ __forceinline__ int64_t cand_slot(const FinishShared<FT>& sh, int row, int nch, int i) {
+__device__ __forceinline__ int64_t cand_slot(const FinishShared<FT>& sh, const LongWs& ws, int row, int nch, int i) {
     int lo = 0, hi = nch;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (sh.coff[mid] <= i) lo = mid;
         else hi = mid;
     }
-    return ((int64_t)row * nch + lo) * kChunk + (i - sh.coff[lo]);
+    return ((int64_t)row * ws.n_chunks + lo) * ws.cstride + (i - sh.coff[lo]);
 }
 
 template <int FT>
@@ -309,7 +324,7 @@ __device__ __forceinline__ void load_flat(CandRegs<FT>& r, const FinishShared<FT
 #pragma unroll
     for (int j = 0; j < kCR; j++) {
         const int i = round * kSlots + threadIdx.x + FT * j;
-        v[j] = i < m ? ws.cand[cand_slot(sh, row, nch, i)] : make_uint2(0u, 0xffffffffu);
+        v[j] = i < m ? ld_cand(ws.cand + cand_slot(sh, ws, row, nch, i)) : make_uint2(0u, 0xffffffffu);
     }
 #pragma unroll
     for (int j = 0; j < kCR; j++) {
@@ -347,7 +362,8 @@ __device__ __forceinline__ void cand_pass(FinishShared<FT>& sh, CandRegs<FT>& r,
 // chunks to sh.before.  FLAT (some chunk has more candidates than its up-front slots):
 // the candidates are read in row order, once when they fit the registers, else again
 // in every pass, round by round.  Otherwise registers [0, 2 * jr) hold them all.
-template <int FT, bool FLAT>
+// Chunks are 2^LCH columns, with 2^(LCH - 5) bitmap words each.
+template <int FT, bool FLAT, int LCH = 12>
 __device__ __forceinline__ void select_candidates(FinishShared<FT>& sh, CandRegs<FT>& r, const LongWs& ws, int row,
                                                   int nch, int m, int rounds, int jr, int d1, int kk, int chunk,
                                                   int nown) {
@@ -385,8 +401,11 @@ __device__ __forceinline__ void select_candidates(FinishShared<FT>& sh, CandRegs
         const int incl = wave_incl_scan(s);
         if (lane == 63) sh.wtot[wave] = incl;
         lds_barrier();
-        int ex = incl - s;  // keys in the bins above this thread's
-        for (int w = 0; w < wave; w++) ex += sh.wtot[w];
+        // keys in the bins above this thread's: the earlier waves' totals (one LDS read
+        // a lane and a wave scan) and this wave's lanes before it
+        const int wt = wave_incl_scan(lane < FT / 64 ? (int)sh.wtot[lane] : 0);
+        const int uw = __builtin_amdgcn_readfirstlane(wave);
+        int ex = incl - s + (uw > 0 ? __builtin_amdgcn_readlane(wt, uw - 1) : 0);
         if (ex < kk && kk <= ex + s) {
 #pragma unroll
             for (int b = 0; b < PB; b++) {
@@ -478,9 +497,10 @@ __device__ __forceinline__ void select_candidates(FinishShared<FT>& sh, CandRegs
             const uint32_t pre = kx >> 8;
             const bool sel = pre > preA || (pre == preA && (kx > T || (kx == T && col <= c_cut)));
             if (!sel) continue;
-            const int c = col / kChunk;
+            const int c = col >> LCH;
             if (c < chunk) before++;
-            else if (c < chunk + nown) atomicOr(&sh.bits[(c - chunk) * kWords + ((col & (kChunk - 1)) >> 5)], 1u << (col & 31));
+            else if (c < chunk + nown)
+                atomicOr(&sh.bits[((c - chunk) << (LCH - 5)) + ((col & ((1 << LCH) - 1)) >> 5)], 1u << (col & 31));
         }
     }
     const int wb = wave_sum_i32(before);
@@ -656,14 +676,418 @@ __global__ __launch_bounds__(FT) void k_finish(const TopkParams p, LongWs ws, in
     }
 }
 
+// ---------------------------------------------------------------- one kernel for few rows
+// With one row a die, every row's chunk workgroups run at once on one die (the
+// dispatcher deals block b to die b % 8; each die has 32 CUs) and meet at two waits in
+// memory instead of two kernel boundaries: a wait costs about 0.6 us among the
+// workgroups of one die (1.1 us across dies), a boundary about 2 us plus slow first
+// loads of what the previous kernel wrote.  All exchange goes through device-scope
+// atomics, loads and stores, so the result does not depend on the placement, only the
+// speed does.  Each row's counters sit on a 256-byte line of their own (sharing one
+// line between rows made each wait about 1.5 us).
+//   1. each chunk (1024 V columns, V keys a thread, kept in registers) adds the
+//      digit-1 histogram of its keys to the row's; wait for the row's chunks;
+//   2. each chunk finds d1 and kk from the row's histogram, keeps the bitmap of its
+//      columns above d1 in LDS, stores its candidates (keys in d1) and both counts;
+//      wait;
+//   3. each chunk reads every candidate of the row, selects as the finishing pass
+//      does, and writes its own columns in order.
+// A wait is bounded (g_wait_limit polls); when one runs out, the row is marked and the
+// last of its workgroups to end recomputes it alone from the scores.  That workgroup
+// (the last to end, failed or not) also clears the row's counters and histogram.
+constexpr int kCoopMaxW = 8;    // chunk workgroups a row (a die holds 32 at once, one a CU)
+constexpr int kCoopRowsMax = 8; // rows a call: one a die
+constexpr int kSc1 = 16;        // cache-policy bit of a device-scope buffer access
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+struct CoopShared {
+    FinishShared<1024> f;
+    int ok;
+    int ncand;
+    int nabove;
+};
+
+// Counts this workgroup's arrival on the row's counter and waits (bounded) until
+// `target` arrivals are in.  Every wave first waits for its own global stores and
+// atomics, so what the workgroup wrote is in place before it is counted.  Returns
+// false (the same in every thread) when the wait ran out or another workgroup's did.
+__device__ __forceinline__ bool coop_wait(uint32_t* ctr, uint32_t target, int limit, int& flag) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int ok = 1;
+        for (int it = 0;; it++) {
+            const uint64_t st = __hip_atomic_load(reinterpret_cast<uint64_t*>(ctr), __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+            if ((uint32_t)(st >> 32) != 0u) { ok = 0; break; }
+            if ((uint32_t)st >= target) break;
+            if (it >= limit) {
+                __hip_atomic_fetch_or(ctr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        flag = ok;
+    }
+    __syncthreads();
+    return flag != 0;
+}
+
+// The row's exact top-k by one workgroup from the scores alone: three digit passes
+// find the k-th key T and how many keys equal to it are kept, then one pass in column
+// order writes the selected columns (keys above T, and the first of those equal to T).
+__device__ void coop_row_alone(const TopkParams& p, int row, int len, FinishShared<1024>& sh) {
+    constexpr int FT = 1024, per = kBins / FT;
+    const float* srow = p.scores + (int64_t)row * p.row_stride;
+    const int k = p.k;
+    auto pass = [&](auto keep, auto digit, int kk) {
+        for (int i = threadIdx.x; i < kBins; i += FT) sh.h[i] = 0u;
+        lds_barrier();
+        for (int i = threadIdx.x; i < len; i += FT) {
+            const uint32_t key = to_key(srow[i]);
+            if (key && keep(key)) atomicAdd(&sh.h[digit(key)], 1u);
+        }
+        lds_barrier();
+        int c[per], bin[per];
+#pragma unroll
+        for (int b = 0; b < per; b++) {
+            bin[b] = kBins - 1 - (threadIdx.x * per + b);
+            c[b] = (int)sh.h[bin[b]];
+        }
+        pick_bin<FT, per>(c, bin, kk, sh.wtot, sh.pick);
+    };
+    int kk = k;
+    pass([](uint32_t) { return true; }, [](uint32_t x) { return (int)(x >> 20); }, kk);
+    uint32_t T = 0u;  // keys above T are kept; of those equal to T, the first take_eq
+    int take_eq = 0;
+    if (sh.pick[2] > kk) {
+        const uint32_t d1 = (uint32_t)sh.pick[0];
+        kk -= sh.pick[1];
+        pass([&](uint32_t x) { return (x >> 20) == d1; }, [](uint32_t x) { return (int)((x >> 8) & 0xfffu); }, kk);
+        const uint32_t pre = (d1 << 12) | (uint32_t)sh.pick[0];
+        kk -= sh.pick[1];
+        pass([&](uint32_t x) { return (x >> 8) == pre; }, [](uint32_t x) { return (int)(x & 0xffu); }, kk);
+        T = (pre << 8) | (uint32_t)sh.pick[0];
+        take_eq = kk - sh.pick[1];
+    }
+    int32_t* oidx = p.out_idx + (int64_t)row * k;
+    float* oval = p.out_vals ? p.out_vals + (int64_t)row * k : nullptr;
+    int n_sel = 0, n_eq = 0;
+    for (int c0 = 0; c0 < len && n_sel < k; c0 += FT) {
+        const int i = c0 + threadIdx.x;
+        const float v = i < len ? srow[i] : -__builtin_inff();
+        const uint32_t key = to_key(v);
+        const bool eq = T != 0u && key == T;
+        int ex, tot;
+        block_excl_scan<FT>(eq ? 1 : 0, sh.wtot, ex, tot);
+        const bool sel = key > T || (eq && n_eq + ex < take_eq);
+        int exs, tots;
+        block_excl_scan<FT>(sel ? 1 : 0, sh.wtot, exs, tots);
+        const int pos = n_sel + exs;
+        if (sel && pos < k) {
+            oidx[pos] = i;
+            if (oval) oval[pos] = v;
+        }
+        n_sel += tots;
+        n_eq += tot;
+    }
+    for (int i = min(n_sel, k) + (int)threadIdx.x; i < k; i += FT) {
+        oidx[i] = -1;
+        if (oval) oval[i] = -__builtin_inff();
+    }
+}
+
+// V: keys a thread (chunks of 1024 V columns); W: chunk workgroups a row; rpd: rows a
+// die.  Grid: 8 * rpd * W blocks; block b serves row (b >> 3) / W * 8 + b % 8, chunk
+// (b >> 3) % W.
+template <int V>
+__global__ __launch_bounds__(1024) void k_coop(const TopkParams p, LongWs ws, int W, int rpd, int limit) {
+    constexpr int FT = 1024, C = FT * V, CW = C / 32;
+    constexpr int LCH = V == 4 ? 12 : 13;
+    static_assert(V == 4 || V == 8, "4 or 8 keys a thread");
+    static_assert(kCoopMaxW <= 32, "every chunk workgroup of a die resident at once");
+    static_assert(C == (1 << LCH) && CW <= 16 * kWords, "chunk bitmap fits the finishing LDS");
+    constexpr int kCR = CandRegs<FT>::kCR;
+    __shared__ CoopShared cs;
+    FinishShared<FT>& sh = cs.f;
+    const int die = blockIdx.x & 7, rest = blockIdx.x >> 3;
+    const int lr = rest / W, m = rest - lr * W;
+    const int row = lr * 8 + die;
+    if (lr >= rpd || row >= p.rows) return;
+    const int len = row_len(p, row);
+    const int wr = max(1, (len + C - 1) / C);  // chunks in use
+    if (m >= wr) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int k = p.k;
+    uint32_t* ctr = ws.ctr + (int64_t)row * 64;
+    uint32_t* gh = ws.hist + (int64_t)row * kBins;
+    const int c0 = m * C;
+    const float* srow = p.scores + (int64_t)row * p.row_stride;
+
+    // ---- 1. the chunk's digit-1 histogram, added to the row's
+    reinterpret_cast<uint4*>(sh.h)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+    static_assert(kBins == 4 * FT, "one 16-byte clear a thread");
+    if (threadIdx.x == 0) {
+        cs.ncand = 0;
+        cs.nabove = 0;
+        sh.nm = 0;
+        sh.before = 0;
+    }
+    uint32_t key[V];
+    {
+        const int n = min(len - c0, C);
+        float v[V];
+#pragma unroll
+        for (int j = 0; j < V; j++) {
+            const int i = threadIdx.x + FT * j;
+            v[j] = i < n ? srow[c0 + i] : -__builtin_inff();
+        }
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < V; j++) {
+            key[j] = to_key(v[j]);
+            if (key[j]) atomicAdd(&sh.h[key[j] >> 20], 1u);
+        }
+    }
+    lds_barrier();
+    // consecutive lanes add consecutive bins: one instruction's atomics touch two lines
+#pragma unroll
+    for (int i = 0; i < kBins / FT; i++) {
+        const uint32_t x = sh.h[threadIdx.x + FT * i];
+        if (x) __hip_atomic_fetch_add(gh + threadIdx.x + FT * i, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    bool ok = coop_wait(ctr, (uint32_t)wr, limit, cs.ok);
+
+    if (ok) {
+        // ---- 2. d1 and kk from the row's histogram (thread t: bins 4095 - 4t down)
+        const v4u hv = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(gh, kBins * 4),
+                                                             (kBins / 4 - 1 - (int)threadIdx.x) * 16, 0, kSc1);
+        int d1, kk;
+        {
+            int c[4] = {(int)hv.w, (int)hv.z, (int)hv.y, (int)hv.x}, bin[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) bin[i] = kBins - 1 - (4 * (int)threadIdx.x + i);
+            pick_bin<FT, 4>(c, bin, k, sh.wtot, sh.pick);
+            if (sh.pick[2] <= k) {
+                d1 = -1;
+                kk = 0;
+            } else {
+                d1 = sh.pick[0];
+                kk = k - sh.pick[1];
+            }
+        }
+        // bitmap of the columns above d1 (LDS) and the candidates in d1 (memory)
+        uint2* dst = ws.cand + ((int64_t)row * ws.n_chunks + m) * ws.cstride;
+        int above = 0, ncw = 0;  // this wave's columns above d1 and candidates (uniform)
+        unsigned long long mc[V];
+#pragma unroll
+        for (int j = 0; j < V; j++) {
+            const uint32_t kj = key[j];
+            const int dig = (int)(kj >> 20);
+            const bool up = kj != 0u && (d1 < 0 || dig > d1);
+            // a wave covers 64 consecutive columns = two bitmap words, from an even word
+            const unsigned long long ma = __ballot(up);
+            above += __popcll(ma);
+            if (lane == 0) *reinterpret_cast<unsigned long long*>(&sh.bits[(threadIdx.x + FT * j) >> 5]) = ma;
+            mc[j] = __ballot(d1 >= 0 && kj != 0u && dig == d1);
+            ncw += __popcll(mc[j]);
+        }
+        // one LDS atomic a wave places its candidates; they are stored in (step, lane) order
+        if (ncw) {
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&cs.ncand, ncw);
+            base = __builtin_amdgcn_readlane(base, 0);
+#pragma unroll
+            for (int j = 0; j < V; j++) {
+                if ((mc[j] >> lane) & 1ull) {
+                    const uint64_t e = (uint64_t)key[j] | ((uint64_t)(uint32_t)(c0 + threadIdx.x + FT * j) << 32);
+                    __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + base + lanes_below(mc[j])), e, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+                base += __popcll(mc[j]);
+            }
+        }
+        if (lane == 0 && above) atomicAdd(&cs.nabove, above);
+        lds_barrier();
+        if (threadIdx.x == 0) {
+            __hip_atomic_store(reinterpret_cast<uint32_t*>(ws.cnum) + (int64_t)row * ws.n_chunks + m, (uint32_t)cs.ncand,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(reinterpret_cast<uint32_t*>(ws.cabove) + (int64_t)row * ws.n_chunks + m,
+                               (uint32_t)cs.nabove, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        ok = coop_wait(ctr, 2u * (uint32_t)wr, limit, cs.ok);
+
+        if (ok) {
+            // ---- 3. every candidate of the row, then the selection
+            const int nch = wr;
+            const int64_t rc = (int64_t)row * ws.n_chunks;
+            // up-front slots a chunk: kSlots / nch rounded down to a power of two
+            int lspec = 5;
+            while (lspec < LCH && (nch << (lspec + 1)) <= kSlots) lspec++;
+            const int spec = 1 << lspec;
+            const int jn = min(kCR / 2, (nch * spec / 2 + FT - 1) / FT);
+            const __amdgpu_buffer_rsrc_t cr = make_rsrc(ws.cand + rc * ws.cstride, (uint32_t)(nch * ws.cstride * 8));
+            int my_cnum = 0, my_above = 0;
+            if (threadIdx.x < nch) {
+                my_cnum = (int)__hip_atomic_load(reinterpret_cast<uint32_t*>(ws.cnum) + rc + threadIdx.x, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+                my_above = (int)__hip_atomic_load(reinterpret_cast<uint32_t*>(ws.cabove) + rc + threadIdx.x,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            v4u sv[kCR / 2];
+#pragma unroll
+            for (int j = 0; j < kCR / 2; j++) {
+                const int q = threadIdx.x + FT * j;
+                const int c = (2 * q) >> lspec, slot = (2 * q) & (spec - 1);
+                sv[j] = j < jn && c < nch ? __builtin_amdgcn_raw_buffer_load_b128(cr, (c * ws.cstride + slot) * 8, 0, kSc1)
+                                          : v4u{0u, 0xffffffffu, 0u, 0xffffffffu};
+            }
+            reinterpret_cast<uint4*>(sh.h)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+            static_assert(kCoopMaxW <= 64, "per-chunk counts fit wave 0");
+            if (wave == 0) {
+                const int ab = wave_sum_i32(lane < m ? my_above : 0);
+                const int at = wave_sum_i32(my_above);
+                const int cs_ = wave_incl_scan(my_cnum);
+                if (lane < nch) sh.coff[lane + 1] = cs_;
+                if (lane == 0) {
+                    sh.coff[0] = 0;
+                    sh.part[0][0] = ab;
+                    sh.part[0][1] = at;
+                }
+                if (lane == 63) sh.part[0][2] = cs_;
+                const int mx = (int)wave_max_u32((uint32_t)my_cnum);
+                if (lane == 0) sh.part[0][3] = mx;
+                if (lane < nch) sh.cnum[lane] = my_cnum;
+            }
+            bool flat = __syncthreads_or(my_cnum > spec) != 0;
+            const int above_before = sh.part[0][0], above_total = sh.part[0][1];
+            const int mtot = sh.part[0][2];
+            int ls = lspec, jr = jn, rounds = 1;
+            if (flat) {
+                // some chunk has more candidates than its up-front slots: wider slots when
+                // every chunk still fits the registers, else round-by-round reloads
+                const int cmax = sh.part[0][3];
+                int lw = lspec + 1;
+                while ((1 << lw) < cmax) lw++;
+                if ((nch << lw) <= kSlots) {
+                    ls = lw;
+                    jr = min(kCR / 2, ((nch << lw) / 2 + FT - 1) / FT);
+#pragma unroll
+                    for (int j = 0; j < kCR / 2; j++) {
+                        const int q = threadIdx.x + FT * j;
+                        const int c = (2 * q) >> ls, slot = (2 * q) & ((1 << ls) - 1);
+                        sv[j] = j < jr && c < nch ? __builtin_amdgcn_raw_buffer_load_b128(cr, (c * ws.cstride + slot) * 8, 0, kSc1)
+                                                  : v4u{0u, 0xffffffffu, 0u, 0xffffffffu};
+                    }
+                    flat = false;
+                } else {
+                    rounds = (mtot + kSlots - 1) / kSlots;
+                }
+            }
+            CandRegs<FT> r;
+            if (!flat) {
+#pragma unroll
+                for (int j = 0; j < kCR / 2; j++) {
+                    const int q = threadIdx.x + FT * j;
+                    const int c = (2 * q) >> ls, slot = (2 * q) & ((1 << ls) - 1);
+                    const int cn = c < nch ? sh.cnum[c] : 0;
+                    r.key[2 * j] = sv[j].x;
+                    r.col[2 * j] = slot < cn ? (int)sv[j].y : -1;
+                    r.key[2 * j + 1] = sv[j].z;
+                    r.col[2 * j + 1] = slot + 1 < cn ? (int)sv[j].w : -1;
+                }
+            }
+            if (d1 >= 0) {
+                if (__builtin_expect(flat, 0))
+                    select_candidates<FT, true, LCH>(sh, r, ws, row, nch, mtot, rounds, kCR / 2, d1, kk, m, 1);
+                else
+                    select_candidates<FT, false, LCH>(sh, r, ws, row, nch, mtot, 1, jr, d1, kk, m, 1);
+            }
+            // ---- this chunk's columns in order: thread t holds bitmap word t
+            const uint32_t wv = threadIdx.x < CW ? sh.bits[threadIdx.x] : 0u;
+            int ex, tot;
+            block_excl_scan<FT>(__popc(wv), sh.wtot, ex, tot);
+            int pos = above_before + sh.before + ex;
+            int32_t* oidx = p.out_idx + (int64_t)row * k;
+            float* oval = p.out_vals ? p.out_vals + (int64_t)row * k : nullptr;
+            uint32_t bits = wv;
+            while (bits && pos < k) {
+                const int col = c0 + 32 * (int)threadIdx.x + __ffs((int)bits) - 1;
+                oidx[pos] = col;
+                if (oval) oval[pos] = srow[col];
+                pos++;
+                bits &= bits - 1u;
+            }
+            // every valid key kept (fewer than k): the row's last chunk pads it
+            if (d1 < 0 && m == wr - 1) {
+                for (int i = min(above_total, k) + (int)threadIdx.x; i < k; i += FT) {
+                    oidx[i] = -1;
+                    if (oval) oval[i] = -__builtin_inff();
+                }
+            }
+        }
+    }
+
+    // ---- the end: the row's last workgroup recomputes it when a wait ran out, then
+    // clears the row's histogram and counters for the next call
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(ctr + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int last = 0;
+        if (old == (uint32_t)(wr - 1)) {
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            last = __hip_atomic_load(ctr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ? 2 : 1;
+        }
+        cs.ok = last;
+    }
+    __syncthreads();
+    const int last = cs.ok;
+    if (last) {
+        if (last == 2) coop_row_alone(p, row, len, sh);
+        __builtin_amdgcn_raw_buffer_store_b128(v4u{0u, 0u, 0u, 0u}, make_rsrc(gh, kBins * 4), (int)threadIdx.x * 16, 0, kSc1);
+        if (threadIdx.x < 3) __hip_atomic_store(ctr + threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Keys a thread, and chunk workgroups a row, for the one-kernel path, or false when it
+// does not apply: more rows than dies, or rows of more than kCoopMaxW chunks.  Its
+// in-kernel time grows with the chunks a row (more adds on each histogram bin, more
+// candidates to read), while the three kernels' does not: a step of 4 rows (scorer +
+// top-k) took 17.1 against 18.7 us at 16384 and 32768 columns (4 and 8 chunks), 18.65
+// against 18.8 at 65536 (16), and 19.5-20.6 against 19.5 at 100k (25; 13 chunks of
+// 8192 columns: 19.7).
+bool coop_shape(int rows, int cols, int& V, int& W) {
+    if (rows < 1 || rows > kCoopRowsMax) return false;
+    V = 4;
+    W = (cols + 1024 * V - 1) / (1024 * V);
+    return W <= kCoopMaxW;
+}
+
+int g_wait_limit = 1 << 16;
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The three-kernel view of the workspace; the one-kernel path (coop_shape) uses the
+// same regions with its own chunk count and candidate stride, so the candidate and
+// count regions are sized for both.
 LongWs carve(void* base, int rows, int cols, size_t* bytes) {
     LongWs w{};
     w.n_chunks = (cols + kChunk - 1) / kChunk;
+    w.cstride = kChunk;
     const size_t rc = (size_t)rows * w.n_chunks;
+    size_t cand_row = (size_t)w.n_chunks * kChunk, cnt_row = (size_t)w.n_chunks;
+    int cv = 0, cw = 0;
+    if (coop_shape(rows, cols, cv, cw)) {
+        cand_row = std::max(cand_row, (size_t)cw * 1024 * cv);
+        cnt_row = std::max(cnt_row, (size_t)cw);
+    }
     unsigned char* b = reinterpret_cast<unsigned char*>(base);
     size_t o = 0;
+    w.ctr = reinterpret_cast<uint32_t*>(b + o);
+    o = align256(o + (size_t)rows * 64 * 4);
     w.st = reinterpret_cast<RowState*>(b + o);
     o = align256(o + (size_t)rows * sizeof(RowState));
     w.hist = reinterpret_cast<uint32_t*>(b + o);
@@ -672,11 +1096,11 @@ LongWs carve(void* base, int rows, int cols, size_t* bytes) {
     w.bitmap = reinterpret_cast<uint32_t*>(b + o);
     o = align256(o + rc * kWords * 4);
     w.cand = reinterpret_cast<uint2*>(b + o);
-    o = align256(o + rc * kChunk * sizeof(uint2));
+    o = align256(o + (size_t)rows * cand_row * sizeof(uint2));
     w.cnum = reinterpret_cast<int32_t*>(b + o);
-    o = align256(o + rc * 4);
+    o = align256(o + (size_t)rows * cnt_row * 4);
     w.cabove = reinterpret_cast<int32_t*>(b + o);
-    o = align256(o + rc * 4);
+    o = align256(o + (size_t)rows * cnt_row * 4);
     if (bytes) *bytes = o;
     return w;
 }
@@ -689,8 +1113,8 @@ LongWs carve(void* base, int rows, int cols, size_t* bytes) {
 // rows keep the chip busy one workgroup each.
 bool topk_long_rows(int rows, int cols) { return cols > 32768 || (cols > 8192 && rows <= 64); }
 
-// Leading workspace bytes that must be zero when a call starts: the row states and the
-// histogram come first in the layout (a caller that cannot keep the workspace
+// Leading workspace bytes that must be zero when a call starts: the one-kernel path's
+// counters, the row states and the histogram come first in the layout (a caller that cannot keep the workspace
 // between calls clears just these).
 size_t topk_long_zero_bytes(int rows, int cols) { return carve(nullptr, rows, cols, nullptr).zero_end; }
 
@@ -701,9 +1125,26 @@ size_t topk_long_workspace_bytes(int rows, int cols, int k) {
     return bytes;
 }
 
+int set_topk_wait_limit(int polls) {
+    const int prev = g_wait_limit;
+    if (polls >= 0) g_wait_limit = polls;
+    return prev;
+}
+
 hipError_t launch_topk_long(const TopkParams& p, void* workspace, hipStream_t stream) {
     LongWs w = carve(workspace, p.rows, p.cols, nullptr);
     if (w.n_chunks > kMaxChunks) return hipErrorInvalidValue;
+    int cv = 0, cw = 0;
+    if (coop_shape(p.rows, p.cols, cv, cw)) {
+        // one kernel: every row's chunk workgroups on one die, all resident at once
+        LongWs c = w;
+        c.n_chunks = cw;
+        c.cstride = 1024 * cv;
+        const int rpd = (p.rows + 7) / 8;
+        const dim3 grid((unsigned)(8 * rpd * cw));
+        hipLaunchKernelGGL(k_coop<4>, grid, dim3(1024), 0, stream, p, c, cw, rpd, g_wait_limit);
+        return hipGetLastError();
+    }
     // Few rows: one workgroup per chunk keeps each one short, with 1024 lanes.  Many
     // rows: 512 lanes; the histogram pass takes up to kHMax chunks per workgroup (fewer
     // global atomics on each row's histogram; 64 rows of 32 chunks: 7.8 us with two

@@ -237,7 +237,8 @@ def topk(scores, k: int, row_lens=None, *, out_idx=None, out_vals=None, want_val
 
     workspace: optional uint8 tensor of at least topk_workspace_bytes(rows, cols, k)
     bytes, zero-filled before its first use (torch.zeros); each call leaves it ready for
-    the next, so it can be reused across calls without clearing.
+    the next one of the same rows and cols, so it can be reused across such calls
+    without clearing (zero it again before a call of another shape).
     """
     _need(scores, "scores", torch.float32, 2)
     dev = scores.device
@@ -260,6 +261,12 @@ def topk(scores, k: int, row_lens=None, *, out_idx=None, out_vals=None, want_val
                            0 if workspace is None else workspace.numel(), _stream())
     check("fp4idx_topk", rc)
     return out_idx, out_vals
+
+
+def set_topk_wait_limit(polls: int) -> int:
+    """Bound on each in-kernel wait of the few-long-rows top-k (0 forces its fallback,
+    where one workgroup recomputes a row); returns the previous bound."""
+    return int(lib().fp4idx_set_topk_wait_limit(int(polls)))
 
 
 def block_topk(scores, k: int, *, out_idx=None, out_count=None):

@@ -195,6 +195,92 @@ def test_workspace_reused_across_calls_without_clearing():
         assert np.array_equal(vals.cpu().numpy().view(np.uint32), ov.view(np.uint32))
 
 
+@pytest.mark.parametrize("rows,cols,k,kind", [(4, 32_768, 2048, "normal"), (6, 20_000, 2048, "ties"),
+                                              (2, 30_000, 7, "normal"), (3, 16_384, 2048, "clustered"),
+                                              (8, 9_000, 8192, "normal")])
+def test_few_long_rows_when_the_waits_run_out(rows, cols, k, kind):
+    """At most 8 rows of 8193..32768 columns take one kernel whose workgroups wait for
+    each other; with the wait bound at 0 polls every row with more than one chunk is
+    recomputed by one workgroup from its scores (the path taken when a row's workgroups
+    cannot all run at once), and the result is the same.  The workspace is then ready
+    for a normal call."""
+    import torch
+
+    import sparse_attention_fp4_amd as fp4
+    from .gpu_helpers import dev
+
+    rng = np.random.default_rng(rows + cols + k)
+    if kind == "ties":
+        s = (rng.integers(-20, 20, (rows, cols)) / 4).astype(np.float32)
+        s[1, ::3] = -0.0
+        s[2, :] = 1.5
+        s[3, :] = -np.inf
+    elif kind == "clustered":
+        s = (1.0 + rng.standard_normal((rows, cols)) * 1e-6).astype(np.float32)
+        s[0, 5] = np.inf
+    else:
+        s = rng.standard_normal((rows, cols)).astype(np.float32)
+        s[0, rng.integers(0, cols, 50)] = -np.inf
+        s[-1, rng.integers(0, cols, 50)] = np.nan
+    lens = np.full(rows, cols, np.int32)
+    lens[-1] = 0 if rows > 4 else cols - 4097
+    if rows > 4:
+        lens[-2] = 1
+    ws = torch.zeros(fp4.topk_workspace_bytes(rows, cols, k), dtype=torch.uint8, device="cuda")
+    oi, ov = orc.topk(s, k, lens)
+    prev = fp4.ops.set_topk_wait_limit(0)
+    try:
+        say(f"[gpu] topk waits run out rows={rows} cols={cols} k={k} {kind}")
+        idx, vals = fp4.topk(dev(s), k, dev(lens), workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        fp4.ops.set_topk_wait_limit(prev)
+    assert np.array_equal(idx.cpu().numpy(), oi)
+    assert np.array_equal(vals.cpu().numpy().view(np.uint32), ov.view(np.uint32))
+    say("[gpu] topk after the fallback, same workspace")
+    idx, vals = fp4.topk(dev(s), k, dev(lens), workspace=ws)
+    assert np.array_equal(idx.cpu().numpy(), oi)
+    assert np.array_equal(vals.cpu().numpy().view(np.uint32), ov.view(np.uint32))
+
+
+def test_workspace_reused_per_shape_and_cleared_between_shapes():
+    """One allocation serves calls of 4 rows (one kernel, in-memory waits) and of 64
+    rows (three kernels): calls of one shape reuse it without clearing, and it is
+    zero-filled when the shape changes (the layout depends on the shape)."""
+    import torch
+
+    import sparse_attention_fp4_amd as fp4
+    from .gpu_helpers import dev
+
+    rng = np.random.default_rng(12)
+    cols, k = 32_768, 2048
+    nb = max(fp4.topk_workspace_bytes(r, cols, k) for r in (4, 64))
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    for rep, rows in enumerate((4, 4, 64, 64, 4, 4)):
+        if rep in (2, 4):
+            ws.zero_()
+        s = rng.standard_normal((rows, cols)).astype(np.float32)
+        lens = rng.integers(1, cols + 1, rows).astype(np.int32)
+        lens[0] = cols
+        say(f"[gpu] topk workspace call {rep} rows={rows}")
+        idx, _ = fp4.topk(dev(s), k, dev(lens), workspace=ws, want_vals=False)
+        oi, _ = orc.topk(s, k, lens)
+        assert np.array_equal(idx.cpu().numpy(), oi)
+
+
+def test_few_rows_in_one_kernel_lengths_and_ties():
+    """8 rows of 32768 columns (one kernel, 8 chunk workgroups a row): a row of equal
+    scores, rows of lengths 0, 1, k - 1, k, k + 1 and 5000, and heavy ties."""
+    rng = np.random.default_rng(33)
+    rows, cols, k = 8, 32_768, 2048
+    s = (rng.integers(-40, 40, (rows, cols)) / 8).astype(np.float32)
+    s[0] = 1.5
+    s[1, rng.integers(0, cols, 300)] = np.nan
+    lens = np.array([cols, cols - 1, 0, 1, k - 1, k, k + 1, 5000], np.int32)
+    say(f"[gpu] topk one kernel lengths and ties rows={rows} cols={cols} k={k}")
+    _same(s, k, lens)
+
+
 def _sampled_columns(length):
     """128 runs of 32 columns at run starts floor(r * length / 128) rounded down to a
     multiple of 32 (the whole row when it has at most 4096 columns): a fixed 4% sample
