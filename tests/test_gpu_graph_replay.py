@@ -66,10 +66,13 @@ def _with(case, meta):
     return c
 
 
+@pytest.mark.parametrize("ctx0", [20000, 40000], ids=["one_kernel_topk", "three_kernel_topk"])
 @pytest.mark.parametrize("fmt", [wl.MXFP4, wl.NVFP4], ids=["mxfp4", "nvfp4"])
-def test_logits_and_long_row_topk_replay_with_new_visibility_and_mapping(fmt):
+def test_logits_and_long_row_topk_replay_with_new_visibility_and_mapping(fmt, ctx0):
+    """5 rows of 20000 columns take the one-kernel long-row top-k (in-memory waits on
+    counters it clears itself), 5 rows of 40000 the three kernels."""
     k = 2048
-    case = wl.make_logits(f"replay_{fmt}", fmt=fmt, q_per_req=[3, 2], ctx=[20000, 12000], H=32,
+    case = wl.make_logits(f"replay_{fmt}_{ctx0}", fmt=fmt, q_per_req=[3, 2], ctx=[ctx0, 12000], H=32,
                           seed=211 + fmt)
     T, oc = case.T, case.out_cols
     q, qs, w, kf, ks = (dev(a) for a in (case.q_fp4, case.q_scale, case.w, case.k_fp4, case.k_scale))
@@ -102,7 +105,7 @@ def test_logits_and_long_row_topk_replay_with_new_visibility_and_mapping(fmt):
         torch.cuda.synchronize()
         e_out, e_idx, e_vals = e_out.cpu().numpy(), e_idx.cpu().numpy(), e_vals.cpu().numpy()
         for rep in range(2):
-            say(f"[gpu] graph replay: logits + top-{k}, fmt={fmt}, variant {v}, replay {rep}")
+            say(f"[gpu] graph replay: logits + top-{k}, fmt={fmt}, ctx {ctx0}, variant {v}, replay {rep}")
             out.fill_(np.nan)
             idx.fill_(-7)
             torch.cuda.synchronize()
