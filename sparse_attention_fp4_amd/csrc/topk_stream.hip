@@ -84,7 +84,9 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
     constexpr int NW = NT / 64;
     constexpr int PB = kSBins / NT;  // histogram bins per thread
     const StreamLds L = carve(lds_words, cap);
-    const int row = blockIdx.x;
+    // last row first: in a causal prefill rows grow with their index, so the longest
+    // start first and short ones fill the kernel's tail (1.044 -> 1.012 ms at 32768 rows)
+    const int row = (int)gridDim.x - 1 - (int)blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -121,6 +123,39 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
         pick_bin<NT, PB>(c, bin, kk, L.wtot, L.pick);
     };
 
+    // The row streams through in chunks of kU 16-byte loads per thread (4 * NT * kU
+    // columns), the next chunk's loads in flight while one is processed.  Column
+    // 4 * (tid + NT * u) + e of a chunk is element e of load u.  A chunk that reaches
+    // past the row end reads dwords, so no 16-byte load straddles the buffer's end.
+    auto load_chunk = [&](int ch, v4f (&buf)[kU]) {
+        const int cb = ch * 4 * NT * kU;
+        // per-thread part of the address in a VGPR, the rest in the scalar offset
+        if (cb + 4 * NT * kU <= len) {
+#pragma unroll
+            for (int u = 0; u < kU; u++)
+                buf[u] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rs, 16 * tid, 4 * cb + 16 * NT * u, 0));
+        } else {
+#pragma unroll
+            for (int u = 0; u < kU; u++)
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    buf[u][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                              rs, 16 * tid + 4 * e, 4 * cb + 16 * NT * u, 0));
+        }
+    };
+    const int n_ch = (len + 4 * NT * kU - 1) / (4 * NT * kU);
+    // The first pass's first two chunks are loaded while the sample is ranked (the
+    // loads are issued after the sample's, so waiting for the sample leaves them in
+    // flight).
+    v4f ba[kU], bb[kU];
+    bool pre = false;
+    auto prefetch = [&]() {
+        if (n_ch > 0) load_chunk(0, ba);
+        if (n_ch > 1) load_chunk(1, bb);
+        pre = true;
+    };
+
     // ---- clear the histogram and the counter
     clear_hist();
     if (tid == 0) L.ctr[0] = 0;
@@ -145,6 +180,7 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
             const int c = (int)(((int64_t)(i >> 5) * len) / runs) + (i & 31);
             sk[j] = i < S ? skey(src[min(c, len - 1)]) : 0u;
         }
+        prefetch();
 #pragma unroll
         for (int j = 0; j < kSPer; j++)
             if (sk[j]) atomicAdd(&L.hist[sk[j] >> 20], 1u);
@@ -164,6 +200,8 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
             lo = (d1 << 20) | ((uint32_t)L.pick[0] << 8);
         }
         lds_barrier();
+    } else {
+        prefetch();
     }
 
     // ---- 2./3. stream passes until the kept keys settle K*
@@ -178,7 +216,6 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
     int kk = k;            // rank of K* among the keys matching the current prefix
     int n_kept = 0;
     bool all_valid = false;  // fewer valid keys than k: every valid key is taken
-    const int n_ch = (len + 4 * NT * kU - 1) / (4 * NT * kU);
     for (;;) {
         clear_hist();
         if (tid == 0) L.ctr[0] = 0;
@@ -187,28 +224,7 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
         const uint32_t hmask = level == 2 ? 0xffu : 0xfffu;
         const int pshift = level == 0 ? 32 : (level == 1 ? 20 : 8);  // prefix bits above the digit
         const uint32_t prefix = pshift == 32 ? 0u : (lo >> pshift);
-        // The row streams through in chunks of kU 16-byte loads per thread (4 * NT * kU
-        // columns), the next chunk's loads in flight while one is processed.  Column
-        // 4 * (tid + NT * u) + e of a chunk is element e of load u.  A chunk that
-        // reaches past the row end reads dwords, so no 16-byte load straddles the
-        // buffer's end.  Kept keys go to LDS with one counter update per wave and chunk.
-        auto load_chunk = [&](int ch, v4f (&buf)[kU]) {
-            const int cb = ch * 4 * NT * kU;
-            // per-thread part of the address in a VGPR, the rest in the scalar offset
-            if (cb + 4 * NT * kU <= len) {
-#pragma unroll
-                for (int u = 0; u < kU; u++)
-                    buf[u] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
-                                                         rs, 16 * tid, 4 * cb + 16 * NT * u, 0));
-            } else {
-#pragma unroll
-                for (int u = 0; u < kU; u++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        buf[u][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                                  rs, 16 * tid + 4 * e, 4 * cb + 16 * NT * u, 0));
-            }
-        };
+        // Kept keys go to LDS with one counter update per wave and chunk.
         // keep test in float space: key(v) >= keep_min, or key(v) > K* in level 3
         // (NaN compares false; -0 and +0 are one key and compare equal)
         const bool keep_all = level < 3 && lo <= 0x00800000u;  // every valid key
@@ -248,17 +264,18 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
                     }
                 }
         };
-        // pairs of chunks alternate between two buffers; the loop body has no exit
-        v4f ba[kU], bb[kU];
+        // pairs of chunks alternate between two buffers; the loop body has no exit.  The
+        // first pass finds chunks 0 and 1 already loaded.
         int ch = 0;
-        if (n_ch > 0) load_chunk(0, ba);
+        if (n_ch > 0 && !pre) load_chunk(0, ba);
         for (; ch + 2 <= n_ch; ch += 2) {
-            load_chunk(ch + 1, bb);
+            if (!(pre && ch == 0)) load_chunk(ch + 1, bb);
             process(ch, ba);
             if (ch + 2 < n_ch) load_chunk(ch + 2, ba);
             process(ch + 1, bb);
         }
         if (ch < n_ch) process(ch, ba);
+        pre = false;
         lds_barrier();
         n_kept = L.ctr[0];
         const bool overflow = n_kept > cap;
@@ -285,7 +302,10 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
             kk -= above;
             ties = inbin;
             const int nk = n_kept;
-            while (lvl < 3) {
+            // a bin whose keys are all taken ends the digits early: K* is then its lowest
+            // possible key (the prefix, low bits zero), every key at or above it is taken
+            // and need == ties
+            while (lvl < 3 && ties != kk) {
                 clear_hist();
                 lds_barrier();
                 const int sh = lvl == 1 ? 8 : 0;
