@@ -6,13 +6,14 @@
 //
 // Same order and output as topk.hip: larger first, ties to the smaller column, -inf
 // and NaN never selected, the chosen columns in increasing order, -1 padded (values
-// -inf).  Scores map to order-preserving 32-bit keys; digit 1 is key bits [31:20],
-// digit 2 bits [19:8], digit 3 bits [7:0].
+// -inf).  Scores map to order-preserving 32-bit keys; digit 1 is key bits [31:21],
+// digit 2 bits [20:10], digit 3 bits [9:0] (2048 histogram bins: 4096 took 4% longer
+// on the prefill rows).
 //
 // One workgroup per row, no workspace and no exchange between workgroups:
 //   1. sample: runs of 32 adjacent columns at evenly spaced starts, about 64 sampled
 //      keys above the k-th largest key in expectation; two digit levels of their keys
-//      give the 97th largest sample key (24 bits of it), `lo`, so about 1.5 k keys of
+//      give the 97th largest sample key (22 bits of it), `lo`, so about 1.5 k keys of
 //      the row are >= lo.
 //   2. stream: one pass over the row keeps every key >= lo in LDS (key and column,
 //      appended in any order) and builds the exact digit-1 histogram of those keys.
@@ -32,7 +33,7 @@ namespace fp4idx {
 
 namespace {
 
-constexpr int kSBins = 4096;
+constexpr int kSBins = 2048;
 constexpr int kU = 4;  // 16-byte loads per thread in one chunk of the row
 
 __device__ __forceinline__ uint32_t skey(float v) {
@@ -50,7 +51,7 @@ __device__ __forceinline__ float from_skey(uint32_t k) {
 // LDS layout: the histogram (uint32 words; once the last digit is settled the same
 // words hold the row's column bitmap, at most 1024 words for 32768 columns), candidate
 // keys (uint32), candidate columns (uint16: rows have at most 32768 columns), then a
-// small area for scan totals and shared scalars.  Under 40 KB with 4080 candidates,
+// small area for scan totals and shared scalars.  32 KB with 4080 candidates,
 // so four row workgroups share a CU.
 constexpr int kStreamMaxCols = 32768;
 
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
     lds_barrier();
 
     // ---- 1. sample: S evenly spaced columns, about 64 of them expected above the
-    // k-th largest key; lo = the first 24 bits of the rho-th largest sample key with
+    // k-th largest key; lo = the first 22 bits of the rho-th largest sample key with
     // rho = 64 + 32 + 1 (four standard deviations of the sample count), so about
     // 1.5 k keys of the row are >= lo and fewer than k only with probability ~1e-4.
     // Short rows (len <= 2k) keep every valid key.
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
         prefetch();
 #pragma unroll
         for (int j = 0; j < kSPer; j++)
-            if (sk[j]) atomicAdd(&L.hist[sk[j] >> 20], 1u);
+            if (sk[j]) atomicAdd(&L.hist[sk[j] >> 21], 1u);
         lds_barrier();
         pick_desc(rho);
         if (L.pick[2] >= rho) {
@@ -194,10 +195,10 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
             lds_barrier();
 #pragma unroll
             for (int j = 0; j < kSPer; j++)
-                if (sk[j] && (sk[j] >> 20) == d1) atomicAdd(&L.hist[(sk[j] >> 8) & 0xfffu], 1u);
+                if (sk[j] && (sk[j] >> 21) == d1) atomicAdd(&L.hist[(sk[j] >> 10) & 0x7ffu], 1u);
             lds_barrier();
             pick_desc(r2);
-            lo = (d1 << 20) | ((uint32_t)L.pick[0] << 8);
+            lo = (d1 << 21) | ((uint32_t)L.pick[0] << 10);
         }
         lds_barrier();
     } else {
@@ -220,9 +221,9 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
         clear_hist();
         if (tid == 0) L.ctr[0] = 0;
         lds_barrier();
-        const int hshift = level == 0 ? 20 : (level == 1 ? 8 : 0);
-        const uint32_t hmask = level == 2 ? 0xffu : 0xfffu;
-        const int pshift = level == 0 ? 32 : (level == 1 ? 20 : 8);  // prefix bits above the digit
+        const int hshift = level == 0 ? 21 : (level == 1 ? 10 : 0);
+        const uint32_t hmask = level == 2 ? 0x3ffu : 0x7ffu;
+        const int pshift = level == 0 ? 32 : (level == 1 ? 21 : 10);  // prefix bits above the digit
         const uint32_t prefix = pshift == 32 ? 0u : (lo >> pshift);
         // Kept keys go to LDS with one counter update per wave and chunk.
         // keep test in float space: key(v) >= keep_min, or key(v) > K* in level 3
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
         lds_barrier();
         if (!overflow) {
             // settle the remaining digits over the kept keys in LDS
-            uint32_t pre = level == 0 ? (d << 20) : (level == 1 ? ((lo & 0xfff00000u) | (d << 8)) : ((lo & 0xffffff00u) | d));
+            uint32_t pre = level == 0 ? (d << 21) : (level == 1 ? ((lo & 0xffe00000u) | (d << 10)) : ((lo & 0xfffffc00u) | d));
             int lvl = level + 1;
             kk -= above;
             ties = inbin;
@@ -308,9 +309,9 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
             while (lvl < 3 && ties != kk) {
                 clear_hist();
                 lds_barrier();
-                const int sh = lvl == 1 ? 8 : 0;
-                const uint32_t msk = lvl == 1 ? 0xfffu : 0xffu;
-                const int ps = lvl == 1 ? 20 : 8;
+                const int sh = lvl == 1 ? 10 : 0;
+                const uint32_t msk = lvl == 1 ? 0x7ffu : 0x3ffu;
+                const int ps = lvl == 1 ? 21 : 10;
                 for (int i = tid; i < nk; i += NT) {
                     const uint32_t key = L.ckey[i];
                     if ((key >> ps) == (pre >> ps)) atomicAdd(&L.hist[(key >> sh) & msk], 1u);
@@ -320,7 +321,7 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
                 const uint32_t dd = (uint32_t)L.pick[0];
                 kk -= L.pick[1];
                 ties = L.pick[3];
-                pre |= lvl == 1 ? (dd << 8) : dd;
+                pre |= lvl == 1 ? (dd << 10) : dd;
                 lds_barrier();
                 lvl++;
             }
@@ -330,10 +331,10 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
         }
         // overflow: narrow what the next pass keeps
         kk -= above;
-        if (level == 0) lo = d << 20;
-        else if (level == 1) lo = (lo & 0xfff00000u) | (d << 8);
+        if (level == 0) lo = d << 21;
+        else if (level == 1) lo = (lo & 0xffe00000u) | (d << 10);
         else {
-            kstar = (lo & 0xffffff00u) | d;
+            kstar = (lo & 0xfffffc00u) | d;
             need = kk;
             ties = inbin;
         }
@@ -420,16 +421,16 @@ __global__ __launch_bounds__(NT) void k_topk_stream(const TopkParams p, int cap)
 }  // namespace
 
 // Candidates kept in LDS: k plus slack (at least k, which the exact fallbacks need).
-// With k plus about 2000 the LDS stays under 40 KB, so four row workgroups share a
-// CU (the waves' registers allow four as well): 4080 candidates for k = 2048; larger k
-// take up to 150 KB.
+// With k plus about 2000 the LDS stays within 32 KB, so four row workgroups share a CU
+// with room to spare (the waves' registers allow four; a fifth by a register cap
+// measured no faster): 4080 candidates for k = 2048; larger k take up to 150 KB.
 int topk_stream_cap(int cols, int k) {
     if (cols > kStreamMaxCols || k < 1) return -1;
     const size_t fixed = topk_stream_lds_bytes(0);
     auto room = [&](size_t budget) { return budget > fixed ? (int)(((budget - fixed) / 6) & ~(size_t)1) : 0; };
     const int want = k + 2048;
-    const int cap40 = room(40u * 1024u);
-    int cap = want <= cap40 + 16 ? (want < cap40 ? want : cap40) : (want < room(150u * 1024u) ? want : room(150u * 1024u));
+    const int cap32 = room(32u * 1024u);
+    int cap = want <= cap32 + 16 ? (want < cap32 ? want : cap32) : (want < room(150u * 1024u) ? want : room(150u * 1024u));
     cap &= ~1;
     return cap < k ? -1 : cap;
 }
