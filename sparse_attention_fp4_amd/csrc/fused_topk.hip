@@ -209,18 +209,19 @@ struct NarrowLds {
     alignas(16) int hist[kBins];  // read 16 bytes at a time
     int red[4];
     uint32_t red8[8];
-    int misc[2];
+    int misc[3];
 };
 
 // One narrowing step over the keys in [klo, khi] (visit(fn) calls fn(key) for each key
 // of the lane): bin (key - klo) >> sh into at most 1024 bins and find the bin holding
 // the want-th largest key (want counted from the top of the range, 1 <= want <= the
-// number of keys in the range); `above` receives the number of keys in higher bins.
+// number of keys in the range); `above` receives the number of keys in higher bins,
+// `inbin` the number in the bin.
 // Offsets from the range's bottom spread close values over many bins, so few lanes
 // add to one bin at a time.
 template <class Visit>
 __device__ __forceinline__ void narrow(Visit visit, uint32_t klo, uint32_t khi, int want,
-                                       NarrowLds& L, int& bin, int& above, int& sh) {
+                                       NarrowLds& L, int& bin, int& above, int& sh, int& inbin) {
     const uint32_t span = khi - klo;
     sh = span >= (uint32_t)kBins ? (32 - __clz((int)span)) - 10 : 0;
     if (span >= 0x80000000u) sh = 22;
@@ -250,6 +251,7 @@ __device__ __forceinline__ void narrow(Visit visit, uint32_t klo, uint32_t khi, 
             if (run + c[i] >= want) {
                 L.misc[0] = kBins - 1 - 4 * (int)threadIdx.x - i;
                 L.misc[1] = run;
+                L.misc[2] = c[i];
                 break;
             }
             run += c[i];
@@ -258,6 +260,7 @@ __device__ __forceinline__ void narrow(Visit visit, uint32_t klo, uint32_t khi, 
     __syncthreads();
     bin = L.misc[0];
     above = L.misc[1];
+    inbin = L.misc[2];
     __syncthreads();
 }
 
@@ -432,14 +435,17 @@ __global__ __launch_bounds__(kSelThreads) void k_fused_select(const SelectParams
         block_minmax(klo, khi, L.red8);
         int above = 0;
         while (klo < khi) {  // uniform; each step shrinks the range 1024-fold
-            int bin, ab, sh;
+            int bin, ab, sh, inb;
             narrow([&](auto&& fn) { visit([&](uint64_t e) { fn(key_of(e)); }); }, klo, khi,
-                   p.k - above, L, bin, ab, sh);
+                   p.k - above, L, bin, ab, sh, inb);
             above += ab;
             const uint32_t nlo = klo + ((uint32_t)bin << sh);
             const uint32_t width = sh >= 32 ? 0xffffffffu : ((1u << sh) - 1u);
             khi = min(khi, nlo + width);
             klo = nlo;
+            // every key of the bin is taken: kth = the bin's bottom (need covers any ties
+            // at it), no further narrowing
+            if (inb == p.k - above) break;
         }
         kth = klo;
         need = p.k - above;  // keys above kth: every key above a range was counted
