@@ -8,7 +8,8 @@
 // and NaN never selected, result in increasing column order, -1 padded).  Scores map
 // to order-preserving 32-bit keys; digit 1 is key bits [31:20], digit 2 bits [19:8].
 // A row is cut into chunks of 4096 columns; chunks past a row's end are skipped.
-// At most 8 rows of at most 8 chunks run as one kernel whose workgroups wait for each
+// Rows of at most 8 chunks, when every die can hold its rows' chunk workgroups at once
+// (rows r, r + 8, ... on die r % 8), run as one kernel whose workgroups wait for each
 // other in memory (k_coop, below).  Otherwise workgroups exchange data only across
 // kernel boundaries (a device-wide fence inside a kernel costs microseconds on this
 // multi-die part), in three kernels:
@@ -677,8 +678,9 @@ __global__ __launch_bounds__(FT) void k_finish(const TopkParams p, LongWs ws, in
 }
 
 // ---------------------------------------------------------------- one kernel for few rows
-// With one row a die, every row's chunk workgroups run at once on one die (the
-// dispatcher deals block b to die b % 8; each die has 32 CUs) and meet at two waits in
+// Rows r, r + 8, ... share die r % 8 and all their chunk workgroups run at once there
+// (the dispatcher deals block b to die b % 8; each die has 32 CUs); a row's chunks
+// meet at two waits in
 // memory instead of two kernel boundaries: a wait costs about 0.6 us among the
 // workgroups of one die (1.1 us across dies), a boundary about 2 us plus slow first
 // loads of what the previous kernel wrote.  All exchange goes through device-scope
@@ -696,7 +698,7 @@ __global__ __launch_bounds__(FT) void k_finish(const TopkParams p, LongWs ws, in
 // last of its workgroups to end recomputes it alone from the scores.  That workgroup
 // (the last to end, failed or not) also clears the row's counters and histogram.
 constexpr int kCoopMaxW = 8;    // chunk workgroups a row (a die holds 32 at once, one a CU)
-constexpr int kCoopRowsMax = 8; // rows a call: one a die
+constexpr int kCoopDieWG = 32;  // chunk workgroups a die holds at once (one a CU)
 constexpr int kSc1 = 16;        // cache-policy bit of a device-scope buffer access
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
@@ -807,7 +809,7 @@ __global__ __launch_bounds__(1024) void k_coop(const TopkParams p, LongWs ws, in
     constexpr int FT = 1024, C = FT * V, CW = C / 32;
     constexpr int LCH = V == 4 ? 12 : 13;
     static_assert(V == 4 || V == 8, "4 or 8 keys a thread");
-    static_assert(kCoopMaxW <= 32, "every chunk workgroup of a die resident at once");
+    static_assert(kCoopMaxW <= kCoopDieWG, "every chunk workgroup of a die resident at once");
     static_assert(C == (1 << LCH) && CW <= 16 * kWords, "chunk bitmap fits the finishing LDS");
     constexpr int kCR = CandRegs<FT>::kCR;
     __shared__ CoopShared cs;
@@ -1053,17 +1055,18 @@ __global__ __launch_bounds__(1024) void k_coop(const TopkParams p, LongWs ws, in
 }
 
 // Keys a thread, and chunk workgroups a row, for the one-kernel path, or false when it
-// does not apply: more rows than dies, or rows of more than kCoopMaxW chunks.  Its
+// does not apply: rows of more than kCoopMaxW chunks, or more rows a die (rows 8 apart
+// share one) than its CUs hold with their chunks.  Its
 // in-kernel time grows with the chunks a row (more adds on each histogram bin, more
 // candidates to read), while the three kernels' does not: a step of 4 rows (scorer +
 // top-k) took 17.1 against 18.7 us at 16384 and 32768 columns (4 and 8 chunks), 18.65
 // against 18.8 at 65536 (16), and 19.5-20.6 against 19.5 at 100k (25; 13 chunks of
 // 8192 columns: 19.7).
 bool coop_shape(int rows, int cols, int& V, int& W) {
-    if (rows < 1 || rows > kCoopRowsMax) return false;
+    if (rows < 1) return false;
     V = 4;
     W = (cols + 1024 * V - 1) / (1024 * V);
-    return W <= kCoopMaxW;
+    return W <= kCoopMaxW && (int64_t)((rows + 7) / 8) * W <= kCoopDieWG;
 }
 
 int g_wait_limit = 1 << 16;
