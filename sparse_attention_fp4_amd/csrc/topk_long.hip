@@ -8,7 +8,7 @@
 // and NaN never selected, result in increasing column order, -1 padded).  Scores map
 // to order-preserving 32-bit keys; digit 1 is key bits [31:20], digit 2 bits [19:8].
 // A row is cut into chunks of 4096 columns; chunks past a row's end are skipped.
-// Rows of at most 8 chunks, when every die can hold its rows' chunk workgroups at once
+// Rows of at most 13 chunks, when every die can hold its rows' chunk workgroups at once
 // (rows r, r + 8, ... on die r % 8), run as one kernel whose workgroups wait for each
 // other in memory (k_coop, below).  Otherwise workgroups exchange data only across
 // kernel boundaries (a device-wide fence inside a kernel costs microseconds on this
@@ -697,7 +697,7 @@ __global__ __launch_bounds__(FT) void k_finish(const TopkParams p, LongWs ws, in
 // A wait is bounded (g_wait_limit polls); when one runs out, the row is marked and the
 // last of its workgroups to end recomputes it alone from the scores.  That workgroup
 // (the last to end, failed or not) also clears the row's counters and histogram.
-constexpr int kCoopMaxW = 8;    // chunk workgroups a row (a die holds 32 at once, one a CU)
+constexpr int kCoopMaxW = 13;   // chunk workgroups a row (a die holds 32 at once, one a CU)
 constexpr int kCoopDieWG = 32;  // chunk workgroups a die holds at once (one a CU)
 constexpr int kSc1 = 16;        // cache-policy bit of a device-scope buffer access
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
@@ -1059,9 +1059,10 @@ __global__ __launch_bounds__(1024) void k_coop(const TopkParams p, LongWs ws, in
 // share one) than its CUs hold with their chunks.  Its
 // in-kernel time grows with the chunks a row (more adds on each histogram bin, more
 // candidates to read), while the three kernels' does not: a step of 4 rows (scorer +
-// top-k) took 17.1 against 18.7 us at 16384 and 32768 columns (4 and 8 chunks), 18.65
-// against 18.8 at 65536 (16), and 19.5-20.6 against 19.5 at 100k (25; 13 chunks of
-// 8192 columns: 19.7).
+// top-k) took 17.1 against 18.7 us at 16384 and 32768 columns (4 and 8 chunks), 17.8
+// against 18.7 at 50000 (13), 18.7 against 18.8 at 65536 (16; the top-k alone on
+// random rows 13.3 against 12.9, and 13.9 against 13.1 with 8 rows), and 19.5-20.6
+// against 19.5 at 100k (25).
 bool coop_shape(int rows, int cols, int& V, int& W) {
     if (rows < 1) return false;
     V = 4;

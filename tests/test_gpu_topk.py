@@ -197,9 +197,10 @@ def test_workspace_reused_across_calls_without_clearing():
 
 @pytest.mark.parametrize("rows,cols,k,kind", [(4, 32_768, 2048, "normal"), (6, 20_000, 2048, "ties"),
                                               (2, 30_000, 7, "normal"), (3, 16_384, 2048, "clustered"),
-                                              (8, 9_000, 8192, "normal"), (20, 12_000, 2048, "normal")])
+                                              (8, 9_000, 8192, "normal"), (20, 12_000, 2048, "normal"),
+                                              (4, 50_000, 2048, "normal")])
 def test_few_long_rows_when_the_waits_run_out(rows, cols, k, kind):
-    """At most 32 rows of 8193..32768 columns take one kernel whose workgroups wait for
+    """Up to 64 rows of 8193..53248 columns take one kernel whose workgroups wait for
     each other; with the wait bound at 0 polls every row with more than one chunk is
     recomputed by one workgroup from its scores (the path taken when a row's workgroups
     cannot all run at once), and the result is the same.  The workspace is then ready
@@ -268,7 +269,8 @@ def test_workspace_reused_per_shape_and_cleared_between_shapes():
         assert np.array_equal(idx.cpu().numpy(), oi)
 
 
-@pytest.mark.parametrize("rows,cols", [(8, 32_768), (27, 32_768), (32, 32_768), (64, 16_384), (45, 12_000)])
+@pytest.mark.parametrize("rows,cols", [(8, 32_768), (27, 32_768), (32, 32_768), (64, 16_384), (45, 12_000),
+                                       (16, 53_248)])
 def test_few_rows_in_one_kernel_lengths_and_ties(rows, cols):
     """Rows of 8193..32768 columns in one kernel (up to 8 chunk workgroups a row, up to
     32 workgroups a die: 32 rows of 8 chunks, 64 of 4): a row of equal scores, rows of
