@@ -705,8 +705,8 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 struct CoopShared {
     FinishShared<1024> f;
     int ok;
-    int ncand;
-    int nabove;
+    int wcand[16];   // candidates of each wave
+    int wabove[16];  // columns above d1 of each wave
 };
 
 // Counts this workgroup's arrival on the row's counter and waits (bounded) until
@@ -832,8 +832,6 @@ __global__ __launch_bounds__(1024) void k_coop(const TopkParams p, LongWs ws, in
     reinterpret_cast<uint4*>(sh.h)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
     static_assert(kBins == 4 * FT, "one 16-byte clear a thread");
     if (threadIdx.x == 0) {
-        cs.ncand = 0;
-        cs.nabove = 0;
         sh.nm = 0;
         sh.before = 0;
     }
@@ -896,11 +894,18 @@ __global__ __launch_bounds__(1024) void k_coop(const TopkParams p, LongWs ws, in
             mc[j] = __ballot(d1 >= 0 && kj != 0u && dig == d1);
             ncw += __popcll(mc[j]);
         }
-        // one LDS atomic a wave places its candidates; they are stored in (step, lane) order
+        // the waves' counts, then every wave's offset from one scan of them (no atomics on
+        // a shared counter); candidates are stored in (wave, step, lane) order
+        if (lane == 0) {
+            cs.wcand[wave] = ncw;
+            cs.wabove[wave] = above;
+        }
+        lds_barrier();
+        static_assert(FT / 64 <= 16, "wave counts fit one scan");
+        const int wsc = wave_incl_scan(lane < FT / 64 ? cs.wcand[lane] : 0);
+        const int uw = __builtin_amdgcn_readfirstlane(wave);
+        int base = uw > 0 ? __builtin_amdgcn_readlane(wsc, uw - 1) : 0;
         if (ncw) {
-            int base = 0;
-            if (lane == 0) base = atomicAdd(&cs.ncand, ncw);
-            base = __builtin_amdgcn_readlane(base, 0);
 #pragma unroll
             for (int j = 0; j < V; j++) {
                 if ((mc[j] >> lane) & 1ull) {
@@ -911,13 +916,15 @@ __global__ __launch_bounds__(1024) void k_coop(const TopkParams p, LongWs ws, in
                 base += __popcll(mc[j]);
             }
         }
-        if (lane == 0 && above) atomicAdd(&cs.nabove, above);
-        lds_barrier();
         if (threadIdx.x == 0) {
-            __hip_atomic_store(reinterpret_cast<uint32_t*>(ws.cnum) + (int64_t)row * ws.n_chunks + m, (uint32_t)cs.ncand,
+            const int ntot = __builtin_amdgcn_readlane(wsc, FT / 64 - 1);
+            int atot = 0;
+#pragma unroll
+            for (int w = 0; w < FT / 64; w++) atot += cs.wabove[w];
+            __hip_atomic_store(reinterpret_cast<uint32_t*>(ws.cnum) + (int64_t)row * ws.n_chunks + m, (uint32_t)ntot,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(reinterpret_cast<uint32_t*>(ws.cabove) + (int64_t)row * ws.n_chunks + m,
-                               (uint32_t)cs.nabove, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(reinterpret_cast<uint32_t*>(ws.cabove) + (int64_t)row * ws.n_chunks + m, (uint32_t)atot,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         ok = coop_wait(ctr, 2u * (uint32_t)wr, limit, cs.ok);
 
