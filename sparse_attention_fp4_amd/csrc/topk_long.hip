@@ -1136,6 +1136,19 @@ size_t topk_long_workspace_bytes(int rows, int cols, int k) {
     return bytes;
 }
 
+// Compute units of the current device (read once per device): the one-kernel path
+// needs all its workgroups resident at once, one a CU.
+static int device_cus() {
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 int set_topk_wait_limit(int polls) {
     const int prev = g_wait_limit;
     if (polls >= 0) g_wait_limit = polls;
@@ -1146,8 +1159,10 @@ hipError_t launch_topk_long(const TopkParams& p, void* workspace, hipStream_t st
     LongWs w = carve(workspace, p.rows, p.cols, nullptr);
     if (w.n_chunks > kMaxChunks) return hipErrorInvalidValue;
     int cv = 0, cw = 0;
-    if (coop_shape(p.rows, p.cols, cv, cw)) {
-        // one kernel: every row's chunk workgroups on one die, all resident at once
+    if (coop_shape(p.rows, p.cols, cv, cw) && 8 * ((p.rows + 7) / 8) * cw <= device_cus()) {
+        // one kernel: every row's chunk workgroups on one die, all resident at once (a
+        // device with fewer CUs than the grid, e.g. one die of a partitioned GPU, takes
+        // the three kernels instead of waiting on workgroups that cannot start)
         LongWs c = w;
         c.n_chunks = cw;
         c.cstride = 1024 * cv;
