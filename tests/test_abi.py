@@ -34,6 +34,22 @@ def test_library_loads_and_exports_every_declared_symbol():
         assert L.fp4idx_strerror(code)
 
 
+def test_topk_wait_limit_setter():
+    """The bound on the one-kernel top-k's in-memory waits: each call returns the previous
+    bound, a negative value only reads it (no GPU call is made)."""
+    L = _lib.lib()
+    prev = L.fp4idx_set_topk_wait_limit(-1)
+    assert prev == 65536
+    try:
+        assert L.fp4idx_set_topk_wait_limit(0) == prev
+        assert L.fp4idx_set_topk_wait_limit(123) == 0
+        assert L.fp4idx_set_topk_wait_limit(-5) == 123
+        assert L.fp4idx_set_topk_wait_limit(-1) == 123
+    finally:
+        L.fp4idx_set_topk_wait_limit(prev)
+    assert L.fp4idx_set_topk_wait_limit(-1) == prev
+
+
 def _logits(**kw):
     L = _lib.lib()
     buf = ctypes.create_string_buffer(1 << 16)
