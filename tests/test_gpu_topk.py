@@ -244,6 +244,44 @@ def test_few_long_rows_when_the_waits_run_out(rows, cols, k, kind):
     assert np.array_equal(vals.cpu().numpy().view(np.uint32), ov.view(np.uint32))
 
 
+def test_one_kernel_rows_beside_other_work_on_the_gpu():
+    """The one-kernel route while a large matrix product runs on another stream: the
+    rows' workgroups may not all be resident at first (their waits are bounded, and a
+    wait that runs out has the row recomputed), so the result is the same either way.
+    Repeated with the wait bound at 200 polls, where running out is likely."""
+    import torch
+
+    import sparse_attention_fp4_amd as fp4
+    from .gpu_helpers import dev
+
+    rng = np.random.default_rng(71)
+    rows, cols, k = 16, 32_768, 2048
+    s = rng.standard_normal((rows, cols)).astype(np.float32)
+    lens = rng.integers(1, cols + 1, rows).astype(np.int32)
+    lens[0] = cols
+    oi, _ = orc.topk(s, k, lens)
+    ds, dl = dev(s), dev(lens)
+    ws = torch.zeros(fp4.topk_workspace_bytes(rows, cols, k), dtype=torch.uint8, device="cuda")
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    other = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for limit in (None, 200):
+        prev = fp4.ops.set_topk_wait_limit(limit) if limit is not None else None
+        try:
+            for rep in range(3):
+                say(f"[gpu] topk beside a matmul, wait bound {limit}, call {rep}")
+                with torch.cuda.stream(other):
+                    c = a @ b
+                idx, _ = fp4.topk(ds, k, dl, want_vals=False, workspace=ws)
+                torch.cuda.synchronize()
+                assert np.array_equal(idx.cpu().numpy(), oi)
+                del c
+        finally:
+            if prev is not None:
+                fp4.ops.set_topk_wait_limit(prev)
+
+
 def test_workspace_reused_per_shape_and_cleared_between_shapes():
     """One allocation serves calls of 4 rows (one kernel, in-memory waits) and of 64
     rows (three kernels): calls of one shape reuse it without clearing, and it is
