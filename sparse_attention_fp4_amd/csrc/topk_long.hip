@@ -91,7 +91,8 @@ __device__ __forceinline__ int row_len(const TopkParams& p, int row) {
 
 // A candidate (key, column) read at device scope: in the one-kernel path other
 // workgroups of the same kernel wrote it (device-scope stores, counted before the wait
-// that ends).
+// that ends).  The three kernels' round-by-round reloads share it (a plain load would
+// do there; those reloads are rare).
 __device__ __forceinline__ uint2 ld_cand(const uint2* q) {
     const uint64_t x = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<uint2*>(q)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return make_uint2((uint32_t)x, (uint32_t)(x >> 32));
@@ -680,10 +681,9 @@ __global__ __launch_bounds__(FT) void k_finish(const TopkParams p, LongWs ws, in
 // ---------------------------------------------------------------- one kernel for few rows
 // Rows r, r + 8, ... share die r % 8 and all their chunk workgroups run at once there
 // (the dispatcher deals block b to die b % 8; each die has 32 CUs); a row's chunks
-// meet at two waits in
-// memory instead of two kernel boundaries: a wait costs about 0.6 us among the
-// workgroups of one die (1.1 us across dies), a boundary about 2 us plus slow first
-// loads of what the previous kernel wrote.  All exchange goes through device-scope
+// meet at two waits in memory instead of two kernel boundaries: a wait costs about 0.6
+// us among the workgroups of one die (1.1 us across dies), a boundary about 2 us plus
+// slow first loads of what the previous kernel wrote.  All exchange goes through device-scope
 // atomics, loads and stores, so the result does not depend on the placement, only the
 // speed does.  Each row's counters sit on a 256-byte line of their own (sharing one
 // line between rows made each wait about 1.5 us).
@@ -697,7 +697,7 @@ __global__ __launch_bounds__(FT) void k_finish(const TopkParams p, LongWs ws, in
 // A wait is bounded (g_wait_limit polls); when one runs out, the row is marked and the
 // last of its workgroups to end recomputes it alone from the scores.  That workgroup
 // (the last to end, failed or not) also clears the row's counters and histogram.
-constexpr int kCoopMaxW = 13;   // chunk workgroups a row (a die holds 32 at once, one a CU)
+constexpr int kCoopMaxW = 13;   // chunk workgroups a row (see coop_shape for the crossover)
 constexpr int kCoopDieWG = 32;  // chunk workgroups a die holds at once (one a CU)
 constexpr int kSc1 = 16;        // cache-policy bit of a device-scope buffer access
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
