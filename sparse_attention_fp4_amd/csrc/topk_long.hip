@@ -699,6 +699,8 @@ __global__ __launch_bounds__(FT) void k_finish(const TopkParams p, LongWs ws, in
 // (the last to end, failed or not) also clears the row's counters and histogram.
 constexpr int kCoopMaxW = 13;   // chunk workgroups a row (see coop_shape for the crossover)
 constexpr int kCoopDieWG = 32;  // chunk workgroups a die holds at once (one a CU)
+constexpr int kCoopMaxW16 = 8;  // chunk workgroups a row with 16 keys a thread
+constexpr int kCoopRowsMin16 = 48;  // fewest rows that take 16 keys a thread
 constexpr int kSc1 = 16;        // cache-policy bit of a device-scope buffer access
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
@@ -805,10 +807,10 @@ __device__ void coop_row_alone(const TopkParams& p, int row, int len, FinishShar
 // die.  Grid: 8 * rpd * W blocks; block b serves row (b >> 3) / W * 8 + b % 8, chunk
 // (b >> 3) % W.
 template <int V>
-__global__ __launch_bounds__(1024) void k_coop(const TopkParams p, LongWs ws, int W, int rpd, int limit) {
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(V == 16 ? 8 : 1, 8))) void k_coop(const TopkParams p, LongWs ws, int W, int rpd, int limit) {
     constexpr int FT = 1024, C = FT * V, CW = C / 32;
-    constexpr int LCH = V == 4 ? 12 : 13;
-    static_assert(V == 4 || V == 8, "4 or 8 keys a thread");
+    constexpr int LCH = V == 4 ? 12 : V == 8 ? 13 : 14;
+    static_assert(V == 4 || V == 8 || V == 16, "4, 8 or 16 keys a thread");
     static_assert(kCoopMaxW <= kCoopDieWG, "every chunk workgroup of a die resident at once");
     static_assert(C == (1 << LCH) && CW <= 16 * kWords, "chunk bitmap fits the finishing LDS");
     constexpr int kCR = CandRegs<FT>::kCR;
@@ -1070,11 +1072,26 @@ __global__ __launch_bounds__(1024) void k_coop(const TopkParams p, LongWs ws, in
 // against 18.7 at 50000 (13), 18.7 against 18.8 at 65536 (16; the top-k alone on
 // random rows 13.3 against 12.9, and 13.9 against 13.1 with 8 rows), and 19.5-20.6
 // against 19.5 at 100k (25).
-bool coop_shape(int rows, int cols, int& V, int& W) {
+// Many rows (48 to 64 rows of up to 131072 columns, more 4096-column chunks than
+// kWaveOfGroups) take 16 keys a thread instead: chunks of 16384 columns, two workgroups
+// a CU (55 VGPRs and 34 KB of LDS allow it).  The top-k alone on full rows against the
+// three kernels: 64 x 131072 26.1 vs 30.3 us, 48 x 131072 24.6 vs 25.9, 64 x 100000
+// 24.7 vs 27.2, 64 x 65536 18.9 vs 20.9; with fewer rows it is no better or worse
+// (40 x 131072 24.1 vs 24.2, 40 x 100000 23.0 vs 21.1, 24 x 100000 18.2 vs 18.1, and
+// 4 x 100k 16.2 vs 13.7), though 32 x 131072 gains (19.4 vs 21.25).
+// per_cu: the one-kernel workgroups a CU holds at once.
+bool coop_shape(int rows, int cols, int& V, int& W, int& per_cu) {
     if (rows < 1) return false;
+    const int64_t rpd = (rows + 7) / 8;
     V = 4;
+    per_cu = 1;
     W = (cols + 1024 * V - 1) / (1024 * V);
-    return W <= kCoopMaxW && (int64_t)((rows + 7) / 8) * W <= kCoopDieWG;
+    if (W <= kCoopMaxW && rpd * W <= kCoopDieWG) return true;
+    if (rows < kCoopRowsMin16 || (int64_t)rows * ((cols + kChunk - 1) / kChunk) <= kWaveOfGroups) return false;
+    V = 16;
+    per_cu = 2;
+    W = (cols + 1024 * V - 1) / (1024 * V);
+    return W <= kCoopMaxW16 && rpd * W <= 2 * kCoopDieWG;
 }
 
 int g_wait_limit = 1 << 16;
@@ -1090,8 +1107,8 @@ LongWs carve(void* base, int rows, int cols, size_t* bytes) {
     w.cstride = kChunk;
     const size_t rc = (size_t)rows * w.n_chunks;
     size_t cand_row = (size_t)w.n_chunks * kChunk, cnt_row = (size_t)w.n_chunks;
-    int cv = 0, cw = 0;
-    if (coop_shape(rows, cols, cv, cw)) {
+    int cv = 0, cw = 0, cpc = 0;
+    if (coop_shape(rows, cols, cv, cw, cpc)) {
         cand_row = std::max(cand_row, (size_t)cw * 1024 * cv);
         cnt_row = std::max(cnt_row, (size_t)cw);
     }
@@ -1158,8 +1175,8 @@ int set_topk_wait_limit(int polls) {
 hipError_t launch_topk_long(const TopkParams& p, void* workspace, hipStream_t stream) {
     LongWs w = carve(workspace, p.rows, p.cols, nullptr);
     if (w.n_chunks > kMaxChunks) return hipErrorInvalidValue;
-    int cv = 0, cw = 0;
-    if (coop_shape(p.rows, p.cols, cv, cw) && 8 * ((p.rows + 7) / 8) * cw <= device_cus()) {
+    int cv = 0, cw = 0, cpc = 0;
+    if (coop_shape(p.rows, p.cols, cv, cw, cpc) && 8 * ((p.rows + 7) / 8) * cw <= cpc * device_cus()) {
         // one kernel: every row's chunk workgroups on one die, all resident at once (a
         // device with fewer CUs than the grid, e.g. one die of a partitioned GPU, takes
         // the three kernels instead of waiting on workgroups that cannot start)
@@ -1168,7 +1185,8 @@ hipError_t launch_topk_long(const TopkParams& p, void* workspace, hipStream_t st
         c.cstride = 1024 * cv;
         const int rpd = (p.rows + 7) / 8;
         const dim3 grid((unsigned)(8 * rpd * cw));
-        hipLaunchKernelGGL(k_coop<4>, grid, dim3(1024), 0, stream, p, c, cw, rpd, g_wait_limit);
+        if (cv == 4) hipLaunchKernelGGL(k_coop<4>, grid, dim3(1024), 0, stream, p, c, cw, rpd, g_wait_limit);
+        else hipLaunchKernelGGL(k_coop<16>, grid, dim3(1024), 0, stream, p, c, cw, rpd, g_wait_limit);
         return hipGetLastError();
     }
     // Few rows: one workgroup per chunk keeps each one short, with 1024 lanes.  Many

@@ -198,13 +198,13 @@ def test_workspace_reused_across_calls_without_clearing():
 @pytest.mark.parametrize("rows,cols,k,kind", [(4, 32_768, 2048, "normal"), (6, 20_000, 2048, "ties"),
                                               (2, 30_000, 7, "normal"), (3, 16_384, 2048, "clustered"),
                                               (8, 9_000, 8192, "normal"), (20, 12_000, 2048, "normal"),
-                                              (4, 50_000, 2048, "normal")])
+                                              (4, 50_000, 2048, "normal"), (64, 70_000, 2048, "ties")])
 def test_few_long_rows_when_the_waits_run_out(rows, cols, k, kind):
-    """Up to 64 rows of 8193..53248 columns take one kernel whose workgroups wait for
-    each other; with the wait bound at 0 polls every row with more than one chunk is
-    recomputed by one workgroup from its scores (the path taken when a row's workgroups
-    cannot all run at once), and the result is the same.  The workspace is then ready
-    for a normal call."""
+    """Up to 64 rows of 8193..53248 columns (and 48 to 64 rows of up to 131072 columns)
+    take one kernel whose workgroups wait for each other; with the wait bound at 0 polls
+    every row with more than one chunk is recomputed by one workgroup from its scores
+    (the path taken when a row's workgroups cannot all run at once), and the result is
+    the same.  The workspace is then ready for a normal call."""
     import torch
 
     import sparse_attention_fp4_amd as fp4
@@ -244,7 +244,8 @@ def test_few_long_rows_when_the_waits_run_out(rows, cols, k, kind):
     assert np.array_equal(vals.cpu().numpy().view(np.uint32), ov.view(np.uint32))
 
 
-def test_one_kernel_rows_beside_other_work_on_the_gpu():
+@pytest.mark.parametrize("many", [False, True], ids=["16x32768", "64x131072"])
+def test_one_kernel_rows_beside_other_work_on_the_gpu(many):
     """The one-kernel route while a large matrix product runs on another stream: the
     rows' workgroups may not all be resident at first (their waits are bounded, and a
     wait that runs out has the row recomputed), so the result is the same either way.
@@ -256,6 +257,8 @@ def test_one_kernel_rows_beside_other_work_on_the_gpu():
 
     rng = np.random.default_rng(71)
     rows, cols, k = 16, 32_768, 2048
+    if many:
+        rows, cols = 64, 131_072
     s = rng.standard_normal((rows, cols)).astype(np.float32)
     lens = rng.integers(1, cols + 1, rows).astype(np.int32)
     lens[0] = cols
