@@ -9,8 +9,9 @@
 // to order-preserving 32-bit keys; digit 1 is key bits [31:20], digit 2 bits [19:8].
 // A row is cut into chunks of 4096 columns; chunks past a row's end are skipped.
 // Rows of at most 13 chunks, when every die can hold its rows' chunk workgroups at once
-// (rows r, r + 8, ... on die r % 8), run as one kernel whose workgroups wait for each
-// other in memory (k_coop, below).  Otherwise workgroups exchange data only across
+// (rows r, r + 8, ... on die r % 8), and 48 to 64 rows of at most 8 chunks of 16384
+// columns, run as one kernel whose workgroups wait for each other in memory (k_coop,
+// below).  Otherwise workgroups exchange data only across
 // kernel boundaries (a device-wide fence inside a kernel costs microseconds on this
 // multi-die part), in three kernels:
 //   1. hist:    each chunk (a few consecutive chunks when many rows fill the chip)
