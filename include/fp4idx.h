@@ -246,7 +246,8 @@ int fp4idx_topk(const float* scores, int64_t row_stride, int rows, int cols,
 
 /* For up to 64 rows of 8193..53248 columns (when the GPU's dies can hold every row's
  * chunk workgroups at once: up to 16 rows of 53248 columns, 32 of 32768, 64 of 16384)
- * and for 48 to 64 rows of up to 131072 columns, fp4idx_topk
+ * and for many rows of up to 131072 columns (more than 512 chunks of 4096 columns in
+ * all; up to 32 rows, or 48 to 64), fp4idx_topk
  * (and the few-rows route of fp4idx_logits_topk_paged) runs one kernel whose workgroups
  * wait for each other in memory.  Each such wait polls at most `polls` times (default 65536, about 30 ms or
  * more); a wait that runs out -- the row's workgroups could not all run at once, e.g.

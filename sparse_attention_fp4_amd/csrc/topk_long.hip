@@ -9,9 +9,9 @@
 // to order-preserving 32-bit keys; digit 1 is key bits [31:20], digit 2 bits [19:8].
 // A row is cut into chunks of 4096 columns; chunks past a row's end are skipped.
 // Rows of at most 13 chunks, when every die can hold its rows' chunk workgroups at once
-// (rows r, r + 8, ... on die r % 8), and 48 to 64 rows of at most 8 chunks of 16384
-// columns, run as one kernel whose workgroups wait for each other in memory (k_coop,
-// below).  Otherwise workgroups exchange data only across
+// (rows r, r + 8, ... on die r % 8), and many rows of at most 8 chunks of 16384
+// columns (up to 32 rows, or 48 to 64), run as one kernel whose workgroups wait for each
+// other in memory (k_coop, below).  Otherwise workgroups exchange data only across
 // kernel boundaries (a device-wide fence inside a kernel costs microseconds on this
 // multi-die part), in three kernels:
 //   1. hist:    each chunk (a few consecutive chunks when many rows fill the chip)
@@ -701,7 +701,7 @@ __global__ __launch_bounds__(FT) void k_finish(const TopkParams p, LongWs ws, in
 constexpr int kCoopMaxW = 13;   // chunk workgroups a row (see coop_shape for the crossover)
 constexpr int kCoopDieWG = 32;  // chunk workgroups a die holds at once (one a CU)
 constexpr int kCoopMaxW16 = 8;  // chunk workgroups a row with 16 keys a thread
-constexpr int kCoopRowsMin16 = 48;  // fewest rows that take 16 keys a thread
+constexpr int kCoopRowsMin16 = 48;  // fewest rows that take 16 keys a thread two a CU
 constexpr int kSc1 = 16;        // cache-policy bit of a device-scope buffer access
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
@@ -1073,13 +1073,15 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(V == 16 ? 
 // against 18.7 at 50000 (13), 18.7 against 18.8 at 65536 (16; the top-k alone on
 // random rows 13.3 against 12.9, and 13.9 against 13.1 with 8 rows), and 19.5-20.6
 // against 19.5 at 100k (25).
-// Many rows (48 to 64 rows of up to 131072 columns, more 4096-column chunks than
-// kWaveOfGroups) take 16 keys a thread instead: chunks of 16384 columns, two workgroups
-// a CU (55 VGPRs and 34 KB of LDS allow it).  The top-k alone on full rows against the
-// three kernels: 64 x 131072 26.1 vs 30.3 us, 48 x 131072 24.6 vs 25.9, 64 x 100000
-// 24.7 vs 27.2, 64 x 65536 18.9 vs 20.9; with fewer rows it is no better or worse
-// (40 x 131072 24.1 vs 24.2, 40 x 100000 23.0 vs 21.1, 24 x 100000 18.2 vs 18.1, and
-// 4 x 100k 16.2 vs 13.7), though 32 x 131072 gains (19.4 vs 21.25).
+// Many rows (more 4096-column chunks than kWaveOfGroups, up to 64 rows of up to 131072
+// columns) take 16 keys a thread instead: chunks of 16384 columns, one workgroup a CU
+// when a die's rows fit that (up to 32 rows of 131072), else two (55 VGPRs and 34 KB
+// of LDS allow it), which pays from 48 rows on.  The top-k alone on full rows against
+// the three kernels: one a CU, 20 x 131072 18.1 vs 18.5 us, 32 x 131072 19.3 vs 21.1,
+// 32 x 100000 18.6 vs 19.9, 24 x 100000 18.1 vs 18.3; two a CU, 64 x 131072 26.1 vs
+// 30.3, 48 x 131072 24.6 vs 25.9, 64 x 100000 24.7 vs 27.2, but 40 x 131072 24.1 vs
+// 24.2 and 40 x 100000 23.0 vs 21.1 (unevenly doubled CUs).  Few rows stay with the
+// three kernels (4 x 100k: 16.2 vs 13.7 us in one kernel).
 // per_cu: the one-kernel workgroups a CU holds at once.
 bool coop_shape(int rows, int cols, int& V, int& W, int& per_cu) {
     if (rows < 1) return false;
@@ -1088,10 +1090,11 @@ bool coop_shape(int rows, int cols, int& V, int& W, int& per_cu) {
     per_cu = 1;
     W = (cols + 1024 * V - 1) / (1024 * V);
     if (W <= kCoopMaxW && rpd * W <= kCoopDieWG) return true;
-    if (rows < kCoopRowsMin16 || (int64_t)rows * ((cols + kChunk - 1) / kChunk) <= kWaveOfGroups) return false;
+    if ((int64_t)rows * ((cols + kChunk - 1) / kChunk) <= kWaveOfGroups) return false;
     V = 16;
-    per_cu = 2;
     W = (cols + 1024 * V - 1) / (1024 * V);
+    per_cu = rpd * W <= kCoopDieWG ? 1 : 2;
+    if (per_cu == 2 && rows < kCoopRowsMin16) return false;
     return W <= kCoopMaxW16 && rpd * W <= 2 * kCoopDieWG;
 }
 

@@ -311,12 +311,13 @@ def test_workspace_reused_per_shape_and_cleared_between_shapes():
 
 
 @pytest.mark.parametrize("rows,cols", [(8, 32_768), (27, 32_768), (32, 32_768), (64, 16_384), (45, 12_000),
-                                       (16, 53_248), (48, 100_000), (47, 100_000)])
+                                       (16, 53_248), (48, 100_000), (47, 100_000), (24, 131_072),
+                                       (40, 100_000)])
 def test_few_rows_in_one_kernel_lengths_and_ties(rows, cols):
     """Rows in one kernel (up to 13 chunk workgroups of 4096 columns a row and 32 a die,
-    or, from 48 rows on, up to 8 of 16384 columns and 64 a die; 47 rows of 100000 take
-    the three kernels): a row of equal scores, rows of lengths 0, 1, k - 1, k, k + 1 and
-    5000, and heavy ties."""
+    or, for many rows, up to 8 of 16384 columns, one a CU up to 32 rows and two from 48;
+    40 and 47 rows of 100000 take the three kernels): a row of equal scores, rows of
+    lengths 0, 1, k - 1, k, k + 1 and 5000, and heavy ties."""
     rng = np.random.default_rng(33 + rows)
     k = 2048
     s = (rng.integers(-40, 40, (rows, cols)) / 8).astype(np.float32)
